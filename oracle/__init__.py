@@ -1,0 +1,8 @@
+"""CPU oracle for exact softmax attention (float64 NumPy).
+
+Test infrastructure only: the test suite, the smoke check and the CPU
+baseline leg of the benchmark use it. The GPU library never imports it.
+"""
+from .dense import NA2D, MASKS, allowed, attention, masked_attention, probs
+
+__all__ = ["NA2D", "MASKS", "allowed", "attention", "masked_attention", "probs"]
