@@ -1,0 +1,153 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step is one attn_fwd launch over one batch of the workload (default:
+SD2.1 512x512 UNet self-attention, B2 H5 N4096 d64, no mask). Inputs are
+resident in HBM before timing starts. Prints one JSON line on stdout.
+
+FLOP accounting (the metric of the workload): 4 N^2 d per head without a
+mask, half of that with the causal mask, 4 N (kh kw) d per head for 2D
+neighbourhood attention (the window-sized work). Algorithmic bytes: q, k, v
+read once and o written once, 2 bytes per element.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+# MI355X published dense bf16 MFMA peak (256 CUs x 2.4 GHz x 4096 FLOP/clk) and HBM3E bandwidth
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(w: workloads.Workload) -> float:
+    per_head = 4.0 * w.N * w.N * w.d
+    if w.mask == "causal":
+        per_head /= 2
+    elif w.mask == "na2d":
+        per_head = 4.0 * w.N * w.na2d["kernel_h"] * w.na2d["kernel_w"] * w.d
+    return per_head * w.B * w.H
+
+
+def algorithmic_bytes(w: workloads.Workload) -> float:
+    return 4.0 * w.B * w.H * w.N * w.d * 2
+
+
+def mask_mode(A, w):
+    return {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D}[w.mask]
+
+
+def cpu_baseline(w: workloads.Workload, q, k, v, budget_s: float = 12.0) -> dict:
+    """Time the float64 oracle on the host cores over whole heads, until about budget_s has passed."""
+    import oracle
+
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((p.get("num_threads", 1) for p in info), default=1)
+    except Exception:  # threadpoolctl missing or unable to inspect
+        threads = os.cpu_count() or 1
+    qf, kf, vf = (t.float().numpy() for t in (q, k, v))
+    na = oracle.NA2D(**{kk: (bool(vv) if kk.startswith("wrap") else vv) for kk, vv in w.na2d.items()}) if w.na2d else None
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.attention(qf[b:b + 1, h:h + 1], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1], w.scale, w.mask, na)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    f = flops(w) * heads / (w.B * w.H)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (float64 NumPy, S materialised per head), "
+                      f"{dt:.2f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from exact_attention_68_amd.build import ensure_built
+    ensure_built()
+    import exact_attention_68_amd as A
+
+    w = workloads.WORKLOADS[args.workload]
+    q, k, v = workloads.workload_qkv(w)
+    dev = torch.device("cuda:0")
+    dq, dk, dv = (t.to(dev) for t in (q, k, v))
+    do = torch.empty_like(dq)
+    params = A.na2d_params(**w.na2d) if w.mask == "na2d" else None
+    mode = mask_mode(A, w)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        A.attn_fwd(dq, dk, dv, do, w.scale, mode, params, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup {args.warmup} done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    F = flops(w)
+    value = F * args.steps / wall / 1e12
+    achieved = F / (kernel_ms * 1e-3) / 1e12
+    nbytes = algorithmic_bytes(w)
+    if w.mask == "na2d":
+        roof = {"bound": "hbm", "achieved": nbytes / (kernel_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+
+    line = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "kernel_us": kernel_ms * 1e3,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+                   "scale": w.scale, **({"na2d": w.na2d} if w.na2d else {})},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

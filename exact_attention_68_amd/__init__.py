@@ -1,0 +1,142 @@
+"""Python binding of libattn, the fused exact-attention forward for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libattn.so, reached through its C ABI (include/attn.h). The names
+mirror the C entry points. PyTorch supplies device memory and streams.
+
+The first call loads exact_attention_68_amd/libattn.so and raises
+ImportError if it has not been built (python -m exact_attention_68_amd.build);
+there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_MASK_NONE = 0
+ATTN_MASK_CAUSAL = 1
+ATTN_MASK_NA2D = 2
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_PARAMS = 3
+ATTN_ERR_ALIGNMENT = 4
+ATTN_ERR_HIP = 5
+
+
+class attn_na2d_params_t(ctypes.Structure):
+    """Mirror of the C struct: 2D neighbourhood window over a row-major grid."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("grid_h", "grid_w", "kernel_h", "kernel_w", "wrap_h", "wrap_w", "dil_h", "dil_w")]
+
+
+def na2d_params(grid_h, grid_w, kernel_h, kernel_w, wrap_h=1, wrap_w=1, dil_h=1, dil_w=1) -> attn_na2d_params_t:
+    return attn_na2d_params_t(grid_h, grid_w, kernel_h, kernel_w, int(wrap_h), int(wrap_w), dil_h, dil_w)
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_attention_68_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_check.argtypes = [i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_fwd_check.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = i32
+    return lib
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn.so (loaded on first use)."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
+
+
+def _params_ptr(params):
+    if params is None:
+        return None
+    if not isinstance(params, attn_na2d_params_t):
+        raise TypeError("params must be an attn_na2d_params_t (see na2d_params)")
+    return ctypes.cast(ctypes.pointer(params), ctypes.c_void_p)
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_abi_version() -> int:
+    return int(lib().attn_abi_version())
+
+
+def attn_fwd_check(B, H, N, d, scale, mask_mode=ATTN_MASK_NONE, params=None) -> int:
+    """Status attn_fwd would return for these sizes and options (no device work)."""
+    return int(lib().attn_fwd_check(B, H, N, d, scale, mask_mode, _params_ptr(params)))
+
+
+def attn_fwd(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, stream=None) -> None:
+    """o <- softmax(scale * q k^T + mask) v, queued on `stream` (torch's current stream by default).
+
+    q, k, v, o: torch bfloat16 CUDA tensors, contiguous, one [B, H, N, d] shape.
+    Raises AttnError with the library's status on any rejected argument.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{name} must be a bfloat16 CUDA tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4 or t.shape != q.shape:
+            raise ValueError("q, k, v and o must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, d,
+                       float(scale), int(mask_mode), _params_ptr(params), int(stream) or None)
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd")
+
+
+def attention(q, k, v, scale=None, causal=False, na2d=None, stream=None):
+    """Allocate the output and run attn_fwd. scale defaults to 1/sqrt(d).
+
+    na2d: an attn_na2d_params_t for 2D neighbourhood attention.
+    """
+    import torch
+
+    if causal and na2d is not None:
+        raise ValueError("choose causal or na2d, not both")
+    o = torch.empty_like(q)
+    mode = ATTN_MASK_NA2D if na2d is not None else (ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE)
+    s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    attn_fwd(q, k, v, o, s, mode, na2d, stream)
+    return o
+
+
+__all__ = [
+    "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "ATTN_MASK_NA2D",
+    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_PARAMS", "ATTN_ERR_ALIGNMENT",
+    "ATTN_ERR_HIP", "AttnError", "attn_na2d_params_t", "na2d_params",
+    "attn_fwd", "attn_fwd_check", "attn_status_string", "attn_abi_version", "attention", "LIB_PATH",
+]

@@ -1,0 +1,60 @@
+// The C ABI of libattn: argument checks, launch geometry, error mapping.
+// The operation and its contract are documented in include/attn.h.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+
+#include "attn.h"
+#include "launch.hpp"
+#include "tile_plan.hpp"
+#include "validate.hpp"
+
+extern "C" {
+
+attn_status_t attn_fwd_check(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int32_t mask_mode,
+                             const void* params) {
+  return attn::check_problem(B, H, N, d, scale, mask_mode, params);
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
+                       int64_t d, float scale, int32_t mask_mode, const void* params, void* stream) {
+  attn_status_t st = attn::check_problem(B, H, N, d, scale, mask_mode, params);
+  if (st != ATTN_OK) return st;
+  st = attn::check_pointers(q, k, v, o, B, H, N, d);
+  if (st != ATTN_OK) return st;
+
+  attn::KernelArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.N = (int32_t)N;
+  a.BH = (int32_t)(B * H);
+  a.n_qtiles = (int32_t)attn::cdiv(N, attn::kBlockM);
+  a.n_kvtiles = (int32_t)attn::cdiv(N, attn::tile_keys());
+  // exp(x) = 2^(x log2 e): the kernel works in base 2 with the scale folded in
+  a.c = (float)(fabs((double)scale) * 1.4426950408889634);
+  a.q_sign = scale < 0.f ? 0x80008000u : 0u;
+  if (mask_mode == ATTN_MASK_NA2D) a.na = attn::na_geom(*static_cast<const attn_na2d_params_t*>(params));
+  const int32_t n_wg = a.BH * a.n_qtiles;
+  const hipError_t e = attn::launch_fwd(a, (int32_t)d, mask_mode, n_wg, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_status_string(int32_t status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, non-finite scale, "
+                                      "unknown mask mode, misplaced params, or output overlapping an input)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32 or 64; sizes must fit 32-bit "
+                                      "launch geometry)";
+    case ATTN_ERR_PARAMS: return "inconsistent 2D neighbourhood parameters (grid_h*grid_w must equal N; "
+                                 "kernels odd and within the grid; wrap 0 or 1; dilation 1)";
+    case ATTN_ERR_ALIGNMENT: return "q, k, v and o must be 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

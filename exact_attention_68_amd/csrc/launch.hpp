@@ -1,0 +1,33 @@
+// Internal interface between the C ABI (attn_api.cpp) and the kernels (attn_fwd.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "tile_plan.hpp"
+#include "validate.hpp"
+
+namespace attn {
+
+// Arguments of one launch, passed by value to the kernel.
+struct KernelArgs {
+  const uint16_t* q;  // bfloat16 bit patterns, [B, H, N, d]
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int32_t N;          // tokens per head
+  int32_t BH;         // B * H
+  int32_t n_qtiles;   // ceil(N / 128)
+  int32_t n_kvtiles;  // ceil(N / key tile)
+  float c;            // |scale| * log2(e)
+  uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q's sign bits), else 0
+  NaGeom na;          // neighbourhood geometry (mask NA2D only)
+};
+
+// Launches the kernel for head size d (32 or 64) and the given mask mode.
+hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, hipStream_t stream);
+
+// Keys per key/value tile of the kernels.
+int32_t tile_keys();
+
+}  // namespace attn

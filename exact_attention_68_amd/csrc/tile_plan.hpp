@@ -1,0 +1,134 @@
+// Which key/value tiles a query tile visits, and which of them need an element mask.
+//
+// Plain constexpr C++: clang compiles constexpr functions for both host and
+// device, so the kernel and a host-only test build share this logic.
+//
+// A query tile covers queries [q0, q0 + BM) (clipped to N). Key tiles are
+// BN consecutive tokens; tile t covers keys [t*BN, t*BN + BN). The tiles to
+// visit form one circular run: tiles (first + i) mod n_tiles for
+// i = 0 .. count-1, each visited once.
+//
+//  * no mask: every tile (all keys are visible; PhotoRoom's xformers post,
+//    the running-softmax paragraph: keys are read tile by tile);
+//  * causal: tiles up to the one holding the tile's last query (keys after a
+//    query are masked, "Profiling in PyTorch", the naive causal module), so
+//    fully masked tiles are never visited;
+//  * 2D neighbourhood: the band of grid rows that any query of the tile can
+//    see (NATTEN issue 142: skipping key tiles that are fully masked is
+//    predictable per query tile). With a wrapped row axis the band is taken
+//    modulo the grid height and the run of tiles wraps modulo the tile
+//    count; no input is padded.
+#pragma once
+
+#include <stdint.h>
+
+namespace attn {
+
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA2D = 2 };
+
+// 2D neighbourhood geometry in the form the kernel uses.
+struct NaGeom {
+  int32_t grid_h, grid_w;
+  int32_t kernel_h, kernel_w;
+  int32_t rad_h, rad_w;    // kernel / 2
+  int32_t wrap_h, wrap_w;  // 1 = circular, 0 = clamped
+};
+
+struct KvRun {
+  int32_t first;  // first tile index
+  int32_t count;  // number of tiles to visit
+};
+
+constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
+constexpr int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
+constexpr int32_t iclamp(int32_t x, int32_t lo, int32_t hi) { return imin(imax(x, lo), hi); }
+constexpr int32_t imod(int32_t a, int32_t m) { return ((a % m) + m) % m; }
+
+// Rows [start, start + count) (mod grid_h when wrapped) holding every key that
+// any query row in [y0, y1] may see.
+struct RowBand {
+  int32_t start, count;
+};
+
+constexpr RowBand na_row_band(const NaGeom& g, int32_t y0, int32_t y1) {
+  if (g.wrap_h) {
+    int32_t count = (y1 - y0 + 1) + 2 * g.rad_h;
+    if (count >= g.grid_h) return RowBand{0, g.grid_h};
+    return RowBand{imod(y0 - g.rad_h, g.grid_h), count};
+  }
+  // clamped windows start at clamp(y - r, 0, H - k), a non-decreasing function of y
+  int32_t s0 = iclamp(y0 - g.rad_h, 0, g.grid_h - g.kernel_h);
+  int32_t s1 = iclamp(y1 - g.rad_h, 0, g.grid_h - g.kernel_h);
+  return RowBand{s0, s1 + g.kernel_h - s0};
+}
+
+constexpr KvRun kv_run(int mask, int32_t N, int32_t BM, int32_t BN, int32_t q0, const NaGeom& g) {
+  const int32_t n_tiles = (int32_t)cdiv(N, BN);
+  const int32_t q_last = imin(q0 + BM, N) - 1;
+  if (mask == MASK_CAUSAL) return KvRun{0, q_last / BN + 1};
+  if (mask != MASK_NA2D) return KvRun{0, n_tiles};
+  const RowBand band = na_row_band(g, q0 / g.grid_w, q_last / g.grid_w);
+  const int32_t tok_start = band.start * g.grid_w;
+  const int32_t tok_len = band.count * g.grid_w;
+  if (tok_len >= N) return KvRun{0, n_tiles};
+  const int32_t tok_end = tok_start + tok_len;  // exclusive, may pass N when the band wraps
+  if (tok_end <= N) {
+    const int32_t a = tok_start / BN, b = (tok_end - 1) / BN;
+    return KvRun{a, b - a + 1};
+  }
+  // wrapped band: tokens [tok_start, N) then [0, tok_end - N)
+  const int32_t a = tok_start / BN;             // first tile of the upper part
+  const int32_t b = (tok_end - N - 1) / BN;     // last tile of the lower part
+  if (b >= a - 1) return KvRun{0, n_tiles};     // the two parts meet: every tile
+  return KvRun{a, (n_tiles - a) + b + 1};
+}
+
+constexpr int32_t kv_tile_at(const KvRun& run, int32_t i, int32_t n_tiles) {
+  int32_t t = run.first + i;
+  return t >= n_tiles ? t - n_tiles : t;
+}
+
+// Does key tile t need the element mask for the query tile starting at q0?
+constexpr bool tile_needs_mask(int mask, int32_t N, int32_t BN, int32_t q0, int32_t t) {
+  const int32_t k_end = t * BN + BN;  // exclusive
+  if (k_end > N) return true;         // ragged last tile: keys past N
+  if (mask == MASK_CAUSAL) return k_end - 1 > q0;  // some key lies after some query
+  return mask == MASK_NA2D;
+}
+
+// Element predicate of the neighbourhood window for query (yq, xq) and key (yk, xk).
+constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, int32_t rad, int32_t wrap) {
+  if (wrap) {
+    int32_t dlt = cq - ck;
+    dlt = dlt < 0 ? -dlt : dlt;
+    dlt = imin(dlt, len - dlt);
+    return dlt <= rad;
+  }
+  const int32_t start = iclamp(cq - rad, 0, len - kernel);
+  return ck >= start && ck < start + kernel;
+}
+
+// Map a work-group index to (head, query tile).
+//
+// Work-groups are dispatched round-robin over the 8 XCDs of the chip, each
+// with its own L2. For equal-length work items the remap gives each XCD a
+// contiguous block of logical items, so the query tiles of one head (which
+// share its K and V) land on the same L2. Causal items differ in length, so
+// they keep the dispatch order, longest first with all heads of one tile
+// index together; round-robin then spreads long and short items evenly over
+// the XCDs (and keeps a head on one XCD when B*H is a multiple of 8).
+struct WorkItem {
+  int32_t bh, qtile;
+};
+
+constexpr WorkItem work_item(int mask, int32_t wg, int32_t n_wg, int32_t n_qtiles, int32_t BH) {
+  if (mask == MASK_CAUSAL) return WorkItem{wg % BH, n_qtiles - 1 - wg / BH};
+  const int32_t per_xcd = n_wg / 8;
+  int32_t logical = wg;
+  if (wg < per_xcd * 8) logical = (wg % 8) * per_xcd + wg / 8;
+  return WorkItem{logical / n_qtiles, logical % n_qtiles};
+}
+
+}  // namespace attn

@@ -1,0 +1,128 @@
+/*
+ * libattn: fused exact-attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only; no framework types cross it.
+ *
+ * The operation, per batch b and head h, with Q, K, V of shape (N, d):
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * as defined by the AWS Neuron NKI tutorial "Fused Self Attention"
+ * (section "Background": S = Q K^T, R = softmax(S) V over (seqlen, d_head)
+ * tensors in bfloat16), with the 1/sqrt(d) scale and the -inf causal mask of
+ * "Profiling in PyTorch" part 3 (section "Deconstructing Naive Attention"),
+ * and the wrap-around 2D neighbourhood window requested in NATTEN issue 142
+ * ("circular windowed attention", the 5x5 kernel_size=3 example).
+ *
+ * The N x N score matrix is never written to memory: scores are produced
+ * tile by tile, reduced with a running row maximum and row sum, and divided
+ * once after the product with V (NKI tutorial, section "Softmax
+ * implementation"; PhotoRoom's xformers post, the running-softmax
+ * paragraph).
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Mask modes. */
+typedef enum {
+    ATTN_MASK_NONE = 0,   /* every key visible to every query */
+    ATTN_MASK_CAUSAL = 1, /* key j visible to query i iff j <= i ("Profiling in PyTorch",
+                             the naive causal module and SDPA's is_causal=True) */
+    ATTN_MASK_NA2D = 2    /* 2D neighbourhood window over a row-major token grid
+                             (NATTEN issue 142); parameters in attn_na2d_params_t */
+} attn_mask_mode_t;
+
+/*
+ * 2D neighbourhood parameters (host memory, read during the call only).
+ *
+ * Token n sits at grid row y = n / grid_w and column x = n % grid_w;
+ * grid_h * grid_w must equal N. Along each axis, with r = kernel / 2:
+ *   wrap = 1: key allowed when the circular distance between the query's and
+ *             the key's coordinate, min((a-b) mod L, (b-a) mod L), is <= r
+ *             (a centred window that wraps at the borders like a convolution
+ *             with circular padding; NATTEN issue 142, the 5x5 example);
+ *   wrap = 0: the standard window of `kernel` cells starting at
+ *             clamp(c - r, 0, L - kernel), i.e. shifted inside the grid at
+ *             the edges (NATTEN issue 142, the replies on window_start and
+ *             window_end and on clamping the window to the edges).
+ * A key is visible when both axes allow it.
+ * Kernels must be odd with 1 <= kernel <= grid size; dilation must be 1.
+ */
+typedef struct {
+    int32_t grid_h, grid_w;
+    int32_t kernel_h, kernel_w;
+    int32_t wrap_h, wrap_w;  /* 1 = circular, 0 = clamped */
+    int32_t dil_h, dil_w;    /* must be 1 */
+} attn_na2d_params_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, non-finite scale, unknown
+                                 mask mode, params given when not NA2D, o overlapping q/k/v */
+    ATTN_ERR_UNSUPPORTED = 2, /* head size d other than 32 or 64, or a problem too large for
+                                 32-bit launch geometry */
+    ATTN_ERR_PARAMS = 3,      /* NA2D parameters inconsistent (grid_h*grid_w != N, even or
+                                 out-of-range kernel, wrap not 0/1, dilation != 1) */
+    ATTN_ERR_ALIGNMENT = 4,   /* q, k, v or o not 16-byte aligned */
+    ATTN_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+/*
+ * attn_fwd: O = softmax(scale * Q K^T + mask) V, asynchronously on `stream`.
+ *
+ * q, k, v : device pointers, bfloat16, contiguous [B, H, N, d] (d fastest),
+ *           16-byte aligned; read only.
+ * o       : device pointer, bfloat16, contiguous [B, H, N, d], 16-byte
+ *           aligned; written with the result rounded to nearest even. Must
+ *           not overlap q, k or v.
+ * B, H, N : batch, heads, tokens (> 0). Queries and keys share N.
+ * d       : head size, 32 or 64.
+ * scale   : finite multiplier applied to Q K^T before the mask (0 and
+ *           negative values are legal; scale = 0 averages V over the
+ *           visible keys).
+ * mask_mode : an attn_mask_mode_t value.
+ * params  : NULL unless mask_mode == ATTN_MASK_NA2D, then a host pointer to
+ *           an attn_na2d_params_t.
+ * stream  : a hipStream_t (NULL = the default stream).
+ *
+ * The caller owns all memory. The library allocates nothing, keeps no state
+ * between calls, never synchronises and is safe to call concurrently on
+ * different streams. Exactly one kernel is launched per call.
+ *
+ * Returns ATTN_OK after the launch is queued. Argument errors are detected
+ * before any device work and leave o untouched. ATTN_ERR_HIP reports a
+ * launch failure; o is then undefined.
+ */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
+                       int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                       int32_t mask_mode, const void* params, void* stream);
+
+/*
+ * attn_fwd_check: the argument checks of attn_fwd alone, for a problem with
+ * the given sizes, scale, mask and parameters; no device work is done and
+ * no pointer is dereferenced (pointer checks are not part of it). Returns
+ * the status attn_fwd would return for valid, aligned, non-overlapping
+ * pointers.
+ */
+attn_status_t attn_fwd_check(int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                             int32_t mask_mode, const void* params);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* attn_status_string(int32_t status);
+
+/* ATTN_ABI_VERSION of the built library. */
+int32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

@@ -1,0 +1,155 @@
+"""Parity of the HIP path against the CPU oracle, element by element, on an MI355X.
+
+Inputs are the seeded bfloat16 tensors of workloads.py. Small cases span
+several query and key tiles plus a ragged tail; the workload sizes are
+compared in full where the oracle finishes in seconds and on sampled query
+rows otherwise. Tolerance: |gpu - ref| <= 4e-3 * max(1, |ref|) + 2e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check_case, compare, run_gpu, to_f64, workload_params
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    from exact_attention_68_amd.build import ensure_built
+
+    ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+
+
+def _qkv(B, H, N, d, seed, q_gain=1.0):
+    return workloads.make_qkv(B, H, N, d, seed, q_gain)
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("name", ["single_head_n256", "sd21_512_selfattn", "causal_n2048", "na2d_wrap_64x64_k7"])
+def test_workload_full(name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.workload_qkv(w)
+    check_case(q, k, v, w.scale, w.mask, workload_params(w), what=name)
+
+
+def test_sd21_768_sampled_rows():
+    w = workloads.WORKLOADS["sd21_768_selfattn"]
+    q, k, v = workloads.workload_qkv(w)
+    rng = np.random.default_rng(7)
+    rows = sorted({0, 1, 63, 64, 127, 128, w.N - 1, w.N - 2, *rng.choice(w.N, 250, replace=False).tolist()})
+    check_case(q, k, v, w.scale, w.mask, rows=rows, what=w.name)
+
+
+# ---------------------------------------------------------------- edge shapes
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("N", [1, 17, 64, 100, 128, 255, 257, 320])
+def test_edge_shapes(N, mask, d):
+    q, k, v = _qkv(1, 2, N, d, 1000 + N + d)
+    check_case(q, k, v, 1 / math.sqrt(d), mask, what=f"edge N{N}")
+
+
+@pytest.mark.parametrize("scale,q_gain", [(0.0, 1.0), (-0.2, 1.0), (0.125, 4.0), (1.0, 1.0), (1e-3, 1.0)])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_scales_and_peaky_rows(scale, q_gain, mask):
+    q, k, v = _qkv(2, 3, 300, 64, 2000, q_gain)
+    check_case(q, k, v, scale, mask, what=f"scale {scale} gain {q_gain}")
+
+
+# ---------------------------------------------------------------- 2D neighbourhood
+def test_na2d_issue_example_5x5():
+    """NATTEN issue 142: q = k = 1, v one-hot at the top-left pixel, 5x5 grid, kernel 3, wrap."""
+    import exact_attention_68_amd as A
+
+    d = 32
+    q = torch.ones(1, 1, 25, d, dtype=torch.bfloat16)
+    k = torch.ones(1, 1, 25, d, dtype=torch.bfloat16)
+    v = torch.zeros(1, 1, 25, d, dtype=torch.bfloat16)
+    v[0, 0, 0, :] = 1
+    o = run_gpu(q, k, v, 1 / math.sqrt(d), A.ATTN_MASK_NA2D, A.na2d_params(5, 5, 3, 3, 1, 1))
+    got = to_f64(o)[0, 0, :, 0].reshape(5, 5)
+    printed = np.loadtxt(__import__("pathlib").Path(__file__).parent / "golden" / "na2d_wrap_5x5_k3.txt")
+    exact = np.where(printed > 0, 1 / 9, 0.0)
+    compare(got, exact, "5x5 wrap example")
+    assert np.all(got[printed == 0] == 0.0)
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("gh,gw,kh,kw,wh,ww", [
+    (8, 9, 5, 5, 1, 1),
+    (5, 5, 3, 3, 1, 1),
+    (7, 13, 3, 5, 0, 0),
+    (10, 6, 5, 3, 1, 0),
+    (6, 10, 3, 7, 0, 1),
+    (5, 7, 5, 7, 1, 1),     # window = grid: full attention
+    (33, 17, 9, 3, 1, 1),   # band crosses tiles and wraps
+    (20, 20, 1, 1, 1, 1),   # self only
+    (3, 200, 3, 11, 1, 1),  # short, wide grid: band is the whole sequence
+    (64, 64, 7, 7, 0, 0),
+])
+def test_na2d_shapes(gh, gw, kh, kw, wh, ww, d):
+    import exact_attention_68_amd as A
+
+    N = gh * gw
+    q, k, v = _qkv(1, 2, N, d, 3000 + N + kh)
+    check_case(q, k, v, 1 / math.sqrt(d), "na2d", A.na2d_params(gh, gw, kh, kw, wh, ww),
+               what=f"na2d {gh}x{gw} k{kh}x{kw} wrap{wh}{ww}")
+
+
+# ---------------------------------------------------------------- properties
+def test_causal_first_row_is_exact():
+    q, k, v = _qkv(2, 2, 200, 64, 4000)
+    import exact_attention_68_amd as A
+
+    o = run_gpu(q, k, v, 0.125, A.ATTN_MASK_CAUSAL)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+def test_deterministic_bitwise():
+    import exact_attention_68_amd as A
+
+    q, k, v = _qkv(2, 5, 1000, 64, 5000)
+    a = run_gpu(q, k, v, 0.125, A.ATTN_MASK_NONE)
+    b = run_gpu(q, k, v, 0.125, A.ATTN_MASK_NONE)
+    assert torch.equal(a, b)
+
+
+def test_no_device_allocation_and_side_stream():
+    import exact_attention_68_amd as A
+
+    q, k, v = (t.cuda() for t in _qkv(1, 2, 512, 64, 6000))
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        A.attn_fwd(q, k, v, o, 0.125, A.ATTN_MASK_NONE)
+    s.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 0.125)
+    compare(to_f64(o), ref, "side stream")
+
+
+def test_rejected_arguments_leave_output_untouched():
+    import exact_attention_68_amd as A
+
+    q, k, v = (t.cuda() for t in _qkv(1, 1, 64, 64, 7000))
+    o = torch.full_like(q, 3.0)
+    lib = A.lib()
+    p = [t.data_ptr() for t in (q, k, v, o)]
+    assert lib.attn_fwd(*p, 1, 1, 64, 64, 0.1, 9, None, None) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd(*p, 1, 1, 64, 48, 0.1, 0, None, None) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_fwd(*p, 1, 1, 64, 64, float("nan"), 0, None, None) == A.ATTN_ERR_INVALID_ARG
+    bad = A.na2d_params(8, 8, 4, 3)
+    import ctypes
+    assert lib.attn_fwd(*p, 1, 1, 64, 64, 0.1, 2, ctypes.cast(ctypes.pointer(bad), ctypes.c_void_p),
+                        None) == A.ATTN_ERR_PARAMS
+    assert lib.attn_fwd(p[0], p[1], p[2], p[0], 1, 1, 64, 64, 0.1, 0, None, None) == A.ATTN_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0)
