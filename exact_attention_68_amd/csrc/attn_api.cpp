@@ -34,7 +34,10 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int
   // exp(x) = 2^(x log2 e): the kernel works in base 2 with the scale folded in
   a.c = (float)(fabs((double)scale) * 1.4426950408889634);
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
-  if (mask_mode == ATTN_MASK_NA2D) a.na = attn::na_geom(*static_cast<const attn_na2d_params_t*>(params));
+  if (mask_mode == ATTN_MASK_NA2D) {
+    a.na = attn::na_geom(*static_cast<const attn_na2d_params_t*>(params));
+    a.na_inv_w = 1.0f / (float)a.na.grid_w;
+  }
   const int32_t n_wg = a.BH * a.n_qtiles;
   const hipError_t e = attn::launch_fwd(a, (int32_t)d, mask_mode, n_wg, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

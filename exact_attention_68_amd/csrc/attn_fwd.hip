@@ -34,6 +34,8 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "attn.h"
 #include "launch.hpp"
 #include "tile_plan.hpp"
@@ -48,32 +50,57 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, fully unrolled.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 template <int D>
 struct Cfg {
   static constexpr int BM = 128;     // queries per work-group (4 wavefronts x 32)
-  static constexpr int BN = 64;      // keys per tile
-  static constexpr int THREADS = 256;
-  // LDS row strides in 16-bit elements. K rows are read 16 bytes per lane,
-  // 32 rows at a time: a stride of 36 (D=64) or 20 (D=32) banks spreads 16
-  // consecutive rows over all 64 banks. V rows are read 8 bytes per lane by
-  // the transposing load, 4 rows x 64 bytes per half-wave: a stride of
-  // 64 bytes modulo 256 puts those 4 rows on disjoint banks.
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D == 64 ? 96 : 32;
-  static constexpr int K_TILE = BN * KSTR;
-  static constexpr int V_TILE = BN * VSTR;
-  static constexpr int CHUNKS_PER_ROW = D / 8;                       // 16-byte chunks
-  static constexpr int CHUNKS_PER_THREAD = BN * CHUNKS_PER_ROW / THREADS;
-  static_assert(BN * CHUNKS_PER_ROW % THREADS == 0, "tile chunks must split evenly");
+  static constexpr int BN = 128;     // keys per tile
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROW_CHUNKS = D / 8;                     // 16-byte chunks per K or V row
+  static constexpr int TILE = BN * D;                          // 16-bit elements per K or V tile
+  static constexpr int LOADS = BN * ROW_CHUNKS / THREADS;      // 16-byte loads per thread per tile
+  static_assert(BN * ROW_CHUNKS % THREADS == 0, "tile chunks must split evenly");
 };
 
 static_assert(Cfg<64>::BM == kBlockM && Cfg<32>::BM == kBlockM, "launch geometry and kernel tile must agree");
 
+// Rows live unpadded in LDS; the 16-byte chunks of a row are permuted by an XOR
+// with a function of the row so that both read patterns are free of bank
+// conflicts (64 banks of 4 bytes):
+//  * S^T = K Q^T reads 16 bytes per lane, 16 consecutive rows at one logical
+//    chunk per 16 lanes: the even rows and the odd rows must each land on 8
+//    different chunk slots;
+//  * the transposing V read takes 8 bytes per lane, 4 consecutive rows x 4
+//    chunks per half-wave: rows r and r+2 must fall in opposite halves of the
+//    8 chunk slots.
+// d = 64 (8 chunks per row): row r uses slot c ^ (((r >> 1) & 1) << 2 | (r >> 2) & 3).
+// d = 32 (4 chunks per row, 4 rows per 256 bytes): slot c ^ ((r >> 2) & 3).
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return (row >> 2) & 3;
+}
+
+template <int D>
+__device__ __forceinline__ int lds_index(int row, int chunk, int within) {
+  return row * D + ((chunk ^ chunk_swizzle<D>(row)) << 3) + within;
+}
+
+// Each lane-pair (l, l + 32) holds the same query column; combine across the two half-waves.
 __device__ __forceinline__ float swap_halves_max(float x) {
-  // each lane ends up with the max of itself and the lane 32 positions away
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -83,57 +110,65 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Global -> LDS copy of one K or V tile without passing through registers
+// (global_load_lds_dwordx4): every instruction of a wavefront fills one
+// contiguous 1 KB block of the tile, lane L writing its bytes [16L, 16L + 16).
+// Each lane therefore fetches the global chunk that the swizzle places at its
+// slot; that per-lane offset inside a tile is the same for every tile.
 template <int D>
-__device__ __forceinline__ void load_tile_regs(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                                               int32_t N, int32_t tile, int tid,
-                                               u32x4_t (&kr)[Cfg<D>::CHUNKS_PER_THREAD],
-                                               u32x4_t (&vr)[Cfg<D>::CHUNKS_PER_THREAD]) {
+struct TileLoader {
   using C = Cfg<D>;
+  int32_t row[C::LOADS];   // tile row (key offset) of each of this lane's loads
+  int32_t off[C::LOADS];   // element offset of the chunk inside the tile
+  int wave;
+
+  __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
 #pragma unroll
-  for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j) {
-    const int c = tid + j * C::THREADS;
-    const int row = c / C::CHUNKS_PER_ROW, col = c % C::CHUNKS_PER_ROW;
-    const int32_t key = tile * C::BN + row;
-    if (key < N) {
-      const size_t off = (size_t)key * D + col * 8;
-      kr[j] = *reinterpret_cast<const u32x4_t*>(kh + off);
-      vr[j] = *reinterpret_cast<const u32x4_t*>(vh + off);
-    } else {
-      kr[j] = u32x4_t{0, 0, 0, 0};
-      vr[j] = u32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int p = (j * C::WAVES + wave_) * 64 + lane;
+      row[j] = p / C::ROW_CHUNKS;
+      const int chunk = (p % C::ROW_CHUNKS) ^ chunk_swizzle<D>(row[j]);
+      off[j] = row[j] * D + chunk * 8;
     }
   }
-}
 
-template <int D>
-__device__ __forceinline__ void store_tile_lds(uint16_t* ks, uint16_t* vs, int tid,
-                                               const u32x4_t (&kr)[Cfg<D>::CHUNKS_PER_THREAD],
-                                               const u32x4_t (&vr)[Cfg<D>::CHUNKS_PER_THREAD]) {
-  using C = Cfg<D>;
+  // Rows past N (ragged last tile) read row N - 1 instead: finite data whose keys
+  // are masked, so their probabilities are exactly 0.
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int32_t N, int32_t tile,
+                                       uint16_t* lds_tile) const {
+    const int32_t key0 = tile * C::BN;
+    const uint16_t* base = src + (size_t)key0 * D;
+    const bool ragged = key0 + C::BN > N;
 #pragma unroll
-  for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j) {
-    const int c = tid + j * C::THREADS;
-    const int row = c / C::CHUNKS_PER_ROW, col = c % C::CHUNKS_PER_ROW;
-    *reinterpret_cast<u32x4_t*>(ks + row * C::KSTR + col * 8) = kr[j];
-    *reinterpret_cast<u32x4_t*>(vs + row * C::VSTR + col * 8) = vr[j];
+    for (int j = 0; j < C::LOADS; ++j) {
+      int32_t o = off[j];
+      if (ragged && key0 + row[j] >= N) o += (N - 1 - key0 - row[j]) * D;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + o), (lptr_t)(lds_tile + (j * C::WAVES + wave) * 512), 16, 0,
+                                       0);
+    }
   }
-}
+};
 
-// Integer division for the small divisors of the grid geometry.
-__device__ __forceinline__ void divmod_u32(uint32_t n, uint32_t d, int32_t& q, int32_t& r) {
-  q = (int32_t)(n / d);
-  r = (int32_t)(n - (uint32_t)q * d);
-}
+__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Probabilities are computed against a reference maximum m that is only moved
+// when a tile's maximum exceeds it by more than this (base-2 exponent), so
+// P <= 2^8 and the rescale of O is rare. Any reference gives the same O / l.
+constexpr float kRescaleThreshold = 8.0f;
 
 template <int D, int MASK>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(KernelArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_kernel(KernelArgs a) {
   using C = Cfg<D>;
-  constexpr int KB = D / 16;     // 16-wide contraction blocks over d for S^T
-  constexpr int DT = D / 32;     // 32-row output tiles over d for O^T
-  constexpr int SB = C::BN / 32; // 32-key blocks per key tile
+  constexpr int KB = D / 16;      // 16-wide contraction blocks over d for S^T
+  constexpr int DT = D / 32;      // 32-row output tiles over d for O^T
+  constexpr int SB = C::BN / 32;  // 32-key blocks per key tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::K_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,135 +198,311 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(KernelArgs a) {
     qf[kb] = __builtin_bit_cast(bf16x8_t, x);
   }
 
-  // ---- neighbourhood coordinates of this lane's query
   int32_t yq = 0, xq = 0;
-  if (MASK == MASK_NA2D) divmod_u32((uint32_t)my_q, (uint32_t)a.na.grid_w, yq, xq);
+  if (MASK == MASK_NA2D) {
+    yq = my_q / a.na.grid_w;
+    xq = my_q - yq * a.na.grid_w;
+  }
 
   const int32_t n_kv = a.n_kvtiles;
   const KvRun run = kv_run(MASK, N, C::BM, C::BN, q0, a.na);
-
-  f32x16_t oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
-  float m_run = -FLT_MAX;  // running max of c * S (finite sentinel: no inf - inf)
-  float l_run = 0.f;       // this lane's share of the row sum
+  const int32_t n = run.count;
   const float c = a.c;
 
-  u32x4_t kr[C::CHUNKS_PER_THREAD], vr[C::CHUNKS_PER_THREAD];
-  load_tile_regs<D>(kh, vh, N, kv_tile_at(run, 0, n_kv), tid, kr, vr);
-  store_tile_lds<D>(k_lds[0], v_lds[0], tid, kr, vr);
-  __syncthreads();
+  const TileLoader<D> ld(wave, lane);
 
-  for (int32_t i = 0; i < run.count; ++i) {
-    const int buf = i & 1;
-    const int32_t t = kv_tile_at(run, i, n_kv);
-    const bool has_next = i + 1 < run.count;
-    if (has_next) load_tile_regs<D>(kh, vh, N, kv_tile_at(run, i + 1, n_kv), tid, kr, vr);
-
-    const uint16_t* ks = k_lds[buf];
-    const uint16_t* vs = v_lds[buf];
-
-    // ---- S^T = K Q^T: lane holds keys 32sb + 8(r/4) + 4*half + r%4 of its query column
-    f32x16_t s[SB];
+  // LDS offsets that depend only on the lane
+  const int k_swz = chunk_swizzle<D>(col);  // rows sb*32 + col share it
+  int v_row[2], v_off[2][DT];
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      s[sb] = f32x16_t{};
+  for (int h = 0; h < 2; ++h) {
+    v_row[h] = h * 8 + half * 4 + ((lane & 15) >> 2);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(ks + (sb * 32 + col) * C::KSTR + kb * 16 + half * 8);
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      v_off[h][dt] = (((dcol >> 3) ^ chunk_swizzle<D>(v_row[h])) << 3) + (dcol & 7);
+    }
+  }
+
+  // S^T = K Q^T for the key tile in `ks`: lane holds keys 32sb + 8(r/4) + 4*half + r%4 of its query
+  auto qk_tile = [&](const uint16_t* ks, f32x16_t (&s)[SB]) {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int row = sb * 32 + col;
+        const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(ks + row * D + (((2 * kb + half) ^ k_swz) << 3));
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qf[kb], s[sb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- element mask on tiles that need it (uniform branch)
-    const bool masked = tile_needs_mask(MASK, N, C::BN, q0, t);
-    if (masked) {
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t key = t * C::BN + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool ok = key < N;
-          if (MASK == MASK_CAUSAL) ok = ok && key <= my_q;
-          if (MASK == MASK_NA2D) {
-            int32_t yk, xk;
-            divmod_u32((uint32_t)key, (uint32_t)a.na.grid_w, yk, xk);
-            ok = ok && na_axis_ok(yq, yk, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h) &&
-                 na_axis_ok(xq, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w);
-          }
-          if (!ok) s[sb][r] = -INFINITY;
-        }
-      }
-    }
-
-    // ---- running max over this tile
-    float mx = s[0][0];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-    mx = swap_halves_max(mx);
-    const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
-    const float m_new = fmaxf(m_run, cand);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // ---- P = 2^(c S - m), rounded to bfloat16 for the second product. The row
-    // sum adds the same rounded values (two per v_dot2 against (1, 1)), so the
-    // weights that multiply V are exactly the ones the final division uses.
-    bf16x8_t pb[SB][2];
-    float psum = 0.f;
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][kb2 * 8 + e], c, -m_new));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][kb2 * 8 + e + 1], c, -m_new));
-          if (masked) {
-            p0 = s[sb][kb2 * 8 + e] == -INFINITY ? 0.f : p0;
-            p1 = s[sb][kb2 * 8 + e + 1] == -INFINITY ? 0.f : p1;
-          }
-          const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
-          pb[sb][kb2][e] = pp[0];
-          pb[sb][kb2][e + 1] = pp[1];
-          psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-        }
-      }
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-
-    // ---- O^T += V^T P^T
+  // O^T += V^T P^T for the value tile in `vs`. Slot 8*half + e of 16-key block (sb, kb2)
+  // holds key 32sb + 16kb2 + 8(e/4) + 4*half + e%4, matching the S^T accumulator layout.
+  auto pv_tile = [&](const uint16_t* vs, const bf16x8_t (&p)[SB][2], f32x16_t (&o)[DT]) {
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          // slot 8*half + e of this block holds key 32sb + 16kb2 + 8(e/4) + 4*half + e%4
           bf16x8_t vf;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int key = sb * 32 + kb2 * 16 + h * 8 + half * 4 + ((lane & 15) >> 2);
-            const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+            const int row0 = sb * 32 + kb2 * 16;  // multiple of 16: leaves the row swizzle unchanged
             const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((lds_u16*)vs + key * C::VSTR + dcol));
+                (lds_s16x4*)((lds_u16*)vs + (row0 + v_row[h]) * D + v_off[h][dt]));
             const bf16x4_t xb = __builtin_bit_cast(bf16x4_t, x);
 #pragma unroll
             for (int e = 0; e < 4; ++e) vf[h * 4 + e] = xb[e];
           }
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][kb2], oacc[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[sb][kb2], o[dt], 0, 0, 0);
         }
       }
     }
+  };
 
-    if (has_next) store_tile_lds<D>(k_lds[buf ^ 1], v_lds[buf ^ 1], tid, kr, vr);
+  // Element mask of key tile t (uniform decision whether to apply it at all). The
+  // conditions are combined with bitwise & and applied with a select: no
+  // per-lane control flow. (A short-circuit && followed by a conditional store
+  // into the accumulator vector compiled, for the neighbourhood mask, into code
+  // that dropped the second axis' condition.)
+  auto apply_mask = [&](f32x16_t (&s)[SB], int32_t t) {
+    int32_t y0 = 0, x0 = 0;
+    if (MASK == MASK_NA2D) {
+      y0 = (t * C::BN) / a.na.grid_w;
+      x0 = t * C::BN - y0 * a.na.grid_w;
+    }
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t off = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int32_t key = t * C::BN + off;
+        bool ok = key < N;
+        if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
+        if (MASK == MASK_NA2D) {
+          // key = (y0, x0) + off in row-major order. For n = x0 + off < grid_w + BN
+          // the quotient (n + 0.5) / grid_w stays at least 0.5 / grid_w away from
+          // an integer, far more than the float error, so truncation is exact.
+          const int32_t qy = (int32_t)(((float)(x0 + off) + 0.5f) * a.na_inv_w);
+          const int32_t yk = y0 + qy, xk = x0 + off - qy * a.na.grid_w;
+          ok = ok & na_axis_ok(yq, yk, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h) &
+               na_axis_ok(xq, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w);
+        }
+        s[sb][r] = ok ? s[sb][r] : -INFINITY;
+      }
+    }
+  };
+
+  // In-lane maximum of the tile; the lane pair (l, l + 32) is combined separately
+  // (swap_halves_max), after the scheduling region of a step.
+  auto lane_max = [&](const f32x16_t (&s)[SB]) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    return mx;
+  };
+
+  // P = 2^(c s - m) rounded to bfloat16; returns this lane's sum of the rounded values.
+  auto exp_tile = [&](const f32x16_t (&s)[SB], float m, bool masked, bf16x8_t (&p)[SB][2]) {
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float s0 = s[sb][kb2 * 8 + e], s1 = s[sb][kb2 * 8 + e + 1];
+          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m));
+          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m));
+          if (masked) {
+            p0 = s0 == -INFINITY ? 0.f : p0;
+            p1 = s1 == -INFINITY ? 0.f : p1;
+          }
+          const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+          p[sb][kb2][e] = pp[0];
+          p[sb][kb2][e + 1] = pp[1];
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+        }
+      }
+    }
+    return psum;
+  };
+
+  f32x16_t oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
+  float m_run, l_run;
+  bf16x8_t p[SB][2];
+
+  // ---- prologue: K and V of tile 0, K of tile 1; scores and probabilities of tile 0
+  {
+    const int32_t t0 = kv_tile_at(run, 0, n_kv);
+    ld.load(kh, N, t0, k_lds[0]);
+    ld.load(vh, N, t0, v_lds[0]);
+    if (n > 1) ld.load(kh, N, kv_tile_at(run, 1, n_kv), k_lds[1]);
+    wait_tile_loads();
     __syncthreads();
+    f32x16_t s[SB];
+    qk_tile(k_lds[0], s);
+    const bool masked = tile_needs_mask(MASK, N, C::BN, q0, t0);
+    if (masked) apply_mask(s, t0);
+    const float mx = swap_halves_max(lane_max(s));
+    m_run = mx == -INFINITY ? -FLT_MAX : mx * c;  // finite sentinel: never inf - inf
+    l_run = exp_tile(s, m_run, masked, p);
+    __syncthreads();  // every wavefront has read K of tile 0 before its buffer is refilled
   }
+
+  // Common tail of a step: move the reference maximum if some row's maximum
+  // passed it by more than the threshold (rare; redo the tile's probabilities),
+  // accumulate the row sum, hand the probabilities to the next step, and wait
+  // for the next tiles to land in LDS.
+  auto finish_step = [&](float mx_lane, float psum, const f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2]) {
+    const float mx = swap_halves_max(mx_lane);
+    const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
+    if (__builtin_amdgcn_ballot_w64(cand > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, cand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      l_run *= alpha;
+      psum = exp_tile(s, m_run, masked, pn);
+    }
+    l_run += psum;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      p[sb][0] = pn[sb][0];
+      p[sb][1] = pn[sb][1];
+    }
+    wait_tile_loads();
+    __syncthreads();
+  };
+
+  // Steady-state step for a key tile that needs no element mask. LDS holds K of
+  // tile j+1 and V of tile j. A wavefront issues in order, so the matrix core and
+  // the VALU only overlap if their instructions alternate; the order is fixed
+  // slot by slot (sched_barrier fences):
+  //   MFMA groups  S^T b0 | S^T b1 | PV b0 | S^T b2 | PV b1 | S^T b3 | PV b2 | PV b3
+  //   (KB MFMAs per group), LDS reads two slots ahead of their MFMA, and the 32
+  //   two-score pieces of softmax work (max, exp2, bf16 pack, row sum) spread over
+  //   the slots after S^T b0, each after its own block's group.
+  // Probabilities use the previous reference maximum, so no piece waits for the
+  // whole tile's maximum.
+  auto step_fast = [&](int32_t j) {
+    const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
+    if (j + 2 < n) ld.load(kh, N, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
+    ld.load(vh, N, t1, v_lds[(j + 1) & 1]);
+    const uint16_t* ks = k_lds[(j + 1) & 1];
+    const uint16_t* vs = v_lds[j & 1];
+
+    constexpr int GS = KB;                 // MFMAs per group (= 2 * DT)
+    constexpr int TOT = 2 * SB * GS;       // MFMAs per step
+    constexpr int NPAIR = SB * 8;          // two-score pieces per lane
+    constexpr int VSLOTS = TOT - GS;       // slots after the first group
+    constexpr int PF = 2;                  // read-ahead distance in slots
+    // group g: kind 0 = S^T, 1 = PV; block of the group
+    constexpr auto kind = [](int g) { return (g == 2 || g == 4 || g >= 6) ? 1 : 0; };
+    constexpr auto blk = [](int g) { return g < 2 ? g : (g == 2 ? 0 : (g == 3 ? 2 : (g == 4 ? 1 : (g == 5 ? 3 : g - 4)))); };
+
+    f32x16_t s[SB];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+    u32x4_t kf[TOT];
+    bf16x8_t vf[TOT];
+    bf16x8_t pn[SB][2];
+    float psum0 = 0.f, psum1 = 0.f;
+    float mx_lane = -INFINITY;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    auto issue_read = [&](auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      constexpr int g = slot / GS, i = slot % GS, b = blk(g);
+      if constexpr (kind(g) == 0) {
+        const int row = b * 32 + col;
+        kf[slot] = *reinterpret_cast<const u32x4_t*>(ks + row * D + (((2 * i + half) ^ k_swz) << 3));
+      } else {
+        constexpr int kb2 = i / DT, dt = i % DT;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)((lds_u16*)vs + (b * 32 + kb2 * 16 + v_row[h]) * D + v_off[h][dt]));
+          const bf16x4_t xb = __builtin_bit_cast(bf16x4_t, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vf[slot][h * 4 + e] = xb[e];
+        }
+      }
+    };
+
+    static_for<PF>([&](auto slot_c) { issue_read(slot_c); });
+    static_for<TOT>([&](auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      if constexpr (slot + PF < TOT) issue_read(std::integral_constant<int, slot + PF>{});
+      constexpr int g = slot / GS, i = slot % GS, b = blk(g);
+      if constexpr (kind(g) == 0) {
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[slot]), qf[i], s[b], 0, 0, 0);
+      } else {
+        constexpr int kb2 = i / DT, dt = i % DT;
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[slot], p[b][kb2], oacc[dt], 0, 0, 0);
+      }
+      // softmax pieces assigned to this slot
+      static_for<NPAIR>([&](auto q_c) {
+        constexpr int q = decltype(q_c)::value;
+        if constexpr (slot >= GS && GS + (q * VSLOTS) / NPAIR == slot) {
+          constexpr int b2 = q / 8, pp = q % 8;
+          const float s0 = s[b2][2 * pp], s1 = s[b2][2 * pp + 1];
+          mx_lane = __builtin_fmaxf(mx_lane, __builtin_fmaxf(s0, s1));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
+          bf16x2_t pp2 = {(__bf16)p0, (__bf16)p1};
+          float& acc = (pp & 1) ? psum1 : psum0;
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pp2, ones, acc, false);
+          // pin this piece to its slot: without a use here, IR passes sink the
+          // arithmetic to the end of the step, below every MFMA
+          uint32_t pk = __builtin_bit_cast(uint32_t, pp2);
+          asm volatile("" : "+v"(pk), "+v"(acc), "+v"(mx_lane));
+          pp2 = __builtin_bit_cast(bf16x2_t, pk);
+          pn[b2][pp / 4][2 * (pp % 4)] = pp2[0];
+          pn[b2][pp / 4][2 * (pp % 4) + 1] = pp2[1];
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    finish_step(mx_lane, psum0 + psum1, s, false, pn);
+  };
+
+  // Step for a key tile that needs the element mask (ragged tail, causal
+  // diagonal, every neighbourhood tile): plain order.
+  auto step_masked = [&](int32_t j) {
+    const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
+    if (j + 2 < n) ld.load(kh, N, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
+    ld.load(vh, N, t1, v_lds[(j + 1) & 1]);
+    f32x16_t s[SB];
+    qk_tile(k_lds[(j + 1) & 1], s);
+    pv_tile(v_lds[j & 1], p, oacc);
+    apply_mask(s, t1);
+    const float mx_lane = lane_max(s);
+    bf16x8_t pn[SB][2];
+    const float psum = exp_tile(s, m_run, true, pn);
+    finish_step(mx_lane, psum, s, true, pn);
+  };
+
+  // Tiles that need no element mask come first for the none and causal masks (only
+  // a ragged last tile or the diagonal tiles need one), so the loop splits once.
+  int32_t j = 0;
+  if (MASK != MASK_NA2D) {
+    for (; j + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, j + 1, n_kv)); ++j) step_fast(j);
+  }
+  for (; j + 1 < n; ++j) step_masked(j);
+
+  // ---- last tile's product with V
+  pv_tile(v_lds[(n - 1) & 1], p, oacc);
 
   // ---- delayed division and store: lane holds d = 32dt + 8(r/4) + 4*half + r%4
   const float l_tot = swap_halves_sum(l_run);
@@ -328,6 +539,9 @@ hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg
   return launch_one<32, MASK_NONE>(a, n_wg, stream);
 }
 
-int32_t tile_keys() { return Cfg<64>::BN; }
+int32_t tile_keys() {
+  static_assert(Cfg<64>::BN == Cfg<32>::BN, "one key-tile size for every head size");
+  return Cfg<64>::BN;
+}
 
 }  // namespace attn

@@ -22,6 +22,7 @@ struct KernelArgs {
   float c;            // |scale| * log2(e)
   uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q's sign bits), else 0
   NaGeom na;          // neighbourhood geometry (mask NA2D only)
+  float na_inv_w;     // 1 / grid_w, rounded to float (mask NA2D only)
 };
 
 // Launches the kernel for head size d (32 or 64) and the given mask mode.

@@ -98,7 +98,9 @@ constexpr bool tile_needs_mask(int mask, int32_t N, int32_t BN, int32_t q0, int3
   return mask == MASK_NA2D;
 }
 
-// Element predicate of the neighbourhood window for query (yq, xq) and key (yk, xk).
+// Element predicate of the neighbourhood window along one axis, for query
+// coordinate cq and key coordinate ck. Branch-free in the coordinates (the
+// wrap flag is uniform), so callers can combine axes with a plain select.
 constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, int32_t rad, int32_t wrap) {
   if (wrap) {
     int32_t dlt = cq - ck;
@@ -107,7 +109,7 @@ constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, i
     return dlt <= rad;
   }
   const int32_t start = iclamp(cq - rad, 0, len - kernel);
-  return ck >= start && ck < start + kernel;
+  return (uint32_t)(ck - start) < (uint32_t)kernel;
 }
 
 // Map a work-group index to (head, query tile).
