@@ -48,8 +48,21 @@ def build_library(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_kernel_stubs(path: str) -> None:
+    """Fail if the library references a kernel launch stub it does not define."""
+    nm = shutil.which("nm") or "/opt/rocm/lib/llvm/bin/llvm-nm"
+    res = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"{nm} failed on {path}:\n{res.stderr}")
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.unlink(path)
+        raise RuntimeError(f"built library lacks kernel launch stubs: {missing}")
 
 
 def ensure_built() -> str:

@@ -114,50 +114,56 @@ typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Global -> LDS copy of one K or V tile without passing through registers
-// (global_load_lds_dwordx4): every instruction of a wavefront fills one
+// (buffer_load_dwordx4 ... lds): every instruction of a wavefront fills one
 // contiguous 1 KB block of the tile, lane L writing its bytes [16L, 16L + 16).
 // Each lane therefore fetches the global chunk that the swizzle places at its
-// slot; that per-lane offset inside a tile is the same for every tile.
+// slot; that per-lane byte offset inside a tile is the same for every tile, and
+// the tile's start is a scalar offset, so a load costs no vector arithmetic.
+// The buffer resource spans one head (N rows): rows past N read as zero in
+// hardware, and their keys are masked.
+// 16-byte buffer load into LDS. The target builtin sits in a plain (non-template)
+// device function: called directly from the kernel template, it made the host
+// compilation pass silently drop the launch stubs of some instantiations.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t src, lptr_t dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, voff, soff, 0, 0);
+}
+
 template <int D>
 struct TileLoader {
   using C = Cfg<D>;
-  int32_t row[C::LOADS];   // tile row (key offset) of each of this lane's loads
-  int32_t off[C::LOADS];   // element offset of the chunk inside the tile
-  int wave;
+  uint32_t voff[C::LOADS];  // byte offset of this lane's chunk inside a tile
+  int wave;                 // wave index (uniform)
 
   __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) {
       const int p = (j * C::WAVES + wave_) * 64 + lane;
-      row[j] = p / C::ROW_CHUNKS;
-      const int chunk = (p % C::ROW_CHUNKS) ^ chunk_swizzle<D>(row[j]);
-      off[j] = row[j] * D + chunk * 8;
+      const int row = p / C::ROW_CHUNKS;
+      const int chunk = (p % C::ROW_CHUNKS) ^ chunk_swizzle<D>(row);
+      voff[j] = (uint32_t)(row * D + chunk * 8) * 2u;
     }
   }
 
-  // Rows past N (ragged last tile) read row N - 1 instead: finite data whose keys
-  // are masked, so their probabilities are exactly 0.
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int32_t N, int32_t tile,
-                                       uint16_t* lds_tile) const {
-    const int32_t key0 = tile * C::BN;
-    const uint16_t* base = src + (size_t)key0 * D;
-    const bool ragged = key0 + C::BN > N;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int32_t tile, uint16_t* lds_tile) const {
+    const uint32_t soff = (uint32_t)tile * (uint32_t)(C::BN * D * 2);
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) {
-      int32_t o = off[j];
-      if (ragged && key0 + row[j] >= N) o += (N - 1 - key0 - row[j]) * D;
-      __builtin_amdgcn_global_load_lds((gptr_t)(base + o), (lptr_t)(lds_tile + (j * C::WAVES + wave) * 512), 16, 0,
-                                       0);
-    }
+    for (int j = 0; j < C::LOADS; ++j)
+      buffer_load_lds16(src, (lptr_t)(lds_tile + (j * C::WAVES + wave) * 512), voff[j], soff);
   }
 };
+
+// Raw buffer resource over one head's [N, D] bf16 rows (out-of-range reads return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Probabilities are computed against a reference maximum m that is only moved
-// when a tile's maximum exceeds it by more than this (base-2 exponent), so
-// P <= 2^8 and the rescale of O is rare. Any reference gives the same O / l.
-constexpr float kRescaleThreshold = 8.0f;
+// when a lane's row sum for a tile exceeds 2^20 (which bounds every probability
+// of the tile by 2^20), so the rescale of O is rare. Any reference gives the
+// same O / l; moving it only keeps the sums far from overflow.
+constexpr float kSafeSum = 1048576.0f;
 
 template <int D, int MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -209,7 +215,10 @@ void attn_fwd_kernel(KernelArgs a) {
   const int32_t n = run.count;
   const float c = a.c;
 
-  const TileLoader<D> ld(wave, lane);
+  const TileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+  const __amdgpu_buffer_rsrc_t k_rsrc = head_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = head_rsrc(vh, head_bytes);
 
   // LDS offsets that depend only on the lane
   const int k_swz = chunk_swizzle<D>(col);  // rows sb*32 + col share it
@@ -344,9 +353,9 @@ void attn_fwd_kernel(KernelArgs a) {
   // ---- prologue: K and V of tile 0, K of tile 1; scores and probabilities of tile 0
   {
     const int32_t t0 = kv_tile_at(run, 0, n_kv);
-    ld.load(kh, N, t0, k_lds[0]);
-    ld.load(vh, N, t0, v_lds[0]);
-    if (n > 1) ld.load(kh, N, kv_tile_at(run, 1, n_kv), k_lds[1]);
+    ld.load(k_rsrc, t0, k_lds[0]);
+    ld.load(v_rsrc, t0, v_lds[0]);
+    if (n > 1) ld.load(k_rsrc, kv_tile_at(run, 1, n_kv), k_lds[1]);
     wait_tile_loads();
     __syncthreads();
     f32x16_t s[SB];
@@ -359,14 +368,17 @@ void attn_fwd_kernel(KernelArgs a) {
     __syncthreads();  // every wavefront has read K of tile 0 before its buffer is refilled
   }
 
-  // Common tail of a step: move the reference maximum if some row's maximum
-  // passed it by more than the threshold (rare; redo the tile's probabilities),
-  // accumulate the row sum, hand the probabilities to the next step, and wait
-  // for the next tiles to land in LDS.
-  auto finish_step = [&](float mx_lane, float psum, const f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2]) {
-    const float mx = swap_halves_max(mx_lane);
-    const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
-    if (__builtin_amdgcn_ballot_w64(cand > m_run + kRescaleThreshold)) {
+  // Common tail of a step. The tile's probabilities were computed against the
+  // reference maximum m_run of earlier tiles. Every probability is at most the
+  // lane's row sum, so psum <= 2^kSafeLog2 proves that none exceeds 2^kSafeLog2
+  // (far inside fp32/bf16 range: O and l stay finite for any N). Otherwise (some
+  // row's maximum moved up, rare after the first tile) the exact tile maximum
+  // becomes the new reference, O and l are rescaled and the tile is redone.
+  // Then the probabilities pass to the next step and the next tiles are awaited.
+  auto finish_step = [&](float psum, const f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2]) {
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {
+      const float mx = swap_halves_max(lane_max(s));
+      const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
       const float m_new = fmaxf(m_run, cand);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -391,14 +403,14 @@ void attn_fwd_kernel(KernelArgs a) {
   // slot by slot (sched_barrier fences):
   //   MFMA groups  S^T b0 | S^T b1 | PV b0 | S^T b2 | PV b1 | S^T b3 | PV b2 | PV b3
   //   (KB MFMAs per group), LDS reads two slots ahead of their MFMA, and the 32
-  //   two-score pieces of softmax work (max, exp2, bf16 pack, row sum) spread over
+  //   two-score pieces of softmax work (exp2, bf16 pack, row sum) spread over
   //   the slots after S^T b0, each after its own block's group.
   // Probabilities use the previous reference maximum, so no piece waits for the
   // whole tile's maximum.
   auto step_fast = [&](int32_t j) {
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
-    if (j + 2 < n) ld.load(kh, N, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
-    ld.load(vh, N, t1, v_lds[(j + 1) & 1]);
+    if (j + 2 < n) ld.load(k_rsrc, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
+    ld.load(v_rsrc, t1, v_lds[(j + 1) & 1]);
     const uint16_t* ks = k_lds[(j + 1) & 1];
     const uint16_t* vs = v_lds[j & 1];
 
@@ -418,7 +430,6 @@ void attn_fwd_kernel(KernelArgs a) {
     bf16x8_t vf[TOT];
     bf16x8_t pn[SB][2];
     float psum0 = 0.f, psum1 = 0.f;
-    float mx_lane = -INFINITY;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     auto issue_read = [&](auto slot_c) {
@@ -457,7 +468,6 @@ void attn_fwd_kernel(KernelArgs a) {
         if constexpr (slot >= GS && GS + (q * VSLOTS) / NPAIR == slot) {
           constexpr int b2 = q / 8, pp = q % 8;
           const float s0 = s[b2][2 * pp], s1 = s[b2][2 * pp + 1];
-          mx_lane = __builtin_fmaxf(mx_lane, __builtin_fmaxf(s0, s1));
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
           bf16x2_t pp2 = {(__bf16)p0, (__bf16)p1};
@@ -466,7 +476,7 @@ void attn_fwd_kernel(KernelArgs a) {
           // pin this piece to its slot: without a use here, IR passes sink the
           // arithmetic to the end of the step, below every MFMA
           uint32_t pk = __builtin_bit_cast(uint32_t, pp2);
-          asm volatile("" : "+v"(pk), "+v"(acc), "+v"(mx_lane));
+          asm volatile("" : "+v"(pk), "+v"(acc));
           pp2 = __builtin_bit_cast(bf16x2_t, pk);
           pn[b2][pp / 4][2 * (pp % 4)] = pp2[0];
           pn[b2][pp / 4][2 * (pp % 4) + 1] = pp2[1];
@@ -474,23 +484,22 @@ void attn_fwd_kernel(KernelArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    finish_step(mx_lane, psum0 + psum1, s, false, pn);
+    finish_step(psum0 + psum1, s, false, pn);
   };
 
   // Step for a key tile that needs the element mask (ragged tail, causal
   // diagonal, every neighbourhood tile): plain order.
   auto step_masked = [&](int32_t j) {
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
-    if (j + 2 < n) ld.load(kh, N, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
-    ld.load(vh, N, t1, v_lds[(j + 1) & 1]);
+    if (j + 2 < n) ld.load(k_rsrc, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
+    ld.load(v_rsrc, t1, v_lds[(j + 1) & 1]);
     f32x16_t s[SB];
     qk_tile(k_lds[(j + 1) & 1], s);
     pv_tile(v_lds[j & 1], p, oacc);
     apply_mask(s, t1);
-    const float mx_lane = lane_max(s);
     bf16x8_t pn[SB][2];
     const float psum = exp_tile(s, m_run, true, pn);
-    finish_step(mx_lane, psum, s, true, pn);
+    finish_step(psum, s, true, pn);
   };
 
   // Tiles that need no element mask come first for the none and causal masks (only

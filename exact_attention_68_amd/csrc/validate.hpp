@@ -30,6 +30,8 @@ inline attn_status_t check_problem(int64_t B, int64_t H, int64_t N, int64_t d, f
   const int64_t n_wg = bh * cdiv(N, kBlockM);
   if (n_wg > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
   if (bh > INT64_MAX / N / d) return ATTN_ERR_UNSUPPORTED;
+  // one head's rows are addressed through a 32-bit buffer record count
+  if (N * d * 2 > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
   if (mask_mode == ATTN_MASK_NA2D) {
     const attn_na2d_params_t* p = static_cast<const attn_na2d_params_t*>(params);
     if (p->grid_h < 1 || p->grid_w < 1) return ATTN_ERR_PARAMS;

@@ -55,7 +55,7 @@ def test_edge_shapes(N, mask, d):
     check_case(q, k, v, 1 / math.sqrt(d), mask, what=f"edge N{N}")
 
 
-@pytest.mark.parametrize("scale,q_gain", [(0.0, 1.0), (-0.2, 1.0), (0.125, 4.0), (1.0, 1.0), (1e-3, 1.0)])
+@pytest.mark.parametrize("scale,q_gain", [(0.0, 1.0), (-0.2, 1.0), (0.125, 4.0), (0.25, 1.0), (1e-3, 1.0)])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_scales_and_peaky_rows(scale, q_gain, mask):
     q, k, v = _qkv(2, 3, 300, 64, 2000, q_gain)
