@@ -121,12 +121,37 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // the tile's start is a scalar offset, so a load costs no vector arithmetic.
 // The buffer resource spans one head (N rows): rows past N read as zero in
 // hardware, and their keys are masked.
-// 16-byte buffer load into LDS. The target builtin sits in a plain (non-template)
-// device function: called directly from the kernel template, it made the host
-// compilation pass silently drop the launch stubs of some instantiations.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t src, lptr_t dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, voff, soff, 0, 0);
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (4 scalar dwords) over `bytes` bytes at `base`: stride 0,
+// so offsets at or past `bytes` read as zero.
+__device__ __forceinline__ i32x4_t head_rsrc(const uint16_t* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
 }
+
+// 16-byte buffer load into LDS at the wave-uniform byte address `lds` (lane L
+// writes bytes [lds + 16L, lds + 16L + 16)). Issued as inline assembly so the
+// compiler's wait insertion does not treat it as a store that may alias every
+// later LDS read: left to the compiler, each step waited for the next tile's
+// loads before its first read of the current tile. Completion is awaited
+// explicitly (wait_tile_loads) before the barrier that publishes the tile.
+__device__ __forceinline__ void dma_lds16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) { return (uint32_t)(uintptr_t)(lptr_t)p; }
 
 template <int D>
 struct TileLoader {
@@ -144,18 +169,21 @@ struct TileLoader {
     }
   }
 
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int32_t tile, uint16_t* lds_tile) const {
-    const uint32_t soff = (uint32_t)tile * (uint32_t)(C::BN * D * 2);
+  // One of the LOADS 16-byte loads of a tile (lets a step spread its loads out).
+  __device__ __forceinline__ void load_part(i32x4_t src, int32_t tile, const uint16_t* lds_tile, int j) const {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile * (C::BN * D * 2));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + wave * 1024);
+    dma_lds16(src, base + j * C::WAVES * 1024, voff[j], soff);
+  }
+
+  __device__ __forceinline__ void load(i32x4_t src, int32_t tile, const uint16_t* lds_tile) const {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile * (C::BN * D * 2));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + wave * 1024);
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j)
-      buffer_load_lds16(src, (lptr_t)(lds_tile + (j * C::WAVES + wave) * 512), voff[j], soff);
+    for (int j = 0; j < C::LOADS; ++j) dma_lds16(src, base + j * C::WAVES * 1024, voff[j], soff);
   }
 };
 
-// Raw buffer resource over one head's [N, D] bf16 rows (out-of-range reads return 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-}
 
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -217,8 +245,8 @@ void attn_fwd_kernel(KernelArgs a) {
 
   const TileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
   const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
-  const __amdgpu_buffer_rsrc_t k_rsrc = head_rsrc(kh, head_bytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc = head_rsrc(vh, head_bytes);
+  const i32x4_t k_rsrc = head_rsrc(kh, head_bytes);
+  const i32x4_t v_rsrc = head_rsrc(vh, head_bytes);
 
   // LDS offsets that depend only on the lane
   const int k_swz = chunk_swizzle<D>(col);  // rows sb*32 + col share it
@@ -368,13 +396,13 @@ void attn_fwd_kernel(KernelArgs a) {
     __syncthreads();  // every wavefront has read K of tile 0 before its buffer is refilled
   }
 
-  // Common tail of a step. The tile's probabilities were computed against the
-  // reference maximum m_run of earlier tiles. Every probability is at most the
+  // Common tail of a step (the new probabilities are in pn). They were computed
+  // against the reference maximum m_run of earlier tiles. Every probability is at most the
   // lane's row sum, so psum <= 2^kSafeLog2 proves that none exceeds 2^kSafeLog2
   // (far inside fp32/bf16 range: O and l stay finite for any N). Otherwise (some
   // row's maximum moved up, rare after the first tile) the exact tile maximum
   // becomes the new reference, O and l are rescaled and the tile is redone.
-  // Then the probabilities pass to the next step and the next tiles are awaited.
+  // Then the next tiles are awaited.
   auto finish_step = [&](float psum, const f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2]) {
     if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {
       const float mx = swap_halves_max(lane_max(s));
@@ -388,11 +416,6 @@ void attn_fwd_kernel(KernelArgs a) {
       psum = exp_tile(s, m_run, masked, pn);
     }
     l_run += psum;
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      p[sb][0] = pn[sb][0];
-      p[sb][1] = pn[sb][1];
-    }
     wait_tile_loads();
     __syncthreads();
   };
@@ -407,12 +430,14 @@ void attn_fwd_kernel(KernelArgs a) {
   //   the slots after S^T b0, each after its own block's group.
   // Probabilities use the previous reference maximum, so no piece waits for the
   // whole tile's maximum.
-  auto step_fast = [&](int32_t j) {
+  auto step_fast = [&](int32_t j, const bf16x8_t (&pc)[SB][2], bf16x8_t (&pn)[SB][2]) {
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
-    if (j + 2 < n) ld.load(k_rsrc, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
-    ld.load(v_rsrc, t1, v_lds[(j + 1) & 1]);
+    // K of tile j+2 (on the last step: a harmless refill of a buffer nobody reads again)
+    const int32_t t2 = kv_tile_at(run, j + 2 < n ? j + 2 : n - 1, n_kv);
     const uint16_t* ks = k_lds[(j + 1) & 1];
     const uint16_t* vs = v_lds[j & 1];
+    const uint16_t* k_dst = k_lds[j & 1];
+    const uint16_t* v_dst = v_lds[(j + 1) & 1];
 
     constexpr int GS = KB;                 // MFMAs per group (= 2 * DT)
     constexpr int TOT = 2 * SB * GS;       // MFMAs per step
@@ -428,7 +453,6 @@ void attn_fwd_kernel(KernelArgs a) {
     for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
     u32x4_t kf[TOT];
     bf16x8_t vf[TOT];
-    bf16x8_t pn[SB][2];
     float psum0 = 0.f, psum1 = 0.f;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -460,7 +484,14 @@ void attn_fwd_kernel(KernelArgs a) {
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[slot]), qf[i], s[b], 0, 0, 0);
       } else {
         constexpr int kb2 = i / DT, dt = i % DT;
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[slot], p[b][kb2], oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[slot], pc[b][kb2], oacc[dt], 0, 0, 0);
+      }
+      // next tiles' loads, one every other slot in the first half of the step: issued
+      // in one burst they back up the CU's path to LDS and stall the issuing wave
+      if constexpr (slot % 2 == 0 && slot / 2 < 2 * C::LOADS) {
+        constexpr int li = slot / 2;
+        if constexpr (li < C::LOADS) ld.load_part(k_rsrc, t2, k_dst, li);
+        else ld.load_part(v_rsrc, t1, v_dst, li - C::LOADS);
       }
       // softmax pieces assigned to this slot
       static_for<NPAIR>([&](auto q_c) {
@@ -500,13 +531,35 @@ void attn_fwd_kernel(KernelArgs a) {
     bf16x8_t pn[SB][2];
     const float psum = exp_tile(s, m_run, true, pn);
     finish_step(psum, s, true, pn);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      p[sb][0] = pn[sb][0];
+      p[sb][1] = pn[sb][1];
+    }
   };
 
   // Tiles that need no element mask come first for the none and causal masks (only
   // a ragged last tile or the diagonal tiles need one), so the loop splits once.
+  // The fast loop is unrolled by two so the probabilities alternate between two
+  // register sets instead of being copied every step.
   int32_t j = 0;
   if (MASK != MASK_NA2D) {
-    for (; j + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, j + 1, n_kv)); ++j) step_fast(j);
+    int32_t n_fast = 0;  // steps whose next tile needs no element mask
+    while (n_fast + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
+    bf16x8_t p_alt[SB][2];
+    for (; j + 1 < n_fast; j += 2) {
+      step_fast(j, p, p_alt);
+      step_fast(j + 1, p_alt, p);
+    }
+    if (j < n_fast) {
+      step_fast(j, p, p_alt);
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        p[sb][0] = p_alt[sb][0];
+        p[sb][1] = p_alt[sb][1];
+      }
+      ++j;
+    }
   }
   for (; j + 1 < n; ++j) step_masked(j);
 
