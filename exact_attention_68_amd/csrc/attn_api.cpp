@@ -37,6 +37,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int
   if (mask_mode == ATTN_MASK_NA2D) {
     a.na = attn::na_geom(*static_cast<const attn_na2d_params_t*>(params));
     a.na_inv_w = 1.0f / (float)a.na.grid_w;
+    a.na_phases = (a.na.grid_w % 32 == 0 && a.na.grid_w <= 128) ? a.na.grid_w / 32 : 0;
   }
   const int32_t n_wg = a.BH * a.n_qtiles;
   const hipError_t e = attn::launch_fwd(a, (int32_t)d, mask_mode, n_wg, static_cast<hipStream_t>(stream));

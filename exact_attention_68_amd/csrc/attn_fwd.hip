@@ -34,6 +34,7 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "attn.h"
@@ -233,9 +234,28 @@ void attn_fwd_kernel(KernelArgs a) {
   }
 
   int32_t yq = 0, xq = 0;
-  if (MASK == MASK_NA2D) {
+  if (is_na2d(MASK)) {
     yq = my_q / a.na.grid_w;
     xq = my_q - yq * a.na.grid_w;
+  }
+  // Neighbourhood grids whose width is a multiple of 32 (up to 128): every
+  // 32-key MFMA block lies in one grid row, and the columns a lane's 16 keys of
+  // a block fall on depend only on the block's phase (its start column / 32).
+  // The column test is therefore done once per lane: bit 16*phase + r of col_bits
+  // says whether accumulator element r of a block with that phase is in the
+  // query's column window.
+  constexpr bool NA_BLOCKS = MASK == MASK_NA2D_BLOCKS;
+  uint32_t col_bits[2] = {0u, 0u};
+  if (NA_BLOCKS) {
+#pragma unroll
+    for (int ph = 0; ph < 4; ++ph) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t xk = ph * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool ok = ph < a.na_phases && na_axis_ok(xq, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w);
+        col_bits[ph >> 1] |= (uint32_t)ok << ((ph & 1) * 16 + r);
+      }
+    }
   }
 
   const int32_t n_kv = a.n_kvtiles;
@@ -285,16 +305,13 @@ void attn_fwd_kernel(KernelArgs a) {
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          bf16x8_t vf;
+          const int row0 = sb * 32 + kb2 * 16;  // multiple of 16: leaves the row swizzle unchanged
+          u32x2_t x[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int row0 = sb * 32 + kb2 * 16;  // multiple of 16: leaves the row swizzle unchanged
-            const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((lds_u16*)vs + (row0 + v_row[h]) * D + v_off[h][dt]));
-            const bf16x4_t xb = __builtin_bit_cast(bf16x4_t, x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vf[h * 4 + e] = xb[e];
-          }
+          for (int h = 0; h < 2; ++h)
+            x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4*)((lds_u16*)vs + (row0 + v_row[h]) * D + v_off[h][dt])));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[sb][kb2], o[dt], 0, 0, 0);
         }
       }
@@ -308,7 +325,7 @@ void attn_fwd_kernel(KernelArgs a) {
   // that dropped the second axis' condition.)
   auto apply_mask = [&](f32x16_t (&s)[SB], int32_t t) {
     int32_t y0 = 0, x0 = 0;
-    if (MASK == MASK_NA2D) {
+    if (is_na2d(MASK)) {
       y0 = (t * C::BN) / a.na.grid_w;
       x0 = t * C::BN - y0 * a.na.grid_w;
     }
@@ -320,7 +337,7 @@ void attn_fwd_kernel(KernelArgs a) {
         const int32_t key = t * C::BN + off;
         bool ok = key < N;
         if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
-        if (MASK == MASK_NA2D) {
+        if (is_na2d(MASK)) {
           // key = (y0, x0) + off in row-major order. For n = x0 + off < grid_w + BN
           // the quotient (n + 0.5) / grid_w stays at least 0.5 / grid_w away from
           // an integer, far more than the float error, so truncation is exact.
@@ -372,6 +389,31 @@ void attn_fwd_kernel(KernelArgs a) {
     return psum;
   };
 
+  // Per 32-key block of key tile t, the lane's 16-bit window mask (structured
+  // neighbourhood grids): the block's grid row passes the row test and its
+  // phase selects the column bits.
+  auto block_masks = [&](int32_t t, uint32_t (&bm)[SB]) {
+    const int32_t k0 = t * C::BN;                 // multiple of 32
+    const int32_t row0 = k0 / a.na.grid_w;        // uniform
+    const int32_t ph0 = (k0 - row0 * a.na.grid_w) >> 5;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      const int32_t ph = ph0 + sb;
+      const int32_t row = row0 + ph / a.na_phases;
+      const int32_t phase = ph % a.na_phases;
+      const bool rok = row < a.na.grid_h && na_axis_ok(yq, row, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h);
+      const uint32_t cb = (col_bits[phase >> 1] >> ((phase & 1) * 16)) & 0xffffu;
+      bm[sb] = rok ? cb : 0u;
+    }
+  };
+  // Masked scores become -inf (rare slow path of a bitmask-masked step).
+  auto apply_bits = [&](f32x16_t (&s)[SB], const uint32_t (&bm)[SB]) {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sb][r] = ((bm[sb] >> r) & 1u) ? s[sb][r] : -INFINITY;
+  };
+
   f32x16_t oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
@@ -389,7 +431,13 @@ void attn_fwd_kernel(KernelArgs a) {
     f32x16_t s[SB];
     qk_tile(k_lds[0], s);
     const bool masked = tile_needs_mask(MASK, N, C::BN, q0, t0);
-    if (masked) apply_mask(s, t0);
+    if constexpr (NA_BLOCKS) {
+      uint32_t bm0[SB];
+      block_masks(t0, bm0);
+      apply_bits(s, bm0);
+    } else {
+      if (masked) apply_mask(s, t0);
+    }
     const float mx = swap_halves_max(lane_max(s));
     m_run = mx == -INFINITY ? -FLT_MAX : mx * c;  // finite sentinel: never inf - inf
     l_run = exp_tile(s, m_run, masked, p);
@@ -403,8 +451,13 @@ void attn_fwd_kernel(KernelArgs a) {
   // row's maximum moved up, rare after the first tile) the exact tile maximum
   // becomes the new reference, O and l are rescaled and the tile is redone.
   // Then the next tiles are awaited.
-  auto finish_step = [&](float psum, const f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2]) {
+  auto finish_step = [&](float psum, f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2],
+                         const uint32_t* bits) {
     if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {
+      if (bits) {
+        apply_bits(s, *reinterpret_cast<const uint32_t(*)[SB]>(bits));
+        masked = true;
+      }
       const float mx = swap_halves_max(lane_max(s));
       const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
       const float m_new = fmaxf(m_run, cand);
@@ -430,8 +483,11 @@ void attn_fwd_kernel(KernelArgs a) {
   //   the slots after S^T b0, each after its own block's group.
   // Probabilities use the previous reference maximum, so no piece waits for the
   // whole tile's maximum.
-  auto step_fast = [&](int32_t j, const bf16x8_t (&pc)[SB][2], bf16x8_t (&pn)[SB][2]) {
+  auto step_fast = [&](int32_t j, const bf16x8_t (&pc)[SB][2], bf16x8_t (&pn)[SB][2], auto bits_tag) {
+    constexpr bool BITS = decltype(bits_tag)::value;  // structured neighbourhood mask
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
+    uint32_t bm[SB];
+    if constexpr (BITS) block_masks(t1, bm);
     // K of tile j+2 (on the last step: a harmless refill of a buffer nobody reads again)
     const int32_t t2 = kv_tile_at(run, j + 2 < n ? j + 2 : n - 1, n_kv);
     const uint16_t* ks = k_lds[(j + 1) & 1];
@@ -453,6 +509,7 @@ void attn_fwd_kernel(KernelArgs a) {
     for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
     u32x4_t kf[TOT];
     bf16x8_t vf[TOT];
+    uint32_t pw[SB][2][4];  // new probabilities, two bf16 per word
     float psum0 = 0.f, psum1 = 0.f;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -464,14 +521,14 @@ void attn_fwd_kernel(KernelArgs a) {
         kf[slot] = *reinterpret_cast<const u32x4_t*>(ks + row * D + (((2 * i + half) ^ k_swz) << 3));
       } else {
         constexpr int kb2 = i / DT, dt = i % DT;
+        u32x2_t x[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)((lds_u16*)vs + (b * 32 + kb2 * 16 + v_row[h]) * D + v_off[h][dt]));
-          const bf16x4_t xb = __builtin_bit_cast(bf16x4_t, x);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vf[slot][h * 4 + e] = xb[e];
-        }
+        for (int h = 0; h < 2; ++h)
+          x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (lds_s16x4*)((lds_u16*)vs + (b * 32 + kb2 * 16 + v_row[h]) * D +
+                                                              v_off[h][dt])));
+        // whole 32-bit words: element-wise 16-bit copies cost a v_perm per word
+        vf[slot] = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
       }
     };
 
@@ -499,23 +556,31 @@ void attn_fwd_kernel(KernelArgs a) {
         if constexpr (slot >= GS && GS + (q * VSLOTS) / NPAIR == slot) {
           constexpr int b2 = q / 8, pp = q % 8;
           const float s0 = s[b2][2 * pp], s1 = s[b2][2 * pp + 1];
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
-          bf16x2_t pp2 = {(__bf16)p0, (__bf16)p1};
+          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
+          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
+          if constexpr (BITS) {
+            // signed one-bit extract: all ones where the key is in the window, else 0
+            p0 = __uint_as_float(__float_as_uint(p0) & (uint32_t)__builtin_amdgcn_sbfe((int)bm[b2], 2 * pp, 1));
+            p1 = __uint_as_float(__float_as_uint(p1) & (uint32_t)__builtin_amdgcn_sbfe((int)bm[b2], 2 * pp + 1, 1));
+          }
+          const bf16x2_t pp2 = {(__bf16)p0, (__bf16)p1};
           float& acc = (pp & 1) ? psum1 : psum0;
           acc = __builtin_amdgcn_fdot2_f32_bf16(pp2, ones, acc, false);
           // pin this piece to its slot: without a use here, IR passes sink the
           // arithmetic to the end of the step, below every MFMA
           uint32_t pk = __builtin_bit_cast(uint32_t, pp2);
           asm volatile("" : "+v"(pk), "+v"(acc));
-          pp2 = __builtin_bit_cast(bf16x2_t, pk);
-          pn[b2][pp / 4][2 * (pp % 4)] = pp2[0];
-          pn[b2][pp / 4][2 * (pp % 4) + 1] = pp2[1];
+          pw[b2][pp / 4][pp % 4] = pk;
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    finish_step(psum0 + psum1, s, false, pn);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        pn[sb][kb2] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[sb][kb2][0], pw[sb][kb2][1], pw[sb][kb2][2], pw[sb][kb2][3]});
+    finish_step(psum0 + psum1, s, false, pn, BITS ? &bm[0] : nullptr);
   };
 
   // Step for a key tile that needs the element mask (ragged tail, causal
@@ -530,7 +595,7 @@ void attn_fwd_kernel(KernelArgs a) {
     apply_mask(s, t1);
     bf16x8_t pn[SB][2];
     const float psum = exp_tile(s, m_run, true, pn);
-    finish_step(psum, s, true, pn);
+    finish_step(psum, s, true, pn, nullptr);
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
       p[sb][0] = pn[sb][0];
@@ -543,16 +608,14 @@ void attn_fwd_kernel(KernelArgs a) {
   // The fast loop is unrolled by two so the probabilities alternate between two
   // register sets instead of being copied every step.
   int32_t j = 0;
-  if (MASK != MASK_NA2D) {
-    int32_t n_fast = 0;  // steps whose next tile needs no element mask
-    while (n_fast + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
+  auto fast_loop = [&](int32_t n_fast, auto bits_tag) {
     bf16x8_t p_alt[SB][2];
     for (; j + 1 < n_fast; j += 2) {
-      step_fast(j, p, p_alt);
-      step_fast(j + 1, p_alt, p);
+      step_fast(j, p, p_alt, bits_tag);
+      step_fast(j + 1, p_alt, p, bits_tag);
     }
     if (j < n_fast) {
-      step_fast(j, p, p_alt);
+      step_fast(j, p, p_alt, bits_tag);
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         p[sb][0] = p_alt[sb][0];
@@ -560,8 +623,17 @@ void attn_fwd_kernel(KernelArgs a) {
       }
       ++j;
     }
+  };
+  if constexpr (NA_BLOCKS) {
+    fast_loop(n - 1, std::true_type{});
+  } else {
+    if constexpr (MASK != MASK_NA2D) {
+      int32_t n_fast = 0;  // steps whose next tile needs no element mask
+      while (n_fast + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
+      fast_loop(n_fast, std::false_type{});
+    }
+    for (; j + 1 < n; ++j) step_masked(j);
   }
-  for (; j + 1 < n; ++j) step_masked(j);
 
   // ---- last tile's product with V
   pv_tile(v_lds[(n - 1) & 1], p, oacc);
@@ -591,12 +663,15 @@ static hipError_t launch_one(const KernelArgs& a, int32_t n_wg, hipStream_t stre
 }
 
 hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, hipStream_t stream) {
+  const bool blocks = mask == MASK_NA2D && a.na_phases > 0;
   if (d == 64) {
     if (mask == MASK_CAUSAL) return launch_one<64, MASK_CAUSAL>(a, n_wg, stream);
+    if (blocks) return launch_one<64, MASK_NA2D_BLOCKS>(a, n_wg, stream);
     if (mask == MASK_NA2D) return launch_one<64, MASK_NA2D>(a, n_wg, stream);
     return launch_one<64, MASK_NONE>(a, n_wg, stream);
   }
   if (mask == MASK_CAUSAL) return launch_one<32, MASK_CAUSAL>(a, n_wg, stream);
+  if (blocks) return launch_one<32, MASK_NA2D_BLOCKS>(a, n_wg, stream);
   if (mask == MASK_NA2D) return launch_one<32, MASK_NA2D>(a, n_wg, stream);
   return launch_one<32, MASK_NONE>(a, n_wg, stream);
 }

@@ -23,6 +23,7 @@ struct KernelArgs {
   uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q's sign bits), else 0
   NaGeom na;          // neighbourhood geometry (mask NA2D only)
   float na_inv_w;     // 1 / grid_w, rounded to float (mask NA2D only)
+  int32_t na_phases;  // grid_w / 32 when grid_w is a multiple of 32 and at most 128, else 0 (NA2D only)
 };
 
 // Launches the kernel for head size d (32 or 64) and the given mask mode.

@@ -25,6 +25,10 @@
 namespace attn {
 
 enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA2D = 2 };
+// Kernel-internal variant of MASK_NA2D for grids whose width is a multiple of 32
+// (at most 128): the window test runs on per-block bit masks.
+enum : int { MASK_NA2D_BLOCKS = 3 };
+constexpr bool is_na2d(int mask) { return mask == MASK_NA2D || mask == MASK_NA2D_BLOCKS; }
 
 // 2D neighbourhood geometry in the form the kernel uses.
 struct NaGeom {
@@ -68,7 +72,7 @@ constexpr KvRun kv_run(int mask, int32_t N, int32_t BM, int32_t BN, int32_t q0, 
   const int32_t n_tiles = (int32_t)cdiv(N, BN);
   const int32_t q_last = imin(q0 + BM, N) - 1;
   if (mask == MASK_CAUSAL) return KvRun{0, q_last / BN + 1};
-  if (mask != MASK_NA2D) return KvRun{0, n_tiles};
+  if (!is_na2d(mask)) return KvRun{0, n_tiles};
   const RowBand band = na_row_band(g, q0 / g.grid_w, q_last / g.grid_w);
   const int32_t tok_start = band.start * g.grid_w;
   const int32_t tok_len = band.count * g.grid_w;
@@ -95,7 +99,7 @@ constexpr bool tile_needs_mask(int mask, int32_t N, int32_t BN, int32_t q0, int3
   const int32_t k_end = t * BN + BN;  // exclusive
   if (k_end > N) return true;         // ragged last tile: keys past N
   if (mask == MASK_CAUSAL) return k_end - 1 > q0;  // some key lies after some query
-  return mask == MASK_NA2D;
+  return is_na2d(mask);
 }
 
 // Element predicate of the neighbourhood window along one axis, for query
