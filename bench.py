@@ -45,12 +45,36 @@ def algorithmic_bytes(w: workloads.Workload) -> float:
     return 4.0 * w.B * w.H * w.N * w.d * 2
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+KERNEL_SOURCES = ["attn_fwd.hip", "launch.hpp", "tile_plan.hpp"]
+
+
+def recorded_traffic(name: str):
+    """Calibrated HBM bytes of one launch from profiles/traffic.txt, if taken on the current kernel sources."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_68_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 4 and not ln.startswith("#") and parts[0] == name and parts[1] == digest:
+            return (float(parts[2]) + float(parts[3])) * 1024.0
+    return None
+
+
 def mask_mode(A, w):
     return {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D}[w.mask]
 
 
 def cpu_baseline(w: workloads.Workload, q, k, v, budget_s: float = 12.0) -> dict:
-    """Time the float64 oracle on the host cores over whole heads, until about budget_s has passed."""
+    """Time the float64 oracle on the host cores: whole heads, repeated until about budget_s has passed."""
     import oracle
 
     try:
@@ -63,19 +87,25 @@ def cpu_baseline(w: workloads.Workload, q, k, v, budget_s: float = 12.0) -> dict
     na = oracle.NA2D(**{kk: (bool(vv) if kk.startswith("wrap") else vv) for kk, vv in w.na2d.items()}) if w.na2d else None
     heads = 0
     t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            oracle.attention(qf[b:b + 1, h:h + 1], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1], w.scale, w.mask, na)
-            heads += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:
+        b, h = divmod(heads % (w.B * w.H), w.H)
+        oracle.attention(qf[b:b + 1, h:h + 1], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1], w.scale, w.mask, na)
+        heads += 1
     dt = time.perf_counter() - t0
     f = flops(w) * heads / (w.B * w.H)
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (float64 NumPy, S materialised per head), "
-                      f"{dt:.2f} s; host has {os.cpu_count()} logical CPUs"}
+            "sample": f"{heads} heads of {w.name} ({heads / (w.B * w.H):.1f} passes over its {w.B * w.H} heads; "
+                      f"float64 NumPy, S materialised per head) in {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def copy_calibration(nbytes: int = 256 << 20, reps: int = 3) -> None:
+    """A plain device-to-device copy of known size, for scaling memory-traffic counters."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
 
 
 def main():
@@ -85,6 +115,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for traffic counters)")
+    ap.add_argument("--traffic-kib", type=float, nargs=2, metavar=("FETCH", "WRITE"), default=None,
+                    help="FETCH_SIZE and WRITE_SIZE of one launch in KiB, already scaled by the copy calibration")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -131,7 +165,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = sum(args.traffic_kib) * 1024.0 if args.traffic_kib else recorded_traffic(w.name)
 
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
@@ -144,6 +178,8 @@ def main():
                    "scale": w.scale, **({"na2d": w.na2d} if w.na2d else {})},
         "roofline": roof,
     }
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(line), flush=True)
