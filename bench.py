@@ -2,9 +2,12 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
-One step is one attn_fwd launch over one batch of the workload (default:
-SD2.1 512x512 UNet self-attention, B2 H5 N4096 d64, no mask). Inputs are
-resident in HBM before timing starts. Prints one JSON line on stdout.
+One step is one launch of the fused forward over one batch of the workload
+(default: SD2.1 512x512 UNet self-attention, B2 H5 N4096 d64, no mask),
+through attn_fwd_ws (keys split evenly over the resident work-groups when
+that balances the chip; --entry attn_fwd for one work-group per query tile).
+Inputs and the workspace are resident in HBM before timing starts. Prints one
+JSON line on stdout.
 
 FLOP accounting (the metric of the workload): 4 N^2 d per head without a
 mask, half of that with the causal mask, 4 N (kh kw) d per head for 2D
@@ -114,6 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--entry", default="attn_fwd_ws", choices=["attn_fwd_ws", "attn_fwd"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for traffic counters)")
@@ -137,8 +141,16 @@ def main():
     mode = mask_mode(A, w)
     stream = torch.cuda.current_stream(dev)
 
+    ws = None
+    if args.entry == "attn_fwd_ws":
+        nbytes = A.attn_fwd_workspace_size(w.B, w.H, w.N, w.d, mode, params)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
     def step():
-        A.attn_fwd(dq, dk, dv, do, w.scale, mode, params, stream.cuda_stream)
+        if args.entry == "attn_fwd_ws":
+            A.attn_fwd_ws(dq, dk, dv, do, w.scale, mode, params, ws, stream.cuda_stream)
+        else:
+            A.attn_fwd(dq, dk, dv, do, w.scale, mode, params, stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -165,7 +177,12 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = sum(args.traffic_kib) * 1024.0 if args.traffic_kib else recorded_traffic(w.name)
+    # what the event-timed step contains: the attention kernel, plus the merge kernel of a split launch
+    split = ws is not None
+    roof["kernels"] = (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
+                       else f"attn_fwd_kernel<{w.d},{w.mask}>")
+    roof["traffic"] = (sum(args.traffic_kib) * 1024.0 if args.traffic_kib
+                       else recorded_traffic(f"{w.name}:{args.entry}"))
 
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
@@ -175,7 +192,8 @@ def main():
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "kernel_us": kernel_ms * 1e3,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
-                   "scale": w.scale, **({"na2d": w.na2d} if w.na2d else {})},
+                   "scale": w.scale, **({"na2d": w.na2d} if w.na2d else {}), "entry": args.entry,
+                   "workspace_bytes": 0 if ws is None else ws.numel()},
         "roofline": roof,
     }
     if args.copy_calibration:

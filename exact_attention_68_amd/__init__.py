@@ -27,6 +27,7 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_PARAMS = 3
 ATTN_ERR_ALIGNMENT = 4
 ATTN_ERR_HIP = 5
+ATTN_ERR_WORKSPACE = 6
 
 
 class attn_na2d_params_t(ctypes.Structure):
@@ -53,6 +54,10 @@ def _load() -> ctypes.CDLL:
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, vp, ctypes.c_uint64, vp]
+    lib.attn_fwd_ws.restype = i32
+    lib.attn_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, vp, ctypes.POINTER(ctypes.c_uint64)]
+    lib.attn_fwd_workspace_size.restype = i32
     lib.attn_fwd_check.argtypes = [i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_check.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -94,12 +99,7 @@ def attn_fwd_check(B, H, N, d, scale, mask_mode=ATTN_MASK_NONE, params=None) -> 
     return int(lib().attn_fwd_check(B, H, N, d, scale, mask_mode, _params_ptr(params)))
 
 
-def attn_fwd(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, stream=None) -> None:
-    """o <- softmax(scale * q k^T + mask) v, queued on `stream` (torch's current stream by default).
-
-    q, k, v, o: torch bfloat16 CUDA tensors, contiguous, one [B, H, N, d] shape.
-    Raises AttnError with the library's status on any rejected argument.
-    """
+def _check_tensors(q, k, v, o):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
@@ -109,17 +109,77 @@ def attn_fwd(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, stream=No
             raise ValueError(f"{name} must be contiguous")
         if t.dim() != 4 or t.shape != q.shape:
             raise ValueError("q, k, v and o must share one [B, H, N, d] shape")
-    B, H, N, d = q.shape
+    return q.shape
+
+
+def _stream_handle(stream, device):
+    import torch
+
     if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+        stream = torch.cuda.current_stream(device).cuda_stream
+    return int(stream) or None
+
+
+def attn_fwd(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, stream=None) -> None:
+    """o <- softmax(scale * q k^T + mask) v, queued on `stream` (torch's current stream by default).
+
+    q, k, v, o: torch bfloat16 CUDA tensors, contiguous, one [B, H, N, d] shape.
+    Raises AttnError with the library's status on any rejected argument.
+    """
+    B, H, N, d = _check_tensors(q, k, v, o)
     rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, d,
-                       float(scale), int(mask_mode), _params_ptr(params), int(stream) or None)
+                        float(scale), int(mask_mode), _params_ptr(params), _stream_handle(stream, q.device))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_fwd")
 
 
+def attn_fwd_workspace_size(B, H, N, d, mask_mode=ATTN_MASK_NONE, params=None) -> int:
+    """Bytes of workspace attn_fwd_ws needs for this problem on the current device (0: none)."""
+    out = ctypes.c_uint64(0)
+    rc = lib().attn_fwd_workspace_size(B, H, N, d, int(mask_mode), _params_ptr(params), ctypes.byref(out))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_workspace_size")
+    return int(out.value)
+
+
+def attn_fwd_ws(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, workspace=None, stream=None) -> None:
+    """attn_fwd with a device workspace (a uint8 CUDA tensor of at least attn_fwd_workspace_size
+    bytes, any content, or None when that size is 0); see include/attn.h."""
+    B, H, N, d = _check_tensors(q, k, v, o)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = lib().attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, d, float(scale),
+                           int(mask_mode), _params_ptr(params), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_ws")
+
+
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device=None, stream=None):
+    """A uint8 device tensor of at least nbytes, cached per (device, stream).
+
+    Calls that use one workspace must not overlap, so each stream gets its own.
+    """
+    import torch
+
+    if nbytes <= 0:
+        return None
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    key = (dev.index, int(s.cuda_stream))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(s):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
 def attention(q, k, v, scale=None, causal=False, na2d=None, stream=None):
-    """Allocate the output and run attn_fwd. scale defaults to 1/sqrt(d).
+    """Allocate the output and run attn_fwd_ws with a cached workspace. scale defaults to 1/sqrt(d).
 
     na2d: an attn_na2d_params_t for 2D neighbourhood attention.
     """
@@ -130,13 +190,18 @@ def attention(q, k, v, scale=None, causal=False, na2d=None, stream=None):
     o = torch.empty_like(q)
     mode = ATTN_MASK_NA2D if na2d is not None else (ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE)
     s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
-    attn_fwd(q, k, v, o, s, mode, na2d, stream)
+    B, H, N, d = q.shape
+    with torch.cuda.device(q.device):
+        ts = torch.cuda.current_stream(q.device) if stream is None else torch.cuda.ExternalStream(stream)
+        ws = workspace(attn_fwd_workspace_size(B, H, N, d, mode, na2d), q.device, ts)
+        attn_fwd_ws(q, k, v, o, s, mode, na2d, ws, ts.cuda_stream)
     return o
 
 
 __all__ = [
     "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "ATTN_MASK_NA2D",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_PARAMS", "ATTN_ERR_ALIGNMENT",
-    "ATTN_ERR_HIP", "AttnError", "attn_na2d_params_t", "na2d_params",
-    "attn_fwd", "attn_fwd_check", "attn_status_string", "attn_abi_version", "attention", "LIB_PATH",
+    "ATTN_ERR_HIP", "ATTN_ERR_WORKSPACE", "AttnError", "attn_na2d_params_t", "na2d_params",
+    "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "workspace", "attn_fwd_check", "attn_status_string",
+    "attn_abi_version", "attention", "LIB_PATH",
 ]

@@ -194,7 +194,36 @@ __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcn
 // same O / l; moving it only keeps the sums far from overflow.
 constexpr float kSafeSum = 1048576.0f;
 
-template <int D, int MASK>
+// Partial result of one part of a shared query tile, in the lanes' own register
+// order so that each write or read instruction moves one contiguous 1 KB row:
+//   o[wave][dt][g][lane][4]  unnormalised output: the lane's oacc[dt][4g .. 4g + 3]
+//   m[wave][lane]            reference maximum of the lane's query (base 2, scaled)
+//   l[wave][lane]            sum of the probabilities of the lane's keys
+template <int D>
+struct PartSlot {
+  static constexpr int DT = D / 32;
+  static constexpr int M = 4 * DT * 4 * 64 * 4;
+  static constexpr int L = M + 4 * 64;
+  static constexpr int FLOATS = L + 4 * 64;
+};
+static_assert(PartSlot<64>::FLOATS * 4 == part_slot_bytes(64) && PartSlot<32>::FLOATS * 4 == part_slot_bytes(32),
+              "workspace slot size and kernel layout must agree");
+
+template <int D>
+__device__ __forceinline__ void write_part(float* slot, int wave, int lane, const f32x16_t (&o)[D / 32], float m,
+                                           float l) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 x = make_float4(o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]);
+      *reinterpret_cast<float4*>(slot + (((wave * (D / 32) + dt) * 4 + g) * 64 + lane) * 4) = x;
+    }
+  slot[PartSlot<D>::M + wave * 64 + lane] = m;
+  slot[PartSlot<D>::L + wave * 64 + lane] = l;
+}
+
+template <int D, int MASK, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(KernelArgs a) {
   using C = Cfg<D>;
@@ -211,14 +240,35 @@ void attn_fwd_kernel(KernelArgs a) {
   const int col = lane & 31;   // query column owned by this lane
   const int half = lane >> 5;  // which half-wave
 
-  const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH);
   const int32_t N = a.N;
-  const int32_t q0 = w.qtile * C::BM;
-  const size_t head_off = (size_t)w.bh * (size_t)N * D;
+  const int32_t n_kv = a.n_kvtiles;
+  const float c = a.c;
+  const TileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+
+  // LDS offsets that depend only on the lane
+  const int k_swz = chunk_swizzle<D>(col);  // rows sb*32 + col share it
+  int v_row[2], v_off[2][DT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v_row[h] = h * 8 + half * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      v_off[h][dt] = (((dcol >> 3) ^ chunk_swizzle<D>(v_row[h])) << 3) + (dcol & 7);
+    }
+  }
+
+  // One query tile of head bh against the key tiles of `run`: leaves the
+  // unnormalised output (O^T rows of the lane's query), the reference maximum
+  // and the lane's row sum. No LDS DMA is in flight on return.
+  auto segment = [&](const int32_t bh, const int32_t qtile, const KvRun run, f32x16_t (&oacc)[DT], float& m_run,
+                     float& l_run) {
+  const int32_t q0 = qtile * C::BM;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ qh = a.q + head_off;
   const uint16_t* __restrict__ kh = a.k + head_off;
   const uint16_t* __restrict__ vh = a.v + head_off;
-  uint16_t* __restrict__ oh = a.o + head_off;
 
   // ---- Q fragment: B operand of S^T = K Q^T; lane holds d = 16kb + 8*half + 0..7 of its query
   const int32_t my_q = q0 + wave * 32 + col;
@@ -258,28 +308,11 @@ void attn_fwd_kernel(KernelArgs a) {
     }
   }
 
-  const int32_t n_kv = a.n_kvtiles;
-  const KvRun run = kv_run(MASK, N, C::BM, C::BN, q0, a.na);
-  const int32_t n = run.count;
-  const float c = a.c;
 
-  const TileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
-  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+  const int32_t n = run.count;
   const i32x4_t k_rsrc = head_rsrc(kh, head_bytes);
   const i32x4_t v_rsrc = head_rsrc(vh, head_bytes);
 
-  // LDS offsets that depend only on the lane
-  const int k_swz = chunk_swizzle<D>(col);  // rows sb*32 + col share it
-  int v_row[2], v_off[2][DT];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    v_row[h] = h * 8 + half * 4 + ((lane & 15) >> 2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-      v_off[h][dt] = (((dcol >> 3) ^ chunk_swizzle<D>(v_row[h])) << 3) + (dcol & 7);
-    }
-  }
 
   // S^T = K Q^T for the key tile in `ks`: lane holds keys 32sb + 8(r/4) + 4*half + r%4 of its query
   auto qk_tile = [&](const uint16_t* ks, f32x16_t (&s)[SB]) {
@@ -414,10 +447,8 @@ void attn_fwd_kernel(KernelArgs a) {
       for (int r = 0; r < 16; ++r) s[sb][r] = ((bm[sb] >> r) & 1u) ? s[sb][r] : -INFINITY;
   };
 
-  f32x16_t oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
-  float m_run, l_run;
   bf16x8_t p[SB][2];
 
   // ---- prologue: K and V of tile 0, K of tile 1; scores and probabilities of tile 0
@@ -637,43 +668,155 @@ void attn_fwd_kernel(KernelArgs a) {
 
   // ---- last tile's product with V
   pv_tile(v_lds[(n - 1) & 1], p, oacc);
+  };
 
-  // ---- delayed division and store: lane holds d = 32dt + 8(r/4) + 4*half + r%4
-  const float l_tot = swap_halves_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_q < N) {
+  // Delayed division and store of query tile qtile of head bh: lane holds d = 32dt + 8(r/4) + 4*half + r%4
+  auto store_rows = [&](const int32_t bh, const int32_t qtile, const f32x16_t (&oacc)[DT], const float l_run) {
+    const int32_t my_q = qtile * C::BM + wave * 32 + col;
+    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)N * D;
+    const float l_tot = swap_halves_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (my_q < N) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4_t ob;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4_t ob;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(oacc[dt][g * 4 + e] * inv);
-        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g * 8 + half * 4) =
-            __builtin_bit_cast(u32x2_t, ob);
+          for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(oacc[dt][g * 4 + e] * inv);
+          *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g * 8 + half * 4) =
+              __builtin_bit_cast(u32x2_t, ob);
+        }
       }
+    }
+  };
+
+  f32x16_t oacc[DT];
+  float m_run, l_run;
+  if constexpr (!SPLIT) {
+    const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH);
+    segment(w.bh, w.qtile, kv_run(MASK, N, C::BM, C::BN, w.qtile * C::BM, a.na), oacc, m_run, l_run);
+    store_rows(w.bh, w.qtile, oacc, l_run);
+  } else {
+    // Remainder split (unmasked problems): whole tiles first, XCD-contiguous so
+    // the tiles of one head share an L2; then the parts of the split tiles,
+    // each of which leaves its partial result in its own workspace slot.
+    const int32_t full = a.split_full, parts = a.split_parts;
+    if ((int32_t)blockIdx.x < full) {
+      const int32_t tile = xcd_contiguous(blockIdx.x, full);
+      const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
+      segment(bh, qtile, KvRun{0, n_kv}, oacc, m_run, l_run);
+      store_rows(bh, qtile, oacc, l_run);
+    } else {
+      const int32_t slot = blockIdx.x - full;
+      const int32_t tile = full + slot / parts;
+      const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
+      segment(bh, qtile, part_run(n_kv, parts, slot % parts), oacc, m_run, l_run);
+      write_part<D>(a.ws_parts + (size_t)slot * PartSlot<D>::FLOATS, wave, lane, oacc, m_run, l_run);
     }
   }
 }
 
-template <int D, int MASK>
+// Second kernel of a split launch: one wavefront per (split tile, wavefront
+// slice of the tile). It reads every part's maximum and row sum, rescales all
+// parts to the largest maximum, sums them in part order (so the result does not
+// depend on timing) and writes the rows. The parts were written by the previous
+// kernel on the same stream, so plain loads see them.
+template <int D, int PARTS>
+__global__ __launch_bounds__(64) void attn_merge_kernel(KernelArgs a) {
+  constexpr int DT = D / 32;
+  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  const int32_t r = blockIdx.x >> 2, wave = blockIdx.x & 3;
+  const float* slots = a.ws_parts + (size_t)r * PARTS * PartSlot<D>::FLOATS;
+  // every load is unconditional, so all parts are in flight together
+  float mp[PARTS], lp[PARTS];
+  float4 x[PARTS][DT][4];
+#pragma unroll
+  for (int p = 0; p < PARTS; ++p) {
+    const float* slot = slots + (size_t)p * PartSlot<D>::FLOATS;
+    mp[p] = slot[PartSlot<D>::M + wave * 64 + lane];
+    lp[p] = slot[PartSlot<D>::L + wave * 64 + lane];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        x[p][dt][g] = *reinterpret_cast<const float4*>(slot + (((wave * DT + dt) * 4 + g) * 64 + lane) * 4);
+  }
+  float m = mp[0];
+#pragma unroll
+  for (int p = 1; p < PARTS; ++p) m = fmaxf(m, mp[p]);
+  float l = 0.f;
+  float o[DT][16];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < PARTS; ++p) {
+    const float w = __builtin_amdgcn_exp2f(mp[p] - m);
+    l += w * lp[p];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        o[dt][4 * g] += w * x[p][dt][g].x;
+        o[dt][4 * g + 1] += w * x[p][dt][g].y;
+        o[dt][4 * g + 2] += w * x[p][dt][g].z;
+        o[dt][4 * g + 3] += w * x[p][dt][g].w;
+      }
+  }
+  const int32_t tile = a.split_full + r;
+  const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
+  const int32_t my_q = qtile * Cfg<D>::BM + wave * 32 + col;
+  const float l_tot = swap_halves_sum(l);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (my_q < a.N) {
+    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)a.N * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[dt][g * 4 + e] * inv);
+        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g * 8 + half * 4) = __builtin_bit_cast(u32x2_t, ob);
+      }
+  }
+}
+
+template <int D, int MASK, bool SPLIT>
 static hipError_t launch_one(const KernelArgs& a, int32_t n_wg, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MASK>), dim3(n_wg), dim3(Cfg<D>::THREADS), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MASK, SPLIT>), dim3(n_wg), dim3(Cfg<D>::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, hipStream_t stream) {
-  const bool blocks = mask == MASK_NA2D && a.na_phases > 0;
-  if (d == 64) {
-    if (mask == MASK_CAUSAL) return launch_one<64, MASK_CAUSAL>(a, n_wg, stream);
-    if (blocks) return launch_one<64, MASK_NA2D_BLOCKS>(a, n_wg, stream);
-    if (mask == MASK_NA2D) return launch_one<64, MASK_NA2D>(a, n_wg, stream);
-    return launch_one<64, MASK_NONE>(a, n_wg, stream);
+template <int D>
+static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream) {
+  if (a.ws_parts != nullptr) {  // remainder split, no mask
+    const hipError_t e = launch_one<D, MASK_NONE, true>(a, n_wg, stream);
+    if (e != hipSuccess) return e;
+    const dim3 grid(rem * Cfg<D>::WAVES), block(64);
+    static_assert(kMaxParts == 8, "one merge kernel per part count");
+    switch (a.split_parts) {
+      case 2: hipLaunchKernelGGL((attn_merge_kernel<D, 2>), grid, block, 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((attn_merge_kernel<D, 3>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((attn_merge_kernel<D, 4>), grid, block, 0, stream, a); break;
+      case 5: hipLaunchKernelGGL((attn_merge_kernel<D, 5>), grid, block, 0, stream, a); break;
+      case 6: hipLaunchKernelGGL((attn_merge_kernel<D, 6>), grid, block, 0, stream, a); break;
+      case 7: hipLaunchKernelGGL((attn_merge_kernel<D, 7>), grid, block, 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((attn_merge_kernel<D, 8>), grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
-  if (mask == MASK_CAUSAL) return launch_one<32, MASK_CAUSAL>(a, n_wg, stream);
-  if (blocks) return launch_one<32, MASK_NA2D_BLOCKS>(a, n_wg, stream);
-  if (mask == MASK_NA2D) return launch_one<32, MASK_NA2D>(a, n_wg, stream);
-  return launch_one<32, MASK_NONE>(a, n_wg, stream);
+  if (mask == MASK_CAUSAL) return launch_one<D, MASK_CAUSAL, false>(a, n_wg, stream);
+  if (mask == MASK_NA2D && a.na_phases > 0) return launch_one<D, MASK_NA2D_BLOCKS, false>(a, n_wg, stream);
+  if (mask == MASK_NA2D) return launch_one<D, MASK_NA2D, false>(a, n_wg, stream);
+  return launch_one<D, MASK_NONE, false>(a, n_wg, stream);
+}
+
+hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream) {
+  return d == 64 ? launch_d<64>(a, mask, n_wg, rem, stream) : launch_d<32>(a, mask, n_wg, rem, stream);
 }
 
 int32_t tile_keys() {

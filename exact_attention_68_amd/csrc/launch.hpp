@@ -24,12 +24,26 @@ struct KernelArgs {
   NaGeom na;          // neighbourhood geometry (mask NA2D only)
   float na_inv_w;     // 1 / grid_w, rounded to float (mask NA2D only)
   int32_t na_phases;  // grid_w / 32 when grid_w is a multiple of 32 and at most 128, else 0 (NA2D only)
+  // remainder split (SplitPlan; ws_parts null = one work-group per query tile)
+  float* ws_parts;      // rem * parts slots of part_slot_bytes(d)
+  int32_t split_full;   // whole-tile work-groups
+  int32_t split_parts;  // parts per split tile
 };
 
-// Launches the kernel for head size d (32 or 64) and the given mask mode.
-hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, hipStream_t stream);
+// Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
+constexpr int64_t part_slot_bytes(int64_t d) { return (4 * (d / 32) * 4 * 64 * 4 + 2 * 4 * 64) * 4; }
+constexpr int64_t split_workspace_bytes(const SplitPlan& p, int64_t d) {
+  return p.rem > 0 ? (int64_t)p.slots() * part_slot_bytes(d) : 0;
+}
+
+// Launches the kernel for head size d (32 or 64) and the given mask mode. With
+// a.ws_parts set (unmasked problems only), n_wg = full + rem * parts work-groups
+// run the whole tiles and the parts, and a second kernel of rem work-groups
+// merges the parts, both on `stream`.
+hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream);
 
 // Keys per key/value tile of the kernels.
 int32_t tile_keys();
+
 
 }  // namespace attn

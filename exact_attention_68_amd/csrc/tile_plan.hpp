@@ -129,12 +129,71 @@ struct WorkItem {
   int32_t bh, qtile;
 };
 
+// Equal-length items: XCD x runs the contiguous block of logical items
+// [x * n / 8, (x + 1) * n / 8); a tail that does not divide keeps dispatch order.
+constexpr int32_t xcd_contiguous(int32_t wg, int32_t n) {
+  const int32_t per_xcd = n / 8;
+  return wg < per_xcd * 8 ? (wg % 8) * per_xcd + wg / 8 : wg;
+}
+
 constexpr WorkItem work_item(int mask, int32_t wg, int32_t n_wg, int32_t n_qtiles, int32_t BH) {
   if (mask == MASK_CAUSAL) return WorkItem{wg % BH, n_qtiles - 1 - wg / BH};
-  const int32_t per_xcd = n_wg / 8;
-  int32_t logical = wg;
-  if (wg < per_xcd * 8) logical = (wg % 8) * per_xcd + wg / 8;
+  const int32_t logical = xcd_contiguous(wg, n_wg);
   return WorkItem{logical / n_qtiles, logical % n_qtiles};
+}
+
+// ---------------------------------------------------------------------------
+// Remainder split of the unmasked problem.
+//
+// One work-group per query tile leaves the chip unevenly loaded when the tile
+// count is not a multiple of the CU count: 320 tiles on 256 CUs give 64 CUs
+// two tiles while 192 CUs hold one. Here the first `full` tiles (whole rounds
+// of one tile per CU) keep one work-group each, and each of the `rem` remaining
+// tiles is cut along its key tiles into `parts` equal ranges, each run by a
+// work-group of its own that sits beside a whole-tile work-group on some CU.
+// With rem * parts close to the CU count every CU then does about the same
+// work. A part ends in a partial result (the unnormalised output rows, the
+// running maximum and the row sums over its keys); a second, small kernel
+// combines the parts of each tile exactly (the rescaling by 2^(m_i - m) of the
+// running-softmax paragraph of PhotoRoom's xformers post, applied across
+// parts) and writes it.
+//
+// Tiles are numbered head-major (tile = bh * n_qtiles + qtile). Work-group g <
+// full takes a whole tile; work-group full + r * parts + p takes part p of tile
+// full + r, which covers key tiles [p * n_kv / parts, (p + 1) * n_kv / parts)
+// and writes workspace slot r * parts + p.
+struct SplitPlan {
+  int32_t full;   // whole tiles (work-groups 0 .. full - 1)
+  int32_t rem;    // split tiles; 0 = no split
+  int32_t parts;  // parts per split tile
+  constexpr int32_t groups() const { return full + rem * parts; }
+  constexpr int32_t slots() const { return rem * parts; }
+};
+
+// A part spans at least this many key tiles; no tile is cut into more parts.
+constexpr int32_t kMinPartTiles = 2;
+constexpr int32_t kMaxParts = 8;
+
+constexpr KvRun part_run(int32_t n_kv, int32_t parts, int32_t p) {
+  const int32_t a = (int32_t)((int64_t)p * n_kv / parts), b = (int32_t)((int64_t)(p + 1) * n_kv / parts);
+  return KvRun{a, b - a};
+}
+
+// The split for n_tiles query tiles of n_kv key tiles on a device with `cus`
+// CUs: rem = 0 (no split) unless the problem is unmasked, leaves a remainder
+// after whole rounds of one tile per CU, and is at most one round deep (deeper
+// problems are balanced by the dispatcher refilling CUs as tiles finish).
+constexpr SplitPlan split_plan(int mask, int64_t n_tiles, int32_t n_kv, int32_t cus) {
+  SplitPlan p{(int32_t)(n_tiles < INT32_MAX ? n_tiles : INT32_MAX), 0, 0};
+  if (mask != MASK_NONE || cus < 1 || n_tiles < 1 || n_tiles >= 2 * (int64_t)cus) return p;
+  const int32_t full = n_tiles >= cus ? cus : 0;
+  const int32_t rem = (int32_t)(n_tiles - full);
+  if (rem == 0) return p;
+  int32_t parts = cus / rem;
+  if (parts > n_kv / kMinPartTiles) parts = n_kv / kMinPartTiles;
+  if (parts > kMaxParts) parts = kMaxParts;
+  if (parts < 2) return p;
+  return SplitPlan{full, rem, parts};
 }
 
 }  // namespace attn

@@ -57,6 +57,21 @@ inline attn_status_t check_pointers(const void* q, const void* k, const void* v,
   return ATTN_OK;
 }
 
+// Workspace checks of attn_fwd_ws: present, large enough, 256-byte aligned,
+// disjoint from the tensors.
+inline attn_status_t check_workspace(const void* ws, uint64_t ws_bytes, int64_t need, const void* q, const void* k,
+                                     const void* v, const void* o, int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (ws == nullptr || ws_bytes < (uint64_t)need) return ATTN_ERR_WORKSPACE;
+  const uintptr_t uw = (uintptr_t)ws;
+  if (uw & 255u) return ATTN_ERR_WORKSPACE;
+  const uintptr_t bytes = (uintptr_t)(B * H * N * d) * 2u;
+  for (const void* t : {q, k, v, o}) {
+    const uintptr_t ut = (uintptr_t)t;
+    if (uw < ut + bytes && ut < uw + (uintptr_t)need) return ATTN_ERR_WORKSPACE;
+  }
+  return ATTN_OK;
+}
+
 inline NaGeom na_geom(const attn_na2d_params_t& p) {
   return NaGeom{p.grid_h, p.grid_w, p.kernel_h, p.kernel_w, p.kernel_h / 2, p.kernel_w / 2, p.wrap_h, p.wrap_w};
 }

@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Mask modes. */
 typedef enum {
@@ -72,7 +72,11 @@ typedef enum {
     ATTN_ERR_PARAMS = 3,      /* NA2D parameters inconsistent (grid_h*grid_w != N, even or
                                  out-of-range kernel, wrap not 0/1, dilation != 1) */
     ATTN_ERR_ALIGNMENT = 4,   /* q, k, v or o not 16-byte aligned */
-    ATTN_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+    ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error (no device, a failed
+                                 device query, or a failed launch) */
+    ATTN_ERR_WORKSPACE = 6    /* attn_fwd_ws: workspace NULL, smaller than
+                                 attn_fwd_workspace_size, not 256-byte aligned, or
+                                 overlapping q, k, v or o */
 } attn_status_t;
 
 /*
@@ -104,6 +108,55 @@ typedef enum {
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                        int32_t mask_mode, const void* params, void* stream);
+
+/*
+ * attn_fwd_ws: the same operation and arguments as attn_fwd, plus a device
+ * workspace that lets unmasked problems spread evenly over the whole chip.
+ *
+ * One work-group per query tile of 128 queries leaves the GPU unevenly
+ * loaded when the tile count is not a multiple of the CU count (for example
+ * 320 tiles on 256 CUs: 64 CUs do two tiles, 192 do one). For unmasked
+ * problems of fewer than two tiles per CU, this entry point keeps one
+ * work-group per tile for a whole round of tiles and cuts each remaining
+ * tile along its keys into parts that run beside them, so every CU does
+ * about the same work; a second, small kernel on the same stream combines
+ * the parts of each such tile exactly (the running-softmax rescaling of
+ * PhotoRoom's xformers post, running-softmax paragraph, applied between
+ * parts). The result equals attn_fwd's up to floating-point summation order.
+ * Other problems (causal and 2D neighbourhood masks, tile counts that fill
+ * the chip for two or more rounds, or that would cut a tile into parts of
+ * fewer than 2 key tiles) run exactly as attn_fwd with one kernel, and the
+ * workspace is then not touched (it may be NULL when
+ * attn_fwd_workspace_size gives 0).
+ *
+ * workspace       : device scratch memory of at least attn_fwd_workspace_size
+ *                   bytes for this problem, 256-byte aligned, disjoint from
+ *                   q, k, v and o; any initial content. Owned by the caller.
+ *                   Calls that share a workspace must not run concurrently
+ *                   (queue them on one stream).
+ * workspace_bytes : its size in bytes.
+ *
+ * The size depends on the current device (its CU count) and the head size;
+ * it is at most the CU count x 34 KB (about 8.9 MB on an MI355X). Returns the
+ * codes of attn_fwd, and ATTN_ERR_WORKSPACE for a workspace that does not
+ * meet the above; all argument errors are detected before any device work.
+ * The library still allocates nothing.
+ */
+attn_status_t attn_fwd_ws(const void* q, const void* k, const void* v, void* o,
+                          int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                          int32_t mask_mode, const void* params, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_workspace_size: bytes of workspace that attn_fwd_ws needs for
+ * this problem on the current HIP device, written to *bytes (0 when the
+ * problem runs without parts). Checks the sizes, mask and parameters like
+ * attn_fwd_check (the scale is not an argument); ATTN_ERR_INVALID_ARG if
+ * bytes is NULL, ATTN_ERR_HIP if there is no usable device.
+ */
+attn_status_t attn_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d,
+                                      int32_t mask_mode, const void* params,
+                                      uint64_t* bytes);
 
 /*
  * attn_fwd_check: the argument checks of attn_fwd alone, for a problem with

@@ -98,6 +98,43 @@ static void check_work_items(int mask, int BH, int n_qtiles) {
   for (int i = 0; i < n_wg; ++i) EXPECT(seen[i] == 1, "work item %d covered %d times", i, seen[i]);
 }
 
+// The remainder split: whole tiles and parts cover every (tile, key tile) once;
+// parts of one tile are contiguous, non-empty key ranges in order; slots are
+// distinct; every CU gets about the same amount of work.
+static void check_split(int64_t n_tiles, int32_t n_kv, int32_t cus) {
+  const SplitPlan p = split_plan(MASK_NONE, n_tiles, n_kv, cus);
+  EXPECT(split_plan(MASK_CAUSAL, n_tiles, n_kv, cus).rem == 0, "causal never splits");
+  EXPECT(split_plan(MASK_NA2D, n_tiles, n_kv, cus).rem == 0, "2D neighbourhood never splits");
+  if (p.rem == 0) return;
+  EXPECT(n_tiles < 2 * (int64_t)cus, "split only below two tiles per CU");
+  EXPECT(p.full == 0 || p.full == cus, "whole tiles fill one round of CUs");
+  EXPECT(p.full + p.rem == n_tiles, "every tile is whole or split");
+  EXPECT(p.parts >= 2 && p.parts <= kMaxParts && p.parts * kMinPartTiles <= n_kv, "parts %d of %d key tiles",
+         p.parts, n_kv);
+  EXPECT((int64_t)p.rem * p.parts <= cus, "parts fit one round of CUs");
+  std::vector<int> seen((size_t)n_tiles * n_kv, 0);
+  for (int32_t g = 0; g < p.groups(); ++g) {
+    if (g < p.full) {
+      const int32_t tile = xcd_contiguous(g, p.full);
+      EXPECT(tile >= 0 && tile < p.full, "whole tile %d out of range", tile);
+      for (int32_t t = 0; t < n_kv; ++t) seen[(size_t)tile * n_kv + t]++;
+    } else {
+      const int32_t slot = g - p.full;
+      const int32_t tile = p.full + slot / p.parts;
+      const KvRun r = part_run(n_kv, p.parts, slot % p.parts);
+      EXPECT(slot < p.slots(), "slot out of range");
+      EXPECT(tile < n_tiles && r.count >= kMinPartTiles - 1 && r.count >= 1 && r.first + r.count <= n_kv,
+             "part out of its tile");
+      if (slot % p.parts > 0) {
+        const KvRun prev = part_run(n_kv, p.parts, slot % p.parts - 1);
+        EXPECT(prev.first + prev.count == r.first, "parts not contiguous");
+      }
+      for (int32_t t = r.first; t < r.first + r.count; ++t) seen[(size_t)tile * n_kv + t]++;
+    }
+  }
+  for (int v : seen) EXPECT(v == 1, "unit done %d times", v);
+}
+
 static void check_validation() {
   attn_na2d_params_t p{64, 64, 7, 7, 1, 1, 1, 1};
   EXPECT(check_problem(2, 5, 4096, 64, 0.125f, ATTN_MASK_NONE, nullptr) == ATTN_OK, "valid none");
@@ -152,6 +189,16 @@ int main() {
   for (int mask : {MASK_NONE, MASK_CAUSAL})
     for (int BH : {1, 3, 8, 10, 64})
       for (int nq : {1, 2, 7, 32, 72}) check_work_items(mask, BH, nq);
+  // split plans: the sizes of the unmasked workloads and small or odd shapes
+  EXPECT(split_plan(MASK_NONE, 320, 32, 256).rem == 64 && split_plan(MASK_NONE, 320, 32, 256).parts == 4,
+         "B2 H5 N4096: 256 whole tiles, 64 tiles in 4 parts");
+  EXPECT(split_plan(MASK_NONE, 720, 72, 256).rem == 0, "B2 H5 N9216 is over two rounds deep: no split");
+  EXPECT(split_plan(MASK_NONE, 512, 32, 256).rem == 0, "two full rounds need no split");
+  EXPECT(split_plan(MASK_NONE, 256, 32, 256).rem == 0, "one full round needs no split");
+  EXPECT(split_plan(MASK_NONE, 2, 2, 256).rem == 0, "tiny problems do not split");
+  for (int32_t cus : {1, 2, 7, 64, 80, 256, 304})
+    for (int64_t n_tiles : {1, 2, 3, 5, 16, 21, 33, 40, 48, 72, 80, 100, 255, 256, 257, 320, 400, 511, 512, 513})
+      for (int32_t n_kv : {1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 32, 33, 72}) check_split(n_tiles, n_kv, cus);
   if (failures) {
     std::printf("%d failures\n", failures);
     return 1;

@@ -40,24 +40,38 @@ def oracle_na2d(p) -> "oracle.NA2D | None":
     return oracle.NA2D(p.grid_h, p.grid_w, p.kernel_h, p.kernel_w, bool(p.wrap_h), bool(p.wrap_w))
 
 
-def run_gpu(q, k, v, scale, mask_mode, params=None):
+def split_workspace(B, H, N, d, mask_mode, params=None):
+    """A fresh workspace for attn_fwd_ws (None when the problem needs none), filled with 0xff bytes
+    (NaN bit patterns): the library must not depend on its initial content."""
+    import exact_attention_68_amd as A
+
+    n = A.attn_fwd_workspace_size(B, H, N, d, mask_mode, params)
+    return torch.full((n,), 255, dtype=torch.uint8, device="cuda") if n else None
+
+
+def run_gpu(q, k, v, scale, mask_mode, params=None, entry="attn_fwd"):
+    """Output of the HIP path through the C ABI entry point `entry` (attn_fwd or attn_fwd_ws)."""
     import exact_attention_68_amd as A
 
     dq, dk, dv = (t.to("cuda") for t in (q, k, v))
     o = torch.empty_like(dq)
-    A.attn_fwd(dq, dk, dv, o, scale, mask_mode, params)
+    if entry == "attn_fwd":
+        A.attn_fwd(dq, dk, dv, o, scale, mask_mode, params)
+    else:
+        ws = split_workspace(*dq.shape, mask_mode, params)
+        A.attn_fwd_ws(dq, dk, dv, o, scale, mask_mode, params, ws)
     torch.cuda.synchronize()
     return o
 
 
-def check_case(q, k, v, scale, mask: str, params=None, rows=None, what="") -> float:
+def check_case(q, k, v, scale, mask: str, params=None, rows=None, what="", entry="attn_fwd") -> float:
     """Run the HIP path and the oracle on the same bf16 inputs and compare (all rows or `rows`)."""
     import exact_attention_68_amd as A
 
     mode = {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D}[mask]
-    print(f"[parity] {what} B{q.shape[0]} H{q.shape[1]} N{q.shape[2]} d{q.shape[3]} mask={mask} scale={scale}",
-          flush=True)
-    o = run_gpu(q, k, v, scale, mode, params)
+    print(f"[parity] {entry} {what} B{q.shape[0]} H{q.shape[1]} N{q.shape[2]} d{q.shape[3]} mask={mask} "
+          f"scale={scale}", flush=True)
+    o = run_gpu(q, k, v, scale, mode, params, entry)
     got = to_f64(o)
     ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale, mask, oracle_na2d(params), rows=rows)
     if rows is not None:

@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(A):
     names = _declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_check", "attn_status_string", "attn_abi_version"}
+    assert set(names) == {"attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_fwd_check",
+                          "attn_status_string", "attn_abi_version"}
     lib = A.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -42,11 +43,11 @@ def test_abi_version_matches_header(A):
 
 def test_status_strings(A):
     seen = set()
-    for code in range(6):
+    for code in range(7):
         s = A.attn_status_string(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7
     assert A.attn_status_string(99) == "unknown status"
     assert A.attn_status_string(-1) == "unknown status"
 
@@ -82,6 +83,27 @@ def test_fwd_rejects_before_device_work(A):
     assert lib.attn_fwd(q, k, v, q + 64, 1, 1, 64, 64, 0.1, 0, None, None) == A.ATTN_ERR_INVALID_ARG
     assert lib.attn_fwd(q, k, v, o, 1, 1, 64, 48, 0.1, 0, None, None) == A.ATTN_ERR_UNSUPPORTED
     assert lib.attn_fwd(q, k, v, o, 1, 1, -4, 64, 0.1, 0, None, None) == A.ATTN_ERR_INVALID_ARG
+
+
+def test_ws_entry_points_reject_before_device_work(A):
+    """attn_fwd_ws and attn_fwd_workspace_size check every argument before touching a device."""
+    import ctypes
+
+    lib = A.lib()
+    base = 1 << 20
+    q, k, v, o = base, base + (1 << 16), base + (2 << 16), base + (3 << 16)
+    ws = base + (4 << 16)
+    n = ctypes.c_uint64(7)
+    assert lib.attn_fwd_workspace_size(1, 1, 64, 64, 0, None, None) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_workspace_size(0, 1, 64, 64, 0, None, ctypes.byref(n)) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_workspace_size(1, 1, 64, 48, 0, None, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_fwd_workspace_size(1, 1, 64, 64, 2, None, ctypes.byref(n)) == A.ATTN_ERR_INVALID_ARG
+    assert n.value == 7
+    assert lib.attn_fwd_ws(None, k, v, o, 1, 1, 64, 64, 0.1, 0, None, ws, 1 << 20, None) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_ws(q + 8, k, v, o, 1, 1, 64, 64, 0.1, 0, None, ws, 1 << 20, None) == A.ATTN_ERR_ALIGNMENT
+    assert lib.attn_fwd_ws(q, k, v, o, 1, 1, 64, 96, 0.1, 0, None, ws, 1 << 20, None) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_fwd_ws(q, k, v, o, 1, 1, 64, 64, float("nan"), 0, None, ws, 1 << 20,
+                           None) == A.ATTN_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")

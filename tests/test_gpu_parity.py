@@ -4,6 +4,11 @@ Inputs are the seeded bfloat16 tensors of workloads.py. Small cases span
 several query and key tiles plus a ragged tail; the workload sizes are
 compared in full where the oracle finishes in seconds and on sampled query
 rows otherwise. Tolerance: |gpu - ref| <= 4e-3 * max(1, |ref|) + 2e-3.
+
+Both C entry points are covered: attn_fwd (one work-group per query tile) and
+attn_fwd_ws (unmasked problems of less than two tiles per CU: a round of whole
+tiles plus the remaining tiles cut into key-range parts, merged by a second
+kernel through the workspace).
 """
 import math
 
@@ -13,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from parity import check_case, compare, run_gpu, to_f64, workload_params
+from parity import check_case, compare, run_gpu, split_workspace, to_f64, workload_params
 
 pytestmark = pytest.mark.gpu
 
@@ -31,19 +36,117 @@ def _qkv(B, H, N, d, seed, q_gain=1.0):
 
 
 # ---------------------------------------------------------------- workloads
+ENTRIES = ["attn_fwd", "attn_fwd_ws"]
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("name", ["single_head_n256", "sd21_512_selfattn", "causal_n2048", "na2d_wrap_64x64_k7"])
-def test_workload_full(name):
+def test_workload_full(name, entry):
     w = workloads.WORKLOADS[name]
     q, k, v = workloads.workload_qkv(w)
-    check_case(q, k, v, w.scale, w.mask, workload_params(w), what=name)
+    check_case(q, k, v, w.scale, w.mask, workload_params(w), what=name, entry=entry)
 
 
-def test_sd21_768_sampled_rows():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_sd21_768_sampled_rows(entry):
     w = workloads.WORKLOADS["sd21_768_selfattn"]
     q, k, v = workloads.workload_qkv(w)
     rng = np.random.default_rng(7)
     rows = sorted({0, 1, 63, 64, 127, 128, w.N - 1, w.N - 2, *rng.choice(w.N, 250, replace=False).tolist()})
-    check_case(q, k, v, w.scale, w.mask, rows=rows, what=w.name)
+    check_case(q, k, v, w.scale, w.mask, rows=rows, what=w.name, entry=entry)
+
+
+
+# ---------------------------------------------------------------- remainder split (attn_fwd_ws)
+def _splits(B, H, N, d):
+    import exact_attention_68_amd as A
+
+    return A.attn_fwd_workspace_size(B, H, N, d, A.ATTN_MASK_NONE) > 0
+
+
+@pytest.mark.parametrize("B,H,N,d", [
+    (1, 2, 1000, 64),    # 16 tiles of 8 key tiles: every tile in parts
+    (2, 3, 1500, 32),    # ragged query and key tails
+    (1, 3, 777, 64),     # parts of 2 and 3 key tiles
+    (3, 1, 2048, 32),
+    (1, 1, 4096 + 77, 64),
+    (2, 5, 4096, 64),    # the SD2.1 512x512 shape: 256 whole tiles, 64 tiles in 4 parts; every row
+])
+def test_split_shapes(B, H, N, d):
+    assert _splits(B, H, N, d), "shape expected to run split on this device"
+    q, k, v = _qkv(B, H, N, d, 8000 + N + d)
+    check_case(q, k, v, 1 / math.sqrt(d), "none", what=f"split B{B}H{H}N{N}d{d}", entry="attn_fwd_ws")
+
+
+@pytest.mark.parametrize("scale,q_gain", [(0.0, 1.0), (-0.2, 1.0), (0.125, 2.0), (1e-3, 1.0)])
+def test_split_scales_and_peaky_rows(scale, q_gain):
+    q, k, v = _qkv(1, 2, 1000, 64, 8100, q_gain)
+    assert _splits(1, 2, 1000, 64)
+    check_case(q, k, v, scale, "none", what=f"split scale {scale} gain {q_gain}", entry="attn_fwd_ws")
+
+
+def test_split_deterministic():
+    """Parts are merged in a fixed order: repeated calls on one workspace agree bit for bit."""
+    import exact_attention_68_amd as A
+
+    B, H, N, d = 2, 5, 4096, 64
+    q, k, v = (t.cuda() for t in _qkv(B, H, N, d, 8200))
+    ws = split_workspace(B, H, N, d, A.ATTN_MASK_NONE)
+    assert ws is not None
+    outs = []
+    for _ in range(3):
+        o = torch.empty_like(q)
+        A.attn_fwd_ws(q, k, v, o, 0.125, A.ATTN_MASK_NONE, None, ws)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_split_workspace_reused_across_shapes():
+    """One workspace, sized for the largest problem, serves other sizes and head sizes in turn."""
+    import exact_attention_68_amd as A
+
+    shapes = [(2, 5, 4096, 64), (1, 2, 1000, 64), (2, 3, 1500, 32), (2, 5, 4096, 64)]
+    need = max(A.attn_fwd_workspace_size(*s, A.ATTN_MASK_NONE) for s in shapes)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    for i, (B, H, N, d) in enumerate(shapes):
+        q, k, v = _qkv(B, H, N, d, 8300 + i)
+        o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device="cuda")
+        print(f"[parity] reuse B{B} H{H} N{N} d{d}", flush=True)
+        A.attn_fwd_ws(q.cuda(), k.cuda(), v.cuda(), o, 1 / math.sqrt(d), A.ATTN_MASK_NONE, None, ws)
+        torch.cuda.synchronize()
+        rows = list(range(0, N, max(1, N // 300)))
+        ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(d), rows=rows)
+        compare(to_f64(o)[:, :, rows], ref, f"reuse {i}")
+
+
+def test_split_rejects_bad_workspace():
+    import exact_attention_68_amd as A
+
+    B, H, N, d = 1, 2, 1000, 64
+    q, k, v = (t.cuda() for t in _qkv(B, H, N, d, 8400))
+    o = torch.full_like(q, 3.0)
+    need = A.attn_fwd_workspace_size(B, H, N, d)
+    assert need > 0
+    big = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
+    lib = A.lib()
+    p = [t.data_ptr() for t in (q, k, v, o)]
+    assert lib.attn_fwd_ws(*p, B, H, N, d, 0.125, 0, None, None, 0, None) == A.ATTN_ERR_WORKSPACE
+    assert lib.attn_fwd_ws(*p, B, H, N, d, 0.125, 0, None, big.data_ptr(), need - 1, None) == A.ATTN_ERR_WORKSPACE
+    assert lib.attn_fwd_ws(*p, B, H, N, d, 0.125, 0, None, big.data_ptr() + 16, need, None) == A.ATTN_ERR_WORKSPACE
+    assert lib.attn_fwd_ws(*p, B, H, N, d, 0.125, 0, None, p[3], need, None) == A.ATTN_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0)
+    assert int(big.count_nonzero()) == 0
+
+
+def test_split_not_used_where_it_cannot_help():
+    import exact_attention_68_amd as A
+
+    assert A.attn_fwd_workspace_size(2, 5, 9216, 64) == 0          # two and more rounds of tiles
+    assert A.attn_fwd_workspace_size(4, 16, 2048, 64, A.ATTN_MASK_CAUSAL) == 0
+    assert A.attn_fwd_workspace_size(1, 1, 256, 64) == 0           # 2 tiles of 2 key tiles
+    assert A.attn_fwd_workspace_size(2, 4, 4096, 32, A.ATTN_MASK_NA2D, A.na2d_params(64, 64, 7, 7)) == 0
 
 
 # ---------------------------------------------------------------- edge shapes
@@ -65,8 +168,9 @@ def test_scales_and_peaky_rows(scale, q_gain, mask):
     check_case(q, k, v, scale, mask, what=f"scale {scale} gain {q_gain}")
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("mask", ["none", "causal"])
-def test_rescale_path_planted_keys(mask):
+def test_rescale_path_planted_keys(mask, entry):
     """Keys whose scores climb by 30 to 60 (base 2) from one key tile to the next, far past
     the 2^20 row-sum guard: every row's reference maximum has to move several times (the
     rare slow path of a step), for both the unmasked and the causal loop."""
@@ -75,7 +179,7 @@ def test_rescale_path_planted_keys(mask):
     q = q.float().abs() + 0.5                                # positive queries
     grow = (1.0 + 2.0 * (torch.arange(N) // 128)).view(1, 1, N, 1)
     k = (k.float().abs() + 0.25) * grow                      # scores grow tile by tile
-    check_case(q.to(torch.bfloat16), k.to(torch.bfloat16), v, 0.25, mask, what="planted keys")
+    check_case(q.to(torch.bfloat16), k.to(torch.bfloat16), v, 0.25, mask, what="planted keys", entry=entry)
 
 
 # ---------------------------------------------------------------- 2D neighbourhood
@@ -136,20 +240,37 @@ def test_deterministic_bitwise():
     assert torch.equal(a, b)
 
 
-def test_no_device_allocation_and_side_stream():
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_no_device_allocation_and_side_stream(entry):
     import exact_attention_68_amd as A
 
-    q, k, v = (t.cuda() for t in _qkv(1, 2, 512, 64, 6000))
+    B, H, N, d = 1, 2, 1000, 64
+    q, k, v = (t.cuda() for t in _qkv(B, H, N, d, 6000))
     o = torch.empty_like(q)
-    torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        A.attn_fwd(q, k, v, o, 0.125, A.ATTN_MASK_NONE)
+        ws = split_workspace(B, H, N, d, A.ATTN_MASK_NONE) if entry == "attn_fwd_ws" else None
+    s.synchronize()
+    before = torch.cuda.memory_allocated()
+    with torch.cuda.stream(s):
+        if entry == "attn_fwd":
+            A.attn_fwd(q, k, v, o, 0.125, A.ATTN_MASK_NONE)
+        else:
+            A.attn_fwd_ws(q, k, v, o, 0.125, A.ATTN_MASK_NONE, None, ws)
     s.synchronize()
     assert torch.cuda.memory_allocated() == before
     ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 0.125)
-    compare(to_f64(o), ref, "side stream")
+    compare(to_f64(o), ref, f"side stream {entry}")
+
+
+def test_attention_convenience_uses_split_path():
+    import exact_attention_68_amd as A
+
+    q, k, v = (t.cuda() for t in _qkv(1, 2, 1000, 64, 6100))
+    o = A.attention(q, k, v)
+    torch.cuda.synchronize()
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1 / 8)
+    compare(to_f64(o), ref, "attention()")
 
 
 def test_rejected_arguments_leave_output_untouched():
