@@ -74,6 +74,14 @@ struct Cfg {
   static constexpr int TILE = BN * D;                          // 16-bit elements per K or V tile
   static constexpr int LOADS = BN * ROW_CHUNKS / THREADS;      // 16-byte loads per thread per tile
   static_assert(BN * ROW_CHUNKS % THREADS == 0, "tile chunks must split evenly");
+  // Buffers of each of the K and V rings: 64 KB of LDS in both cases, so two
+  // work-groups fit per CU. A tile's loads are issued STAGES - 1 steps before the
+  // step that reads it (d = 32 steps are short, so their tiles start earlier).
+  static constexpr int STAGES = D == 32 ? 4 : 2;
+  static_assert((STAGES & (STAGES - 1)) == 0, "ring indices use a mask");
+  // 16-byte loads a wavefront may still have in flight at the end of a step: those
+  // of the STAGES - 2 later steps (each step issues one K and one V tile).
+  static constexpr int LOADS_AHEAD = (STAGES - 2) * 2 * LOADS;
 };
 
 static_assert(Cfg<64>::BM == kBlockM && Cfg<32>::BM == kBlockM, "launch geometry and kernel tile must agree");
@@ -186,7 +194,14 @@ struct TileLoader {
 };
 
 
-__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wavefront's tile loads are still in flight (loads
+// complete in issue order). Every step issues the same number of loads, so a
+// fixed count names exactly the tiles the next step reads.
+template <int N>
+__device__ __forceinline__ void wait_tile_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Probabilities are computed against a reference maximum m that is only moved
 // when a lane's row sum for a tile exceeds 2^20 (which bounds every probability
@@ -231,8 +246,9 @@ void attn_fwd_kernel(KernelArgs a) {
   constexpr int DT = D / 32;      // 32-row output tiles over d for O^T
   constexpr int SB = C::BN / 32;  // 32-key blocks per key tile
 
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][C::TILE];
+  constexpr int S = C::STAGES;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[S][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[S][C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -296,17 +312,7 @@ void attn_fwd_kernel(KernelArgs a) {
   // query's column window.
   constexpr bool NA_BLOCKS = MASK == MASK_NA2D_BLOCKS;
   uint32_t col_bits[2] = {0u, 0u};
-  if (NA_BLOCKS) {
-#pragma unroll
-    for (int ph = 0; ph < 4; ++ph) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t xk = ph * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = ph < a.na_phases && na_axis_ok(xq, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w);
-        col_bits[ph >> 1] |= (uint32_t)ok << ((ph & 1) * 16 + r);
-      }
-    }
-  }
+  if (NA_BLOCKS) na_col_bits(xq, half, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w, a.na_phases, col_bits);
 
 
   const int32_t n = run.count;
@@ -427,16 +433,30 @@ void attn_fwd_kernel(KernelArgs a) {
   // phase selects the column bits.
   auto block_masks = [&](int32_t t, uint32_t (&bm)[SB]) {
     const int32_t k0 = t * C::BN;                 // multiple of 32
-    const int32_t row0 = k0 / a.na.grid_w;        // uniform
-    const int32_t ph0 = (k0 - row0 * a.na.grid_w) >> 5;
+    const int32_t row0 = k0 / a.na.grid_w;        // uniform: one division per tile
+    int32_t row = row0, phase = (k0 - row0 * a.na.grid_w) >> 5;
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
-      const int32_t ph = ph0 + sb;
-      const int32_t row = row0 + ph / a.na_phases;
-      const int32_t phase = ph % a.na_phases;
+      if (sb > 0 && ++phase == a.na_phases) {  // next 32-key block: next phase, or the next grid row
+        phase = 0;
+        ++row;
+      }
       const bool rok = row < a.na.grid_h && na_axis_ok(yq, row, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h);
       const uint32_t cb = (col_bits[phase >> 1] >> ((phase & 1) * 16)) & 0xffffu;
       bm[sb] = rok ? cb : 0u;
+    }
+  };
+  // The 16-bit element masks of key tile t for a bit-masked step: the window bits
+  // for the structured neighbourhood grids, else the keys up to the lane's last
+  // visible one (its query for the causal mask, N - 1 for a ragged last tile).
+  auto tile_bits = [&](int32_t t, uint32_t (&bm)[SB]) {
+    if constexpr (NA_BLOCKS) {
+      block_masks(t, bm);
+    } else {
+      int32_t last = N - 1;
+      if constexpr (MASK == MASK_CAUSAL) last = last < my_q ? last : my_q;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) bm[sb] = limit_bits(last - (t * C::BN + sb * 32 + 4 * half));
     }
   };
   // Masked scores become -inf (rare slow path of a bitmask-masked step).
@@ -451,13 +471,21 @@ void attn_fwd_kernel(KernelArgs a) {
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
   bf16x8_t p[SB][2];
 
-  // ---- prologue: K and V of tile 0, K of tile 1; scores and probabilities of tile 0
+  // Tile i of the run, clamped to the last one: loads past the end refill a
+  // buffer nobody reads again, and keep the number of loads per step fixed.
+  auto run_tile = [&](int32_t i) { return kv_tile_at(run, i < n ? i : n - 1, n_kv); };
+
+  // ---- prologue: K of tile 0, then (K of tile i, V of tile i - 1) for i = 1 .. S - 1,
+  // in the order the steps issue them; scores and probabilities of tile 0
   {
     const int32_t t0 = kv_tile_at(run, 0, n_kv);
     ld.load(k_rsrc, t0, k_lds[0]);
-    ld.load(v_rsrc, t0, v_lds[0]);
-    if (n > 1) ld.load(k_rsrc, kv_tile_at(run, 1, n_kv), k_lds[1]);
-    wait_tile_loads();
+#pragma unroll
+    for (int i = 1; i < S; ++i) {
+      ld.load(k_rsrc, run_tile(i), k_lds[i]);
+      ld.load(v_rsrc, run_tile(i - 1), v_lds[i - 1]);
+    }
+    wait_tile_loads<C::LOADS_AHEAD + 2 * C::LOADS>();  // K of tile 0
     __syncthreads();
     f32x16_t s[SB];
     qk_tile(k_lds[0], s);
@@ -472,7 +500,8 @@ void attn_fwd_kernel(KernelArgs a) {
     const float mx = swap_halves_max(lane_max(s));
     m_run = mx == -INFINITY ? -FLT_MAX : mx * c;  // finite sentinel: never inf - inf
     l_run = exp_tile(s, m_run, masked, p);
-    __syncthreads();  // every wavefront has read K of tile 0 before its buffer is refilled
+    wait_tile_loads<C::LOADS_AHEAD>();  // K of tile 1 and V of tile 0
+    __syncthreads();  // ... published, and every wavefront has read K of tile 0 before its buffer is refilled
   }
 
   // Common tail of a step (the new probabilities are in pn). They were computed
@@ -483,10 +512,10 @@ void attn_fwd_kernel(KernelArgs a) {
   // becomes the new reference, O and l are rescaled and the tile is redone.
   // Then the next tiles are awaited.
   auto finish_step = [&](float psum, f32x16_t (&s)[SB], bool masked, bf16x8_t (&pn)[SB][2],
-                         const uint32_t* bits) {
+                         const uint32_t (&bm)[SB], auto bits_tag) {
     if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {
-      if (bits) {
-        apply_bits(s, *reinterpret_cast<const uint32_t(*)[SB]>(bits));
+      if constexpr (decltype(bits_tag)::value) {
+        apply_bits(s, bm);
         masked = true;
       }
       const float mx = swap_halves_max(lane_max(s));
@@ -500,7 +529,7 @@ void attn_fwd_kernel(KernelArgs a) {
       psum = exp_tile(s, m_run, masked, pn);
     }
     l_run += psum;
-    wait_tile_loads();
+    wait_tile_loads<C::LOADS_AHEAD>();  // K of tile j + 2 and V of tile j + 1
     __syncthreads();
   };
 
@@ -518,13 +547,14 @@ void attn_fwd_kernel(KernelArgs a) {
     constexpr bool BITS = decltype(bits_tag)::value;  // structured neighbourhood mask
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
     uint32_t bm[SB];
-    if constexpr (BITS) block_masks(t1, bm);
-    // K of tile j+2 (on the last step: a harmless refill of a buffer nobody reads again)
-    const int32_t t2 = kv_tile_at(run, j + 2 < n ? j + 2 : n - 1, n_kv);
-    const uint16_t* ks = k_lds[(j + 1) & 1];
-    const uint16_t* vs = v_lds[j & 1];
-    const uint16_t* k_dst = k_lds[j & 1];
-    const uint16_t* v_dst = v_lds[(j + 1) & 1];
+    if constexpr (BITS) tile_bits(t1, bm);
+    // this step loads K of tile j + S into the buffer of K(j) and V of tile j + S - 1
+    // into the buffer of V(j - 1): both were last read in step j - 1
+    const int32_t tk = run_tile(j + S), tv = run_tile(j + S - 1);
+    const uint16_t* ks = k_lds[(j + 1) & (S - 1)];
+    const uint16_t* vs = v_lds[j & (S - 1)];
+    const uint16_t* k_dst = k_lds[j & (S - 1)];
+    const uint16_t* v_dst = v_lds[(j + S - 1) & (S - 1)];
 
     constexpr int GS = KB;                 // MFMAs per group (= 2 * DT)
     constexpr int TOT = 2 * SB * GS;       // MFMAs per step
@@ -578,8 +608,8 @@ void attn_fwd_kernel(KernelArgs a) {
       // in one burst they back up the CU's path to LDS and stall the issuing wave
       if constexpr (slot % 2 == 0 && slot / 2 < 2 * C::LOADS) {
         constexpr int li = slot / 2;
-        if constexpr (li < C::LOADS) ld.load_part(k_rsrc, t2, k_dst, li);
-        else ld.load_part(v_rsrc, t1, v_dst, li - C::LOADS);
+        if constexpr (li < C::LOADS) ld.load_part(k_rsrc, tk, k_dst, li);
+        else ld.load_part(v_rsrc, tv, v_dst, li - C::LOADS);
       }
       // softmax pieces assigned to this slot
       static_for<NPAIR>([&](auto q_c) {
@@ -611,22 +641,23 @@ void attn_fwd_kernel(KernelArgs a) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
         pn[sb][kb2] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[sb][kb2][0], pw[sb][kb2][1], pw[sb][kb2][2], pw[sb][kb2][3]});
-    finish_step(psum0 + psum1, s, false, pn, BITS ? &bm[0] : nullptr);
+    finish_step(psum0 + psum1, s, false, pn, bm, bits_tag);
   };
 
-  // Step for a key tile that needs the element mask (ragged tail, causal
-  // diagonal, every neighbourhood tile): plain order.
+  // Step for a key tile of a neighbourhood grid that has no bit-mask form
+  // (every tile needs the element predicate): plain order.
   auto step_masked = [&](int32_t j) {
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
-    if (j + 2 < n) ld.load(k_rsrc, kv_tile_at(run, j + 2, n_kv), k_lds[j & 1]);
-    ld.load(v_rsrc, t1, v_lds[(j + 1) & 1]);
+    ld.load(k_rsrc, run_tile(j + S), k_lds[j & (S - 1)]);
+    ld.load(v_rsrc, run_tile(j + S - 1), v_lds[(j + S - 1) & (S - 1)]);
     f32x16_t s[SB];
-    qk_tile(k_lds[(j + 1) & 1], s);
-    pv_tile(v_lds[j & 1], p, oacc);
+    qk_tile(k_lds[(j + 1) & (S - 1)], s);
+    pv_tile(v_lds[j & (S - 1)], p, oacc);
     apply_mask(s, t1);
     bf16x8_t pn[SB][2];
     const float psum = exp_tile(s, m_run, true, pn);
-    finish_step(psum, s, true, pn, nullptr);
+    const uint32_t no_bits[SB] = {};
+    finish_step(psum, s, true, pn, no_bits, std::false_type{});
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
       p[sb][0] = pn[sb][0];
@@ -657,17 +688,17 @@ void attn_fwd_kernel(KernelArgs a) {
   };
   if constexpr (NA_BLOCKS) {
     fast_loop(n - 1, std::true_type{});
+  } else if constexpr (MASK != MASK_NA2D) {
+    int32_t n_fast = 0;  // steps whose next tile needs no element mask
+    while (n_fast + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
+    fast_loop(n_fast, std::false_type{});
+    fast_loop(n - 1, std::true_type{});  // the causal diagonal and a ragged last tile, on bit masks
   } else {
-    if constexpr (MASK != MASK_NA2D) {
-      int32_t n_fast = 0;  // steps whose next tile needs no element mask
-      while (n_fast + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
-      fast_loop(n_fast, std::false_type{});
-    }
     for (; j + 1 < n; ++j) step_masked(j);
   }
 
   // ---- last tile's product with V
-  pv_tile(v_lds[(n - 1) & 1], p, oacc);
+  pv_tile(v_lds[(n - 1) & (S - 1)], p, oacc);
   };
 
   // Delayed division and store of query tile qtile of head bh: lane holds d = 32dt + 8(r/4) + 4*half + r%4
@@ -702,18 +733,13 @@ void attn_fwd_kernel(KernelArgs a) {
     // the tiles of one head share an L2; then the parts of the split tiles,
     // each of which leaves its partial result in its own workspace slot.
     const int32_t full = a.split_full, parts = a.split_parts;
-    if ((int32_t)blockIdx.x < full) {
-      const int32_t tile = xcd_contiguous(blockIdx.x, full);
-      const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
-      segment(bh, qtile, KvRun{0, n_kv}, oacc, m_run, l_run);
-      store_rows(bh, qtile, oacc, l_run);
-    } else {
-      const int32_t slot = blockIdx.x - full;
-      const int32_t tile = full + slot / parts;
-      const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
-      segment(bh, qtile, part_run(n_kv, parts, slot % parts), oacc, m_run, l_run);
-      write_part<D>(a.ws_parts + (size_t)slot * PartSlot<D>::FLOATS, wave, lane, oacc, m_run, l_run);
-    }
+    const bool whole = (int32_t)blockIdx.x < full;
+    const int32_t slot = blockIdx.x - full;  // part slot (parts only)
+    const int32_t tile = whole ? xcd_contiguous(blockIdx.x, full) : full + slot / parts;
+    const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
+    segment(bh, qtile, whole ? KvRun{0, n_kv} : part_run(n_kv, parts, slot % parts), oacc, m_run, l_run);
+    if (whole) store_rows(bh, qtile, oacc, l_run);
+    else write_part<D>(a.ws_parts + (size_t)slot * PartSlot<D>::FLOATS, wave, lane, oacc, m_run, l_run);
   }
 }
 

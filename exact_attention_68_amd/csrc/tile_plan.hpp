@@ -116,6 +116,65 @@ constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, i
   return (uint32_t)(ck - start) < (uint32_t)kernel;
 }
 
+// Bits [a, b) of a 128-bit column mask, in its 64-bit half h (bit i = column 64h + i).
+constexpr uint64_t col_range_bits(int32_t a, int32_t b, int32_t h) {
+  const int32_t lo = imax(a - 64 * h, 0), hi = imin(b - 64 * h, 64);
+  if (hi <= lo) return 0;
+  const uint64_t m = hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1);
+  return m << lo;
+}
+
+// Column window of a query in column cq of a grid of width W <= 128, as a
+// 128-bit mask (two halves): bit x set iff na_axis_ok(cq, x, W, kernel, rad, wrap).
+constexpr void na_col_window(int32_t cq, int32_t W, int32_t kernel, int32_t rad, int32_t wrap, uint64_t (&m)[2]) {
+  int32_t s = 0, e = 0, s2 = 0, e2 = 0;  // [s, e) and, for a wrapped window, [s2, e2)
+  if (wrap) {
+    s = imod(cq - rad, W);
+    e = s + kernel;
+    if (e > W) {
+      s2 = 0;
+      e2 = e - W;
+      e = W;
+    }
+  } else {
+    s = iclamp(cq - rad, 0, W - kernel);
+    e = s + kernel;
+  }
+  for (int32_t h = 0; h < 2; ++h) m[h] = col_range_bits(s, e, h) | col_range_bits(s2, e2, h);
+}
+
+// Per-lane column bits of the block-masked neighbourhood kernel (grid width a
+// multiple of 32, at most 128): bit 16 * (phase & 1) + r of bits[phase >> 1] says
+// whether accumulator element r of a 32-key block starting at column 32 * phase
+// lies in the window. Element r of half-wave `half` holds column
+// 32 * phase + 8 * (r / 4) + 4 * half + r % 4, so each group of 4 elements is one
+// aligned nibble of the window mask.
+constexpr void na_col_bits(int32_t cq, int32_t half, int32_t W, int32_t kernel, int32_t rad, int32_t wrap,
+                           int32_t phases, uint32_t (&bits)[2]) {
+  uint64_t m[2] = {0, 0};
+  na_col_window(cq, W, kernel, rad, wrap, m);
+  bits[0] = bits[1] = 0;
+  for (int32_t ph = 0; ph < 4; ++ph) {
+    if (ph >= phases) break;
+    for (int32_t g = 0; g < 4; ++g) {
+      const int32_t pos = 32 * ph + 8 * g + 4 * half;  // multiple of 4: the nibble stays in one half
+      const uint32_t nib = (uint32_t)(m[pos >> 6] >> (pos & 63)) & 0xFu;
+      bits[ph >> 1] |= nib << ((ph & 1) * 16 + 4 * g);
+    }
+  }
+}
+
+// 16-bit mask of the accumulator elements of one 32-key block that a lane keeps
+// when the keys it may see end at `lim` keys past the lane's first key of the
+// block: element r holds key offset 8 * (r / 4) + r % 4, kept iff <= lim (so
+// lim < 0 keeps none and lim >= 27 keeps all). Used for the causal diagonal
+// (lim = query - first key) and the ragged last tile (lim = N - 1 - first key).
+constexpr uint32_t limit_bits(int32_t lim) {
+  uint32_t m = 0;
+  for (int32_t g = 0; g < 4; ++g) m |= ((1u << iclamp(lim - 8 * g + 1, 0, 4)) - 1u) << (4 * g);
+  return m;
+}
+
 // Map a work-group index to (head, query tile).
 //
 // Work-groups are dispatched round-robin over the 8 XCDs of the chip, each

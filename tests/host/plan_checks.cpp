@@ -135,6 +135,34 @@ static void check_split(int64_t n_tiles, int32_t n_kv, int32_t cus) {
   for (int v : seen) EXPECT(v == 1, "unit done %d times", v);
 }
 
+// The column bits of the block-masked neighbourhood kernel agree with the element predicate.
+static void check_col_bits() {
+  for (int W : {32, 64, 96, 128})
+    for (int kw = 1; kw <= W; kw += 2)
+      for (int wrap = 0; wrap < 2; ++wrap)
+        for (int cq = 0; cq < W; ++cq)
+          for (int half = 0; half < 2; ++half) {
+            uint32_t bits[2] = {7u, 7u};
+            na_col_bits(cq, half, W, kw, kw / 2, wrap, W / 32, bits);
+            for (int ph = 0; ph < 4; ++ph)
+              for (int r = 0; r < 16; ++r) {
+                const int xk = ph * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const bool want = ph < W / 32 && na_axis_ok(cq, xk, W, kw, kw / 2, wrap);
+                const bool got = (bits[ph >> 1] >> ((ph & 1) * 16 + r)) & 1u;
+                EXPECT(got == want, "col bits W %d kw %d wrap %d cq %d half %d ph %d r %d", W, kw, wrap, cq, half, ph, r);
+              }
+          }
+}
+
+static void check_limit_bits() {
+  for (int lim = -40; lim <= 40; ++lim) {
+    uint32_t want = 0;
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) <= lim) want |= 1u << r;
+    EXPECT(limit_bits(lim) == want, "limit_bits(%d) = %x, want %x", lim, limit_bits(lim), want);
+  }
+}
+
 static void check_validation() {
   attn_na2d_params_t p{64, 64, 7, 7, 1, 1, 1, 1};
   EXPECT(check_problem(2, 5, 4096, 64, 0.125f, ATTN_MASK_NONE, nullptr) == ATTN_OK, "valid none");
@@ -171,6 +199,8 @@ static void check_validation() {
 
 int main() {
   check_validation();
+  check_col_bits();
+  check_limit_bits();
   for (int BN : {64, 128}) {
     for (int N : {1, 2, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 600}) check_causal(N, kBlockM, BN);
     const int dims[] = {1, 2, 3, 5, 7, 9, 12, 17};
