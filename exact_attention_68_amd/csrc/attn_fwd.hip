@@ -10,9 +10,11 @@
 //
 // Work decomposition: one work-group = 4 wavefronts = one tile of 128
 // queries of one head; each wavefront owns 32 queries. Key/value tiles of
-// 64 tokens stream through a double-buffered LDS ring shared by the 4
-// wavefronts; the next tile's global loads are in flight while the current
-// tile is computed.
+// 128 tokens stream through LDS rings (2 tiles deep at d = 64, 4 at d = 32)
+// shared by the 4 wavefronts; later tiles' global loads are in flight while
+// the current tile is computed. An unmasked launch may instead run a round of
+// whole tiles plus key-range parts of the remaining tiles, merged by a second
+// small kernel (remainder split, tile_plan.hpp).
 //
 // Per key tile and wavefront:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS (A operand), Q held
@@ -20,10 +22,12 @@
 //                   holds 16 keys of one query column per 32-key block, so
 //                   row reductions are in-lane plus one exchange between the
 //                   two half-waves (v_permlane32_swap).
-//   running max     m_new = max(m, c * rowmax(S)), alpha = 2^(m - m_new), with
-//                   c = |scale| * log2(e) (exp2 replaces exp).
+//   reference max   P is taken against a reference maximum m (base 2, with
+//                   c = |scale| * log2(e)); m only moves, with O and l rescaled
+//                   by 2^(m_old - m_new), when a tile's row sum shows that some
+//                   probability would pass 2^20 (see kSafeSum).
 //   P = 2^(c S - m) fp32, rounded to bfloat16 for the second product;
-//                   l = alpha * l + rowsum of the rounded P, kept per lane.
+//                   l = l + rowsum of the rounded P, kept per lane.
 //   O^T = V^T P^T   v_mfma_f32_32x32x16_bf16 with P straight from registers
 //                   (B operand) and V read from LDS with ds_read_b64_tr_b16,
 //                   which hands each lane 4 consecutive keys of one d column.

@@ -212,6 +212,10 @@ def test_na2d_issue_example_5x5():
     (20, 20, 1, 1, 1, 1),   # self only
     (3, 200, 3, 11, 1, 1),  # short, wide grid: band is the whole sequence
     (64, 64, 7, 7, 0, 0),
+    (16, 32, 5, 5, 0, 1),   # width 32: one 32-column phase per grid row (bit-mask path)
+    (8, 96, 5, 7, 1, 1),    # width 96: three phases
+    (6, 128, 3, 9, 1, 0),   # width 128: four phases, clamped columns
+    (5, 128, 5, 127, 0, 1), # window almost the whole row
 ])
 def test_na2d_shapes(gh, gw, kh, kw, wh, ww, d):
     import exact_attention_68_amd as A
