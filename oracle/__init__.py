@@ -3,6 +3,6 @@
 Test infrastructure only: the test suite, the smoke check and the CPU
 baseline leg of the benchmark use it. The GPU library never imports it.
 """
-from .dense import NA2D, MASKS, allowed, attention, masked_attention, probs
+from .dense import MASKS, NA2D, NA3D, allowed, attention, masked_attention, probs
 
-__all__ = ["NA2D", "MASKS", "allowed", "attention", "masked_attention", "probs"]
+__all__ = ["NA2D", "NA3D", "MASKS", "allowed", "attention", "masked_attention", "probs"]

@@ -7,12 +7,14 @@ it.
 
 What it computes
 ----------------
-For every batch b and head h, with Q, K, V of shape (N, d):
+For every batch b and head h, with Q of shape (Nq, d) and K, V of shape
+(Nkv, d) (Nq = Nkv = N for self-attention):
 
-    S = scale * Q K^T                      (N x N, materialised)
+    S = scale * Q K^T                      (Nq x Nkv, materialised)
     S[i, j] = -inf where key j is not allowed for query i
-    P = exp(S - rowmax(S)),  l = rowsum(P)
+    m = rowmax(S), P = exp(S - m),  l = rowsum(P)
     O = (P V) / l                          (rows with no allowed key give 0)
+    LSE = m + log(l)                       (optional; -inf for such rows)
 
 Sources, as the pages state them:
   * Attention itself, S = Q K^T and R = softmax(S) V over (seqlen, d_head)
@@ -54,6 +56,23 @@ Readings taken where the pages leave a point open
     the grid size. Each key counts once.
   * Inputs are the bfloat16 values both sides consume, widened exactly to
     float64; the result is returned unrounded.
+  * Dilation d along an axis: the window takes every d-th cell. Wrapped, a
+    key is allowed when its coordinate is (c + d*t) mod L for some
+    t in -r..r (which is what padding by r*d, a dilated window and cropping
+    give in the issue's 1D recipe); this needs (kernel - 1) * d < L so each
+    key counts once. Clamped, the axis splits into the d interleaved
+    sub-grids of cells with equal coordinate mod d, and the undilated clamped
+    window is taken inside the query's sub-grid; this needs kernel * d <= L
+    so every sub-grid holds a whole window.
+  * A 3D grid is row-major: token n sits at depth z, row y, column x with
+    n = (z * grid_h + y) * grid_w + x. A key is visible when all three axes
+    allow it.
+  * Queries and keys may differ in number (cross-attention; the issue notes
+    that the neighbourhood kernels assume they are equal, so the
+    neighbourhood masks require Nq = Nkv). The causal mask keeps key j for
+    query i when j <= i (top-left aligned, as SDPA's is_causal does for
+    non-square masks).
+  * logsumexp of a row with no allowed key is -inf (the log of an empty sum).
 
 Every function is plain NumPy. Internal steps live in module-level functions
 so a test can substitute a planted mistake and check that a pin catches it.
@@ -64,7 +83,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-MASKS = ("none", "causal", "na2d")
+MASKS = ("none", "causal", "na2d", "na3d")
 
 
 @dataclass(frozen=True)
@@ -72,7 +91,8 @@ class NA2D:
     """A 2D neighbourhood window over a row-major grid of grid_h x grid_w tokens.
 
     wrap_h / wrap_w select, per axis, the circular window (True) or the
-    standard clamped window (False) of NATTEN issue 142.
+    standard clamped window (False) of NATTEN issue 142; dil_h / dil_w are the
+    dilations (1 = contiguous window).
     """
 
     grid_h: int
@@ -81,6 +101,42 @@ class NA2D:
     kernel_w: int
     wrap_h: bool = True
     wrap_w: bool = True
+    dil_h: int = 1
+    dil_w: int = 1
+
+    def grid(self):
+        return (self.grid_h, self.grid_w)
+
+    def axes(self):
+        """(length, kernel, wrap, dilation) per axis, slowest axis first."""
+        return ((self.grid_h, self.kernel_h, self.wrap_h, self.dil_h),
+                (self.grid_w, self.kernel_w, self.wrap_w, self.dil_w))
+
+
+@dataclass(frozen=True)
+class NA3D:
+    """A 3D neighbourhood window over a row-major grid of grid_d x grid_h x grid_w tokens."""
+
+    grid_d: int
+    grid_h: int
+    grid_w: int
+    kernel_d: int
+    kernel_h: int
+    kernel_w: int
+    wrap_d: bool = True
+    wrap_h: bool = True
+    wrap_w: bool = True
+    dil_d: int = 1
+    dil_h: int = 1
+    dil_w: int = 1
+
+    def grid(self):
+        return (self.grid_d, self.grid_h, self.grid_w)
+
+    def axes(self):
+        return ((self.grid_d, self.kernel_d, self.wrap_d, self.dil_d),
+                (self.grid_h, self.kernel_h, self.wrap_h, self.dil_h),
+                (self.grid_w, self.kernel_w, self.wrap_w, self.dil_w))
 
 
 def _as_f64(x) -> np.ndarray:
@@ -88,13 +144,16 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _axis_allowed(cq: np.ndarray, ck: np.ndarray, length: int, kernel: int, wrap: bool) -> np.ndarray:
+def _axis_allowed(cq: np.ndarray, ck: np.ndarray, length: int, kernel: int, wrap: bool, dil: int = 1) -> np.ndarray:
     """Allowed (query, key) pairs along one grid axis.
 
-    Wrapped: the circular distance min((a-b) mod L, (b-a) mod L) is at most
-    r = kernel // 2 (a centred window that wraps at the borders).
-    Clamped: the window of `kernel` cells starts at clamp(c - r, 0, L - kernel)
-    and the key coordinate must fall inside it.
+    Wrapped: the key coordinate is (c + dil * t) mod L for some t in -r..r,
+    r = kernel // 2 (a centred window that wraps at the borders; with
+    dil = 1, the circular distance is at most r).
+    Clamped: inside the query's sub-grid of cells congruent to it mod dil,
+    the window of `kernel` cells starts at clamp(i - r, 0, L_g - kernel),
+    where i is the query's index in its sub-grid and L_g the sub-grid's
+    length; the key must lie in the same sub-grid and inside that window.
     """
     r = kernel // 2
     cq = cq[:, None]
@@ -102,32 +161,53 @@ def _axis_allowed(cq: np.ndarray, ck: np.ndarray, length: int, kernel: int, wrap
     if wrap:
         fwd = np.mod(ck - cq, length)
         bwd = np.mod(cq - ck, length)
-        return np.minimum(fwd, bwd) <= r
-    start = np.clip(cq - r, 0, length - kernel)
-    return (ck >= start) & (ck < start + kernel)
+        return ((fwd % dil == 0) & (fwd <= r * dil)) | ((bwd % dil == 0) & (bwd <= r * dil))
+    g = np.mod(cq, dil)
+    sub_len = (length - 1 - g) // dil + 1
+    start = np.clip(cq // dil - r, 0, sub_len - kernel)
+    j = ck // dil
+    return (np.mod(ck, dil) == g) & (j >= start) & (j < start + kernel)
 
 
-def allowed(N: int, mask: str = "none", na2d: NA2D | None = None, rows=None) -> np.ndarray:
-    """Boolean matrix A[i, j]: may query rows[i] attend to key j (True = allowed)."""
+def _check_na(na, N: int, mask: str) -> None:
+    want = {"na2d": NA2D, "na3d": NA3D}[mask]
+    if not isinstance(na, want):
+        raise ValueError(f"{mask} mask needs {want.__name__} parameters")
+    if int(np.prod(na.grid())) != N:
+        raise ValueError("the grid must hold exactly N tokens")
+    for length, kern, wrap, dil in na.axes():
+        if dil < 1:
+            raise ValueError("dilation must be at least 1")
+        if kern < 1 or kern % 2 == 0:
+            raise ValueError("kernel sizes must be odd and positive")
+        if wrap and (kern - 1) * dil >= length:
+            raise ValueError("a wrapped window must satisfy (kernel - 1) * dilation < grid size")
+        if not wrap and kern * dil > length:
+            raise ValueError("a clamped window must satisfy kernel * dilation <= grid size")
+
+
+def allowed(N: int, mask: str = "none", na=None, rows=None, n_kv: int | None = None) -> np.ndarray:
+    """Boolean matrix A[i, j]: may query rows[i] attend to key j (True = allowed).
+
+    N is the number of queries, n_kv the number of keys (default N).
+    """
+    n_kv = N if n_kv is None else n_kv
     qi = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    kj = np.arange(N)
+    kj = np.arange(n_kv)
     if mask == "none":
-        return np.ones((qi.size, N), dtype=bool)
+        return np.ones((qi.size, n_kv), dtype=bool)
     if mask == "causal":
         return kj[None, :] <= qi[:, None]
-    if mask == "na2d":
-        if na2d is None:
-            raise ValueError("na2d mask needs NA2D parameters")
-        p = na2d
-        if p.grid_h * p.grid_w != N:
-            raise ValueError("grid_h * grid_w must equal N")
-        for kern, length in ((p.kernel_h, p.grid_h), (p.kernel_w, p.grid_w)):
-            if kern < 1 or kern % 2 == 0 or kern > length:
-                raise ValueError("kernel sizes must be odd and between 1 and the grid size")
-        yq, xq = np.divmod(qi, p.grid_w)
-        yk, xk = np.divmod(kj, p.grid_w)
-        return (_axis_allowed(yq, yk, p.grid_h, p.kernel_h, p.wrap_h)
-                & _axis_allowed(xq, xk, p.grid_w, p.kernel_w, p.wrap_w))
+    if mask in ("na2d", "na3d"):
+        if n_kv != N:
+            raise ValueError("neighbourhood masks need as many keys as queries")
+        _check_na(na, N, mask)
+        cq = np.unravel_index(qi, na.grid())
+        ck = np.unravel_index(kj, na.grid())
+        out = np.ones((qi.size, n_kv), dtype=bool)
+        for a, (length, kern, wrap, dil) in enumerate(na.axes()):
+            out &= _axis_allowed(cq[a], ck[a], length, kern, wrap, dil)
+        return out
     raise ValueError(f"unknown mask {mask!r}")
 
 
@@ -160,39 +240,49 @@ def _combine(p: np.ndarray, l: np.ndarray, v: np.ndarray) -> np.ndarray:
     return np.where(l > 0, num / safe, 0.0)
 
 
-def masked_attention(q, k, v, scale: float, allow: np.ndarray) -> np.ndarray:
-    """One head: q (R, d), k and v (N, d), allow (R, N) boolean. Returns (R, d) float64."""
+def _logsumexp(m: np.ndarray, l: np.ndarray) -> np.ndarray:
+    """log(sum_j exp(S[i, j])) = m + log(l) per row; -inf where no key is allowed."""
+    with np.errstate(divide="ignore"):
+        return np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)[:, 0]
+
+
+def masked_attention(q, k, v, scale: float, allow: np.ndarray, return_lse: bool = False):
+    """One head: q (R, d), k and v (M, d), allow (R, M) boolean. Returns (R, d) float64
+    (and the (R,) logsumexp when return_lse)."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     s = _apply_mask(_scores(q, k, float(scale)), allow)
-    _, p, l = _softmax_parts(s)
-    return _combine(p, l, v)
+    m, p, l = _softmax_parts(s)
+    out = _combine(p, l, v)
+    return (out, _logsumexp(m, l)) if return_lse else out
 
 
-def attention(q, k, v, scale: float, mask: str = "none", na2d: NA2D | None = None, rows=None) -> np.ndarray:
-    """Attention over [B, H, N, d] inputs; returns float64 [B, H, R, d].
+def attention(q, k, v, scale: float, mask: str = "none", na=None, rows=None, return_lse: bool = False):
+    """Attention over q [B, H, Nq, d] and k, v [B, H, Nkv, d]; returns float64 [B, H, R, d]
+    (and the logsumexp, float64 [B, H, R], when return_lse).
 
     rows, if given, selects the query rows to evaluate (the definition is
     evaluated at those rows only; every key still takes part).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    B, H, N, d = q.shape
-    sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    allow = allowed(N, mask, na2d, sel)
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v one [B, H, Nkv, d] shape")
+    B, H, Nq, d = q.shape
+    sel = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    allow = allowed(Nq, mask, na, sel, n_kv=k.shape[2])
     out = np.empty((B, H, sel.size, d), dtype=np.float64)
+    lse = np.empty((B, H, sel.size), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            out[b, h] = masked_attention(q[b, h, sel], k[b, h], v[b, h], scale, allow)
-    return out
+            out[b, h], lse[b, h] = masked_attention(q[b, h, sel], k[b, h], v[b, h], scale, allow, True)
+    return (out, lse) if return_lse else out
 
 
-def probs(q, k, scale: float, mask: str = "none", na2d: NA2D | None = None) -> np.ndarray:
-    """Normalised attention weights P / l, float64 [B, H, N, N] (small shapes only)."""
+def probs(q, k, scale: float, mask: str = "none", na=None) -> np.ndarray:
+    """Normalised attention weights P / l, float64 [B, H, Nq, Nkv] (small shapes only)."""
     q, k = _as_f64(q), _as_f64(k)
-    B, H, N, d = q.shape
-    allow = allowed(N, mask, na2d)
-    out = np.empty((B, H, N, N), dtype=np.float64)
+    B, H, Nq, d = q.shape
+    allow = allowed(Nq, mask, na, n_kv=k.shape[2])
+    out = np.empty((B, H, Nq, k.shape[2]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             s = _apply_mask(_scores(q[b, h], k[b, h], float(scale)), allow)

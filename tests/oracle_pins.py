@@ -15,10 +15,19 @@ Independent routes used here:
   * torch's scaled_dot_product_attention on the CPU in float64 (the math
     backend "Profiling in PyTorch" calls the reference implementation);
   * the pad -> clamped window -> crop route of NATTEN issue 142;
-  * symmetries (torus translation, key permutation) and special cases.
+  * symmetries (torus translation, key permutation) and special cases;
+  * for dilation, the interleaved sub-grids (a dilated window is the
+    undilated window inside the sub-grid of cells congruent mod the
+    dilation) and the issue's 1D recipe (circular pad by kernel//2 * dilation,
+    dilated window, crop);
+  * for 3D grids, the 2D case at depth 1, a 3D box filter built from array
+    shifts, and the pad/crop route along the wrapped axes;
+  * for logsumexp, log(count) at scale 0 and torch.logsumexp in float64;
+  * for Nq != Nkv, SDPA in float64 (its is_causal is top-left aligned).
 """
 from __future__ import annotations
 
+import itertools
 import math
 import pathlib
 
@@ -42,52 +51,76 @@ def _rand(seed, *shape, gain=1.0):
 
 
 # ---------------------------------------------------------------- brute force
-def _window_keys(i, mask, N, na2d):
+def _axis_cells(c, length, kernel, wrap, dil):
+    """Window cells of coordinate c along one axis, enumerated from offsets.
+
+    Wrapped: c + dil*t for t = -r..r, taken mod the length. Clamped: the list
+    of cells congruent to c mod dil, with a kernel-long window slid inside it
+    so that it stays whole at the ends.
+    """
+    r = kernel // 2
+    if wrap:
+        return [(c + dil * t) % length for t in range(-r, r + 1)]
+    sub = list(range(c % dil, length, dil))
+    i = sub.index(c)
+    s = min(max(i - r, 0), len(sub) - kernel)
+    return sub[s:s + kernel]
+
+
+def _window_keys(i, mask, N, na=None, n_kv=None):
     """Key indices visible to query i, enumerated directly (each once)."""
+    n_kv = N if n_kv is None else n_kv
     if mask == "none":
-        return list(range(N))
+        return list(range(n_kv))
     if mask == "causal":
-        return list(range(i + 1))
-    p = na2d
-    y, x = divmod(i, p.grid_w)
-    rh, rw = p.kernel_h // 2, p.kernel_w // 2
-    if p.wrap_h:
-        rows = [(y + dy) % p.grid_h for dy in range(-rh, rh + 1)]
-    else:
-        sy = min(max(y - rh, 0), p.grid_h - p.kernel_h)
-        rows = list(range(sy, sy + p.kernel_h))
-    if p.wrap_w:
-        cols = [(x + dx) % p.grid_w for dx in range(-rw, rw + 1)]
-    else:
-        sx = min(max(x - rw, 0), p.grid_w - p.kernel_w)
-        cols = list(range(sx, sx + p.kernel_w))
-    keys = sorted({r * p.grid_w + c for r in rows for c in cols})
-    assert len(keys) == p.kernel_h * p.kernel_w
+        return list(range(min(i + 1, n_kv)))
+    grid = na.grid()
+    coords = []
+    rest = i
+    for length in reversed(grid):
+        rest, c = divmod(rest, length)
+        coords.append(c)
+    coords.reverse()
+    cells = [_axis_cells(c, *ax) for c, ax in zip(coords, na.axes())]
+    keys = set()
+    for combo in itertools.product(*cells):
+        n = 0
+        for c, length in zip(combo, grid):
+            n = n * length + c
+        keys.add(n)
+    keys = sorted(keys)
+    assert len(keys) == math.prod(ax[1] for ax in na.axes())
     return keys
 
 
-def brute_head(q, k, v, scale, mask="none", na2d=None, subtract_max=False):
-    """One head by the textbook formula, in pure Python floats."""
+def brute_head(q, k, v, scale, mask="none", na=None, subtract_max=False, with_lse=False):
+    """One head by the textbook formula, in pure Python floats (lse = log of the plain sum)."""
     n_keys, d = len(k), len(q[0])
-    out = []
+    out, lse = [], []
     for i in range(len(q)):
-        keys = _window_keys(i, mask, n_keys, na2d)
+        keys = _window_keys(i, mask, len(q), na, n_keys)
         s = [scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
         ref = max(s) if subtract_max else 0.0
         w = [math.exp(x - ref) for x in s]
         den = math.fsum(w)
         out.append([math.fsum(w[a] * v[j][t] for a, j in enumerate(keys)) / den for t in range(d)])
-    return np.array(out)
+        lse.append(ref + math.log(den))
+    return (np.array(out), np.array(lse)) if with_lse else np.array(out)
 
 
-def _check_brute(mask, na2d, N, d, seed, scale, gain=1.0, subtract_max=False):
-    q, k, v = (_rand(seed + i, 1, 2, N, d, gain=gain if i == 0 else 1.0) for i in range(3))
-    got = O.attention(q, k, v, scale, mask, na2d)
+def _check_brute(mask, na, N, d, seed, scale, gain=1.0, subtract_max=False, n_kv=None):
+    n_kv = N if n_kv is None else n_kv
+    q = _rand(seed, 1, 2, N, d, gain=gain)
+    k, v = _rand(seed + 1, 1, 2, n_kv, d), _rand(seed + 2, 1, 2, n_kv, d)
+    got, got_lse = O.attention(q, k, v, scale, mask, na, return_lse=True)
     for h in range(2):
-        want = brute_head(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), scale, mask, na2d, subtract_max)
+        want, want_lse = brute_head(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), scale, mask, na,
+                                    subtract_max, with_lse=True)
         assert np.all(np.isfinite(got[0, h]))
         err = np.max(np.abs(got[0, h] - want))
-        assert err <= TIGHT, f"{mask} {na2d} brute-force mismatch {err}"
+        assert err <= TIGHT, f"{mask} {na} brute-force mismatch {err}"
+        err = np.max(np.abs(got_lse[0, h] - want_lse) / np.maximum(1.0, np.abs(want_lse)))
+        assert err <= TIGHT, f"{mask} {na} brute-force logsumexp mismatch {err}"
 
 
 # ---------------------------------------------------------------- pins
@@ -261,6 +294,212 @@ def pin_row_subset_matches_full():
         assert np.max(np.abs(part - full[:, :, rows])) <= TIGHT
 
 
+# ---------------------------------------------------------------- logsumexp
+def pin_logsumexp_uniform_is_log_count():
+    """scale = 0: every allowed score is 0, so the row's logsumexp is log(number of allowed keys)."""
+    d = 4
+    cases = (("none", None, 10, 10), ("causal", None, 10, 10), ("none", None, 6, 15), ("causal", None, 12, 5),
+             ("na2d", O.NA2D(4, 5, 3, 5, True, False), 20, 20),
+             ("na2d", O.NA2D(6, 7, 3, 3, False, True, 2, 2), 42, 42),
+             ("na3d", O.NA3D(3, 4, 5, 3, 3, 3, True, False, True), 60, 60))
+    for mask, na, nq, nkv in cases:
+        q, k, v = _rand(130, 1, 2, nq, d), _rand(131, 1, 2, nkv, d), _rand(132, 1, 2, nkv, d)
+        _, lse = O.attention(q, k, v, 0.0, mask, na, return_lse=True)
+        i = np.arange(nq)
+        if mask == "none":
+            count = np.full(nq, nkv)
+        elif mask == "causal":
+            count = np.minimum(i + 1, nkv)
+        else:
+            count = np.full(nq, math.prod(ax[1] for ax in na.axes()))
+        assert np.max(np.abs(lse - np.log(count)[None, None, :])) <= TIGHT, (mask, na)
+
+
+def pin_logsumexp_torch():
+    """torch.logsumexp over the masked float64 score matrix (window masks enumerated by brute force)."""
+    B, H, d = 1, 2, 8
+    cases = (("none", None, 24, 24, 1.0), ("causal", None, 24, 24, 1.0), ("causal", None, 9, 20, 1.0),
+             ("none", None, 16, 16, 64.0),
+             ("na2d", O.NA2D(4, 6, 3, 5, True, True), 24, 24, 1.0),
+             ("na3d", O.NA3D(2, 3, 4, 1, 3, 3, False, True, True), 24, 24, 1.0))
+    for mask, na, nq, nkv, gain in cases:
+        q = _rand(140, B, H, nq, d, gain=gain)
+        k, v = _rand(141, B, H, nkv, d), _rand(142, B, H, nkv, d)
+        _, lse = O.attention(q, k, v, 0.35, mask, na, return_lse=True)
+        allow = np.zeros((nq, nkv), dtype=bool)
+        for i in range(nq):
+            allow[i, _window_keys(i, mask, nq, na, nkv)] = True
+        s = torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2) * 0.35
+        s = s.masked_fill(~torch.from_numpy(allow), -math.inf)
+        want = torch.logsumexp(s, dim=-1).numpy()
+        assert np.all(np.isfinite(lse))
+        assert np.max(np.abs(lse - want) / np.maximum(1.0, np.abs(want))) <= TIGHT, (mask, na, gain)
+
+
+# ---------------------------------------------------------------- queries and keys of different lengths
+def pin_cross_attention_sdpa():
+    """Nq != Nkv against torch's SDPA math path in float64; its is_causal keeps key j <= query i."""
+    B, H, d = 2, 2, 8
+    F = torch.nn.functional.scaled_dot_product_attention
+    for nq, nkv in ((20, 13), (7, 30), (1, 9)):
+        q, k, v = _rand(150, B, H, nq, d), _rand(151, B, H, nkv, d), _rand(152, B, H, nkv, d)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+            for mask in ("none", "causal"):
+                ref = F(tq, tk, tv, is_causal=mask == "causal", scale=0.4).numpy()
+                assert np.max(np.abs(O.attention(q, k, v, 0.4, mask) - ref)) <= 1e-10, (nq, nkv, mask)
+
+
+def pin_cross_attention_uniform_and_brute():
+    """scale = 0 with Nq != Nkv: means of V over all keys, or over keys 0..min(i, Nkv-1) (causal)."""
+    B, H, d = 1, 2, 5
+    for nq, nkv in ((12, 5), (4, 11)):
+        q, k, v = _rand(160, B, H, nq, d), _rand(161, B, H, nkv, d), _rand(162, B, H, nkv, d)
+        out = O.attention(q, k, v, 0.0, "none")
+        assert np.max(np.abs(out - v.mean(axis=2, keepdims=True))) <= TIGHT
+        out = O.attention(q, k, v, 0.0, "causal")
+        prefix = np.cumsum(v, axis=2) / np.arange(1, nkv + 1)[None, None, :, None]
+        want = prefix[:, :, np.minimum(np.arange(nq), nkv - 1)]
+        assert np.max(np.abs(out - want)) <= TIGHT
+    _check_brute("none", None, 7, 4, 163, 0.5, n_kv=12)
+    _check_brute("causal", None, 12, 4, 164, 0.5, n_kv=5)
+
+
+# ---------------------------------------------------------------- dilation
+def _subgrid_attention(q, k, v, scale, grid, dils, make_na):
+    """Undilated neighbourhood attention run separately on each interleaved sub-grid
+    (cells with equal coordinates mod the dilations), scattered back."""
+    B, H, N, d = q.shape
+    coords = np.stack(np.unravel_index(np.arange(N), grid), axis=1)
+    out = np.full((B, H, N, d), np.nan)
+    for res in itertools.product(*(range(dl) for dl in dils)):
+        sel = np.flatnonzero(np.all(coords % np.array(dils) == np.array(res), axis=1))
+        sub_grid = tuple(len(range(r, g, dl)) for r, g, dl in zip(res, grid, dils))
+        assert math.prod(sub_grid) == sel.size
+        out[:, :, sel] = O.attention(q[:, :, sel], k[:, :, sel], v[:, :, sel], scale,
+                                     "na2d" if len(grid) == 2 else "na3d", make_na(sub_grid))
+    return out
+
+
+def pin_dilation_is_undilated_window_on_subgrids():
+    """A dilated window equals the undilated window inside each interleaved sub-grid
+    (clamped axes: any size with kernel * dilation <= L; wrapped axes: L divisible by the dilation)."""
+    B, H, d = 1, 2, 4
+    cases = ((7, 9, 3, 3, False, False, 2, 3), (8, 6, 3, 3, True, True, 2, 2), (12, 9, 3, 3, True, False, 4, 3),
+             (6, 10, 3, 5, False, True, 2, 2), (5, 12, 5, 3, False, True, 1, 4))
+    for gh, gw, kh, kw, wh, ww, dh, dw in cases:
+        N = gh * gw
+        q, k, v = _rand(170, B, H, N, d), _rand(171, B, H, N, d), _rand(172, B, H, N, d)
+        got = O.attention(q, k, v, 0.55, "na2d", O.NA2D(gh, gw, kh, kw, wh, ww, dh, dw))
+        want = _subgrid_attention(q, k, v, 0.55, (gh, gw), (dh, dw),
+                                  lambda sg: O.NA2D(sg[0], sg[1], kh, kw, wh, ww))
+        assert np.max(np.abs(got - want)) <= TIGHT, (gh, gw, kh, kw, wh, ww, dh, dw)
+    gd, gh, gw = 4, 6, 5
+    N = gd * gh * gw
+    q, k, v = _rand(173, B, H, N, d), _rand(174, B, H, N, d), _rand(175, B, H, N, d)
+    got = O.attention(q, k, v, 0.55, "na3d", O.NA3D(gd, gh, gw, 1, 3, 3, True, False, True, 2, 2, 1))
+    want = _subgrid_attention(q, k, v, 0.55, (gd, gh, gw), (2, 2, 1),
+                              lambda sg: O.NA3D(sg[0], sg[1], sg[2], 1, 3, 3, True, False, True))
+    assert np.max(np.abs(got - want)) <= TIGHT
+
+
+def _pad_crop(q, k, v, scale, grid, kernels, wraps, dils):
+    """NATTEN issue 142's recipe: pad the wrapped axes circularly by kernel//2 * dilation,
+    run the clamped (dilated) window on the padded grid, crop the output back."""
+    B, H, N, d = q.shape
+    pads = [(kk // 2) * dl if w else 0 for kk, w, dl in zip(kernels, wraps, dils)]
+    widths = ((0, 0), (0, 0)) + tuple((p, p) for p in pads) + ((0, 0),)
+    padded = tuple(g + 2 * p for g, p in zip(grid, pads))
+    pad = lambda t: np.pad(t.reshape(B, H, *grid, d), widths, mode="wrap").reshape(B, H, -1, d)
+    qp, kp, vp = (pad(t) for t in (q, k, v))
+    if len(grid) == 2:
+        na = O.NA2D(*padded, *kernels, False, False, *dils)
+        outp = O.attention(qp, kp, vp, scale, "na2d", na)
+    else:
+        na = O.NA3D(*padded, *kernels, False, False, False, *dils)
+        outp = O.attention(qp, kp, vp, scale, "na3d", na)
+    crop = tuple(slice(p, p + g) for p, g in zip(pads, grid))
+    return outp.reshape(B, H, *padded, d)[(slice(None), slice(None)) + crop].reshape(B, H, N, d)
+
+
+def pin_dilated_wrap_equals_pad_then_crop():
+    B, H, d = 1, 2, 4
+    for gh, gw, kh, kw, wh, ww, dh, dw in ((7, 8, 3, 3, True, True, 2, 3), (9, 5, 5, 3, True, False, 2, 1),
+                                           (6, 11, 3, 5, False, True, 2, 2)):
+        N = gh * gw
+        q, k, v = _rand(180, B, H, N, d), _rand(181, B, H, N, d), _rand(182, B, H, N, d)
+        got = O.attention(q, k, v, 0.6, "na2d", O.NA2D(gh, gw, kh, kw, wh, ww, dh, dw))
+        want = _pad_crop(q, k, v, 0.6, (gh, gw), (kh, kw), (wh, ww), (dh, dw))
+        assert np.max(np.abs(got - want)) <= TIGHT, (gh, gw, kh, kw, wh, ww, dh, dw)
+
+
+# ---------------------------------------------------------------- 3D neighbourhoods
+def pin_na3d_depth_one_is_na2d():
+    B, H, d, gh, gw = 1, 2, 4, 5, 6
+    N = gh * gw
+    q, k, v = _rand(190, B, H, N, d), _rand(191, B, H, N, d), _rand(192, B, H, N, d)
+    for kh, kw, wh, ww, dh, dw in ((3, 5, True, False, 1, 1), (3, 3, False, True, 1, 2)):
+        a = O.attention(q, k, v, 0.45, "na2d", O.NA2D(gh, gw, kh, kw, wh, ww, dh, dw))
+        for wd in (True, False):
+            b = O.attention(q, k, v, 0.45, "na3d", O.NA3D(1, gh, gw, 1, kh, kw, wd, wh, ww, 1, dh, dw))
+            assert np.max(np.abs(a - b)) <= TIGHT
+
+
+def pin_na3d_brute_force():
+    _check_brute("na3d", O.NA3D(3, 3, 4, 3, 3, 3, True, True, True), 36, 4, 200, 0.5)
+    _check_brute("na3d", O.NA3D(4, 3, 3, 3, 1, 3, False, True, False), 36, 4, 201, 0.5)
+    _check_brute("na3d", O.NA3D(5, 2, 4, 3, 1, 3, True, False, True, 2, 1, 1), 40, 3, 202, 0.7)
+    _check_brute("na2d", O.NA2D(7, 6, 3, 3, True, False, 2, 2), 42, 3, 203, 0.7)
+
+
+def pin_na3d_uniform_box_filter():
+    """scale = 0, every axis wrapped: the mean of V over the (dilated) window, as a sum of array shifts."""
+    B, H, d = 1, 2, 3
+    gd, gh, gw = 4, 5, 6
+    N = gd * gh * gw
+    q, k, v = _rand(210, B, H, N, d), _rand(211, B, H, N, d), _rand(212, B, H, N, d)
+    for (kd, kh, kw), (dd, dh, dw) in (((3, 3, 5), (1, 1, 1)), ((3, 1, 3), (1, 1, 2)), ((1, 3, 3), (1, 2, 1))):
+        out = O.attention(q, k, v, 0.0, "na3d", O.NA3D(gd, gh, gw, kd, kh, kw, True, True, True, dd, dh, dw))
+        vg = v.reshape(B, H, gd, gh, gw, d)
+        box = sum(np.roll(vg, shift=(-a * dd, -b * dh, -c * dw), axis=(2, 3, 4))
+                  for a in range(-(kd // 2), kd // 2 + 1)
+                  for b in range(-(kh // 2), kh // 2 + 1)
+                  for c in range(-(kw // 2), kw // 2 + 1)) / (kd * kh * kw)
+        assert np.max(np.abs(out - box.reshape(B, H, N, d))) <= TIGHT
+
+
+def pin_na3d_translation_and_pad_crop():
+    B, H, d = 1, 2, 4
+    gd, gh, gw = 4, 5, 6
+    N = gd * gh * gw
+    q, k, v = _rand(220, B, H, N, d), _rand(221, B, H, N, d), _rand(222, B, H, N, d)
+    p = O.NA3D(gd, gh, gw, 3, 3, 5, True, True, True)
+    base = O.attention(q, k, v, 0.5, "na3d", p)
+    roll = lambda t: np.roll(t.reshape(B, H, gd, gh, gw, d), shift=(1, -2, 3), axis=(2, 3, 4)).reshape(B, H, N, d)
+    moved = O.attention(roll(q), roll(k), roll(v), 0.5, "na3d", p)
+    assert np.max(np.abs(moved - roll(base))) <= TIGHT
+    for kernels, wraps, dils in (((3, 3, 5), (True, True, True), (1, 1, 1)),
+                                 ((3, 3, 3), (True, False, True), (1, 1, 2)),
+                                 ((1, 3, 3), (False, True, True), (1, 2, 1))):
+        got = O.attention(q, k, v, 0.5, "na3d", O.NA3D(gd, gh, gw, *kernels, *wraps, *dils))
+        want = _pad_crop(q, k, v, 0.5, (gd, gh, gw), kernels, wraps, dils)
+        assert np.max(np.abs(got - want)) <= TIGHT, (kernels, wraps, dils)
+
+
+def pin_na3d_sdpa():
+    B, H, d = 1, 2, 8
+    p = O.NA3D(3, 4, 5, 3, 3, 3, True, False, True, 1, 1, 2)
+    N = 60
+    q, k, v = _rand(230, B, H, N, d), _rand(231, B, H, N, d), _rand(232, B, H, N, d)
+    m = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        m[i, _window_keys(i, "na3d", N, p)] = True
+    F = torch.nn.functional.scaled_dot_product_attention
+    with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+        ref = F(*(torch.from_numpy(x) for x in (q, k, v)), attn_mask=torch.from_numpy(m), scale=0.35).numpy()
+    assert np.max(np.abs(O.attention(q, k, v, 0.35, "na3d", p) - ref)) <= 1e-10
+
+
 ALL_PINS = [
     pin_wrap_5x5_example,
     pin_probability_rows_sum_to_one,
@@ -275,4 +514,15 @@ ALL_PINS = [
     pin_stability_large_scores,
     pin_fully_masked_row_gives_zero,
     pin_row_subset_matches_full,
+    pin_logsumexp_uniform_is_log_count,
+    pin_logsumexp_torch,
+    pin_cross_attention_sdpa,
+    pin_cross_attention_uniform_and_brute,
+    pin_dilation_is_undilated_window_on_subgrids,
+    pin_dilated_wrap_equals_pad_then_crop,
+    pin_na3d_depth_one_is_na2d,
+    pin_na3d_brute_force,
+    pin_na3d_uniform_box_filter,
+    pin_na3d_translation_and_pad_crop,
+    pin_na3d_sdpa,
 ]
