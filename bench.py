@@ -1,18 +1,19 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--entry E] [--lse] [--no-cpu]
 
 One step is one launch of the fused forward over one batch of the workload
 (default: SD2.1 512x512 UNet self-attention, B2 H5 N4096 d64, no mask),
 through attn_fwd_ws (keys split evenly over the resident work-groups when
-that balances the chip; --entry attn_fwd for one work-group per query tile).
-Inputs and the workspace are resident in HBM before timing starts. Prints one
-JSON line on stdout.
+that balances the chip; --entry attn_fwd for one work-group per query tile;
+attn_fwd_ex, the default for cross-attention, also writes the logsumexp with
+--lse). Inputs and the workspace are resident in HBM before timing starts.
+Prints one JSON line on stdout.
 
-FLOP accounting (the metric of the workload): 4 N^2 d per head without a
-mask, half of that with the causal mask, 4 N (kh kw) d per head for 2D
+FLOP accounting (the metric of the workload): 4 Nq Nkv d per head without a
+mask, half of 4 N^2 d with the causal mask, 4 N (window cells) d per head for
 neighbourhood attention (the window-sized work). Algorithmic bytes: q, k, v
-read once and o written once, 2 bytes per element.
+read once and o (and the float32 logsumexp, if asked for) written once.
 """
 from __future__ import annotations
 
@@ -36,16 +37,21 @@ PEAK_HBM_GBS = 8000.0
 
 
 def flops(w: workloads.Workload) -> float:
-    per_head = 4.0 * w.N * w.N * w.d
+    per_head = 4.0 * w.N * w.n_kv * w.d
     if w.mask == "causal":
+        assert w.n_kv == w.N, "causal metric defined for self-attention"
         per_head /= 2
-    elif w.mask == "na2d":
-        per_head = 4.0 * w.N * w.na2d["kernel_h"] * w.na2d["kernel_w"] * w.d
+    elif w.mask in ("na2d", "na3d"):
+        cells = w.na.get("kernel_d", 1) * w.na["kernel_h"] * w.na["kernel_w"]
+        per_head = 4.0 * w.N * cells * w.d
     return per_head * w.B * w.H
 
 
-def algorithmic_bytes(w: workloads.Workload) -> float:
-    return 4.0 * w.B * w.H * w.N * w.d * 2
+def algorithmic_bytes(w: workloads.Workload, lse: bool = False) -> float:
+    return w.B * w.H * (2.0 * (w.N + w.n_kv) * w.d * 2 + (4.0 * w.N if lse else 0.0))
+
+
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
@@ -73,7 +79,16 @@ def recorded_traffic(name: str):
 
 
 def mask_mode(A, w):
-    return {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D}[w.mask]
+    return {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D,
+            "na3d": A.ATTN_MASK_NA3D}[w.mask]
+
+
+def window_params(A, w):
+    if w.mask == "na2d":
+        return A.na2d_params(**w.na)
+    if w.mask == "na3d":
+        return A.na3d_params(**w.na)
+    return None
 
 
 def cpu_baseline(w: workloads.Workload, q, k, v, budget_s: float = 12.0) -> dict:
@@ -87,7 +102,10 @@ def cpu_baseline(w: workloads.Workload, q, k, v, budget_s: float = 12.0) -> dict
     except Exception:  # threadpoolctl missing or unable to inspect
         threads = os.cpu_count() or 1
     qf, kf, vf = (t.float().numpy() for t in (q, k, v))
-    na = oracle.NA2D(**{kk: (bool(vv) if kk.startswith("wrap") else vv) for kk, vv in w.na2d.items()}) if w.na2d else None
+    na = None
+    if w.na:
+        kind = oracle.NA3D if w.mask == "na3d" else oracle.NA2D
+        na = kind(**{kk: (bool(vv) if kk.startswith("wrap") else vv) for kk, vv in w.na.items()})
     heads = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
@@ -117,7 +135,9 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--entry", default="attn_fwd_ws", choices=["attn_fwd_ws", "attn_fwd"])
+    ap.add_argument("--entry", default=None, choices=["attn_fwd_ws", "attn_fwd", "attn_fwd_ex"],
+                    help="C entry point (default attn_fwd_ws, attn_fwd_ex for cross-attention)")
+    ap.add_argument("--lse", action="store_true", help="attn_fwd_ex also writes the logsumexp")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for traffic counters)")
@@ -133,22 +153,28 @@ def main():
     import exact_attention_68_amd as A
 
     w = workloads.WORKLOADS[args.workload]
+    entry = args.entry or ("attn_fwd_ex" if (w.n_kv != w.N or args.lse) else "attn_fwd_ws")
+    if entry != "attn_fwd_ex" and (w.n_kv != w.N or args.lse):
+        ap.error("cross-attention and --lse need --entry attn_fwd_ex")
     q, k, v = workloads.workload_qkv(w)
     dev = torch.device("cuda:0")
     dq, dk, dv = (t.to(dev) for t in (q, k, v))
     do = torch.empty_like(dq)
-    params = A.na2d_params(**w.na2d) if w.mask == "na2d" else None
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev) if args.lse else None
+    params = window_params(A, w)
     mode = mask_mode(A, w)
     stream = torch.cuda.current_stream(dev)
 
     ws = None
-    if args.entry == "attn_fwd_ws":
-        nbytes = A.attn_fwd_workspace_size(w.B, w.H, w.N, w.d, mode, params)
+    if entry != "attn_fwd":
+        nbytes = A.attn_fwd_ex_workspace_size(w.B, w.H, w.N, w.n_kv, w.d, mode, params)
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
 
     def step():
-        if args.entry == "attn_fwd_ws":
+        if entry == "attn_fwd_ws":
             A.attn_fwd_ws(dq, dk, dv, do, w.scale, mode, params, ws, stream.cuda_stream)
+        elif entry == "attn_fwd_ex":
+            A.attn_fwd_ex(dq, dk, dv, do, lse, w.scale, mode, params, ws, stream.cuda_stream)
         else:
             A.attn_fwd(dq, dk, dv, do, w.scale, mode, params, stream.cuda_stream)
 
@@ -171,8 +197,9 @@ def main():
     F = flops(w)
     value = F * args.steps / wall / 1e12
     achieved = F / (kernel_ms * 1e-3) / 1e12
-    nbytes = algorithmic_bytes(w)
-    if w.mask == "na2d":
+    nbytes = algorithmic_bytes(w, args.lse)
+    # neighbourhood windows and short key sequences sit below the ridge of the roofline: HBM-bound
+    if w.mask in ("na2d", "na3d") or F / nbytes < RIDGE_FLOP_PER_BYTE:
         roof = {"bound": "hbm", "achieved": nbytes / (kernel_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
@@ -182,7 +209,7 @@ def main():
     roof["kernels"] = (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
                        else f"attn_fwd_kernel<{w.d},{w.mask}>")
     roof["traffic"] = (sum(args.traffic_kib) * 1024.0 if args.traffic_kib
-                       else recorded_traffic(f"{w.name}:{args.entry}"))
+                       else recorded_traffic(f"{w.name}:{entry}{':lse' if args.lse else ''}"))
 
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
@@ -191,8 +218,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "kernel_us": kernel_ms * 1e3,
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
-                   "scale": w.scale, **({"na2d": w.na2d} if w.na2d else {}), "entry": args.entry,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nkv": w.n_kv, "d": w.d, "mask": w.mask,
+                   "scale": w.scale, **({"window": w.na} if w.na else {}), "entry": entry, "lse": args.lse,
                    "workspace_bytes": 0 if ws is None else ws.numel()},
         "roofline": roof,
     }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 ATTN_MASK_NONE = 0
 ATTN_MASK_CAUSAL = 1
 ATTN_MASK_NA2D = 2
+ATTN_MASK_NA3D = 3
 
 ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = 1
@@ -41,6 +42,20 @@ def na2d_params(grid_h, grid_w, kernel_h, kernel_w, wrap_h=1, wrap_w=1, dil_h=1,
     return attn_na2d_params_t(grid_h, grid_w, kernel_h, kernel_w, int(wrap_h), int(wrap_w), dil_h, dil_w)
 
 
+class attn_na3d_params_t(ctypes.Structure):
+    """Mirror of the C struct: 3D neighbourhood window over a row-major volume."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("grid_d", "grid_h", "grid_w", "kernel_d", "kernel_h", "kernel_w",
+                 "wrap_d", "wrap_h", "wrap_w", "dil_d", "dil_h", "dil_w")]
+
+
+def na3d_params(grid_d, grid_h, grid_w, kernel_d, kernel_h, kernel_w, wrap_d=1, wrap_h=1, wrap_w=1,
+                dil_d=1, dil_h=1, dil_w=1) -> attn_na3d_params_t:
+    return attn_na3d_params_t(grid_d, grid_h, grid_w, kernel_d, kernel_h, kernel_w,
+                              int(wrap_d), int(wrap_h), int(wrap_w), dil_d, dil_h, dil_w)
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
@@ -60,6 +75,12 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd_workspace_size.restype = i32
     lib.attn_fwd_check.argtypes = [i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_check.restype = i32
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, vp, vp, ctypes.c_uint64, vp]
+    lib.attn_fwd_ex.restype = i32
+    lib.attn_fwd_ex_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, vp, ctypes.POINTER(ctypes.c_uint64)]
+    lib.attn_fwd_ex_workspace_size.restype = i32
+    lib.attn_fwd_ex_check.argtypes = [i64, i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_fwd_ex_check.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -81,8 +102,8 @@ def lib() -> ctypes.CDLL:
 def _params_ptr(params):
     if params is None:
         return None
-    if not isinstance(params, attn_na2d_params_t):
-        raise TypeError("params must be an attn_na2d_params_t (see na2d_params)")
+    if not isinstance(params, (attn_na2d_params_t, attn_na3d_params_t)):
+        raise TypeError("params must be an attn_na2d_params_t or attn_na3d_params_t (see na2d_params, na3d_params)")
     return ctypes.cast(ctypes.pointer(params), ctypes.c_void_p)
 
 
@@ -99,7 +120,8 @@ def attn_fwd_check(B, H, N, d, scale, mask_mode=ATTN_MASK_NONE, params=None) -> 
     return int(lib().attn_fwd_check(B, H, N, d, scale, mask_mode, _params_ptr(params)))
 
 
-def _check_tensors(q, k, v, o):
+def _check_tensors(q, k, v, o, same_n=True):
+    """Shapes [B, H, Nq, d] for q and o and [B, H, Nkv, d] for k and v (Nq = Nkv when same_n)."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
@@ -107,9 +129,13 @@ def _check_tensors(q, k, v, o):
             raise TypeError(f"{name} must be a bfloat16 CUDA tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-        if t.dim() != 4 or t.shape != q.shape:
-            raise ValueError("q, k, v and o must share one [B, H, N, d] shape")
-    return q.shape
+        if t.dim() != 4:
+            raise ValueError(f"{name} must have four dimensions [B, H, N, d]")
+    if o.shape != q.shape or v.shape != k.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q and o must be [B, H, Nq, d] and k, v [B, H, Nkv, d]")
+    if same_n and k.shape != q.shape:
+        raise ValueError("q, k, v and o must share one [B, H, N, d] shape")
+    return q.shape[0], q.shape[1], q.shape[2], k.shape[2], q.shape[3]
 
 
 def _stream_handle(stream, device):
@@ -126,7 +152,7 @@ def attn_fwd(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, stream=No
     q, k, v, o: torch bfloat16 CUDA tensors, contiguous, one [B, H, N, d] shape.
     Raises AttnError with the library's status on any rejected argument.
     """
-    B, H, N, d = _check_tensors(q, k, v, o)
+    B, H, N, _, d = _check_tensors(q, k, v, o)
     rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, d,
                         float(scale), int(mask_mode), _params_ptr(params), _stream_handle(stream, q.device))
     if rc != ATTN_OK:
@@ -145,7 +171,7 @@ def attn_fwd_workspace_size(B, H, N, d, mask_mode=ATTN_MASK_NONE, params=None) -
 def attn_fwd_ws(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, workspace=None, stream=None) -> None:
     """attn_fwd with a device workspace (a uint8 CUDA tensor of at least attn_fwd_workspace_size
     bytes, any content, or None when that size is 0); see include/attn.h."""
-    B, H, N, d = _check_tensors(q, k, v, o)
+    B, H, N, _, d = _check_tensors(q, k, v, o)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -153,6 +179,45 @@ def attn_fwd_ws(q, k, v, o, scale, mask_mode=ATTN_MASK_NONE, params=None, worksp
                            int(mask_mode), _params_ptr(params), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_fwd_ws")
+
+
+def attn_fwd_ex_check(B, H, Nq, Nkv, d, scale, mask_mode=ATTN_MASK_NONE, params=None) -> int:
+    """Status attn_fwd_ex would return for these sizes and options (no device work)."""
+    return int(lib().attn_fwd_ex_check(B, H, Nq, Nkv, d, scale, mask_mode, _params_ptr(params)))
+
+
+def attn_fwd_ex_workspace_size(B, H, Nq, Nkv, d, mask_mode=ATTN_MASK_NONE, params=None) -> int:
+    """Bytes of workspace attn_fwd_ex needs for this problem on the current device (0: none)."""
+    out = ctypes.c_uint64(0)
+    rc = lib().attn_fwd_ex_workspace_size(B, H, Nq, Nkv, d, int(mask_mode), _params_ptr(params), ctypes.byref(out))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_ex_workspace_size")
+    return int(out.value)
+
+
+def attn_fwd_ex(q, k, v, o, lse=None, scale=1.0, mask_mode=ATTN_MASK_NONE, params=None, workspace=None,
+                stream=None) -> None:
+    """o <- softmax(scale * q k^T + mask) v with q, o [B, H, Nq, d] and k, v [B, H, Nkv, d];
+    lse, if given (a float32 CUDA tensor [B, H, Nq], contiguous), receives each row's logsumexp.
+    See include/attn.h."""
+    import torch
+
+    B, H, Nq, Nkv, d = _check_tensors(q, k, v, o, same_n=False)
+    lse_ptr = None
+    if lse is not None:
+        if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda:
+            raise TypeError("lse must be a float32 CUDA tensor")
+        if not lse.is_contiguous() or tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be a contiguous [B, H, Nq] tensor")
+        lse_ptr = lse.data_ptr()
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = lib().attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr, B, H, Nq, Nkv, d,
+                           float(scale), int(mask_mode), _params_ptr(params), ws_ptr, ws_bytes,
+                           _stream_handle(stream, q.device))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_ex")
 
 
 _workspaces: dict = {}
@@ -178,28 +243,35 @@ def workspace(nbytes: int, device=None, stream=None):
     return ws
 
 
-def attention(q, k, v, scale=None, causal=False, na2d=None, stream=None):
-    """Allocate the output and run attn_fwd_ws with a cached workspace. scale defaults to 1/sqrt(d).
+def attention(q, k, v, scale=None, causal=False, na=None, stream=None, return_lse=False):
+    """Allocate the output (and the logsumexp when return_lse) and run attn_fwd_ex with a cached
+    workspace. q is [B, H, Nq, d], k and v [B, H, Nkv, d]; scale defaults to 1/sqrt(d).
 
-    na2d: an attn_na2d_params_t for 2D neighbourhood attention.
+    na: an attn_na2d_params_t or attn_na3d_params_t for a neighbourhood window.
     """
     import torch
 
-    if causal and na2d is not None:
-        raise ValueError("choose causal or na2d, not both")
+    if causal and na is not None:
+        raise ValueError("choose causal or a neighbourhood window, not both")
     o = torch.empty_like(q)
-    mode = ATTN_MASK_NA2D if na2d is not None else (ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE)
+    if na is None:
+        mode = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
+    else:
+        mode = ATTN_MASK_NA3D if isinstance(na, attn_na3d_params_t) else ATTN_MASK_NA2D
     s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
-    B, H, N, d = q.shape
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
         ts = torch.cuda.current_stream(q.device) if stream is None else torch.cuda.ExternalStream(stream)
-        ws = workspace(attn_fwd_workspace_size(B, H, N, d, mode, na2d), q.device, ts)
-        attn_fwd_ws(q, k, v, o, s, mode, na2d, ws, ts.cuda_stream)
-    return o
+        ws = workspace(attn_fwd_ex_workspace_size(B, H, Nq, Nkv, d, mode, na), q.device, ts)
+        attn_fwd_ex(q, k, v, o, lse, s, mode, na, ws, ts.cuda_stream)
+    return (o, lse) if return_lse else o
 
 
 __all__ = [
-    "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "ATTN_MASK_NA2D",
+    "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "ATTN_MASK_NA2D", "ATTN_MASK_NA3D", "attn_na3d_params_t", "na3d_params",
+    "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_PARAMS", "ATTN_ERR_ALIGNMENT",
     "ATTN_ERR_HIP", "ATTN_ERR_WORKSPACE", "AttnError", "attn_na2d_params_t", "na2d_params",
     "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "workspace", "attn_fwd_check", "attn_status_string",

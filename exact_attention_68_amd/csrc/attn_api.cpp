@@ -10,15 +10,6 @@
 #include "tile_plan.hpp"
 #include "validate.hpp"
 
-extern "C" {
-
-attn_status_t attn_fwd_check(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int32_t mask_mode,
-                             const void* params) {
-  return attn::check_problem(B, H, N, d, scale, mask_mode, params);
-}
-
-}  // extern "C"
-
 namespace {
 
 // CU count of the current device, cached per device.
@@ -42,31 +33,43 @@ attn_status_t device_cus(int32_t* cus) {
   return ATTN_OK;
 }
 
-attn::SplitPlan plan_for(int64_t B, int64_t H, int64_t N, int32_t mask_mode, int32_t cus) {
-  const int64_t n_tiles = B * H * attn::cdiv(N, attn::kBlockM);
-  return attn::split_plan(mask_mode, n_tiles, (int32_t)attn::cdiv(N, attn::tile_keys()), cus);
+attn::SplitPlan plan_for(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int32_t mask_mode, int32_t cus) {
+  const int64_t n_tiles = B * H * attn::cdiv(Nq, attn::kBlockM);
+  return attn::split_plan(mask_mode, n_tiles, (int32_t)attn::cdiv(Nkv, attn::tile_keys(d)), cus);
 }
 
-attn_status_t run_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N, int64_t d,
-                      float scale, int32_t mask_mode, const void* params, const attn::SplitPlan* split,
-                      void* workspace, void* stream) {
+// Kernel mask kind for a checked problem: the block-masked neighbourhood kernel
+// for undilated 2D windows on grids of width 32, 64, 96 or 128.
+int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
+  if (p.mask == ATTN_MASK_NONE) return attn::MASK_NONE;
+  if (p.mask == ATTN_MASK_CAUSAL) return attn::MASK_CAUSAL;
+  const bool blocks = g.grid_d == 1 && g.dil_h == 1 && g.dil_w == 1 && g.grid_w % 32 == 0 && g.grid_w <= 128;
+  return blocks ? attn::MASK_NA_BLOCKS : attn::MASK_NA;
+}
+
+attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void* workspace, void* stream) {
   attn::KernelArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.N = (int32_t)N;
-  a.BH = (int32_t)(B * H);
-  a.n_qtiles = (int32_t)attn::cdiv(N, attn::kBlockM);
-  a.n_kvtiles = (int32_t)attn::cdiv(N, attn::tile_keys());
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.o = static_cast<uint16_t*>(p.o);
+  a.lse = p.lse;
+  a.Nq = (int32_t)p.Nq;
+  a.Nkv = (int32_t)p.Nkv;
+  a.BH = (int32_t)(p.B * p.H);
+  a.n_qtiles = (int32_t)attn::cdiv(p.Nq, attn::kBlockM);
+  a.n_kvtiles = (int32_t)attn::cdiv(p.Nkv, attn::tile_keys(p.d));
   // exp(x) = 2^(x log2 e): the kernel works in base 2 with the scale folded in
-  a.c = (float)(fabs((double)scale) * 1.4426950408889634);
-  a.q_sign = scale < 0.f ? 0x80008000u : 0u;
-  if (mask_mode == ATTN_MASK_NA2D) {
-    a.na = attn::na_geom(*static_cast<const attn_na2d_params_t*>(params));
+  a.c = (float)(fabs((double)p.scale) * 1.4426950408889634);
+  a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
+  int32_t mask = attn::MASK_NONE;
+  if (attn::is_na_mode(p.mask)) {
+    a.na = attn::na_geom(p.mask, p.params);
     a.na_inv_w = 1.0f / (float)a.na.grid_w;
-    a.na_phases = (a.na.grid_w % 32 == 0 && a.na.grid_w <= 128) ? a.na.grid_w / 32 : 0;
+    a.na_inv_h = 1.0f / (float)a.na.grid_h;
   }
+  mask = kernel_mask(p, a.na);
+  a.na_phases = mask == attn::MASK_NA_BLOCKS ? a.na.grid_w / 32 : 0;
   int32_t n_wg = a.BH * a.n_qtiles, rem = 0;
   if (split != nullptr && split->rem > 0) {
     a.ws_parts = static_cast<float*>(workspace);
@@ -75,66 +78,102 @@ attn_status_t run_fwd(const void* q, const void* k, const void* v, void* o, int6
     n_wg = split->groups();
     rem = split->rem;
   }
-  const hipError_t e = attn::launch_fwd(a, (int32_t)d, mask_mode, n_wg, rem, static_cast<hipStream_t>(stream));
+  const hipError_t e = attn::launch_fwd(a, (int32_t)p.d, mask, n_wg, rem, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// The shared body of attn_fwd_ws and attn_fwd_ex.
+attn_status_t run_with_workspace(const attn::Problem& p, void* workspace, uint64_t workspace_bytes, void* stream) {
+  attn_status_t st = attn::check_problem(p);
+  if (st != ATTN_OK) return st;
+  st = attn::check_pointers(p);
+  if (st != ATTN_OK) return st;
+  int32_t cus = 0;
+  st = device_cus(&cus);
+  if (st != ATTN_OK) return st;
+  const attn::SplitPlan plan = plan_for(p.B, p.H, p.Nq, p.Nkv, p.d, p.mask, cus);
+  const int64_t need = attn::split_workspace_bytes(plan, p.d);
+  if (need > 0) {
+    st = attn::check_workspace(workspace, workspace_bytes, need, p);
+    if (st != ATTN_OK) return st;
+  }
+  return run_fwd(p, &plan, workspace, stream);
+}
+
+attn_status_t workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int32_t mask_mode,
+                             const void* params, uint64_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  attn_status_t st = attn::check_problem(B, H, Nq, Nkv, d, 1.0f, mask_mode, params);
+  if (st != ATTN_OK) return st;
+  int32_t cus = 0;
+  st = device_cus(&cus);
+  if (st != ATTN_OK) return st;
+  *bytes = (uint64_t)attn::split_workspace_bytes(plan_for(B, H, Nq, Nkv, d, mask_mode, cus), d);
+  return ATTN_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
+attn_status_t attn_fwd_check(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int32_t mask_mode,
+                             const void* params) {
+  return attn::check_problem(B, H, N, N, d, scale, mask_mode, params);
+}
+
+attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
+                                int32_t mask_mode, const void* params) {
+  return attn::check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
+}
+
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
                        int64_t d, float scale, int32_t mask_mode, const void* params, void* stream) {
-  attn_status_t st = attn::check_problem(B, H, N, d, scale, mask_mode, params);
+  const attn::Problem p{q, k, v, o, nullptr, B, H, N, N, d, scale, mask_mode, params};
+  attn_status_t st = attn::check_problem(p);
   if (st != ATTN_OK) return st;
-  st = attn::check_pointers(q, k, v, o, B, H, N, d);
+  st = attn::check_pointers(p);
   if (st != ATTN_OK) return st;
-  return run_fwd(q, k, v, o, B, H, N, d, scale, mask_mode, params, nullptr, nullptr, stream);
+  return run_fwd(p, nullptr, nullptr, stream);
 }
 
 attn_status_t attn_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int32_t mask_mode,
                                       const void* params, uint64_t* bytes) {
-  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
-  attn_status_t st = attn::check_problem(B, H, N, d, 1.0f, mask_mode, params);
-  if (st != ATTN_OK) return st;
-  int32_t cus = 0;
-  st = device_cus(&cus);
-  if (st != ATTN_OK) return st;
-  *bytes = (uint64_t)attn::split_workspace_bytes(plan_for(B, H, N, mask_mode, cus), d);
-  return ATTN_OK;
+  return workspace_size(B, H, N, N, d, mask_mode, params, bytes);
+}
+
+attn_status_t attn_fwd_ex_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
+                                         int32_t mask_mode, const void* params, uint64_t* bytes) {
+  return workspace_size(B, H, Nq, Nkv, d, mask_mode, params, bytes);
 }
 
 attn_status_t attn_fwd_ws(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H, int64_t N,
                           int64_t d, float scale, int32_t mask_mode, const void* params, void* workspace,
                           uint64_t workspace_bytes, void* stream) {
-  attn_status_t st = attn::check_problem(B, H, N, d, scale, mask_mode, params);
-  if (st != ATTN_OK) return st;
-  st = attn::check_pointers(q, k, v, o, B, H, N, d);
-  if (st != ATTN_OK) return st;
-  int32_t cus = 0;
-  st = device_cus(&cus);
-  if (st != ATTN_OK) return st;
-  const attn::SplitPlan plan = plan_for(B, H, N, mask_mode, cus);
-  const int64_t need = attn::split_workspace_bytes(plan, d);
-  if (need > 0) {
-    st = attn::check_workspace(workspace, workspace_bytes, need, q, k, v, o, B, H, N, d);
-    if (st != ATTN_OK) return st;
-  }
-  return run_fwd(q, k, v, o, B, H, N, d, scale, mask_mode, params, &plan, workspace, stream);
+  const attn::Problem p{q, k, v, o, nullptr, B, H, N, N, d, scale, mask_mode, params};
+  return run_with_workspace(p, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                          int64_t Nq, int64_t Nkv, int64_t d, float scale, int32_t mask_mode, const void* params,
+                          void* workspace, uint64_t workspace_bytes, void* stream) {
+  const attn::Problem p{q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask_mode, params};
+  return run_with_workspace(p, workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_string(int32_t status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, non-finite scale, "
-                                      "unknown mask mode, misplaced params, or output overlapping an input)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32 or 64; sizes must fit 32-bit "
-                                      "launch geometry)";
-    case ATTN_ERR_PARAMS: return "inconsistent 2D neighbourhood parameters (grid_h*grid_w must equal N; "
-                                 "kernels odd and within the grid; wrap 0 or 1; dilation 1)";
-    case ATTN_ERR_ALIGNMENT: return "q, k, v and o must be 16-byte aligned";
+                                      "unknown mask mode, misplaced params, or an output overlapping an input "
+                                      "or the other output)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128; sizes must fit "
+                                      "32-bit launch geometry)";
+    case ATTN_ERR_PARAMS: return "inconsistent neighbourhood parameters (grid size must equal Nq and Nkv; "
+                                 "kernels odd; wrap 0 or 1; dilation >= 1; (kernel-1)*dilation < size when "
+                                 "wrapped, kernel*dilation <= size when clamped)";
+    case ATTN_ERR_ALIGNMENT: return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_HIP: return "HIP runtime error (no device, or a failed query or launch)";
-    case ATTN_ERR_WORKSPACE: return "workspace missing, too small, not 256-byte aligned, or overlapping q, k, v or o";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, too small, not 256-byte aligned, or overlapping a tensor";
     default: return "unknown status";
   }
 }

@@ -10,8 +10,8 @@
 //
 // Work decomposition: one work-group = 4 wavefronts = one tile of 128
 // queries of one head; each wavefront owns 32 queries. Key/value tiles of
-// 128 tokens stream through LDS rings (2 tiles deep at d = 64, 4 at d = 32)
-// shared by the 4 wavefronts; later tiles' global loads are in flight while
+// 128 tokens (64 at d = 128) stream through LDS rings (2 tiles deep at d = 64
+// and 128, 4 at d = 32) shared by the 4 wavefronts; later tiles' global loads are in flight while
 // the current tile is computed. An unmasked launch may instead run a round of
 // whole tiles plus key-range parts of the remaining tiles, merged by a second
 // small kernel (remainder split, tile_plan.hpp).
@@ -71,7 +71,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 template <int D>
 struct Cfg {
   static constexpr int BM = 128;     // queries per work-group (4 wavefronts x 32)
-  static constexpr int BN = 128;     // keys per tile
+  static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile (16 KB of K or V at d = 64 and 128)
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROW_CHUNKS = D / 8;                     // 16-byte chunks per K or V row
@@ -88,7 +88,10 @@ struct Cfg {
   static constexpr int LOADS_AHEAD = (STAGES - 2) * 2 * LOADS;
 };
 
-static_assert(Cfg<64>::BM == kBlockM && Cfg<32>::BM == kBlockM, "launch geometry and kernel tile must agree");
+static_assert(Cfg<128>::BM == kBlockM && Cfg<64>::BM == kBlockM && Cfg<32>::BM == kBlockM,
+              "launch geometry and kernel tile must agree");
+static_assert(Cfg<128>::BN == tile_keys(128) && Cfg<64>::BN == tile_keys(64) && Cfg<32>::BN == tile_keys(32),
+              "host tile counts and kernel tiles must agree");
 
 // Rows live unpadded in LDS; the 16-byte chunks of a row are permuted by an XOR
 // with a function of the row so that both read patterns are free of bank
@@ -99,10 +102,15 @@ static_assert(Cfg<64>::BM == kBlockM && Cfg<32>::BM == kBlockM, "launch geometry
 //  * the transposing V read takes 8 bytes per lane, 4 consecutive rows x 4
 //    chunks per half-wave: rows r and r+2 must fall in opposite halves of the
 //    8 chunk slots.
+// d = 128 (16 chunks per row, a row spans every bank): the 16 rows of one K read
+// need 16 different slots, and the 4 rows of one transposing V read (4 chunks
+// each) need 4 different slot quarters: row r uses slot c ^ ((r & 3) << 2 | (r >> 2) & 3).
 // d = 64 (8 chunks per row): row r uses slot c ^ (((r >> 1) & 1) << 2 | (r >> 2) & 3).
 // d = 32 (4 chunks per row, 4 rows per 256 bytes): slot c ^ ((r >> 2) & 3).
+// Every form depends on r mod 16 only.
 template <int D>
 __device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   return (row >> 2) & 3;
 }
@@ -132,7 +140,7 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // Each lane therefore fetches the global chunk that the swizzle places at its
 // slot; that per-lane byte offset inside a tile is the same for every tile, and
 // the tile's start is a scalar offset, so a load costs no vector arithmetic.
-// The buffer resource spans one head (N rows): rows past N read as zero in
+// The buffer resource spans one head (Nkv rows): rows past Nkv read as zero in
 // hardware, and their keys are masked.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -213,6 +221,13 @@ __device__ __forceinline__ void wait_tile_loads() {
 // same O / l; moving it only keeps the sums far from overflow.
 constexpr float kSafeSum = 1048576.0f;
 
+// Natural-log logsumexp of a row from its reference maximum m (base 2, scale
+// folded in) and the sum l of its probabilities 2^(c s - m): ln 2 * (m + log2 l);
+// -inf when no key was visible (l = 0).
+__device__ __forceinline__ float row_lse(float m, float l) {
+  return l > 0.f ? 0.69314718055994531f * (m + log2f(l)) : -INFINITY;
+}
+
 // Partial result of one part of a shared query tile, in the lanes' own register
 // order so that each write or read instruction moves one contiguous 1 KB row:
 //   o[wave][dt][g][lane][4]  unnormalised output: the lane's oacc[dt][4g .. 4g + 3]
@@ -225,7 +240,8 @@ struct PartSlot {
   static constexpr int L = M + 4 * 64;
   static constexpr int FLOATS = L + 4 * 64;
 };
-static_assert(PartSlot<64>::FLOATS * 4 == part_slot_bytes(64) && PartSlot<32>::FLOATS * 4 == part_slot_bytes(32),
+static_assert(PartSlot<128>::FLOATS * 4 == part_slot_bytes(128) && PartSlot<64>::FLOATS * 4 == part_slot_bytes(64) &&
+                  PartSlot<32>::FLOATS * 4 == part_slot_bytes(32),
               "workspace slot size and kernel layout must agree");
 
 template <int D>
@@ -260,11 +276,11 @@ void attn_fwd_kernel(KernelArgs a) {
   const int col = lane & 31;   // query column owned by this lane
   const int half = lane >> 5;  // which half-wave
 
-  const int32_t N = a.N;
+  const int32_t Nq = a.Nq, Nkv = a.Nkv;
   const int32_t n_kv = a.n_kvtiles;
   const float c = a.c;
   const TileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
-  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+  const uint32_t head_bytes = (uint32_t)Nkv * (uint32_t)(D * 2);
 
   // LDS offsets that depend only on the lane
   const int k_swz = chunk_swizzle<D>(col);  // rows sb*32 + col share it
@@ -285,10 +301,9 @@ void attn_fwd_kernel(KernelArgs a) {
   auto segment = [&](const int32_t bh, const int32_t qtile, const KvRun run, f32x16_t (&oacc)[DT], float& m_run,
                      float& l_run) {
   const int32_t q0 = qtile * C::BM;
-  const size_t head_off = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ qh = a.q + head_off;
-  const uint16_t* __restrict__ kh = a.k + head_off;
-  const uint16_t* __restrict__ vh = a.v + head_off;
+  const uint16_t* __restrict__ qh = a.q + (size_t)bh * (size_t)Nq * D;
+  const uint16_t* __restrict__ kh = a.k + (size_t)bh * (size_t)Nkv * D;
+  const uint16_t* __restrict__ vh = a.v + (size_t)bh * (size_t)Nkv * D;
 
   // ---- Q fragment: B operand of S^T = K Q^T; lane holds d = 16kb + 8*half + 0..7 of its query
   const int32_t my_q = q0 + wave * 32 + col;
@@ -296,17 +311,24 @@ void attn_fwd_kernel(KernelArgs a) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     u32x4_t x = u32x4_t{0, 0, 0, 0};
-    if (my_q < N) {
+    if (my_q < Nq) {
       x = *reinterpret_cast<const u32x4_t*>(qh + (size_t)my_q * D + kb * 16 + half * 8);
       x ^= a.q_sign;  // negative scale: flip Q's sign bits, use |scale|
     }
     qf[kb] = __builtin_bit_cast(bf16x8_t, x);
   }
 
-  int32_t yq = 0, xq = 0;
-  if (is_na2d(MASK)) {
-    yq = my_q / a.na.grid_w;
-    xq = my_q - yq * a.na.grid_w;
+  // the query's grid coordinates and, for dilated windows, its per-axis anchors (na_dil_anchor)
+  int32_t zq = 0, yq = 0, xq = 0, az = 0, ay = 0, ax = 0;
+  if (is_na(MASK)) {
+    const int32_t plane = a.na.grid_h * a.na.grid_w;
+    zq = my_q / plane;
+    const int32_t rq = my_q - zq * plane;
+    yq = rq / a.na.grid_w;
+    xq = rq - yq * a.na.grid_w;
+    az = na_dil_anchor(zq, a.na.grid_d, a.na.kernel_d, a.na.rad_d, a.na.wrap_d, a.na.dil_d);
+    ay = na_dil_anchor(yq, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h, a.na.dil_h);
+    ax = na_dil_anchor(xq, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w, a.na.dil_w);
   }
   // Neighbourhood grids whose width is a multiple of 32 (up to 128): every
   // 32-key MFMA block lies in one grid row, and the columns a lane's 16 keys of
@@ -314,7 +336,7 @@ void attn_fwd_kernel(KernelArgs a) {
   // The column test is therefore done once per lane: bit 16*phase + r of col_bits
   // says whether accumulator element r of a block with that phase is in the
   // query's column window.
-  constexpr bool NA_BLOCKS = MASK == MASK_NA2D_BLOCKS;
+  constexpr bool NA_BLOCKS = MASK == MASK_NA_BLOCKS;
   uint32_t col_bits[2] = {0u, 0u};
   if (NA_BLOCKS) na_col_bits(xq, half, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w, a.na_phases, col_bits);
 
@@ -367,10 +389,15 @@ void attn_fwd_kernel(KernelArgs a) {
   // into the accumulator vector compiled, for the neighbourhood mask, into code
   // that dropped the second axis' condition.)
   auto apply_mask = [&](f32x16_t (&s)[SB], int32_t t) {
-    int32_t y0 = 0, x0 = 0;
-    if (is_na2d(MASK)) {
-      y0 = (t * C::BN) / a.na.grid_w;
-      x0 = t * C::BN - y0 * a.na.grid_w;
+    // key = (row0, x0) + off in row-major order over all grid rows of all planes
+    int32_t row0 = 0, x0 = 0, z0 = 0, y0 = 0;
+    bool dilated = false;
+    if (is_na(MASK)) {
+      row0 = (t * C::BN) / a.na.grid_w;
+      x0 = t * C::BN - row0 * a.na.grid_w;
+      z0 = row0 / a.na.grid_h;
+      y0 = row0 - z0 * a.na.grid_h;
+      dilated = (a.na.dil_d | a.na.dil_h | a.na.dil_w) != 1;  // uniform
     }
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
@@ -378,16 +405,26 @@ void attn_fwd_kernel(KernelArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int32_t off = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         const int32_t key = t * C::BN + off;
-        bool ok = key < N;
+        bool ok = key < Nkv;
         if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
-        if (is_na2d(MASK)) {
-          // key = (y0, x0) + off in row-major order. For n = x0 + off < grid_w + BN
-          // the quotient (n + 0.5) / grid_w stays at least 0.5 / grid_w away from
-          // an integer, far more than the float error, so truncation is exact.
-          const int32_t qy = (int32_t)(((float)(x0 + off) + 0.5f) * a.na_inv_w);
-          const int32_t yk = y0 + qy, xk = x0 + off - qy * a.na.grid_w;
-          ok = ok & na_axis_ok(yq, yk, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h) &
-               na_axis_ok(xq, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w);
+        if (is_na(MASK)) {
+          // For n < 2^21 the quotient (n + 0.5) / L stays at least 0.5 / L away
+          // from an integer, far more than the float error, so truncation is
+          // exact; here n = x0 + off < grid_w + BN and y0 + dy < grid_h + BN.
+          const int32_t dy = (int32_t)(((float)(x0 + off) + 0.5f) * a.na_inv_w);
+          const int32_t xk = x0 + off - dy * a.na.grid_w;
+          const int32_t yy = y0 + dy;
+          const int32_t dz = (int32_t)(((float)yy + 0.5f) * a.na_inv_h);
+          const int32_t yk = yy - dz * a.na.grid_h, zk = z0 + dz;
+          if (!dilated) {
+            ok = ok & na_axis_ok(zq, zk, a.na.grid_d, a.na.kernel_d, a.na.rad_d, a.na.wrap_d) &
+                 na_axis_ok(yq, yk, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h) &
+                 na_axis_ok(xq, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w);
+          } else {
+            ok = ok & na_dil_ok(az, zk, a.na.grid_d, a.na.kernel_d, a.na.rad_d, a.na.wrap_d, a.na.dil_d) &
+                 na_dil_ok(ay, yk, a.na.grid_h, a.na.kernel_h, a.na.rad_h, a.na.wrap_h, a.na.dil_h) &
+                 na_dil_ok(ax, xk, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w, a.na.dil_w);
+          }
         }
         s[sb][r] = ok ? s[sb][r] : -INFINITY;
       }
@@ -452,12 +489,12 @@ void attn_fwd_kernel(KernelArgs a) {
   };
   // The 16-bit element masks of key tile t for a bit-masked step: the window bits
   // for the structured neighbourhood grids, else the keys up to the lane's last
-  // visible one (its query for the causal mask, N - 1 for a ragged last tile).
+  // visible one (its query for the causal mask, Nkv - 1 for a ragged last tile).
   auto tile_bits = [&](int32_t t, uint32_t (&bm)[SB]) {
     if constexpr (NA_BLOCKS) {
       block_masks(t, bm);
     } else {
-      int32_t last = N - 1;
+      int32_t last = Nkv - 1;
       if constexpr (MASK == MASK_CAUSAL) last = last < my_q ? last : my_q;
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) bm[sb] = limit_bits(last - (t * C::BN + sb * 32 + 4 * half));
@@ -493,7 +530,7 @@ void attn_fwd_kernel(KernelArgs a) {
     __syncthreads();
     f32x16_t s[SB];
     qk_tile(k_lds[0], s);
-    const bool masked = tile_needs_mask(MASK, N, C::BN, q0, t0);
+    const bool masked = tile_needs_mask(MASK, Nkv, C::BN, q0, t0);
     if constexpr (NA_BLOCKS) {
       uint32_t bm0[SB];
       block_masks(t0, bm0);
@@ -511,7 +548,7 @@ void attn_fwd_kernel(KernelArgs a) {
   // Common tail of a step (the new probabilities are in pn). They were computed
   // against the reference maximum m_run of earlier tiles. Every probability is at most the
   // lane's row sum, so psum <= 2^kSafeLog2 proves that none exceeds 2^kSafeLog2
-  // (far inside fp32/bf16 range: O and l stay finite for any N). Otherwise (some
+  // (far inside fp32/bf16 range: O and l stay finite for any Nkv). Otherwise (some
   // row's maximum moved up, rare after the first tile) the exact tile maximum
   // becomes the new reference, O and l are rescaled and the tile is redone.
   // Then the next tiles are awaited.
@@ -565,9 +602,18 @@ void attn_fwd_kernel(KernelArgs a) {
     constexpr int NPAIR = SB * 8;          // two-score pieces per lane
     constexpr int VSLOTS = TOT - GS;       // slots after the first group
     constexpr int PF = 2;                  // read-ahead distance in slots
-    // group g: kind 0 = S^T, 1 = PV; block of the group
-    constexpr auto kind = [](int g) { return (g == 2 || g == 4 || g >= 6) ? 1 : 0; };
-    constexpr auto blk = [](int g) { return g < 2 ? g : (g == 2 ? 0 : (g == 3 ? 2 : (g == 4 ? 1 : (g == 5 ? 3 : g - 4)))); };
+    // group g: kind 0 = S^T, 1 = PV; block of the group. Four blocks (128-key tiles):
+    // S^T b0 | S^T b1 | PV b0 | S^T b2 | PV b1 | S^T b3 | PV b2 | PV b3; two blocks
+    // (64-key tiles): S^T b0 | S^T b1 | PV b0 | PV b1.
+    static_assert(SB == 4 || SB == 2, "group order for 2 or 4 blocks per tile");
+    constexpr auto kind = [](int g) {
+      if constexpr (SB == 2) return g >= 2 ? 1 : 0;
+      return (g == 2 || g == 4 || g >= 6) ? 1 : 0;
+    };
+    constexpr auto blk = [](int g) {
+      if constexpr (SB == 2) return g & 1;
+      return g < 2 ? g : (g == 2 ? 0 : (g == 3 ? 2 : (g == 4 ? 1 : (g == 5 ? 3 : g - 4))));
+    };
 
     f32x16_t s[SB];
 #pragma unroll
@@ -692,9 +738,9 @@ void attn_fwd_kernel(KernelArgs a) {
   };
   if constexpr (NA_BLOCKS) {
     fast_loop(n - 1, std::true_type{});
-  } else if constexpr (MASK != MASK_NA2D) {
+  } else if constexpr (MASK != MASK_NA) {
     int32_t n_fast = 0;  // steps whose next tile needs no element mask
-    while (n_fast + 1 < n && !tile_needs_mask(MASK, N, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
+    while (n_fast + 1 < n && !tile_needs_mask(MASK, Nkv, C::BN, q0, kv_tile_at(run, n_fast + 1, n_kv))) ++n_fast;
     fast_loop(n_fast, std::false_type{});
     fast_loop(n - 1, std::true_type{});  // the causal diagonal and a ragged last tile, on bit masks
   } else {
@@ -705,13 +751,16 @@ void attn_fwd_kernel(KernelArgs a) {
   pv_tile(v_lds[(n - 1) & (S - 1)], p, oacc);
   };
 
-  // Delayed division and store of query tile qtile of head bh: lane holds d = 32dt + 8(r/4) + 4*half + r%4
-  auto store_rows = [&](const int32_t bh, const int32_t qtile, const f32x16_t (&oacc)[DT], const float l_run) {
+  // Delayed division and store of query tile qtile of head bh: lane holds d = 32dt + 8(r/4) + 4*half + r%4.
+  // With an lse output, lane `col` of the first half-wave also writes its row's
+  // logsumexp: P = 2^(c s - m), so log(sum exp(scale s)) = ln 2 * (m + log2 l).
+  auto store_rows = [&](const int32_t bh, const int32_t qtile, const f32x16_t (&oacc)[DT], const float m_run,
+                        const float l_run) {
     const int32_t my_q = qtile * C::BM + wave * 32 + col;
-    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)N * D;
+    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)Nq * D;
     const float l_tot = swap_halves_sum(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (my_q < N) {
+    if (my_q < Nq) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -723,6 +772,7 @@ void attn_fwd_kernel(KernelArgs a) {
               __builtin_bit_cast(u32x2_t, ob);
         }
       }
+      if (a.lse != nullptr && half == 0) a.lse[(size_t)bh * Nq + my_q] = row_lse(m_run, l_tot);
     }
   };
 
@@ -730,8 +780,8 @@ void attn_fwd_kernel(KernelArgs a) {
   float m_run, l_run;
   if constexpr (!SPLIT) {
     const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH);
-    segment(w.bh, w.qtile, kv_run(MASK, N, C::BM, C::BN, w.qtile * C::BM, a.na), oacc, m_run, l_run);
-    store_rows(w.bh, w.qtile, oacc, l_run);
+    segment(w.bh, w.qtile, kv_run(MASK, Nq, Nkv, C::BM, C::BN, w.qtile * C::BM, a.na), oacc, m_run, l_run);
+    store_rows(w.bh, w.qtile, oacc, m_run, l_run);
   } else {
     // Remainder split (unmasked problems): whole tiles first, XCD-contiguous so
     // the tiles of one head share an L2; then the parts of the split tiles,
@@ -742,57 +792,64 @@ void attn_fwd_kernel(KernelArgs a) {
     const int32_t tile = whole ? xcd_contiguous(blockIdx.x, full) : full + slot / parts;
     const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
     segment(bh, qtile, whole ? KvRun{0, n_kv} : part_run(n_kv, parts, slot % parts), oacc, m_run, l_run);
-    if (whole) store_rows(bh, qtile, oacc, l_run);
+    if (whole) store_rows(bh, qtile, oacc, m_run, l_run);
     else write_part<D>(a.ws_parts + (size_t)slot * PartSlot<D>::FLOATS, wave, lane, oacc, m_run, l_run);
   }
 }
 
 // Second kernel of a split launch: one wavefront per (split tile, wavefront
-// slice of the tile). It reads every part's maximum and row sum, rescales all
-// parts to the largest maximum, sums them in part order (so the result does not
-// depend on timing) and writes the rows. The parts were written by the previous
-// kernel on the same stream, so plain loads see them.
+// slice of the tile, half of the head dimension at d = 128). It reads every
+// part's maximum and row sum, rescales all parts to the largest maximum, sums
+// them in part order (so the result does not depend on timing) and writes the
+// rows. The parts were written by the previous kernel on the same stream, so
+// plain loads see them.
+template <int D>
+constexpr int kMergeSlices = D == 128 ? 2 : 1;  // d-slices per wavefront slice (keeps the loads in registers)
+
 template <int D, int PARTS>
 __global__ __launch_bounds__(64) void attn_merge_kernel(KernelArgs a) {
-  constexpr int DT = D / 32;
+  constexpr int DS = kMergeSlices<D>;
+  constexpr int DT = D / 32, DTB = DT / DS;
   const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
-  const int32_t r = blockIdx.x >> 2, wave = blockIdx.x & 3;
+  const int32_t ds = blockIdx.x % DS, rw = blockIdx.x / DS;
+  const int32_t r = rw >> 2, wave = rw & 3;
   const float* slots = a.ws_parts + (size_t)r * PARTS * PartSlot<D>::FLOATS;
   // every load is unconditional, so all parts are in flight together
   float mp[PARTS], lp[PARTS];
-  float4 x[PARTS][DT][4];
+  float4 x[PARTS][DTB][4];
 #pragma unroll
   for (int p = 0; p < PARTS; ++p) {
     const float* slot = slots + (size_t)p * PartSlot<D>::FLOATS;
     mp[p] = slot[PartSlot<D>::M + wave * 64 + lane];
     lp[p] = slot[PartSlot<D>::L + wave * 64 + lane];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int i = 0; i < DTB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        x[p][dt][g] = *reinterpret_cast<const float4*>(slot + (((wave * DT + dt) * 4 + g) * 64 + lane) * 4);
+        x[p][i][g] =
+            *reinterpret_cast<const float4*>(slot + (((wave * DT + ds * DTB + i) * 4 + g) * 64 + lane) * 4);
   }
   float m = mp[0];
 #pragma unroll
   for (int p = 1; p < PARTS; ++p) m = fmaxf(m, mp[p]);
   float l = 0.f;
-  float o[DT][16];
+  float o[DTB][16];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int i = 0; i < DTB; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
 #pragma unroll
   for (int p = 0; p < PARTS; ++p) {
     const float w = __builtin_amdgcn_exp2f(mp[p] - m);
     l += w * lp[p];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int i = 0; i < DTB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        o[dt][4 * g] += w * x[p][dt][g].x;
-        o[dt][4 * g + 1] += w * x[p][dt][g].y;
-        o[dt][4 * g + 2] += w * x[p][dt][g].z;
-        o[dt][4 * g + 3] += w * x[p][dt][g].w;
+        o[i][4 * g] += w * x[p][i][g].x;
+        o[i][4 * g + 1] += w * x[p][i][g].y;
+        o[i][4 * g + 2] += w * x[p][i][g].z;
+        o[i][4 * g + 3] += w * x[p][i][g].w;
       }
   }
   const int32_t tile = a.split_full + r;
@@ -800,16 +857,18 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(KernelArgs a) {
   const int32_t my_q = qtile * Cfg<D>::BM + wave * 32 + col;
   const float l_tot = swap_halves_sum(l);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_q < a.N) {
-    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)a.N * D;
+  if (my_q < a.Nq) {
+    if (a.lse != nullptr && half == 0 && ds == 0) a.lse[(size_t)bh * a.Nq + my_q] = row_lse(m, l_tot);
+    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)a.Nq * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int i = 0; i < DTB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4_t ob;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[dt][g * 4 + e] * inv);
-        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g * 8 + half * 4) = __builtin_bit_cast(u32x2_t, ob);
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[i][g * 4 + e] * inv);
+        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + (ds * DTB + i) * 32 + g * 8 + half * 4) =
+            __builtin_bit_cast(u32x2_t, ob);
       }
   }
 }
@@ -825,7 +884,7 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
   if (a.ws_parts != nullptr) {  // remainder split, no mask
     const hipError_t e = launch_one<D, MASK_NONE, true>(a, n_wg, stream);
     if (e != hipSuccess) return e;
-    const dim3 grid(rem * Cfg<D>::WAVES), block(64);
+    const dim3 grid(rem * Cfg<D>::WAVES * kMergeSlices<D>), block(64);
     static_assert(kMaxParts == 8, "one merge kernel per part count");
     switch (a.split_parts) {
       case 2: hipLaunchKernelGGL((attn_merge_kernel<D, 2>), grid, block, 0, stream, a); break;
@@ -839,19 +898,22 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
     }
     return hipGetLastError();
   }
-  if (mask == MASK_CAUSAL) return launch_one<D, MASK_CAUSAL, false>(a, n_wg, stream);
-  if (mask == MASK_NA2D && a.na_phases > 0) return launch_one<D, MASK_NA2D_BLOCKS, false>(a, n_wg, stream);
-  if (mask == MASK_NA2D) return launch_one<D, MASK_NA2D, false>(a, n_wg, stream);
-  return launch_one<D, MASK_NONE, false>(a, n_wg, stream);
+  switch (mask) {
+    case MASK_NONE: return launch_one<D, MASK_NONE, false>(a, n_wg, stream);
+    case MASK_CAUSAL: return launch_one<D, MASK_CAUSAL, false>(a, n_wg, stream);
+    case MASK_NA: return launch_one<D, MASK_NA, false>(a, n_wg, stream);
+    case MASK_NA_BLOCKS: return launch_one<D, MASK_NA_BLOCKS, false>(a, n_wg, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream) {
-  return d == 64 ? launch_d<64>(a, mask, n_wg, rem, stream) : launch_d<32>(a, mask, n_wg, rem, stream);
-}
-
-int32_t tile_keys() {
-  static_assert(Cfg<64>::BN == Cfg<32>::BN, "one key-tile size for every head size");
-  return Cfg<64>::BN;
+  switch (d) {
+    case 32: return launch_d<32>(a, mask, n_wg, rem, stream);
+    case 64: return launch_d<64>(a, mask, n_wg, rem, stream);
+    case 128: return launch_d<128>(a, mask, n_wg, rem, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

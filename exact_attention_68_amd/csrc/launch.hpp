@@ -11,19 +11,21 @@ namespace attn {
 
 // Arguments of one launch, passed by value to the kernel.
 struct KernelArgs {
-  const uint16_t* q;  // bfloat16 bit patterns, [B, H, N, d]
-  const uint16_t* k;
+  const uint16_t* q;  // bfloat16 bit patterns, [B, H, Nq, d]
+  const uint16_t* k;  // [B, H, Nkv, d]
   const uint16_t* v;
-  uint16_t* o;
-  int32_t N;          // tokens per head
+  uint16_t* o;        // [B, H, Nq, d]
+  float* lse;         // [B, H, Nq] or null
+  int32_t Nq, Nkv;    // queries and keys per head
   int32_t BH;         // B * H
-  int32_t n_qtiles;   // ceil(N / 128)
-  int32_t n_kvtiles;  // ceil(N / key tile)
+  int32_t n_qtiles;   // ceil(Nq / 128)
+  int32_t n_kvtiles;  // ceil(Nkv / key tile)
   float c;            // |scale| * log2(e)
   uint32_t q_sign;    // 0x80008000 when scale < 0 (flips Q's sign bits), else 0
-  NaGeom na;          // neighbourhood geometry (mask NA2D only)
-  float na_inv_w;     // 1 / grid_w, rounded to float (mask NA2D only)
-  int32_t na_phases;  // grid_w / 32 when grid_w is a multiple of 32 and at most 128, else 0 (NA2D only)
+  NaGeom na;          // neighbourhood geometry (neighbourhood masks only)
+  float na_inv_w;     // 1 / grid_w, rounded to float
+  float na_inv_h;     // 1 / grid_h, rounded to float
+  int32_t na_phases;  // grid_w / 32 for the block-masked kernel, else 0
   // remainder split (SplitPlan; ws_parts null = one work-group per query tile)
   float* ws_parts;      // rem * parts slots of part_slot_bytes(d)
   int32_t split_full;   // whole-tile work-groups
@@ -36,14 +38,14 @@ constexpr int64_t split_workspace_bytes(const SplitPlan& p, int64_t d) {
   return p.rem > 0 ? (int64_t)p.slots() * part_slot_bytes(d) : 0;
 }
 
-// Launches the kernel for head size d (32 or 64) and the given mask mode. With
-// a.ws_parts set (unmasked problems only), n_wg = full + rem * parts work-groups
-// run the whole tiles and the parts, and a second kernel of rem work-groups
-// merges the parts, both on `stream`.
+// Keys per key/value tile of the kernel for head size d: 128 for d = 32 and 64,
+// 64 for d = 128 (the same 16 KB of LDS per K or V tile).
+constexpr int32_t tile_keys(int64_t d) { return d == 128 ? 64 : 128; }
+
+// Launches the kernel for head size d (32, 64 or 128) and kernel mask `mask`
+// (MASK_*). With a.ws_parts set (unmasked problems only), n_wg = full + rem *
+// parts work-groups run the whole tiles and the parts, and a second kernel of
+// rem work-groups merges the parts, both on `stream`.
 hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream);
-
-// Keys per key/value tile of the kernels.
-int32_t tile_keys();
-
 
 }  // namespace attn

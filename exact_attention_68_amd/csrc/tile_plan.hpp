@@ -3,39 +3,44 @@
 // Plain constexpr C++: clang compiles constexpr functions for both host and
 // device, so the kernel and a host-only test build share this logic.
 //
-// A query tile covers queries [q0, q0 + BM) (clipped to N). Key tiles are
-// BN consecutive tokens; tile t covers keys [t*BN, t*BN + BN). The tiles to
-// visit form one circular run: tiles (first + i) mod n_tiles for
-// i = 0 .. count-1, each visited once.
+// A query tile covers queries [q0, q0 + BM) (clipped to Nq). Key tiles are
+// BN consecutive tokens; tile t covers keys [t*BN, t*BN + BN) (clipped to
+// Nkv). The tiles to visit form one circular run: tiles (first + i) mod
+// n_tiles for i = 0 .. count-1, each visited once.
 //
 //  * no mask: every tile (all keys are visible; PhotoRoom's xformers post,
 //    the running-softmax paragraph: keys are read tile by tile);
 //  * causal: tiles up to the one holding the tile's last query (keys after a
 //    query are masked, "Profiling in PyTorch", the naive causal module), so
 //    fully masked tiles are never visited;
-//  * 2D neighbourhood: the band of grid rows that any query of the tile can
-//    see (NATTEN issue 142: skipping key tiles that are fully masked is
-//    predictable per query tile). With a wrapped row axis the band is taken
-//    modulo the grid height and the run of tiles wraps modulo the tile
-//    count; no input is padded.
+//  * neighbourhood (2D, or 3D as for the MR volumes of NATTEN issue 142):
+//    the band of grid planes, or of rows of one plane, that any query of the
+//    tile can see (the same issue: skipping key tiles that are fully masked is
+//    predictable per query tile). With a wrapped axis the band is taken modulo
+//    its length and the run of tiles wraps modulo the tile count; no input is
+//    padded.
 #pragma once
 
 #include <stdint.h>
 
 namespace attn {
 
-enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA2D = 2 };
-// Kernel-internal variant of MASK_NA2D for grids whose width is a multiple of 32
-// (at most 128): the window test runs on per-block bit masks.
-enum : int { MASK_NA2D_BLOCKS = 3 };
-constexpr bool is_na2d(int mask) { return mask == MASK_NA2D || mask == MASK_NA2D_BLOCKS; }
+// Kernel mask kinds. MASK_NA covers the 2D and 3D neighbourhood windows with any
+// dilation (an element predicate); MASK_NA_BLOCKS is the 2D, undilated window on
+// grids whose width is a multiple of 32 (at most 128), tested on per-block bit masks.
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3 };
+constexpr bool is_na(int mask) { return mask == MASK_NA || mask == MASK_NA_BLOCKS; }
 
-// 2D neighbourhood geometry in the form the kernel uses.
+// Neighbourhood geometry in the form the kernel uses. Token n sits at depth
+// z = n / (grid_h * grid_w), row y and column x of its plane (row-major); a 2D
+// grid has one plane (grid_d = kernel_d = dil_d = 1, rad_d = wrap_d = 0).
 struct NaGeom {
   int32_t grid_h, grid_w;
   int32_t kernel_h, kernel_w;
   int32_t rad_h, rad_w;    // kernel / 2
   int32_t wrap_h, wrap_w;  // 1 = circular, 0 = clamped
+  int32_t dil_h, dil_w;    // dilation (1 = contiguous window)
+  int32_t grid_d, kernel_d, rad_d, wrap_d, dil_d;  // depth axis
 };
 
 struct KvRun {
@@ -50,32 +55,49 @@ constexpr int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
 constexpr int32_t iclamp(int32_t x, int32_t lo, int32_t hi) { return imin(imax(x, lo), hi); }
 constexpr int32_t imod(int32_t a, int32_t m) { return ((a % m) + m) % m; }
 
-// Rows [start, start + count) (mod grid_h when wrapped) holding every key that
-// any query row in [y0, y1] may see.
-struct RowBand {
+// Coordinates [start, start + count) (mod len when wrapped) holding every
+// window cell of every query coordinate in [c0, c1] along one axis.
+struct Band {
   int32_t start, count;
 };
 
-constexpr RowBand na_row_band(const NaGeom& g, int32_t y0, int32_t y1) {
-  if (g.wrap_h) {
-    int32_t count = (y1 - y0 + 1) + 2 * g.rad_h;
-    if (count >= g.grid_h) return RowBand{0, g.grid_h};
-    return RowBand{imod(y0 - g.rad_h, g.grid_h), count};
+constexpr Band na_band(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil) {
+  if (wrap) {  // cells (c + dil * t) mod len, |t| <= rad
+    const int32_t count = (c1 - c0 + 1) + 2 * rad * dil;
+    if (count >= len) return Band{0, len};
+    return Band{imod(c0 - rad * dil, len), count};
   }
-  // clamped windows start at clamp(y - r, 0, H - k), a non-decreasing function of y
-  int32_t s0 = iclamp(y0 - g.rad_h, 0, g.grid_h - g.kernel_h);
-  int32_t s1 = iclamp(y1 - g.rad_h, 0, g.grid_h - g.kernel_h);
-  return RowBand{s0, s1 + g.kernel_h - s0};
+  if (dil == 1) {
+    // clamped windows start at clamp(c - r, 0, L - k), a non-decreasing function of c
+    const int32_t s0 = iclamp(c0 - rad, 0, len - kernel);
+    const int32_t s1 = iclamp(c1 - rad, 0, len - kernel);
+    return Band{s0, s1 + kernel - s0};
+  }
+  // a clamped dilated window holds its query's cell and spans (kernel - 1) * dil cells
+  const int32_t reach = (kernel - 1) * dil;
+  const int32_t s = imax(c0 - reach, 0), e = imin(c1 + reach, len - 1);
+  return Band{s, e - s + 1};
 }
 
-constexpr KvRun kv_run(int mask, int32_t N, int32_t BM, int32_t BN, int32_t q0, const NaGeom& g) {
-  const int32_t n_tiles = (int32_t)cdiv(N, BN);
-  const int32_t q_last = imin(q0 + BM, N) - 1;
-  if (mask == MASK_CAUSAL) return KvRun{0, q_last / BN + 1};
-  if (!is_na2d(mask)) return KvRun{0, n_tiles};
-  const RowBand band = na_row_band(g, q0 / g.grid_w, q_last / g.grid_w);
-  const int32_t tok_start = band.start * g.grid_w;
-  const int32_t tok_len = band.count * g.grid_w;
+constexpr KvRun kv_run(int mask, int32_t Nq, int32_t Nkv, int32_t BM, int32_t BN, int32_t q0, const NaGeom& g) {
+  const int32_t n_tiles = (int32_t)cdiv(Nkv, BN);
+  const int32_t q_last = imin(q0 + BM, Nq) - 1;
+  if (mask == MASK_CAUSAL) return KvRun{0, imin(q_last / BN + 1, n_tiles)};
+  if (!is_na(mask)) return KvRun{0, n_tiles};
+  const int32_t N = Nkv;  // = Nq for the neighbourhood masks
+  const int32_t plane = g.grid_h * g.grid_w;
+  const int32_t z0 = q0 / plane, z1 = q_last / plane;
+  const Band bz = na_band(z0, z1, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+  int32_t tok_start = bz.start * plane, tok_len = bz.count * plane;
+  if (bz.count == 1) {  // one plane (then z0 = z1): narrow it to the band of rows
+    const Band by = na_band((q0 - z0 * plane) / g.grid_w, (q_last - z1 * plane) / g.grid_w, g.grid_h, g.kernel_h,
+                            g.rad_h, g.wrap_h, g.dil_h);
+    // a row band that wraps inside one plane of several is not one run of tokens
+    if (g.grid_d == 1 || by.start + by.count <= g.grid_h) {
+      tok_start += by.start * g.grid_w;
+      tok_len = by.count * g.grid_w;
+    }
+  }
   if (tok_len >= N) return KvRun{0, n_tiles};
   const int32_t tok_end = tok_start + tok_len;  // exclusive, may pass N when the band wraps
   if (tok_end <= N) {
@@ -95,15 +117,15 @@ constexpr int32_t kv_tile_at(const KvRun& run, int32_t i, int32_t n_tiles) {
 }
 
 // Does key tile t need the element mask for the query tile starting at q0?
-constexpr bool tile_needs_mask(int mask, int32_t N, int32_t BN, int32_t q0, int32_t t) {
+constexpr bool tile_needs_mask(int mask, int32_t Nkv, int32_t BN, int32_t q0, int32_t t) {
   const int32_t k_end = t * BN + BN;  // exclusive
-  if (k_end > N) return true;         // ragged last tile: keys past N
+  if (k_end > Nkv) return true;       // ragged last tile: keys past Nkv
   if (mask == MASK_CAUSAL) return k_end - 1 > q0;  // some key lies after some query
-  return is_na2d(mask);
+  return is_na(mask);
 }
 
-// Element predicate of the neighbourhood window along one axis, for query
-// coordinate cq and key coordinate ck. Branch-free in the coordinates (the
+// Element predicate of the undilated neighbourhood window along one axis, for
+// query coordinate cq and key coordinate ck. Branch-free in the coordinates (the
 // wrap flag is uniform), so callers can combine axes with a plain select.
 constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, int32_t rad, int32_t wrap) {
   if (wrap) {
@@ -114,6 +136,33 @@ constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, i
   }
   const int32_t start = iclamp(cq - rad, 0, len - kernel);
   return (uint32_t)(ck - start) < (uint32_t)kernel;
+}
+
+// The query-side part of the dilated window test along one axis, computed once
+// per query: wrapped, the query coordinate itself; clamped, the first cell of
+// its window, g + dil * clamp(c / dil - r, 0, L_g - kernel), where g = c mod dil
+// and L_g is the length of the sub-grid of cells congruent to g.
+constexpr int32_t na_dil_anchor(int32_t cq, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil) {
+  if (wrap) return cq;
+  const int32_t g = cq % dil;
+  const int32_t sub_len = (len - 1 - g) / dil + 1;
+  return g + dil * iclamp(cq / dil - rad, 0, sub_len - kernel);
+}
+
+// Dilated window test for key coordinate ck against a query's anchor. Wrapped:
+// ck = (c + dil * t) mod len for some |t| <= rad. Clamped: ck is one of the
+// kernel cells anchor, anchor + dil, ..., anchor + (kernel - 1) * dil.
+constexpr bool na_dil_ok(int32_t anchor, int32_t ck, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
+                         int32_t dil) {
+  if (wrap) {
+    int32_t f = ck - anchor;
+    f += f < 0 ? len : 0;          // forward distance in [0, len)
+    const int32_t b = len - f;     // backward distance in (0, len]
+    const int32_t reach = rad * dil;
+    return (f <= reach && f % dil == 0) || (b <= reach && b % dil == 0);
+  }
+  const int32_t off = ck - anchor;
+  return (uint32_t)off <= (uint32_t)((kernel - 1) * dil) && off % dil == 0;
 }
 
 // Bits [a, b) of a 128-bit column mask, in its 64-bit half h (bit i = column 64h + i).

@@ -3,9 +3,11 @@
  *
  * C ABI. Plain pointers and sizes only; no framework types cross it.
  *
- * The operation, per batch b and head h, with Q, K, V of shape (N, d):
+ * The operation, per batch b and head h, with Q of shape (Nq, d) and K, V of
+ * shape (Nkv, d) (Nq = Nkv = N for self-attention):
  *
  *     O = softmax(scale * Q K^T + mask) V
+ *     LSE = log(rowsum(exp(scale * Q K^T + mask)))   (optional, attn_fwd_ex)
  *
  * as defined by the AWS Neuron NKI tutorial "Fused Self Attention"
  * (section "Background": S = Q K^T, R = softmax(S) V over (seqlen, d_head)
@@ -29,49 +31,72 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Mask modes. */
 typedef enum {
     ATTN_MASK_NONE = 0,   /* every key visible to every query */
     ATTN_MASK_CAUSAL = 1, /* key j visible to query i iff j <= i ("Profiling in PyTorch",
-                             the naive causal module and SDPA's is_causal=True) */
-    ATTN_MASK_NA2D = 2    /* 2D neighbourhood window over a row-major token grid
+                             the naive causal module and SDPA's is_causal=True; with
+                             Nq != Nkv this is SDPA's top-left alignment) */
+    ATTN_MASK_NA2D = 2,   /* 2D neighbourhood window over a row-major token grid
                              (NATTEN issue 142); parameters in attn_na2d_params_t */
+    ATTN_MASK_NA3D = 3    /* 3D neighbourhood window over a row-major token volume (the MR
+                             volumes of NATTEN issue 142); parameters in attn_na3d_params_t */
 } attn_mask_mode_t;
 
 /*
  * 2D neighbourhood parameters (host memory, read during the call only).
  *
  * Token n sits at grid row y = n / grid_w and column x = n % grid_w;
- * grid_h * grid_w must equal N. Along each axis, with r = kernel / 2:
- *   wrap = 1: key allowed when the circular distance between the query's and
- *             the key's coordinate, min((a-b) mod L, (b-a) mod L), is <= r
- *             (a centred window that wraps at the borders like a convolution
- *             with circular padding; NATTEN issue 142, the 5x5 example);
- *   wrap = 0: the standard window of `kernel` cells starting at
- *             clamp(c - r, 0, L - kernel), i.e. shifted inside the grid at
- *             the edges (NATTEN issue 142, the replies on window_start and
- *             window_end and on clamping the window to the edges).
- * A key is visible when both axes allow it.
- * Kernels must be odd with 1 <= kernel <= grid size; dilation must be 1.
+ * grid_h * grid_w must equal N (and queries and keys must be equally many).
+ * Along each axis, with r = kernel / 2 and dilation dil >= 1:
+ *   wrap = 1: key allowed when its coordinate is (c + dil * t) mod L for some
+ *             t in -r..r, c the query's coordinate (a centred window that wraps
+ *             at the borders like a convolution with circular padding; NATTEN
+ *             issue 142, the 5x5 example and the 1D recipe that pads by
+ *             kernel / 2 * dilation). Requires (kernel - 1) * dil < L, so each
+ *             key counts once.
+ *   wrap = 0: the standard window: among the cells congruent to c mod dil,
+ *             the `kernel` consecutive ones starting at clamp(i - r, 0, L_g -
+ *             kernel), where i is the query's index among them and L_g their
+ *             number, i.e. shifted inside the grid at the edges (NATTEN issue
+ *             142, the replies on window_start and window_end and on clamping
+ *             the window to the edges). Requires kernel * dil <= L.
+ * A key is visible when both axes allow it. Kernels must be odd and >= 1.
  */
 typedef struct {
     int32_t grid_h, grid_w;
     int32_t kernel_h, kernel_w;
     int32_t wrap_h, wrap_w;  /* 1 = circular, 0 = clamped */
-    int32_t dil_h, dil_w;    /* must be 1 */
+    int32_t dil_h, dil_w;    /* dilation, >= 1 */
 } attn_na2d_params_t;
+
+/*
+ * 3D neighbourhood parameters (host memory, read during the call only).
+ * Token n sits at depth z, row y and column x with
+ * n = (z * grid_h + y) * grid_w + x; grid_d * grid_h * grid_w must equal N.
+ * Each axis follows the rules of attn_na2d_params_t; a key is visible when
+ * all three axes allow it.
+ */
+typedef struct {
+    int32_t grid_d, grid_h, grid_w;
+    int32_t kernel_d, kernel_h, kernel_w;
+    int32_t wrap_d, wrap_h, wrap_w;
+    int32_t dil_d, dil_h, dil_w;
+} attn_na3d_params_t;
 
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, non-finite scale, unknown
-                                 mask mode, params given when not NA2D, o overlapping q/k/v */
-    ATTN_ERR_UNSUPPORTED = 2, /* head size d other than 32 or 64, or a problem too large for
-                                 32-bit launch geometry */
-    ATTN_ERR_PARAMS = 3,      /* NA2D parameters inconsistent (grid_h*grid_w != N, even or
-                                 out-of-range kernel, wrap not 0/1, dilation != 1) */
-    ATTN_ERR_ALIGNMENT = 4,   /* q, k, v or o not 16-byte aligned */
+                                 mask mode, params given when not a neighbourhood mode,
+                                 o or lse overlapping an input or each other */
+    ATTN_ERR_UNSUPPORTED = 2, /* head size d other than 32, 64 or 128, or a problem too large
+                                 for 32-bit launch geometry */
+    ATTN_ERR_PARAMS = 3,      /* neighbourhood parameters inconsistent (grid size != Nq or
+                                 != Nkv, even or out-of-range kernel, wrap not 0/1,
+                                 dilation < 1, window too large for its axis) */
+    ATTN_ERR_ALIGNMENT = 4,   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error (no device, a failed
                                  device query, or a failed launch) */
     ATTN_ERR_WORKSPACE = 6    /* attn_fwd_ws: workspace NULL, smaller than
@@ -88,13 +113,13 @@ typedef enum {
  *           aligned; written with the result rounded to nearest even. Must
  *           not overlap q, k or v.
  * B, H, N : batch, heads, tokens (> 0). Queries and keys share N.
- * d       : head size, 32 or 64.
+ * d       : head size, 32, 64 or 128.
  * scale   : finite multiplier applied to Q K^T before the mask (0 and
  *           negative values are legal; scale = 0 averages V over the
  *           visible keys).
  * mask_mode : an attn_mask_mode_t value.
- * params  : NULL unless mask_mode == ATTN_MASK_NA2D, then a host pointer to
- *           an attn_na2d_params_t.
+ * params  : NULL unless mask_mode is ATTN_MASK_NA2D or ATTN_MASK_NA3D, then a
+ *           host pointer to an attn_na2d_params_t or attn_na3d_params_t.
  * stream  : a hipStream_t (NULL = the default stream).
  *
  * The caller owns all memory. The library allocates nothing, keeps no state
@@ -112,6 +137,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
 /*
  * attn_fwd_ws: the same operation and arguments as attn_fwd, plus a device
  * workspace that lets unmasked problems spread evenly over the whole chip.
+ * (attn_fwd_ex is the same call with Nq, Nkv and the optional lse output.)
  *
  * One work-group per query tile of 128 queries leaves the GPU unevenly
  * loaded when the tile count is not a multiple of the CU count (for example
@@ -123,7 +149,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
  * the parts of each such tile exactly (the running-softmax rescaling of
  * PhotoRoom's xformers post, running-softmax paragraph, applied between
  * parts). The result equals attn_fwd's up to floating-point summation order.
- * Other problems (causal and 2D neighbourhood masks, tile counts that fill
+ * Other problems (causal and neighbourhood masks, tile counts that fill
  * the chip for two or more rounds, or that would cut a tile into parts of
  * fewer than 2 key tiles) run exactly as attn_fwd with one kernel, and the
  * workspace is then not touched (it may be NULL when
@@ -137,9 +163,10 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
  * workspace_bytes : its size in bytes.
  *
  * The size depends on the current device (its CU count) and the head size;
- * it is at most the CU count x 34 KB (about 8.9 MB on an MI355X). Returns the
- * codes of attn_fwd, and ATTN_ERR_WORKSPACE for a workspace that does not
- * meet the above; all argument errors are detected before any device work.
+ * it is at most the CU count x 18, 34 or 66 KB for d = 32, 64 or 128 (about
+ * 8.9 MB at d = 64 on an MI355X). Returns the codes of attn_fwd, and
+ * ATTN_ERR_WORKSPACE for a workspace that does not meet the above; all
+ * argument errors are detected before any device work.
  * The library still allocates nothing.
  */
 attn_status_t attn_fwd_ws(const void* q, const void* k, const void* v, void* o,
@@ -167,6 +194,39 @@ attn_status_t attn_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d
  */
 attn_status_t attn_fwd_check(int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                              int32_t mask_mode, const void* params);
+
+/*
+ * attn_fwd_ex: the general form of attn_fwd_ws.
+ *
+ *     O = softmax(scale * Q K^T + mask) V,  LSE = log(sum_j exp(scale * (Q K^T)_ij + mask_ij))
+ *
+ * q       : device, bfloat16 [B, H, Nq, d]; k, v: device, bfloat16 [B, H, Nkv, d]
+ *           (cross-attention when Nq != Nkv); o: device, bfloat16 [B, H, Nq, d].
+ *           Contiguous, 16-byte aligned; o disjoint from q, k and v.
+ * lse     : NULL, or a device pointer to float32 [B, H, Nq], 4-byte aligned,
+ *           disjoint from q, k, v, o and the workspace: receives each row's
+ *           natural-log logsumexp of the scaled, masked scores (the statistic a
+ *           backward pass recomputes the probabilities from; NATTEN issue 142's
+ *           fused forward saves it beside the output). -inf for a row with no
+ *           visible key (not reachable with these masks).
+ * Nq, Nkv : query and key counts (> 0). The neighbourhood masks need Nq = Nkv.
+ * d       : 32, 64 or 128.
+ * Other arguments, the workspace rules and the errors are those of
+ * attn_fwd_ws, with Nq and Nkv in place of N; the workspace size comes from
+ * attn_fwd_ex_workspace_size.
+ */
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
+                          int32_t mask_mode, const void* params, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/* attn_fwd_workspace_size for attn_fwd_ex's problem (Nq queries, Nkv keys). */
+attn_status_t attn_fwd_ex_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
+                                         int32_t mask_mode, const void* params, uint64_t* bytes);
+
+/* attn_fwd_check for attn_fwd_ex's problem (Nq queries, Nkv keys). */
+attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
+                                int32_t mask_mode, const void* params);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(int32_t status);

@@ -21,69 +21,116 @@ static int failures = 0;
     }                                           \
   } while (0)
 
-// Keys a query may see, by enumerating the window offsets (independent of na_axis_ok).
+// Window cells of coordinate c along one axis, enumerated (independent of
+// na_axis_ok and na_dil_ok): wrapped, c + dil * t mod len for |t| <= r; clamped,
+// the list of cells congruent to c mod dil with a kernel-long window slid inside it.
+static std::vector<int> axis_cells(int c, int len, int kernel, int wrap, int dil) {
+  std::vector<int> out;
+  const int r = kernel / 2;
+  if (wrap) {
+    for (int t = -r; t <= r; ++t) out.push_back(((c + dil * t) % len + len) % len);
+    return out;
+  }
+  std::vector<int> sub;
+  for (int x = c % dil; x < len; x += dil) sub.push_back(x);
+  int i = 0;
+  while (sub[i] != c) ++i;
+  int s = i - r;
+  s = s < 0 ? 0 : (s > (int)sub.size() - kernel ? (int)sub.size() - kernel : s);
+  for (int t = 0; t < kernel; ++t) out.push_back(sub[s + t]);
+  return out;
+}
+
+static NaGeom geom(int gd, int gh, int gw, int kd, int kh, int kw, int wd, int wh, int ww, int dd, int dh, int dw) {
+  return NaGeom{gh, gw, kh, kw, kh / 2, kw / 2, wh, ww, dh, dw, gd, kd, kd / 2, wd, dd};
+}
+
+// Keys a query may see, by enumerating the window cells of each axis.
 static std::set<int> window_keys(const NaGeom& g, int q) {
-  const int y = q / g.grid_w, x = q % g.grid_w;
-  std::vector<int> rows, cols;
-  if (g.wrap_h) {
-    for (int d = -g.rad_h; d <= g.rad_h; ++d) rows.push_back(((y + d) % g.grid_h + g.grid_h) % g.grid_h);
-  } else {
-    int s = y - g.rad_h;
-    s = s < 0 ? 0 : (s > g.grid_h - g.kernel_h ? g.grid_h - g.kernel_h : s);
-    for (int i = 0; i < g.kernel_h; ++i) rows.push_back(s + i);
-  }
-  if (g.wrap_w) {
-    for (int d = -g.rad_w; d <= g.rad_w; ++d) cols.push_back(((x + d) % g.grid_w + g.grid_w) % g.grid_w);
-  } else {
-    int s = x - g.rad_w;
-    s = s < 0 ? 0 : (s > g.grid_w - g.kernel_w ? g.grid_w - g.kernel_w : s);
-    for (int i = 0; i < g.kernel_w; ++i) cols.push_back(s + i);
-  }
+  const int plane = g.grid_h * g.grid_w;
+  const int z = q / plane, y = q % plane / g.grid_w, x = q % g.grid_w;
   std::set<int> keys;
-  for (int r : rows)
-    for (int c : cols) keys.insert(r * g.grid_w + c);
+  for (int zc : axis_cells(z, g.grid_d, g.kernel_d, g.wrap_d, g.dil_d))
+    for (int yc : axis_cells(y, g.grid_h, g.kernel_h, g.wrap_h, g.dil_h))
+      for (int xc : axis_cells(x, g.grid_w, g.kernel_w, g.wrap_w, g.dil_w)) keys.insert((zc * g.grid_h + yc) * g.grid_w + xc);
   return keys;
 }
 
-static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int BN) {
-  const NaGeom g{gh, gw, kh, kw, kh / 2, kw / 2, wh, ww};
-  const int N = gh * gw;
+// The kernel's element predicate for (query, key): the undilated form when every
+// dilation is 1, else the anchor form.
+static bool kernel_predicate(const NaGeom& g, int q, int key) {
+  const int plane = g.grid_h * g.grid_w;
+  const int zq = q / plane, yq = q % plane / g.grid_w, xq = q % g.grid_w;
+  const int zk = key / plane, yk = key % plane / g.grid_w, xk = key % g.grid_w;
+  if ((g.dil_d | g.dil_h | g.dil_w) == 1)
+    return na_axis_ok(zq, zk, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d) &&
+           na_axis_ok(yq, yk, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h) &&
+           na_axis_ok(xq, xk, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w);
+  const int az = na_dil_anchor(zq, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+  const int ay = na_dil_anchor(yq, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+  const int ax = na_dil_anchor(xq, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w);
+  return na_dil_ok(az, zk, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d) &&
+         na_dil_ok(ay, yk, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h) &&
+         na_dil_ok(ax, xk, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w);
+}
+
+static bool geom_valid(const NaGeom& g) {
+  return na_axis_valid(g.grid_d, g.kernel_d, g.wrap_d, g.dil_d) && na_axis_valid(g.grid_h, g.kernel_h, g.wrap_h, g.dil_h) &&
+         na_axis_valid(g.grid_w, g.kernel_w, g.wrap_w, g.dil_w);
+}
+
+// The run of key tiles of every query tile visits each tile once and holds every
+// key the window allows; the kernel's predicate equals the enumerated window.
+static void check_na_geom(const NaGeom& g, int BM, int BN) {
+  if (!geom_valid(g)) return;
+  const int N = g.grid_d * g.grid_h * g.grid_w;
   const int n_tiles = (int)cdiv(N, BN);
+  const int window = g.kernel_d * g.kernel_h * g.kernel_w;
   for (int q0 = 0; q0 < N; q0 += BM) {
-    const KvRun run = kv_run(MASK_NA2D, N, BM, BN, q0, g);
+    const KvRun run = kv_run(MASK_NA, N, N, BM, BN, q0, g);
     EXPECT(run.first >= 0 && run.first < n_tiles && run.count >= 1 && run.count <= n_tiles,
-           "run out of range grid %dx%d k%dx%d wrap%d%d q0 %d", gh, gw, kh, kw, wh, ww, q0);
+           "run out of range grid %dx%dx%d q0 %d", g.grid_d, g.grid_h, g.grid_w, q0);
     std::set<int> visited;
     for (int i = 0; i < run.count; ++i) {
       const int t = kv_tile_at(run, i, n_tiles);
       EXPECT(t >= 0 && t < n_tiles, "tile index %d out of range", t);
-      EXPECT(visited.insert(t).second, "tile %d visited twice (grid %dx%d k%dx%d q0 %d)", t, gh, gw, kh, kw, q0);
+      EXPECT(visited.insert(t).second, "tile %d visited twice (grid %dx%dx%d q0 %d)", t, g.grid_d, g.grid_h, g.grid_w, q0);
     }
     for (int q = q0; q < N && q < q0 + BM; ++q) {
       const std::set<int> want = window_keys(g, q);
-      EXPECT((int)want.size() == kh * kw, "window size");
-      const int yq = q / gw, xq = q % gw;
+      EXPECT((int)want.size() == window, "window size %d, want %d (grid %dx%dx%d k %d,%d,%d dil %d,%d,%d)",
+             (int)want.size(), window, g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.dil_d,
+             g.dil_h, g.dil_w);
       for (int key = 0; key < N; ++key) {
-        const bool ok = na_axis_ok(yq, key / gw, gh, kh, g.rad_h, wh) && na_axis_ok(xq, key % gw, gw, kw, g.rad_w, ww);
-        EXPECT(ok == (want.count(key) == 1), "predicate vs window, grid %dx%d k%dx%d wrap%d%d q %d key %d", gh, gw,
-               kh, kw, wh, ww, q, key);
+        const bool ok = kernel_predicate(g, q, key);
+        EXPECT(ok == (want.count(key) == 1), "predicate vs window, grid %dx%dx%d k %d,%d,%d wrap %d%d%d dil %d,%d,%d q %d key %d",
+               g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w,
+               g.dil_d, g.dil_h, g.dil_w, q, key);
         if (ok) EXPECT(visited.count(key / BN) == 1, "allowed key %d of query %d in a skipped tile", key, q);
       }
     }
   }
 }
 
-static void check_causal(int N, int BM, int BN) {
-  const int n_tiles = (int)cdiv(N, BN);
-  for (int q0 = 0; q0 < N; q0 += BM) {
-    const KvRun run = kv_run(MASK_CAUSAL, N, BM, BN, q0, NaGeom{});
-    const int q_last = (q0 + BM < N ? q0 + BM : N) - 1;
-    EXPECT(run.first == 0 && run.count == q_last / BN + 1 && run.count <= n_tiles, "causal run N %d q0 %d", N, q0);
+static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int BN) {
+  check_na_geom(geom(1, gh, gw, 1, kh, kw, 0, wh, ww, 1, 1, 1), BM, BN);
+}
+
+static void check_causal(int Nq, int Nkv, int BM, int BN) {
+  const int n_tiles = (int)cdiv(Nkv, BN);
+  for (int q0 = 0; q0 < Nq; q0 += BM) {
+    const KvRun run = kv_run(MASK_CAUSAL, Nq, Nkv, BM, BN, q0, NaGeom{});
+    const int q_last = (q0 + BM < Nq ? q0 + BM : Nq) - 1;
+    const int want = q_last / BN + 1 < n_tiles ? q_last / BN + 1 : n_tiles;
+    EXPECT(run.first == 0 && run.count == want, "causal run Nq %d Nkv %d q0 %d", Nq, Nkv, q0);
     for (int i = 0; i < run.count; ++i) {
       const int t = kv_tile_at(run, i, n_tiles);
-      // a tile needs no element mask only if every key is <= every query of the tile and < N
-      if (!tile_needs_mask(MASK_CAUSAL, N, BN, q0, t)) EXPECT((t + 1) * BN - 1 <= q0 && (t + 1) * BN <= N, "mask flag");
+      // a tile needs no element mask only if every key is <= every query of the tile and < Nkv
+      if (!tile_needs_mask(MASK_CAUSAL, Nkv, BN, q0, t))
+        EXPECT((t + 1) * BN - 1 <= q0 && (t + 1) * BN <= Nkv, "mask flag");
     }
+    // every key j <= q_last, j < Nkv lies in a visited tile
+    for (int j = 0; j <= q_last && j < Nkv; ++j) EXPECT(j / BN < run.count, "causal key %d skipped", j);
   }
 }
 
@@ -104,7 +151,8 @@ static void check_work_items(int mask, int BH, int n_qtiles) {
 static void check_split(int64_t n_tiles, int32_t n_kv, int32_t cus) {
   const SplitPlan p = split_plan(MASK_NONE, n_tiles, n_kv, cus);
   EXPECT(split_plan(MASK_CAUSAL, n_tiles, n_kv, cus).rem == 0, "causal never splits");
-  EXPECT(split_plan(MASK_NA2D, n_tiles, n_kv, cus).rem == 0, "2D neighbourhood never splits");
+  EXPECT(split_plan(ATTN_MASK_NA2D, n_tiles, n_kv, cus).rem == 0, "2D neighbourhood never splits");
+  EXPECT(split_plan(ATTN_MASK_NA3D, n_tiles, n_kv, cus).rem == 0, "3D neighbourhood never splits");
   if (p.rem == 0) return;
   EXPECT(n_tiles < 2 * (int64_t)cus, "split only below two tiles per CU");
   EXPECT(p.full == 0 || p.full == cus, "whole tiles fill one round of CUs");
@@ -165,36 +213,81 @@ static void check_limit_bits() {
 
 static void check_validation() {
   attn_na2d_params_t p{64, 64, 7, 7, 1, 1, 1, 1};
-  EXPECT(check_problem(2, 5, 4096, 64, 0.125f, ATTN_MASK_NONE, nullptr) == ATTN_OK, "valid none");
-  EXPECT(check_problem(2, 4, 4096, 32, 0.17f, ATTN_MASK_NA2D, &p) == ATTN_OK, "valid na2d");
-  EXPECT(check_problem(0, 5, 4096, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "B=0");
-  EXPECT(check_problem(2, -1, 4096, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "H<0");
-  EXPECT(check_problem(2, 5, 0, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "N=0");
-  EXPECT(check_problem(2, 5, 64, 128, 0.125f, 0, nullptr) == ATTN_ERR_UNSUPPORTED, "d=128");
-  EXPECT(check_problem(2, 5, 64, 64, 1.0f / 0.0f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "inf scale");
-  EXPECT(check_problem(2, 5, 64, 64, 0.1f, 3, nullptr) == ATTN_ERR_INVALID_ARG, "mode 3");
-  EXPECT(check_problem(2, 5, 64, 64, 0.1f, ATTN_MASK_CAUSAL, &p) == ATTN_ERR_INVALID_ARG, "params with causal");
-  EXPECT(check_problem(2, 5, 64, 64, 0.1f, ATTN_MASK_NA2D, nullptr) == ATTN_ERR_INVALID_ARG, "na2d no params");
-  EXPECT(check_problem(1, 1, (int64_t)1 << 31, 64, 0.1f, 0, nullptr) == ATTN_ERR_UNSUPPORTED, "N too large");
-  EXPECT(check_problem((int64_t)1 << 20, (int64_t)1 << 20, 4096, 64, 0.1f, 0, nullptr) == ATTN_ERR_UNSUPPORTED,
+  EXPECT(check_problem(2, 5, 4096, 4096, 64, 0.125f, ATTN_MASK_NONE, nullptr) == ATTN_OK, "valid none");
+  EXPECT(check_problem(2, 5, 4096, 77, 64, 0.125f, ATTN_MASK_NONE, nullptr) == ATTN_OK, "valid cross");
+  EXPECT(check_problem(2, 5, 100, 300, 64, 0.125f, ATTN_MASK_CAUSAL, nullptr) == ATTN_OK, "valid causal cross");
+  EXPECT(check_problem(2, 4, 4096, 4096, 32, 0.17f, ATTN_MASK_NA2D, &p) == ATTN_OK, "valid na2d");
+  EXPECT(check_problem(2, 5, 64, 64, 128, 0.1f, 0, nullptr) == ATTN_OK, "d=128");
+  EXPECT(check_problem(0, 5, 4096, 4096, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "B=0");
+  EXPECT(check_problem(2, -1, 4096, 4096, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "H<0");
+  EXPECT(check_problem(2, 5, 0, 4096, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "Nq=0");
+  EXPECT(check_problem(2, 5, 4096, 0, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "Nkv=0");
+  EXPECT(check_problem(2, 5, 64, 64, 96, 0.125f, 0, nullptr) == ATTN_ERR_UNSUPPORTED, "d=96");
+  EXPECT(check_problem(2, 5, 64, 64, 64, 1.0f / 0.0f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "inf scale");
+  EXPECT(check_problem(2, 5, 64, 64, 64, 0.1f, 4, nullptr) == ATTN_ERR_INVALID_ARG, "mode 4");
+  EXPECT(check_problem(2, 5, 64, 64, 64, 0.1f, ATTN_MASK_CAUSAL, &p) == ATTN_ERR_INVALID_ARG, "params with causal");
+  EXPECT(check_problem(2, 5, 64, 64, 64, 0.1f, ATTN_MASK_NA2D, nullptr) == ATTN_ERR_INVALID_ARG, "na2d no params");
+  EXPECT(check_problem(2, 5, 64, 64, 64, 0.1f, ATTN_MASK_NA3D, nullptr) == ATTN_ERR_INVALID_ARG, "na3d no params");
+  EXPECT(check_problem(1, 1, (int64_t)1 << 31, 1 << 20, 64, 0.1f, 0, nullptr) == ATTN_ERR_UNSUPPORTED, "Nq too large");
+  EXPECT(check_problem(1, 1, 1 << 20, (int64_t)1 << 31, 64, 0.1f, 0, nullptr) == ATTN_ERR_UNSUPPORTED, "Nkv too large");
+  EXPECT(check_problem((int64_t)1 << 20, (int64_t)1 << 20, 4096, 4096, 64, 0.1f, 0, nullptr) == ATTN_ERR_UNSUPPORTED,
          "too many work-groups");
   attn_na2d_params_t bad = p;
   bad.grid_h = 63;
-  EXPECT(check_problem(1, 1, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "grid mismatch");
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "grid mismatch");
+  EXPECT(check_problem(1, 1, 4096, 4000, 32, 0.1f, ATTN_MASK_NA2D, &p) == ATTN_ERR_PARAMS, "Nq != Nkv");
   bad = p; bad.kernel_h = 6;
-  EXPECT(check_problem(1, 1, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "even kernel");
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "even kernel");
   bad = p; bad.kernel_w = 65;
-  EXPECT(check_problem(1, 1, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "kernel > grid");
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "kernel > grid");
   bad = p; bad.wrap_w = 2;
-  EXPECT(check_problem(1, 1, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "wrap 2");
-  bad = p; bad.dil_h = 2;
-  EXPECT(check_problem(1, 1, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "dilation");
-  char buf[256];
-  const void* a = buf + 16;
-  EXPECT(check_pointers(a, buf + 32, buf + 48, buf + 64, 1, 1, 1, 8) == ATTN_OK, "disjoint aligned");
-  EXPECT(check_pointers(a, buf + 32, buf + 48, buf + 72, 1, 1, 1, 8) == ATTN_ERR_ALIGNMENT, "misaligned o");
-  EXPECT(check_pointers(a, buf + 32, buf + 48, buf + 48, 1, 1, 1, 8) == ATTN_ERR_INVALID_ARG, "o aliases v");
-  EXPECT(check_pointers(nullptr, buf + 32, buf + 48, buf + 64, 1, 1, 1, 8) == ATTN_ERR_INVALID_ARG, "null q");
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "wrap 2");
+  bad = p; bad.dil_h = 0;
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "dilation 0");
+  bad = p; bad.dil_h = 10;  // wrapped: (7 - 1) * 10 < 64
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_OK, "wrapped dilation 10");
+  bad.dil_h = 11;           // (7 - 1) * 11 >= 64
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "wrapped dilation 11");
+  bad = p; bad.wrap_w = 0; bad.dil_w = 9;  // clamped: 7 * 9 <= 64
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_OK, "clamped dilation 9");
+  bad.dil_w = 10;                          // 7 * 10 > 64
+  EXPECT(check_problem(1, 1, 4096, 4096, 32, 0.1f, ATTN_MASK_NA2D, &bad) == ATTN_ERR_PARAMS, "clamped dilation 10");
+  attn_na3d_params_t v3{20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1};
+  EXPECT(check_problem(2, 4, 8000, 8000, 32, 0.1f, ATTN_MASK_NA3D, &v3) == ATTN_OK, "valid na3d");
+  attn_na3d_params_t b3 = v3;
+  b3.grid_d = 19;
+  EXPECT(check_problem(2, 4, 8000, 8000, 32, 0.1f, ATTN_MASK_NA3D, &b3) == ATTN_ERR_PARAMS, "3D grid mismatch");
+  b3 = v3; b3.kernel_d = 4;
+  EXPECT(check_problem(2, 4, 8000, 8000, 32, 0.1f, ATTN_MASK_NA3D, &b3) == ATTN_ERR_PARAMS, "even depth kernel");
+  b3 = v3; b3.wrap_d = 3;
+  EXPECT(check_problem(2, 4, 8000, 8000, 32, 0.1f, ATTN_MASK_NA3D, &b3) == ATTN_ERR_PARAMS, "depth wrap 3");
+  b3 = v3; b3.dil_w = 5;  // clamped: 5 * 5 > 20
+  EXPECT(check_problem(2, 4, 8000, 8000, 32, 0.1f, ATTN_MASK_NA3D, &b3) == ATTN_ERR_PARAMS, "3D clamped dilation");
+  alignas(256) char buf[512];
+  auto prob = [&](const void* q, const void* k, const void* v, void* o, float* lse) {
+    return Problem{q, k, v, o, lse, 1, 1, 1, 1, 8, 0.5f, ATTN_MASK_NONE, nullptr};
+  };
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 64, nullptr)) == ATTN_OK, "disjoint aligned");
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 72, nullptr)) == ATTN_ERR_ALIGNMENT, "misaligned o");
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 48, nullptr)) == ATTN_ERR_INVALID_ARG, "o aliases v");
+  EXPECT(check_pointers(prob(nullptr, buf + 32, buf + 48, buf + 64, nullptr)) == ATTN_ERR_INVALID_ARG, "null q");
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 64, (float*)(buf + 80))) == ATTN_OK, "lse");
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 64, (float*)(buf + 82))) == ATTN_ERR_ALIGNMENT,
+         "misaligned lse");
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 64, (float*)(buf + 64))) == ATTN_ERR_INVALID_ARG,
+         "lse aliases o");
+  EXPECT(check_pointers(prob(buf + 16, buf + 32, buf + 48, buf + 64, (float*)(buf + 36))) == ATTN_ERR_INVALID_ARG,
+         "lse inside k");
+  // Nq != Nkv: k and v are [1, 1, 3, 8] (48 bytes), q and o [1, 1, 1, 8]
+  Problem x{buf + 16, buf + 32, buf + 80, buf + 128, nullptr, 1, 1, 1, 3, 8, 0.5f, ATTN_MASK_NONE, nullptr};
+  EXPECT(check_pointers(x) == ATTN_OK, "cross disjoint");
+  x.o = buf + 112;  // inside v's 48 bytes
+  EXPECT(check_pointers(x) == ATTN_ERR_INVALID_ARG, "o inside the longer v");
+  x.o = buf + 128;
+  EXPECT(check_workspace(buf + 256, 64, 64, x) == ATTN_OK, "workspace disjoint");
+  EXPECT(check_workspace(buf + 256, 32, 64, x) == ATTN_ERR_WORKSPACE, "workspace small");
+  x.lse = (float*)(buf + 260);
+  EXPECT(check_workspace(buf + 256, 64, 64, x) == ATTN_ERR_WORKSPACE, "workspace overlaps lse");
 }
 
 int main() {
@@ -202,7 +295,10 @@ int main() {
   check_col_bits();
   check_limit_bits();
   for (int BN : {64, 128}) {
-    for (int N : {1, 2, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 600}) check_causal(N, kBlockM, BN);
+    for (int N : {1, 2, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 600}) {
+      check_causal(N, N, kBlockM, BN);
+      for (int Nkv : {1, 77, 128, 300}) check_causal(N, Nkv, kBlockM, BN);
+    }
     const int dims[] = {1, 2, 3, 5, 7, 9, 12, 17};
     for (int gh : dims)
       for (int gw : dims)
@@ -215,6 +311,26 @@ int main() {
     check_na(33, 17, 9, 3, 1, 1, kBlockM, BN);
     check_na(3, 200, 3, 11, 1, 1, kBlockM, BN);
     check_na(96, 40, 5, 5, 1, 0, kBlockM, BN);
+    // dilation in 2D
+    for (int gh : {5, 7, 12, 17})
+      for (int gw : {6, 9, 20})
+        for (int dh : {1, 2, 3})
+          for (int dw : {1, 2, 4})
+            for (int k : {1, 3, 5})
+              for (int wh = 0; wh < 2; ++wh)
+                for (int ww = 0; ww < 2; ++ww) check_na_geom(geom(1, gh, gw, 1, k, 3, 0, wh, ww, 1, dh, dw), kBlockM, BN);
+    // 3D, with and without dilation
+    const int d3[][3] = {{2, 3, 4}, {3, 5, 4}, {4, 4, 8}, {5, 3, 7}, {6, 6, 6}, {9, 2, 5}};
+    for (const auto& gd : d3)
+      for (int kd : {1, 3, 5})
+        for (int kh : {1, 3})
+          for (int wd = 0; wd < 2; ++wd)
+            for (int wh = 0; wh < 2; ++wh)
+              for (int ww = 0; ww < 2; ++ww)
+                for (int dd : {1, 2})
+                  check_na_geom(geom(gd[0], gd[1], gd[2], kd, kh, 3, wd, wh, ww, dd, 1, gd[2] >= 7 ? 2 : 1), kBlockM, BN);
+    check_na_geom(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), kBlockM, BN);
+    check_na_geom(geom(16, 16, 16, 3, 3, 3, 1, 0, 1, 2, 2, 2), kBlockM, BN);
   }
   for (int mask : {MASK_NONE, MASK_CAUSAL})
     for (int BH : {1, 3, 8, 10, 64})
@@ -228,7 +344,7 @@ int main() {
   EXPECT(split_plan(MASK_NONE, 2, 2, 256).rem == 0, "tiny problems do not split");
   for (int32_t cus : {1, 2, 7, 64, 80, 256, 304})
     for (int64_t n_tiles : {1, 2, 3, 5, 16, 21, 33, 40, 48, 72, 80, 100, 255, 256, 257, 320, 400, 511, 512, 513})
-      for (int32_t n_kv : {1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 32, 33, 72}) check_split(n_tiles, n_kv, cus);
+      for (int32_t n_kv : {1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 32, 33, 64, 72, 144}) check_split(n_tiles, n_kv, cus);
   if (failures) {
     std::printf("%d failures\n", failures);
     return 1;

@@ -34,52 +34,92 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def oracle_na2d(p) -> "oracle.NA2D | None":
+def oracle_na(p):
+    """The oracle's window for an attn_na2d_params_t / attn_na3d_params_t (None for no window)."""
     if p is None:
         return None
-    return oracle.NA2D(p.grid_h, p.grid_w, p.kernel_h, p.kernel_w, bool(p.wrap_h), bool(p.wrap_w))
+    if hasattr(p, "grid_d"):
+        return oracle.NA3D(p.grid_d, p.grid_h, p.grid_w, p.kernel_d, p.kernel_h, p.kernel_w,
+                           bool(p.wrap_d), bool(p.wrap_h), bool(p.wrap_w), p.dil_d, p.dil_h, p.dil_w)
+    return oracle.NA2D(p.grid_h, p.grid_w, p.kernel_h, p.kernel_w, bool(p.wrap_h), bool(p.wrap_w), p.dil_h, p.dil_w)
 
 
-def split_workspace(B, H, N, d, mask_mode, params=None):
-    """A fresh workspace for attn_fwd_ws (None when the problem needs none), filled with 0xff bytes
-    (NaN bit patterns): the library must not depend on its initial content."""
+def split_workspace(B, H, N, d, mask_mode, params=None, n_kv=None):
+    """A fresh workspace for attn_fwd_ws / attn_fwd_ex (None when the problem needs none), filled
+    with 0xff bytes (NaN bit patterns): the library must not depend on its initial content."""
     import exact_attention_68_amd as A
 
-    n = A.attn_fwd_workspace_size(B, H, N, d, mask_mode, params)
+    n = A.attn_fwd_ex_workspace_size(B, H, N, N if n_kv is None else n_kv, d, mask_mode, params)
     return torch.full((n,), 255, dtype=torch.uint8, device="cuda") if n else None
 
 
-def run_gpu(q, k, v, scale, mask_mode, params=None, entry="attn_fwd"):
-    """Output of the HIP path through the C ABI entry point `entry` (attn_fwd or attn_fwd_ws)."""
+def run_gpu(q, k, v, scale, mask_mode, params=None, entry="attn_fwd", want_lse=False):
+    """Output (and, for attn_fwd_ex with want_lse, the logsumexp) of the HIP path through the C ABI
+    entry point `entry` (attn_fwd, attn_fwd_ws or attn_fwd_ex)."""
     import exact_attention_68_amd as A
 
     dq, dk, dv = (t.to("cuda") for t in (q, k, v))
     o = torch.empty_like(dq)
+    lse = None
     if entry == "attn_fwd":
         A.attn_fwd(dq, dk, dv, o, scale, mask_mode, params)
-    else:
+    elif entry == "attn_fwd_ws":
         ws = split_workspace(*dq.shape, mask_mode, params)
         A.attn_fwd_ws(dq, dk, dv, o, scale, mask_mode, params, ws)
+    else:
+        B, H, Nq, d = dq.shape
+        ws = split_workspace(B, H, Nq, d, mask_mode, params, n_kv=dk.shape[2])
+        if want_lse:
+            lse = torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
+        A.attn_fwd_ex(dq, dk, dv, o, lse, scale, mask_mode, params, ws)
     torch.cuda.synchronize()
-    return o
+    return (o, lse) if want_lse else o
 
 
-def check_case(q, k, v, scale, mask: str, params=None, rows=None, what="", entry="attn_fwd") -> float:
-    """Run the HIP path and the oracle on the same bf16 inputs and compare (all rows or `rows`)."""
-    import exact_attention_68_amd as A
+MASK_MODES = {"none": 0, "causal": 1, "na2d": 2, "na3d": 3}
 
-    mode = {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D}[mask]
-    print(f"[parity] {entry} {what} B{q.shape[0]} H{q.shape[1]} N{q.shape[2]} d{q.shape[3]} mask={mask} "
-          f"scale={scale}", flush=True)
-    o = run_gpu(q, k, v, scale, mode, params, entry)
+# logsumexp: the row sum of bfloat16-rounded probabilities is within 2^-8 (relative) of the
+# exact sum, so log l is within log(1 + 2^-8) = 3.9e-3; the float32 scores, exp2 and log2
+# add far less. Bound: |gpu - ref| <= 6e-3 + 1e-5 * |ref|.
+def lse_tolerance(ref: np.ndarray) -> np.ndarray:
+    return 6e-3 + 1e-5 * np.abs(ref)
+
+
+def check_case(q, k, v, scale, mask: str, params=None, rows=None, what="", entry="attn_fwd",
+               want_lse=None) -> float:
+    """Run the HIP path and the oracle on the same bf16 inputs and compare (all rows or `rows`).
+    With attn_fwd_ex the logsumexp is compared too (unless want_lse is False)."""
+    mode = MASK_MODES[mask]
+    want_lse = entry == "attn_fwd_ex" if want_lse is None else want_lse
+    print(f"[parity] {entry} {what} B{q.shape[0]} H{q.shape[1]} Nq{q.shape[2]} Nkv{k.shape[2]} d{q.shape[3]} "
+          f"mask={mask} scale={scale}", flush=True)
+    res = run_gpu(q, k, v, scale, mode, params, entry, want_lse)
+    o, lse = res if want_lse else (res, None)
     got = to_f64(o)
-    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale, mask, oracle_na2d(params), rows=rows)
+    ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale, mask, oracle_na(params), rows=rows,
+                                    return_lse=True)
     if rows is not None:
         got = got[:, :, rows]
-    return compare(got, ref, what or mask)
+    worst = compare(got, ref, what or mask)
+    if want_lse:
+        g = lse.cpu().numpy().astype(np.float64)
+        if rows is not None:
+            g = g[:, :, rows]
+        assert np.all(np.isfinite(g)), f"{what}: non-finite logsumexp"
+        ratio = np.abs(g - ref_lse) / lse_tolerance(ref_lse)
+        if ratio.max() > 1.0:
+            idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+            raise AssertionError(f"{what}: logsumexp {int((ratio > 1).sum())} of {ratio.size} out of tolerance; "
+                                 f"worst err/tol {ratio.max():.3f} at {idx}: got {g[idx]}, ref {ref_lse[idx]}")
+        worst = max(worst, float(ratio.max()))
+    return worst
 
 
 def workload_params(w: workloads.Workload):
     import exact_attention_68_amd as A
 
-    return A.na2d_params(**w.na2d) if w.mask == "na2d" else None
+    if w.mask == "na2d":
+        return A.na2d_params(**w.na)
+    if w.mask == "na3d":
+        return A.na3d_params(**w.na)
+    return None

@@ -30,6 +30,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol(A):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_fwd_check",
+                          "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check",
                           "attn_status_string", "attn_abi_version"}
     lib = A.lib()
     for n in names:
@@ -70,7 +71,24 @@ def test_check_codes(A):
     assert A.attn_fwd_check(2, 4, 4096, 32, 0.1, A.ATTN_MASK_NA2D, A.na2d_params(64, 64, 8, 7)) == A.ATTN_ERR_PARAMS
     assert A.attn_fwd_check(2, 4, 4096, 32, 0.1, A.ATTN_MASK_NA2D, A.na2d_params(64, 64, 7, 7, 1, 3)) == A.ATTN_ERR_PARAMS
     assert A.attn_fwd_check(2, 4, 4096, 32, 0.1, A.ATTN_MASK_NA2D,
-                            A.na2d_params(64, 64, 7, 7, dil_h=2)) == A.ATTN_ERR_PARAMS
+                            A.na2d_params(64, 64, 7, 7, dil_h=2)) == A.ATTN_OK
+    assert A.attn_fwd_check(2, 4, 4096, 32, 0.1, A.ATTN_MASK_NA2D,
+                            A.na2d_params(64, 64, 7, 7, dil_h=11)) == A.ATTN_ERR_PARAMS
+    assert A.attn_fwd_check(2, 4, 4096, 32, 0.1, A.ATTN_MASK_NA2D,
+                            A.na2d_params(64, 64, 7, 7, 1, 0, 1, 10)) == A.ATTN_ERR_PARAMS
+    assert A.attn_fwd_check(2, 5, 4096, 128, 0.125) == A.ATTN_OK
+    p3 = A.na3d_params(20, 20, 20, 5, 5, 5, 1, 1, 0)
+    assert A.attn_fwd_check(2, 4, 8000, 32, 0.1, A.ATTN_MASK_NA3D, p3) == A.ATTN_OK
+    assert A.attn_fwd_check(2, 4, 8000, 32, 0.1, A.ATTN_MASK_NA3D, A.na3d_params(20, 20, 19, 5, 5, 5)) == A.ATTN_ERR_PARAMS
+    assert A.attn_fwd_check(2, 4, 8000, 32, 0.1, A.ATTN_MASK_NA3D, None) == A.ATTN_ERR_INVALID_ARG
+
+
+def test_ex_check_codes(A):
+    assert A.attn_fwd_ex_check(2, 5, 4096, 77, 64, 0.125) == A.ATTN_OK
+    assert A.attn_fwd_ex_check(2, 5, 100, 4096, 128, 0.125, A.ATTN_MASK_CAUSAL) == A.ATTN_OK
+    assert A.attn_fwd_ex_check(2, 5, 4096, 0, 64, 0.125) == A.ATTN_ERR_INVALID_ARG
+    assert A.attn_fwd_ex_check(2, 4, 4096, 4095, 32, 0.1, A.ATTN_MASK_NA2D, A.na2d_params(64, 64, 7, 7)) == \
+        A.ATTN_ERR_PARAMS
 
 
 def test_fwd_rejects_before_device_work(A):
@@ -104,6 +122,29 @@ def test_ws_entry_points_reject_before_device_work(A):
     assert lib.attn_fwd_ws(q, k, v, o, 1, 1, 64, 96, 0.1, 0, None, ws, 1 << 20, None) == A.ATTN_ERR_UNSUPPORTED
     assert lib.attn_fwd_ws(q, k, v, o, 1, 1, 64, 64, float("nan"), 0, None, ws, 1 << 20,
                            None) == A.ATTN_ERR_INVALID_ARG
+
+
+def test_ex_entry_points_reject_before_device_work(A):
+    """attn_fwd_ex and attn_fwd_ex_workspace_size check every argument before touching a device."""
+    import ctypes
+
+    lib = A.lib()
+    base = 1 << 20
+    q, k, v, o, lse = base, base + (1 << 16), base + (2 << 16), base + (3 << 16), base + (4 << 16)
+    n = ctypes.c_uint64(7)
+    assert lib.attn_fwd_ex_workspace_size(1, 1, 64, 64, 64, 0, None, None) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_ex_workspace_size(1, 1, 64, 0, 64, 0, None, ctypes.byref(n)) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_ex_workspace_size(1, 1, 64, 64, 48, 0, None, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    assert n.value == 7
+    args = (1, 1, 64, 32, 64, 0.1, 0, None, None, 0, None)
+    assert lib.attn_fwd_ex(None, k, v, o, lse, *args) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_ex(q, k, v, o, lse + 2, *args) == A.ATTN_ERR_ALIGNMENT
+    assert lib.attn_fwd_ex(q, k, v, o, o + 64, *args) == A.ATTN_ERR_INVALID_ARG      # lse inside o
+    assert lib.attn_fwd_ex(q, k, v, k + 1024, lse, *args) == A.ATTN_ERR_INVALID_ARG  # o inside k
+    assert lib.attn_fwd_ex(q, k, v, o, lse, 1, 1, 64, 32, 96, 0.1, 0, None, None, 0, None) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_fwd_ex(q, k, v, o, lse, 1, 1, 64, 32, 64, 0.1, A.ATTN_MASK_NA2D,
+                           ctypes.cast(ctypes.pointer(A.na2d_params(8, 8, 3, 3)), ctypes.c_void_p),
+                           None, 0, None) == A.ATTN_ERR_PARAMS                      # neighbourhood needs Nq = Nkv
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
