@@ -39,12 +39,15 @@ attn::SplitPlan plan_for(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t 
 }
 
 // Kernel mask kind for a checked problem: the block-masked neighbourhood kernel
-// for undilated 2D windows on grids of width 32, 64, 96 or 128.
+// for undilated 2D windows on grids of width 32, 64, 96 or 128; the grid-mask
+// kernel for other grids of width 4..124 with rows and planes <= 128; the element
+// predicate for the rest.
 int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
   if (p.mask == ATTN_MASK_NONE) return attn::MASK_NONE;
   if (p.mask == ATTN_MASK_CAUSAL) return attn::MASK_CAUSAL;
   const bool blocks = g.grid_d == 1 && g.dil_h == 1 && g.dil_w == 1 && g.grid_w % 32 == 0 && g.grid_w <= 128;
-  return blocks ? attn::MASK_NA_BLOCKS : attn::MASK_NA;
+  if (blocks) return attn::MASK_NA_BLOCKS;
+  return attn::na_grid_eligible(g) ? attn::MASK_NA_GRID : attn::MASK_NA;
 }
 
 attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void* workspace, void* stream) {

@@ -339,6 +339,11 @@ void attn_fwd_kernel(KernelArgs a) {
   constexpr bool NA_BLOCKS = MASK == MASK_NA_BLOCKS;
   uint32_t col_bits[2] = {0u, 0u};
   if (NA_BLOCKS) na_col_bits(xq, half, a.na.grid_w, a.na.kernel_w, a.na.rad_w, a.na.wrap_w, a.na_phases, col_bits);
+  // Other grids of width 4..124 (3D, dilated): one window mask per axis and lane (GridMasks).
+  constexpr bool NA_GRID = MASK == MASK_NA_GRID;
+  constexpr bool NA_BITS = NA_BLOCKS || NA_GRID;
+  GridMasks gm{};
+  if constexpr (NA_GRID) gm = na_grid_masks(zq, yq, xq, a.na);
 
 
   const int32_t n = run.count;
@@ -487,12 +492,36 @@ void attn_fwd_kernel(KernelArgs a) {
       bm[sb] = rok ? cb : 0u;
     }
   };
+  // Per 32-key block of key tile t, the lane's 16-bit window mask on a grid of
+  // width 4..124: the tile's row bits once, then each group of 4 consecutive keys
+  // from the column mask (na_grid_nibble). Keys past Nkv lie in rows past the grid.
+  auto grid_bits = [&](int32_t t, uint32_t (&bm)[SB]) {
+    const int32_t W = a.na.grid_w;
+    const int32_t k0 = t * C::BN;
+    const int32_t row0 = k0 / W;  // uniform: one division per tile
+    const int32_t x0 = k0 - row0 * W;
+    const uint64_t trow = na_tile_rows(gm, row0, na_tile_row_count(x0, C::BN, W), a.na);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // column offset from the tile's first row; (n + 0.5) / W truncates exactly for n < W + BN
+        const int32_t n = x0 + sb * 32 + 8 * g4 + 4 * half;
+        const int32_t dy = (int32_t)(((float)n + 0.5f) * a.na_inv_w);
+        m |= na_grid_nibble(gm, trow, dy, n - dy * W, W) << (4 * g4);
+      }
+      bm[sb] = m;
+    }
+  };
   // The 16-bit element masks of key tile t for a bit-masked step: the window bits
-  // for the structured neighbourhood grids, else the keys up to the lane's last
-  // visible one (its query for the causal mask, Nkv - 1 for a ragged last tile).
+  // for the neighbourhood grids, else the keys up to the lane's last visible one
+  // (its query for the causal mask, Nkv - 1 for a ragged last tile).
   auto tile_bits = [&](int32_t t, uint32_t (&bm)[SB]) {
     if constexpr (NA_BLOCKS) {
       block_masks(t, bm);
+    } else if constexpr (NA_GRID) {
+      grid_bits(t, bm);
     } else {
       int32_t last = Nkv - 1;
       if constexpr (MASK == MASK_CAUSAL) last = last < my_q ? last : my_q;
@@ -531,9 +560,9 @@ void attn_fwd_kernel(KernelArgs a) {
     f32x16_t s[SB];
     qk_tile(k_lds[0], s);
     const bool masked = tile_needs_mask(MASK, Nkv, C::BN, q0, t0);
-    if constexpr (NA_BLOCKS) {
+    if constexpr (NA_BITS) {
       uint32_t bm0[SB];
-      block_masks(t0, bm0);
+      tile_bits(t0, bm0);
       apply_bits(s, bm0);
     } else {
       if (masked) apply_mask(s, t0);
@@ -736,7 +765,7 @@ void attn_fwd_kernel(KernelArgs a) {
       ++j;
     }
   };
-  if constexpr (NA_BLOCKS) {
+  if constexpr (NA_BITS) {
     fast_loop(n - 1, std::true_type{});
   } else if constexpr (MASK != MASK_NA) {
     int32_t n_fast = 0;  // steps whose next tile needs no element mask
@@ -903,6 +932,7 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
     case MASK_CAUSAL: return launch_one<D, MASK_CAUSAL, false>(a, n_wg, stream);
     case MASK_NA: return launch_one<D, MASK_NA, false>(a, n_wg, stream);
     case MASK_NA_BLOCKS: return launch_one<D, MASK_NA_BLOCKS, false>(a, n_wg, stream);
+    case MASK_NA_GRID: return launch_one<D, MASK_NA_GRID, false>(a, n_wg, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -25,11 +25,13 @@
 
 namespace attn {
 
-// Kernel mask kinds. MASK_NA covers the 2D and 3D neighbourhood windows with any
-// dilation (an element predicate); MASK_NA_BLOCKS is the 2D, undilated window on
-// grids whose width is a multiple of 32 (at most 128), tested on per-block bit masks.
-enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3 };
-constexpr bool is_na(int mask) { return mask == MASK_NA || mask == MASK_NA_BLOCKS; }
+// Kernel mask kinds. MASK_NA covers every 2D and 3D neighbourhood window with any
+// dilation (an element predicate). The bit-mask kinds cover the common grids:
+// MASK_NA_BLOCKS the 2D, undilated window on grids whose width is a multiple of
+// 32 (at most 128); MASK_NA_GRID any window on grids of width 4..124 whose
+// height and depth are at most 128 (na_grid_eligible).
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3, MASK_NA_GRID = 4 };
+constexpr bool is_na(int mask) { return mask == MASK_NA || mask == MASK_NA_BLOCKS || mask == MASK_NA_GRID; }
 
 // Neighbourhood geometry in the form the kernel uses. Token n sits at depth
 // z = n / (grid_h * grid_w), row y and column x of its plane (row-major); a 2D
@@ -163,6 +165,91 @@ constexpr bool na_dil_ok(int32_t anchor, int32_t ck, int32_t len, int32_t kernel
   }
   const int32_t off = ck - anchor;
   return (uint32_t)off <= (uint32_t)((kernel - 1) * dil) && off % dil == 0;
+}
+
+// ---------------------------------------------------------------------------
+// Grid-window bit masks (MASK_NA_GRID).
+//
+// A query's window is the product of one window per axis, so each lane keeps one
+// bit mask per axis: bit c of an axis mask says whether coordinate c lies in the
+// query's window along that axis (the dilated cells of na_dil_ok). A key tile's
+// rows (over all planes) then get one bit each, and the 4 consecutive keys that
+// a lane holds in each group of an MFMA block (a "nibble") get their column bits
+// from the column mask and their row bits from the tile's row mask; a nibble
+// spans at most two grid rows when the width is at least 4.
+constexpr bool na_grid_eligible(const NaGeom& g) {
+  return g.grid_w >= 4 && g.grid_w <= 124 && g.grid_h <= 128 && g.grid_d <= 128;
+}
+
+// Per-axis window masks of one query, as pairs of 64-bit words (bit c of the pair
+// is coordinate c). Named words, not arrays: an array indexed by a lane-dependent
+// value would be placed in scratch memory.
+struct GridMasks {
+  uint64_t x0, x1;  // columns; bits [W, W + 4) repeat bits [0, 4) (a nibble running into the next row)
+  uint64_t y0, y1;  // rows of a plane
+  uint64_t z0, z1;  // planes
+};
+
+// Window cells of coordinate c along one axis (len <= 128) as a 128-bit mask (lo, hi).
+constexpr void na_axis_mask(int32_t c, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil,
+                            uint64_t& lo, uint64_t& hi) {
+  lo = hi = 0;
+  const int32_t anchor = na_dil_anchor(c, len, kernel, rad, wrap, dil);
+  for (int32_t t = 0; t < kernel; ++t) {
+    const int32_t cell = wrap ? imod(c + dil * (t - rad), len) : anchor + dil * t;
+    const uint64_t bit = 1ull << (cell & 63);
+    lo |= cell < 64 ? bit : 0ull;
+    hi |= cell < 64 ? 0ull : bit;
+  }
+}
+
+constexpr GridMasks na_grid_masks(int32_t zq, int32_t yq, int32_t xq, const NaGeom& g) {
+  GridMasks m{};
+  na_axis_mask(xq, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w, m.x0, m.x1);
+  na_axis_mask(yq, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h, m.y0, m.y1);
+  na_axis_mask(zq, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d, m.z0, m.z1);
+  // repeat columns 0..3 at W..W+3 (W <= 124, so they stay inside the 128 bits)
+  const int32_t W = g.grid_w;
+  const uint64_t head = m.x0 & 0xFull;
+  m.x0 |= W < 64 ? head << (W & 63) : 0ull;
+  m.x1 |= W < 64 ? (W > 60 ? head >> ((64 - W) & 63) : 0ull) : head << ((W - 64) & 63);
+  return m;
+}
+
+// Bit c of a 128-bit mask (lo, hi), c < 128.
+constexpr uint64_t bit128(uint64_t lo, uint64_t hi, int32_t c) { return ((c < 64 ? lo : hi) >> (c & 63)) & 1ull; }
+
+// Row bits of a key tile: bit r says whether grid row row0 + r (counting rows over
+// all planes) is in the query's window along the depth and row axes; rows past
+// the last one (keys past N) are 0. n_rows <= 64.
+constexpr uint64_t na_tile_rows(const GridMasks& m, int32_t row0, int32_t n_rows, const NaGeom& g) {
+  uint64_t bits = 0;
+  int32_t z = row0 / g.grid_h, y = row0 - z * g.grid_h;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (z < g.grid_d) bits |= (bit128(m.z0, m.z1, z) & bit128(m.y0, m.y1, y)) << r;
+    if (++y == g.grid_h) {
+      y = 0;
+      ++z;
+    }
+  }
+  return bits;
+}
+
+// Rows a key tile of BN keys starting at column x0 touches, plus one for a nibble
+// that runs into the next row.
+constexpr int32_t na_tile_row_count(int32_t x0, int32_t BN, int32_t W) { return (x0 + BN - 1) / W + 2; }
+
+// 4-bit mask of the keys at column x .. x + 3 of tile row dy (columns past the
+// row's end continue in row dy + 1): column bits from the column mask, row bits
+// from the tile's row mask.
+constexpr uint32_t na_grid_nibble(const GridMasks& m, uint64_t trow, int32_t dy, int32_t x, int32_t W) {
+  // bits x .. x + 3 of the 128-bit column mask (x + 3 < 128)
+  const uint64_t low = (m.x0 >> (x & 63)) | (x > 60 && x < 64 ? m.x1 << ((64 - x) & 63) : 0ull);
+  const uint32_t col = (uint32_t)(x < 64 ? low : m.x1 >> (x & 63)) & 0xFu;
+  const int32_t first = imin(W - x, 4);          // keys still in row dy
+  const uint32_t lim = (1u << first) - 1u;
+  const uint32_t r0 = (uint32_t)(trow >> dy) & 1u, r1 = (uint32_t)(trow >> (dy + 1)) & 1u;
+  return col & ((r0 ? lim : 0u) | (r1 ? (~lim & 0xFu) : 0u));
 }
 
 // Bits [a, b) of a 128-bit column mask, in its 64-bit half h (bit i = column 64h + i).

@@ -112,6 +112,38 @@ static void check_na_geom(const NaGeom& g, int BM, int BN) {
   }
 }
 
+// The grid-window bit masks (nibbles of 4 keys from per-axis masks and tile row bits)
+// agree with the enumerated window for every query and key tile.
+static void check_grid_bits(const NaGeom& g, int BN) {
+  if (!geom_valid(g) || !na_grid_eligible(g)) return;
+  const int W = g.grid_w, plane = g.grid_h * W, N = g.grid_d * plane;
+  const int n_tiles = (int)cdiv(N, BN);
+  for (int q = 0; q < N; ++q) {
+    const GridMasks m = na_grid_masks(q / plane, q % plane / W, q % W, g);
+    const std::set<int> want = window_keys(g, q);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int k0 = t * BN, row0 = k0 / W, x0 = k0 - row0 * W;
+      const int n_rows = na_tile_row_count(x0, BN, W);
+      EXPECT(n_rows <= 64, "tile rows %d", n_rows);
+      const uint64_t trow = na_tile_rows(m, row0, n_rows, g);
+      for (int half = 0; half < 2; ++half)
+        for (int sb = 0; sb < BN / 32; ++sb)
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int off = sb * 32 + 8 * g4 + 4 * half;
+            const int dy = (x0 + off) / W, x = x0 + off - dy * W;
+            const uint32_t nib = na_grid_nibble(m, trow, dy, x, W);
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + off + i;
+              const bool w = key < N && want.count(key) == 1;
+              EXPECT((((nib >> i) & 1u) == 1u) == w, "grid bits %dx%dx%d k %d,%d,%d wrap %d%d%d dil %d,%d,%d BN %d q %d key %d",
+                     g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w,
+                     g.dil_d, g.dil_h, g.dil_w, BN, q, key);
+            }
+          }
+    }
+  }
+}
+
 static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int BN) {
   check_na_geom(geom(1, gh, gw, 1, kh, kw, 0, wh, ww, 1, 1, 1), BM, BN);
 }
@@ -331,6 +363,19 @@ int main() {
                   check_na_geom(geom(gd[0], gd[1], gd[2], kd, kh, 3, wd, wh, ww, dd, 1, gd[2] >= 7 ? 2 : 1), kBlockM, BN);
     check_na_geom(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), kBlockM, BN);
     check_na_geom(geom(16, 16, 16, 3, 3, 3, 1, 0, 1, 2, 2, 2), kBlockM, BN);
+  }
+  // grid-window bit masks: widths 4..124 (incl. 61..64, where the repeated columns cross a word), 3D, dilation
+  for (int BN : {64, 128}) {
+    for (int W : {4, 5, 7, 20, 31, 33, 40, 61, 62, 63, 64, 65, 100, 124})
+      for (int kw : {1, 3, 5})
+        for (int ww = 0; ww < 2; ++ww)
+          check_grid_bits(geom(1, 3, W, 1, 3, kw, 0, 1, ww, 1, 1, W >= 20 ? 2 : 1), BN);
+    check_grid_bits(geom(4, 5, 6, 3, 3, 3, 1, 0, 1, 1, 1, 1), BN);
+    check_grid_bits(geom(6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2), BN);
+    check_grid_bits(geom(10, 9, 8, 3, 3, 3, 0, 0, 0, 3, 3, 2), BN);
+    check_grid_bits(geom(3, 4, 20, 3, 3, 5, 1, 1, 0, 1, 1, 3), BN);
+    check_grid_bits(geom(2, 66, 4, 1, 5, 3, 0, 1, 1, 1, 9, 1), BN);   // 66 rows: row bits in the upper word
+    check_grid_bits(geom(70, 2, 4, 5, 1, 1, 1, 0, 0, 3, 1, 1), BN);   // 70 planes
   }
   for (int mask : {MASK_NONE, MASK_CAUSAL})
     for (int BH : {1, 3, 8, 10, 64})

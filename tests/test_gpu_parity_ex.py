@@ -154,6 +154,24 @@ def test_na2d_dilated(gh, gw, kh, kw, wh, ww, dh, dw, d):
                what=f"na2d {gh}x{gw} k{kh}x{kw} wrap{wh}{ww} dil{dh}{dw}", entry=EX)
 
 
+# ---------------------------------------------------------------- the element-predicate fallback
+# Grids outside the bit-mask kernels' range: width below 4 or above 124, more than 128 rows.
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("mode,geo", [
+    ("na2d", (40, 3, 5, 3, 1, 1, 2, 1)),
+    ("na2d", (2, 200, 1, 7, 0, 1, 1, 3)),
+    ("na3d", (3, 4, 2, 3, 3, 1, 1, 0, 1, 1, 1, 1)),
+    ("na3d", (2, 130, 4, 1, 5, 3, 0, 1, 1, 1, 2, 1)),
+])
+def test_na_element_predicate_path(mode, geo, d):
+    import exact_attention_68_amd as A
+
+    params = A.na2d_params(*geo) if mode == "na2d" else A.na3d_params(*geo)
+    N = geo[0] * geo[1] * (geo[2] if mode == "na3d" else 1)
+    q, k, v = _qkv(1, 2, N, N, d, 9750 + N)
+    check_case(q, k, v, 1 / math.sqrt(d), mode, params, what=f"{mode} predicate path {geo}", entry=EX)
+
+
 # ---------------------------------------------------------------- logsumexp on the rare paths
 @pytest.mark.parametrize("q_gain", [1.0, 2.0])
 def test_lse_split_path(q_gain):
