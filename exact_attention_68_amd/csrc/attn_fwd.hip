@@ -493,26 +493,14 @@ void attn_fwd_kernel(KernelArgs a) {
     }
   };
   // Per 32-key block of key tile t, the lane's 16-bit window mask on a grid of
-  // width 4..124: the tile's row bits once, then each group of 4 consecutive keys
-  // from the column mask (na_grid_nibble). Keys past Nkv lie in rows past the grid.
+  // width 4..124: the tile's window (na_tile_window), then the lane's own keys.
   auto grid_bits = [&](int32_t t, uint32_t (&bm)[SB]) {
-    const int32_t W = a.na.grid_w;
     const int32_t k0 = t * C::BN;
-    const int32_t row0 = k0 / W;  // uniform: one division per tile
-    const int32_t x0 = k0 - row0 * W;
-    const uint64_t trow = na_tile_rows(gm, row0, na_tile_row_count(x0, C::BN, W), a.na);
+    const int32_t row0 = k0 / a.na.grid_w;  // uniform: one division per tile
+    uint32_t w[SB];
+    na_tile_window(gm, row0, k0 - row0 * a.na.grid_w, a.na, w);
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // column offset from the tile's first row; (n + 0.5) / W truncates exactly for n < W + BN
-        const int32_t n = x0 + sb * 32 + 8 * g4 + 4 * half;
-        const int32_t dy = (int32_t)(((float)n + 0.5f) * a.na_inv_w);
-        m |= na_grid_nibble(gm, trow, dy, n - dy * W, W) << (4 * g4);
-      }
-      bm[sb] = m;
-    }
+    for (int sb = 0; sb < SB; ++sb) bm[sb] = lane_block_bits(w[sb], half);
   };
   // The 16-bit element masks of key tile t for a bit-masked step: the window bits
   // for the neighbourhood grids, else the keys up to the lane's last visible one

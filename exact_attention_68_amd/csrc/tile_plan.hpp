@@ -172,11 +172,11 @@ constexpr bool na_dil_ok(int32_t anchor, int32_t ck, int32_t len, int32_t kernel
 //
 // A query's window is the product of one window per axis, so each lane keeps one
 // bit mask per axis: bit c of an axis mask says whether coordinate c lies in the
-// query's window along that axis (the dilated cells of na_dil_ok). A key tile's
-// rows (over all planes) then get one bit each, and the 4 consecutive keys that
-// a lane holds in each group of an MFMA block (a "nibble") get their column bits
-// from the column mask and their row bits from the tile's row mask; a nibble
-// spans at most two grid rows when the width is at least 4.
+// query's window along that axis (the dilated cells of na_dil_ok). For a key
+// tile, one pass over the grid rows it touches ORs the column mask, shifted to
+// where each row starts in the tile, into a tile mask wherever the row's plane and
+// row bits are set; the shifts are the same for every lane. Each lane then takes
+// the 16 bits of its own keys in each 32-key block.
 constexpr bool na_grid_eligible(const NaGeom& g) {
   return g.grid_w >= 4 && g.grid_w <= 124 && g.grid_h <= 128 && g.grid_d <= 128;
 }
@@ -185,7 +185,7 @@ constexpr bool na_grid_eligible(const NaGeom& g) {
 // is coordinate c). Named words, not arrays: an array indexed by a lane-dependent
 // value would be placed in scratch memory.
 struct GridMasks {
-  uint64_t x0, x1;  // columns; bits [W, W + 4) repeat bits [0, 4) (a nibble running into the next row)
+  uint64_t x0, x1;  // columns
   uint64_t y0, y1;  // rows of a plane
   uint64_t z0, z1;  // planes
 };
@@ -208,48 +208,47 @@ constexpr GridMasks na_grid_masks(int32_t zq, int32_t yq, int32_t xq, const NaGe
   na_axis_mask(xq, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w, m.x0, m.x1);
   na_axis_mask(yq, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h, m.y0, m.y1);
   na_axis_mask(zq, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d, m.z0, m.z1);
-  // repeat columns 0..3 at W..W+3 (W <= 124, so they stay inside the 128 bits)
-  const int32_t W = g.grid_w;
-  const uint64_t head = m.x0 & 0xFull;
-  m.x0 |= W < 64 ? head << (W & 63) : 0ull;
-  m.x1 |= W < 64 ? (W > 60 ? head >> ((64 - W) & 63) : 0ull) : head << ((W - 64) & 63);
   return m;
 }
 
 // Bit c of a 128-bit mask (lo, hi), c < 128.
 constexpr uint64_t bit128(uint64_t lo, uint64_t hi, int32_t c) { return ((c < 64 ? lo : hi) >> (c & 63)) & 1ull; }
 
-// Row bits of a key tile: bit r says whether grid row row0 + r (counting rows over
-// all planes) is in the query's window along the depth and row axes; rows past
-// the last one (keys past N) are 0. n_rows <= 64.
-constexpr uint64_t na_tile_rows(const GridMasks& m, int32_t row0, int32_t n_rows, const NaGeom& g) {
-  uint64_t bits = 0;
+// Bits o .. o + 31 of a 128-bit mask (lo, hi); bits below 0 or past 127 read as 0.
+constexpr uint32_t mask_bits32(uint64_t lo, uint64_t hi, int32_t o) {
+  if (o <= -32 || o >= 128) return 0u;
+  if (o < 0) return (uint32_t)(lo << (-o));
+  if (o < 64) return (uint32_t)((lo >> o) | (o > 32 ? hi << (64 - o) : 0ull));
+  return (uint32_t)(hi >> (o - 64));
+}
+
+// Window of one query over a key tile of 32 * WORDS keys starting at grid row row0,
+// column x0 (rows counted over all planes): bit i of w[i / 32] says whether key
+// k0 + i lies in the window; keys past the last row read as 0. Every branch and
+// shift depends on the tile only, not on the lane.
+template <int WORDS>
+constexpr void na_tile_window(const GridMasks& m, int32_t row0, int32_t x0, const NaGeom& g, uint32_t (&w)[WORDS]) {
+  for (int i = 0; i < WORDS; ++i) w[i] = 0u;
   int32_t z = row0 / g.grid_h, y = row0 - z * g.grid_h;
-  for (int32_t r = 0; r < n_rows; ++r) {
-    if (z < g.grid_d) bits |= (bit128(m.z0, m.z1, z) & bit128(m.y0, m.y1, y)) << r;
+  for (int32_t sh = -x0; sh < 32 * WORDS && z < g.grid_d; sh += g.grid_w) {  // sh: tile offset of the row's column 0
+    const bool ok = (bit128(m.z0, m.z1, z) & bit128(m.y0, m.y1, y)) != 0;
+    for (int i = 0; i < WORDS; ++i) {
+      const int32_t o = 32 * i - sh;  // column at bit 0 of word i
+      if (o > -32 && o < g.grid_w) w[i] |= ok ? mask_bits32(m.x0, m.x1, o) : 0u;
+    }
     if (++y == g.grid_h) {
       y = 0;
       ++z;
     }
   }
-  return bits;
 }
 
-// Rows a key tile of BN keys starting at column x0 touches, plus one for a nibble
-// that runs into the next row.
-constexpr int32_t na_tile_row_count(int32_t x0, int32_t BN, int32_t W) { return (x0 + BN - 1) / W + 2; }
-
-// 4-bit mask of the keys at column x .. x + 3 of tile row dy (columns past the
-// row's end continue in row dy + 1): column bits from the column mask, row bits
-// from the tile's row mask.
-constexpr uint32_t na_grid_nibble(const GridMasks& m, uint64_t trow, int32_t dy, int32_t x, int32_t W) {
-  // bits x .. x + 3 of the 128-bit column mask (x + 3 < 128)
-  const uint64_t low = (m.x0 >> (x & 63)) | (x > 60 && x < 64 ? m.x1 << ((64 - x) & 63) : 0ull);
-  const uint32_t col = (uint32_t)(x < 64 ? low : m.x1 >> (x & 63)) & 0xFu;
-  const int32_t first = imin(W - x, 4);          // keys still in row dy
-  const uint32_t lim = (1u << first) - 1u;
-  const uint32_t r0 = (uint32_t)(trow >> dy) & 1u, r1 = (uint32_t)(trow >> (dy + 1)) & 1u;
-  return col & ((r0 ? lim : 0u) | (r1 ? (~lim & 0xFu) : 0u));
+// The 16 keys a lane holds in a 32-key MFMA block are block offsets 8g + 4*half +
+// (0..3), g = 0..3; element r = 4g + j of the block. Gathers their bits from the
+// block's word of a tile mask.
+constexpr uint32_t lane_block_bits(uint32_t w, int32_t half) {
+  const uint32_t v = w >> (4 * half);
+  return (v & 0xFu) | ((v >> 4) & 0xF0u) | ((v >> 8) & 0xF00u) | ((v >> 12) & 0xF000u);
 }
 
 // Bits [a, b) of a 128-bit column mask, in its 64-bit half h (bit i = column 64h + i).

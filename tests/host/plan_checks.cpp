@@ -112,36 +112,40 @@ static void check_na_geom(const NaGeom& g, int BM, int BN) {
   }
 }
 
-// The grid-window bit masks (nibbles of 4 keys from per-axis masks and tile row bits)
-// agree with the enumerated window for every query and key tile.
-static void check_grid_bits(const NaGeom& g, int BN) {
-  if (!geom_valid(g) || !na_grid_eligible(g)) return;
+// The grid-window bit masks (a tile window from the per-axis masks, then each
+// lane's 16 keys per block) agree with the enumerated window for every query and
+// key tile.
+template <int WORDS>
+static void check_grid_bits_bn(const NaGeom& g) {
+  const int BN = 32 * WORDS;
   const int W = g.grid_w, plane = g.grid_h * W, N = g.grid_d * plane;
   const int n_tiles = (int)cdiv(N, BN);
   for (int q = 0; q < N; ++q) {
     const GridMasks m = na_grid_masks(q / plane, q % plane / W, q % W, g);
     const std::set<int> want = window_keys(g, q);
     for (int t = 0; t < n_tiles; ++t) {
-      const int k0 = t * BN, row0 = k0 / W, x0 = k0 - row0 * W;
-      const int n_rows = na_tile_row_count(x0, BN, W);
-      EXPECT(n_rows <= 64, "tile rows %d", n_rows);
-      const uint64_t trow = na_tile_rows(m, row0, n_rows, g);
+      const int k0 = t * BN, row0 = k0 / W;
+      uint32_t w[WORDS];
+      na_tile_window(m, row0, k0 - row0 * W, g, w);
       for (int half = 0; half < 2; ++half)
-        for (int sb = 0; sb < BN / 32; ++sb)
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int off = sb * 32 + 8 * g4 + 4 * half;
-            const int dy = (x0 + off) / W, x = x0 + off - dy * W;
-            const uint32_t nib = na_grid_nibble(m, trow, dy, x, W);
-            for (int i = 0; i < 4; ++i) {
-              const int key = k0 + off + i;
-              const bool w = key < N && want.count(key) == 1;
-              EXPECT((((nib >> i) & 1u) == 1u) == w, "grid bits %dx%dx%d k %d,%d,%d wrap %d%d%d dil %d,%d,%d BN %d q %d key %d",
-                     g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w,
-                     g.dil_d, g.dil_h, g.dil_w, BN, q, key);
-            }
+        for (int sb = 0; sb < WORDS; ++sb) {
+          const uint32_t bits = lane_block_bits(w[sb], half);
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool x = key < N && want.count(key) == 1;
+            EXPECT((((bits >> r) & 1u) == 1u) == x, "grid bits %dx%dx%d k %d,%d,%d wrap %d%d%d dil %d,%d,%d BN %d q %d key %d",
+                   g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w,
+                   g.dil_d, g.dil_h, g.dil_w, BN, q, key);
           }
+        }
     }
   }
+}
+
+static void check_grid_bits(const NaGeom& g, int BN) {
+  if (!geom_valid(g) || !na_grid_eligible(g)) return;
+  if (BN == 64) check_grid_bits_bn<2>(g);
+  else check_grid_bits_bn<4>(g);
 }
 
 static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int BN) {
@@ -364,7 +368,7 @@ int main() {
     check_na_geom(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), kBlockM, BN);
     check_na_geom(geom(16, 16, 16, 3, 3, 3, 1, 0, 1, 2, 2, 2), kBlockM, BN);
   }
-  // grid-window bit masks: widths 4..124 (incl. 61..64, where the repeated columns cross a word), 3D, dilation
+  // grid-window bit masks: widths 4..124 (incl. 61..65 around the 64-bit word boundary), 3D, dilation
   for (int BN : {64, 128}) {
     for (int W : {4, 5, 7, 20, 31, 33, 40, 61, 62, 63, 64, 65, 100, 124})
       for (int kw : {1, 3, 5})
