@@ -16,6 +16,12 @@ For every batch b and head h, with Q of shape (Nq, d) and K, V of shape
     O = (P V) / l                          (rows with no allowed key give 0)
     LSE = m + log(l)                       (optional; -inf for such rows)
 
+and, for an output gradient dO (backward), with P = softmax(S):
+
+    dV = P^T dO,  dP = dO V^T
+    dS = P * (dP - rowsum(P * dP))         (the softmax Jacobian applied to dP)
+    dQ = scale * dS K,  dK = scale * dS^T Q
+
 Sources, as the pages state them:
   * Attention itself, S = Q K^T and R = softmax(S) V over (seqlen, d_head)
     tensors: AWS Neuron NKI tutorial "Fused Self Attention", section
@@ -40,6 +46,14 @@ Sources, as the pages state them:
     when it falls between the query's window start and end: the same issue,
     the replies on window_start/window_end and on clamping the sliding
     window to the edges.
+  * 3D neighbourhoods (the MR volumes of the same issue, wrapping in some
+    axes only) and dilation (the issue's 1D wrap recipe pads by
+    kernel // 2 * dilation before a dilated window).
+  * The logsumexp of each row, log(sum_j exp(S[i, j])), which the fused
+    forward of the same issue saves beside the output for the backward pass.
+  * The backward pass: the gradients of the forward with respect to Q, K and
+    V for an output gradient dO (the same issue's autograd function and its
+    gradcheck; its backward revisits query tiles per key tile).
 
 Readings taken where the pages leave a point open
 --------------------------------------------------
@@ -289,3 +303,48 @@ def probs(q, k, scale: float, mask: str = "none", na=None) -> np.ndarray:
             _, p, l = _softmax_parts(s)
             out[b, h] = np.where(l > 0, p / np.where(l > 0, l, 1.0), 0.0)
     return out
+
+
+def _softmax_grad(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """dS = P * (dP - rowsum(P * dP)): the Jacobian of a row softmax applied to dP."""
+    return p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+
+
+def _grad_v(p: np.ndarray, do: np.ndarray) -> np.ndarray:
+    """dV = P^T dO."""
+    return p.T @ do
+
+
+def _grad_q(ds: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """dQ = scale * dS K."""
+    return scale * (ds @ k)
+
+
+def _grad_k(ds: np.ndarray, q: np.ndarray, scale: float) -> np.ndarray:
+    """dK = scale * dS^T Q."""
+    return scale * (ds.T @ q)
+
+
+def masked_attention_backward(q, k, v, do, scale: float, allow: np.ndarray):
+    """One head: gradients (dq, dk, dv) of O = softmax(scale q k^T masked) v for output gradient do."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    s = _apply_mask(_scores(q, k, float(scale)), allow)
+    _, e, l = _softmax_parts(s)
+    p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)
+    ds = _softmax_grad(p, do @ v.T)
+    return _grad_q(ds, k, float(scale)), _grad_k(ds, q, float(scale)), _grad_v(p, do)
+
+
+def attention_backward(q, k, v, do, scale: float, mask: str = "none", na=None):
+    """Gradients (dq, dk, dv) of attention(q, k, v, scale, mask, na) for output gradient do [B, H, Nq, d];
+    float64, shaped like q, k and v."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if do.shape != q.shape:
+        raise ValueError("do must be shaped like q")
+    B, H, Nq, d = q.shape
+    allow = allowed(Nq, mask, na, n_kv=k.shape[2])
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = masked_attention_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, allow)
+    return dq, dk, dv

@@ -500,6 +500,118 @@ def pin_na3d_sdpa():
     assert np.max(np.abs(O.attention(q, k, v, 0.35, "na3d", p) - ref)) <= 1e-10
 
 
+# ---------------------------------------------------------------- backward
+def pin_backward_autograd_sdpa():
+    """Gradients against torch autograd through SDPA's math path in float64 (none, causal square and
+    cross, boolean window masks in 2D and 3D, a negative scale)."""
+    B, H, d = 1, 2, 6
+    F = torch.nn.functional.scaled_dot_product_attention
+    cases = (("none", None, 14, 14, 0.4), ("causal", None, 14, 14, 0.4), ("none", None, 9, 17, -0.3),
+             ("causal", None, 12, 7, 0.5), ("na2d", O.NA2D(4, 5, 3, 3, True, False, 1, 1), 20, 20, 0.45),
+             ("na3d", O.NA3D(3, 3, 5, 3, 1, 3, False, True, True, 1, 1, 2), 45, 45, 0.45))
+    for mask, na, nq, nkv, scale in cases:
+        q, k, v = _rand(240, B, H, nq, d), _rand(241, B, H, nkv, d), _rand(242, B, H, nkv, d)
+        do = _rand(243, B, H, nq, d)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        kw = {}
+        if mask == "causal":
+            kw["is_causal"] = True
+        elif mask in ("na2d", "na3d"):
+            m = np.zeros((nq, nkv), dtype=bool)
+            for i in range(nq):
+                m[i, _window_keys(i, mask, nq, na, nkv)] = True
+            kw["attn_mask"] = torch.from_numpy(m)
+        with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+            out = F(tq, tk, tv, scale=scale, **kw)
+        out.backward(torch.from_numpy(do))
+        got = O.attention_backward(q, k, v, do, scale, mask, na)
+        for g, t in zip(got, (tq, tk, tv)):
+            assert np.max(np.abs(g - t.grad.numpy())) <= 1e-10, (mask, nq, nkv)
+
+
+def pin_backward_finite_differences():
+    """Central differences of L = sum(dO * O) through the pure-Python forward, at every input element."""
+    for mask, na, n, nkv in (("causal", None, 4, 4), ("none", None, 3, 5), ("na2d", O.NA2D(2, 3, 1, 3, True, True), 6, 6)):
+        d = 3
+        q, k, v = _rand(250, 1, 1, n, d), _rand(251, 1, 1, nkv, d), _rand(252, 1, 1, nkv, d)
+        do = _rand(253, 1, 1, n, d)
+        scale = 0.7
+        dq, dk, dv = O.attention_backward(q, k, v, do, scale, mask, na)
+
+        def loss(qq, kk, vv):
+            out = brute_head(qq[0, 0].tolist(), kk[0, 0].tolist(), vv[0, 0].tolist(), scale, mask, na)
+            return math.fsum((out * do[0, 0]).ravel().tolist())
+
+        h = 1e-5
+        for which, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in np.ndindex(arr.shape):
+                plus, minus = arr.copy(), arr.copy()
+                plus[idx] += h
+                minus[idx] -= h
+                args_p = {"q": (plus, k, v), "k": (q, plus, v), "v": (q, k, plus)}[which]
+                args_m = {"q": (minus, k, v), "k": (q, minus, v), "v": (q, k, minus)}[which]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (mask, which, idx, fd, grad[idx])
+
+
+def pin_backward_identities():
+    """Rows of P sum to 1, so the key gradients of V add up to the output gradients; scale = 0 makes
+    dQ and dK vanish and dV the window-count-weighted sums of dO."""
+    B, H, d = 1, 2, 5
+    for mask, na, nq, nkv in (("none", None, 10, 13), ("causal", None, 11, 11),
+                              ("na2d", O.NA2D(4, 5, 3, 3, True, True, 1, 1), 20, 20),
+                              ("na3d", O.NA3D(3, 4, 5, 3, 3, 3, True, False, True, 1, 1, 2), 60, 60)):
+        q, k, v = _rand(260, B, H, nq, d), _rand(261, B, H, nkv, d), _rand(262, B, H, nkv, d)
+        do = _rand(263, B, H, nq, d)
+        dq, dk, dv = O.attention_backward(q, k, v, do, 0.6, mask, na)
+        assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= TIGHT, mask
+        # dQ_i = scale * sum_j dS_ij k_j with sum_j dS_ij = 0: adding one vector to every key changes nothing
+        shift = k + _rand(264, 1, 1, 1, d)
+        dq2, _, _ = O.attention_backward(q, shift, v, do, 0.6, mask, na)
+        assert np.max(np.abs(dq2 - dq)) <= 1e-10, mask
+        dq0, dk0, dv0 = O.attention_backward(q, k, v, do, 0.0, mask, na)
+        assert np.all(dq0 == 0.0) and np.all(dk0 == 0.0)
+        want = np.zeros_like(dv0)
+        for i in range(nq):
+            keys = _window_keys(i, mask, nq, na, nkv)
+            want[:, :, keys] += do[:, :, i:i + 1] / len(keys)
+        assert np.max(np.abs(dv0 - want)) <= TIGHT, mask
+
+
+def pin_backward_wrap_equals_pad_fold():
+    """NATTEN issue 142's 1D backward recipe in 2D: pad q, k, v circularly by r, pad dO with zeros, take the
+    clamped window's gradients on the padded grid, crop, and fold the margins back onto the cells they copy."""
+    B, H, d = 1, 2, 4
+    for gh, gw, kh, kw in ((5, 6, 3, 3), (6, 7, 5, 3)):
+        N = gh * gw
+        q, k, v = _rand(270, B, H, N, d), _rand(271, B, H, N, d), _rand(272, B, H, N, d)
+        do = _rand(273, B, H, N, d)
+        want = O.attention_backward(q, k, v, do, 0.5, "na2d", O.NA2D(gh, gw, kh, kw, True, True))
+        rh, rw = kh // 2, kw // 2
+        ph, pw = gh + 2 * rh, gw + 2 * rw
+        grid = lambda t: t.reshape(B, H, gh, gw, d)
+        pad = lambda t, mode: np.pad(grid(t), ((0, 0), (0, 0), (rh, rh), (rw, rw), (0, 0)), mode=mode).reshape(B, H, ph * pw, d)
+        got = O.attention_backward(pad(q, "wrap"), pad(k, "wrap"), pad(v, "wrap"), pad(do, "constant"), 0.5, "na2d",
+                                   O.NA2D(ph, pw, kh, kw, False, False))
+
+        def fold(x):
+            x = x.reshape(B, H, ph, pw, d).copy()
+            for ax, r, n in ((2, rh, gh), (3, rw, gw)):
+                if r == 0:
+                    continue
+                core = [slice(None)] * 5
+                lo, hi = list(core), list(core)
+                lo[ax], hi[ax] = slice(r, 2 * r), slice(n, n + r)             # cells the margins copy
+                top, bot = list(core), list(core)
+                top[ax], bot[ax] = slice(n + r, n + 2 * r), slice(0, r)        # the margins
+                x[tuple(lo)] += x[tuple(top)]
+                x[tuple(hi)] += x[tuple(bot)]
+            return x[:, :, rh:rh + gh, rw:rw + gw].reshape(B, H, N, d)
+
+        for g, w in zip(got, want):
+            assert np.max(np.abs(fold(g) - w)) <= TIGHT, (gh, gw, kh, kw)
+
+
 ALL_PINS = [
     pin_wrap_5x5_example,
     pin_probability_rows_sum_to_one,
@@ -525,4 +637,8 @@ ALL_PINS = [
     pin_na3d_uniform_box_filter,
     pin_na3d_translation_and_pad_crop,
     pin_na3d_sdpa,
+    pin_backward_autograd_sdpa,
+    pin_backward_finite_differences,
+    pin_backward_identities,
+    pin_backward_wrap_equals_pad_fold,
 ]

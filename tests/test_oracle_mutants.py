@@ -189,6 +189,13 @@ MUTANTS = {
     "lse_log2": ("_logsumexp", _lse_log2),
     "lse_no_max": ("_logsumexp", _lse_no_max),
     "lse_max_only": ("_logsumexp", _lse_max_only),
+    "softmax_grad_no_rowsum": ("_softmax_grad", lambda p, dp: p * dp),
+    "softmax_grad_wrong_axis": ("_softmax_grad", lambda p, dp: p * (dp - np.sum(p * dp, axis=0, keepdims=True))),
+    "softmax_grad_sign": ("_softmax_grad", lambda p, dp: p * (np.sum(p * dp, axis=1, keepdims=True) - dp)),
+    "grad_v_untransposed": ("_grad_v", lambda p, do: p @ do),
+    "grad_q_no_scale": ("_grad_q", lambda ds, k, s: ds @ k),
+    "grad_k_untransposed_ds": ("_grad_k", lambda ds, q, s: s * (ds @ q)),
+    "grad_k_scale_squared": ("_grad_k", lambda ds, q, s: s * s * (ds.T @ q)),
 }
 
 
