@@ -55,7 +55,7 @@ RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
-KERNEL_SOURCES = ["attn_fwd.hip", "launch.hpp", "tile_plan.hpp"]
+KERNEL_SOURCES = ["attn_fwd.hip", "kernel_common.hpp", "launch.hpp", "tile_plan.hpp"]
 
 
 def recorded_traffic(name: str):

@@ -81,6 +81,11 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd_ex_workspace_size.restype = i32
     lib.attn_fwd_ex_check.argtypes = [i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_ex_check.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, vp, vp,
+                             ctypes.c_uint64, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, vp, ctypes.POINTER(ctypes.c_uint64)]
+    lib.attn_bwd_workspace_size.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -220,6 +225,40 @@ def attn_fwd_ex(q, k, v, o, lse=None, scale=1.0, mask_mode=ATTN_MASK_NONE, param
         raise AttnError(rc, "attn_fwd_ex")
 
 
+def attn_bwd_workspace_size(B, H, Nq, Nkv, d, mask_mode=ATTN_MASK_NONE, params=None) -> int:
+    """Bytes of workspace attn_bwd needs (float32 row sums, B * H * Nq * 4)."""
+    out = ctypes.c_uint64(0)
+    rc = lib().attn_bwd_workspace_size(B, H, Nq, Nkv, d, int(mask_mode), _params_ptr(params), ctypes.byref(out))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_workspace_size")
+    return int(out.value)
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, mask_mode=ATTN_MASK_NONE, params=None, workspace=None,
+             stream=None) -> None:
+    """Gradients dq, dk, dv (bfloat16 CUDA tensors shaped like q, k, v) of attn_fwd_ex's output o for the
+    output gradient dout, from the forward's logsumexp lse (float32 [B, H, Nq]); see include/attn.h."""
+    import torch
+
+    B, H, Nq, Nkv, d = _check_tensors(q, k, v, o, same_n=False)
+    for name, t, like in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must be shaped like {'q' if like is q else ('k' if like is k else 'v')}")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, Nq):
+        raise TypeError("lse must be a contiguous float32 CUDA tensor [B, H, Nq]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nkv, d, float(scale), int(mask_mode),
+                        _params_ptr(params), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd")
+
+
 _workspaces: dict = {}
 
 
@@ -271,7 +310,7 @@ def attention(q, k, v, scale=None, causal=False, na=None, stream=None, return_ls
 
 __all__ = [
     "ATTN_MASK_NONE", "ATTN_MASK_CAUSAL", "ATTN_MASK_NA2D", "ATTN_MASK_NA3D", "attn_na3d_params_t", "na3d_params",
-    "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check",
+    "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check", "attn_bwd", "attn_bwd_workspace_size",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_PARAMS", "ATTN_ERR_ALIGNMENT",
     "ATTN_ERR_HIP", "ATTN_ERR_WORKSPACE", "AttnError", "attn_na2d_params_t", "na2d_params",
     "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "workspace", "attn_fwd_check", "attn_status_string",

@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip"]
-HEADERS = ["launch.hpp", "tile_plan.hpp", "validate.hpp"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+HEADERS = ["kernel_common.hpp", "launch.hpp", "tile_plan.hpp", "validate.hpp"]
 
 # Packed fp32 VALU forms are switched off for all device code; the kernels rely on
 # plain fp32 arithmetic only. The kernels never produce or test NaN (masked scores

@@ -163,14 +163,57 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   return run_with_workspace(p, workspace, workspace_bytes, stream);
 }
 
+attn_status_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int32_t mask_mode,
+                                      const void* params, uint64_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn_status_t st = attn::check_bwd_problem(B, H, Nq, Nkv, d, 1.0f, mask_mode, params);
+  if (st != ATTN_OK) return st;
+  *bytes = (uint64_t)(B * H * Nq) * 4u;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                       void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
+                       float scale, int32_t mask_mode, const void* params, void* workspace, uint64_t workspace_bytes,
+                       void* stream) {
+  attn_status_t st = attn::check_bwd_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
+  if (st != ATTN_OK) return st;
+  st = attn::check_bwd_pointers(attn::BwdPointers{q, k, v, o, dout, lse, dq, dk, dv}, B, H, Nq, Nkv, d, workspace,
+                                workspace_bytes);
+  if (st != ATTN_OK) return st;
+  attn::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.delta = static_cast<float*>(workspace);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.Nq = (int32_t)Nq;
+  a.Nkv = (int32_t)Nkv;
+  a.BH = (int32_t)(B * H);
+  a.n_qtiles = (int32_t)attn::cdiv(Nq, attn::kBlockM);
+  a.n_ktiles = (int32_t)attn::cdiv(Nkv, attn::kBlockM);
+  a.c = (float)(fabs((double)scale) * 1.4426950408889634);
+  a.scale = scale;
+  a.q_sign = scale < 0.f ? 0x80008000u : 0u;
+  if ((int64_t)a.BH * a.n_ktiles > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  const int32_t mask = mask_mode == ATTN_MASK_CAUSAL ? attn::MASK_CAUSAL : attn::MASK_NONE;
+  const hipError_t e = attn::launch_bwd(a, (int32_t)d, mask, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 const char* attn_status_string(int32_t status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, non-finite scale, "
                                       "unknown mask mode, misplaced params, or an output overlapping an input "
                                       "or the other output)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128; sizes must fit "
-                                      "32-bit launch geometry)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128, and 32 or 64 with no "
+                                      "mask or the causal mask for the backward; sizes must fit 32-bit launch geometry)";
     case ATTN_ERR_PARAMS: return "inconsistent neighbourhood parameters (grid size must equal Nq and Nkv; "
                                  "kernels odd; wrap 0 or 1; dilation >= 1; (kernel-1)*dilation < size when "
                                  "wrapped, kernel*dilation <= size when clamped)";

@@ -1,0 +1,387 @@
+// Backward pass of the fused exact attention for gfx950: the gradients of
+// O = softmax(scale * Q K^T + mask) V with respect to Q, K and V, for an output
+// gradient dO, without writing the score matrix (NATTEN issue 142: the fused
+// forward saves the logsumexp for the backward, whose kernels visit query
+// tiles per key tile; the gradients are those of its autograd function).
+//
+// With P = exp(scale * S - LSE) recomputed tile by tile from the saved row
+// logsumexp, and D_i = sum_d dO_id O_id (the row sum of P * dP):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Three kernels on the caller's stream:
+//   attn_bwd_prep_kernel  D per query row into the workspace (fp32);
+//   attn_bwd_dq_kernel    one work-group per 128-query tile (4 wavefronts x 32
+//                         queries), key/value tiles streamed through LDS:
+//                         S^T = K Q^T, dP^T = V dO^T (the forward's S^T layout,
+//                         one query per lane column), dS^T, then dQ^T += K^T dS^T
+//                         (the forward's O^T += V^T P^T layout, K read through
+//                         the transposing LDS read);
+//   attn_bwd_dkv_kernel   one work-group per 128-key tile (one key per lane
+//                         column), query/dO tiles streamed: S = Q K^T,
+//                         dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+// Both multiply bf16 operands on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation; P and dS are rounded to bf16 as MFMA operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "kernel_common.hpp"
+#include "launch.hpp"
+#include "tile_plan.hpp"
+
+namespace attn {
+
+namespace {
+
+template <int D>
+struct BwdCfg {
+  static constexpr int ROWS = 128;  // rows of a streamed tile; a work-group holds 4 x 32 resident rows
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROW_CHUNKS = D / 8;
+  static constexpr int TILE = ROWS * D;
+  static constexpr int LOADS = ROWS * ROW_CHUNKS / THREADS;  // 16-byte loads per thread per tile
+  static constexpr int SB = ROWS / 32;                       // 32-row blocks per streamed tile
+  static constexpr int KB = D / 16;
+  static constexpr int DT = D / 32;
+  static_assert(ROWS * ROW_CHUNKS % THREADS == 0, "tile chunks must split evenly");
+};
+
+// Global -> LDS copy of a tile of ROWS rows of one head (the forward's layout and swizzle).
+template <int D>
+struct RowTileLoader {
+  using C = BwdCfg<D>;
+  uint32_t voff[C::LOADS];
+  int wave;
+
+  __device__ __forceinline__ RowTileLoader(int wave_, int lane) : wave(wave_) {
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int p = (j * C::WAVES + wave_) * 64 + lane;
+      const int row = p / C::ROW_CHUNKS;
+      const int chunk = (p % C::ROW_CHUNKS) ^ chunk_swizzle<D>(row);
+      voff[j] = (uint32_t)(row * D + chunk * 8) * 2u;
+    }
+  }
+
+  __device__ __forceinline__ void load(i32x4_t src, int32_t tile, const uint16_t* lds_tile) const {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile * (C::ROWS * D * 2));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) dma_lds16(src, base + j * C::WAVES * 1024, voff[j], soff);
+  }
+};
+
+// Fragment of a resident row (the lane's query or key) as the B operand of a
+// 32x32x16 MFMA: d = 16kb + 8*half + 0..7; zero past the last row.
+template <int D>
+__device__ __forceinline__ void row_fragment(const uint16_t* rows, int32_t row, int32_t n_rows, uint32_t sign, int half,
+                                             bf16x8_t (&f)[D / 16]) {
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    u32x4_t x = u32x4_t{0, 0, 0, 0};
+    if (row < n_rows) {
+      x = *reinterpret_cast<const u32x4_t*>(rows + (size_t)row * D + kb * 16 + half * 8);
+      x ^= sign;
+    }
+    f[kb] = __builtin_bit_cast(bf16x8_t, x);
+  }
+}
+
+// One 32-row block of a streamed tile times the resident fragments: acc = T[rows] R^T,
+// lane holds rows 32sb + 8(r/4) + 4*half + r%4 of its resident column.
+template <int D>
+__device__ __forceinline__ f32x16_t block_product(const uint16_t* tile, int sb, int col, int half, int swz,
+                                                  const bf16x8_t (&f)[D / 16]) {
+  f32x16_t acc = f32x16_t{};
+  const int row = sb * 32 + col;
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(tile + row * D + (((2 * kb + half) ^ swz) << 3));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), f[kb], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// acc^T += tile[block rows]^T W^T for the 32 rows of block sb, with W (bf16, two
+// 16-row halves) in the accumulator order of block_product: the forward's P V step.
+template <int D>
+__device__ __forceinline__ void block_transpose_product(const uint16_t* tile, int sb, const int (&v_row)[2],
+                                                        const int (&v_off)[2][D / 32], const bf16x8_t (&w)[2],
+                                                        f32x16_t (&acc)[D / 32]) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int row0 = sb * 32 + kb2 * 16;
+      u32x2_t x[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                               (lds_s16x4*)((lds_u16*)tile + (row0 + v_row[h]) * D + v_off[h][dt])));
+      const bf16x8_t tf = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, w[kb2], acc[dt], 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void transpose_offsets(int lane, int half, int (&v_row)[2], int (&v_off)[2][D / 32]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v_row[h] = h * 8 + half * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      v_off[h][dt] = (((dcol >> 3) ^ chunk_swizzle<D>(v_row[h])) << 3) + (dcol & 7);
+    }
+  }
+}
+
+// Rounds an accumulator block to the bf16 MFMA operand (two halves of 8 elements).
+__device__ __forceinline__ void to_bf16_operand(const f32x16_t& x, bf16x8_t (&w)[2]) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2_t pr = {(__bf16)x[kb2 * 8 + e], (__bf16)x[kb2 * 8 + e + 1]};
+      w[kb2][e] = pr[0];
+      w[kb2][e + 1] = pr[1];
+    }
+}
+
+// Stores scale * acc^T (d x 32 columns, the lane's column = one row of the output) as bf16 rows.
+template <int D>
+__device__ __forceinline__ void store_rows_scaled(uint16_t* out, int32_t row, int32_t n_rows, int half,
+                                                  const f32x16_t (&acc)[D / 32], float scale) {
+  if (row >= n_rows) return;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4_t ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(acc[dt][g * 4 + e] * scale);
+      *reinterpret_cast<u32x2_t*>(out + (size_t)row * D + dt * 32 + g * 8 + half * 4) = __builtin_bit_cast(u32x2_t, ob);
+    }
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+// D_i = sum_d dO_id O_id, one thread per query row.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (int64_t)a.BH * a.Nq) return;
+  const uint16_t* o = a.o + row * D;
+  const uint16_t* g = a.dout + row * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(o + c);
+    const u32x4_t y = *reinterpret_cast<const u32x4_t*>(g + c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += __uint_as_float(x[w] << 16) * __uint_as_float(y[w] << 16);
+      acc += __uint_as_float(x[w] & 0xffff0000u) * __uint_as_float(y[w] & 0xffff0000u);
+    }
+  }
+  a.delta[row] = acc;
+}
+
+// dQ for one 128-query tile: key/value tiles through a two-buffer LDS ring.
+template <int D, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][C::TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int32_t Nq = a.Nq, Nkv = a.Nkv;
+  const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH);
+  const int32_t q0 = w.qtile * C::ROWS, my_q = q0 + wave * 32 + col;
+  const size_t qhead = (size_t)w.bh * Nq, khead = (size_t)w.bh * Nkv;
+
+  bf16x8_t qf[C::KB], gf[C::KB];
+  row_fragment<D>(a.q + qhead * D, my_q, Nq, a.q_sign, half, qf);
+  row_fragment<D>(a.dout + qhead * D, my_q, Nq, 0u, half, gf);
+  const float l2 = my_q < Nq ? a.lse[qhead + my_q] * kLog2e : 0.f;
+  const float dlt = my_q < Nq ? a.delta[qhead + my_q] : 0.f;
+
+  int v_row[2], v_off[2][C::DT];
+  transpose_offsets<D>(lane, half, v_row, v_off);
+  const int swz = chunk_swizzle<D>(col);
+  const RowTileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
+  const uint32_t head_bytes = (uint32_t)Nkv * (uint32_t)(D * 2);
+  const i32x4_t k_rsrc = head_rsrc(a.k + khead * D, head_bytes);
+  const i32x4_t v_rsrc = head_rsrc(a.v + khead * D, head_bytes);
+
+  const KvRun run = kv_run(MASK, Nq, Nkv, C::ROWS, C::ROWS, q0, NaGeom{});
+  const int32_t n = run.count;
+  f32x16_t dq[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) dq[dt] = f32x16_t{};
+
+  ld.load(k_rsrc, kv_tile_at(run, 0, a.n_ktiles), k_lds[0]);
+  ld.load(v_rsrc, kv_tile_at(run, 0, a.n_ktiles), v_lds[0]);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t t = kv_tile_at(run, i, a.n_ktiles);
+    const int buf = i & 1;
+    if (i + 1 < n) {  // the other buffer was last read before the previous barrier
+      const int32_t tn = kv_tile_at(run, i + 1, a.n_ktiles);
+      ld.load(k_rsrc, tn, k_lds[buf ^ 1]);
+      ld.load(v_rsrc, tn, v_lds[buf ^ 1]);
+      wait_tile_loads<2 * C::LOADS>();
+    } else {
+      wait_tile_loads<0>();
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) {
+      const f32x16_t s = block_product<D>(k_lds[buf], sb, col, half, swz, qf);
+      const f32x16_t dp = block_product<D>(v_lds[buf], sb, col, half, swz, gf);
+      f32x16_t ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t key = t * C::ROWS + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        bool ok = (key < Nkv) & (my_q < Nq);
+        if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l2));
+        ds[r] = ok ? p * (dp[r] - dlt) : 0.f;
+      }
+      bf16x8_t dsb[2];
+      to_bf16_operand(ds, dsb);
+      block_transpose_product<D>(k_lds[buf], sb, v_row, v_off, dsb, dq);
+    }
+    __syncthreads();  // every wavefront is done with this buffer before it is refilled
+  }
+  store_rows_scaled<D>(a.dq + qhead * D, my_q, Nq, half, dq, a.scale);
+}
+
+// dK and dV for one 128-key tile: query/dO tiles and their logsumexp and D values
+// through a two-buffer LDS ring.
+template <int D, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dkv_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) float l2_lds[2][C::ROWS];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][C::ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int32_t Nq = a.Nq, Nkv = a.Nkv;
+  const int32_t bh = blockIdx.x / a.n_ktiles, ktile = blockIdx.x - bh * a.n_ktiles;
+  const int32_t k0 = ktile * C::ROWS, my_k = k0 + wave * 32 + col;
+  const size_t qhead = (size_t)bh * Nq, khead = (size_t)bh * Nkv;
+
+  // scale < 0: K's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
+  bf16x8_t kf[C::KB], vf[C::KB];
+  row_fragment<D>(a.k + khead * D, my_k, Nkv, a.q_sign, half, kf);
+  row_fragment<D>(a.v + khead * D, my_k, Nkv, 0u, half, vf);
+
+  int v_row[2], v_off[2][C::DT];
+  transpose_offsets<D>(lane, half, v_row, v_off);
+  const int swz = chunk_swizzle<D>(col);
+  const RowTileLoader<D> ld(__builtin_amdgcn_readfirstlane(wave), lane);
+  const uint32_t head_bytes = (uint32_t)Nq * (uint32_t)(D * 2);
+  const i32x4_t q_rsrc = head_rsrc(a.q + qhead * D, head_bytes);
+  const i32x4_t g_rsrc = head_rsrc(a.dout + qhead * D, head_bytes);
+
+  // query tiles that see some key of this tile: all, or (causal, key j <= query i) from the
+  // tile holding query k0 on
+  const int32_t first = MASK == MASK_CAUSAL ? k0 / C::ROWS : 0;
+  const int32_t n = first < a.n_qtiles ? a.n_qtiles - first : 0;
+
+  f32x16_t dk[C::DT], dv[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) dk[dt] = dv[dt] = f32x16_t{};
+
+  // logsumexp (base 2) and D of query tile qt, one value per thread of the first 128
+  auto stats = [&](int32_t qt, float& l2v, float& dlv) {
+    const int32_t qi = qt * C::ROWS + tid;
+    const bool in = tid < C::ROWS && qi < Nq;
+    l2v = in ? a.lse[qhead + qi] * kLog2e : INFINITY;  // rows past Nq: P = 0
+    dlv = in ? a.delta[qhead + qi] : 0.f;
+  };
+  float l2n = 0.f, dln = 0.f;
+  if (n > 0) {
+    ld.load(q_rsrc, first, q_lds[0]);
+    ld.load(g_rsrc, first, g_lds[0]);
+    stats(first, l2n, dln);
+    wait_tile_loads<0>();
+    if (tid < C::ROWS) {
+      l2_lds[0][tid] = l2n;
+      dl_lds[0][tid] = dln;
+    }
+    __syncthreads();
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t qt = first + i;
+    const int buf = i & 1;
+    if (i + 1 < n) {  // next tile into the other buffers (last read before the previous barrier)
+      ld.load(q_rsrc, qt + 1, q_lds[buf ^ 1]);
+      ld.load(g_rsrc, qt + 1, g_lds[buf ^ 1]);
+      stats(qt + 1, l2n, dln);
+    }
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) {
+      const f32x16_t s = block_product<D>(q_lds[buf], sb, col, half, swz, kf);
+      const f32x16_t dp = block_product<D>(g_lds[buf], sb, col, half, swz, vf);
+      f32x16_t p, ds;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qr = sb * 32 + 8 * g4 + 4 * half;  // first of the 4 queries of this group
+        const float4 l4 = *reinterpret_cast<const float4*>(&l2_lds[buf][qr]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][qr]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g4 + j;
+          const int32_t qi = qt * C::ROWS + qr + j;
+          bool ok = (qi < Nq) & (my_k < Nkv);
+          if (MASK == MASK_CAUSAL) ok = ok & (my_k <= qi);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lv[j]));
+          p[r] = ok ? pv : 0.f;
+          ds[r] = ok ? pv * (dp[r] - dv4[j]) : 0.f;
+        }
+      }
+      bf16x8_t pb[2], dsb[2];
+      to_bf16_operand(p, pb);
+      to_bf16_operand(ds, dsb);
+      block_transpose_product<D>(g_lds[buf], sb, v_row, v_off, pb, dv);
+      block_transpose_product<D>(q_lds[buf], sb, v_row, v_off, dsb, dk);
+    }
+    wait_tile_loads<0>();
+    if (i + 1 < n && tid < C::ROWS) {
+      l2_lds[buf ^ 1][tid] = l2n;
+      dl_lds[buf ^ 1][tid] = dln;
+    }
+    __syncthreads();  // next tile published; this buffer free for refill
+  }
+  store_rows_scaled<D>(a.dk + khead * D, my_k, Nkv, half, dk, a.scale);
+  store_rows_scaled<D>(a.dv + khead * D, my_k, Nkv, half, dv, 1.0f);
+}
+
+template <int D, int MASK>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.BH * a.Nq;
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3(a.BH * a.n_qtiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, MASK>), dim3(a.BH * a.n_ktiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream) {
+  if (d == 64) return mask == MASK_CAUSAL ? launch_bwd_d<64, MASK_CAUSAL>(a, stream) : launch_bwd_d<64, MASK_NONE>(a, stream);
+  if (d == 32) return mask == MASK_CAUSAL ? launch_bwd_d<32, MASK_CAUSAL>(a, stream) : launch_bwd_d<32, MASK_NONE>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

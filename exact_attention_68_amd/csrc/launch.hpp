@@ -42,6 +42,34 @@ constexpr int64_t split_workspace_bytes(const SplitPlan& p, int64_t d) {
 // 64 for d = 128 (the same 16 KB of LDS per K or V tile).
 constexpr int32_t tile_keys(int64_t d) { return d == 128 ? 64 : 128; }
 
+// Arguments of the backward kernels (attn_bwd.hip), passed by value.
+struct BwdArgs {
+  const uint16_t* q;     // bfloat16 [B, H, Nq, d]
+  const uint16_t* k;     // [B, H, Nkv, d]
+  const uint16_t* v;
+  const uint16_t* o;     // forward output [B, H, Nq, d]
+  const uint16_t* dout;  // output gradient [B, H, Nq, d]
+  const float* lse;      // forward logsumexp (natural log) [B, H, Nq]
+  float* delta;          // workspace: rowsum(dO * O) [B, H, Nq]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int32_t Nq, Nkv, BH;
+  int32_t n_qtiles;  // ceil(Nq / 128)
+  int32_t n_ktiles;  // ceil(Nkv / 128)
+  float c;           // |scale| * log2(e)
+  float scale;       // signed
+  uint32_t q_sign;   // 0x80008000 when scale < 0, else 0
+};
+
+// Head sizes and masks the backward kernels are built for.
+constexpr bool bwd_supported(int64_t d, int32_t mask_mode) {
+  return (d == 32 || d == 64) && (mask_mode == ATTN_MASK_NONE || mask_mode == ATTN_MASK_CAUSAL);
+}
+
+// Launches the three backward kernels (D per row, dQ, dK and dV) on `stream`.
+hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream);
+
 // Launches the kernel for head size d (32, 64 or 128) and kernel mask `mask`
 // (MASK_*). With a.ws_parts set (unmasked problems only), n_wg = full + rem *
 // parts work-groups run the whole tiles and the parts, and a second kernel of

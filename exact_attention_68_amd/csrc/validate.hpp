@@ -140,4 +140,43 @@ inline attn_status_t check_workspace(const void* ws, uint64_t ws_bytes, int64_t 
   return ATTN_OK;
 }
 
+// Backward: the problem checks of the forward, then the head sizes and masks the
+// backward kernels support.
+inline attn_status_t check_bwd_problem(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
+                                       int32_t mask_mode, const void* params) {
+  const attn_status_t st = check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
+  if (st != ATTN_OK) return st;
+  if (!((d == 32 || d == 64) && (mask_mode == ATTN_MASK_NONE || mask_mode == ATTN_MASK_CAUSAL)))
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// Backward pointers: every tensor present and aligned (lse 4 bytes, the rest 16),
+// outputs disjoint from the inputs and from each other, the workspace (if any
+// bytes are needed) large enough, 256-byte aligned and disjoint from all tensors.
+struct BwdPointers {
+  const void *q, *k, *v, *o, *dout, *lse;
+  void *dq, *dk, *dv;
+};
+
+inline attn_status_t check_bwd_pointers(const BwdPointers& p, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                                        int64_t d, const void* ws, uint64_t ws_bytes) {
+  const void* all[9] = {p.q, p.k, p.v, p.o, p.dout, p.lse, p.dq, p.dk, p.dv};
+  for (const void* x : all)
+    if (x == nullptr) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < 9; ++i)
+    if ((uintptr_t)all[i] & (i == 5 ? 3u : 15u)) return ATTN_ERR_ALIGNMENT;
+  const uintptr_t qb = (uintptr_t)(B * H * Nq * d) * 2u, kb = (uintptr_t)(B * H * Nkv * d) * 2u;
+  const uintptr_t lb = (uintptr_t)(B * H * Nq) * 4u;
+  const uintptr_t bytes[9] = {qb, kb, kb, qb, qb, lb, qb, kb, kb};
+  for (int out = 6; out < 9; ++out)
+    for (int i = 0; i < 9; ++i)
+      if (i != out && overlaps((uintptr_t)all[out], bytes[out], (uintptr_t)all[i], bytes[i])) return ATTN_ERR_INVALID_ARG;
+  const uint64_t need = (uint64_t)lb;
+  if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 255u)) return ATTN_ERR_WORKSPACE;
+  for (int i = 0; i < 9; ++i)
+    if (overlaps((uintptr_t)ws, (uintptr_t)need, (uintptr_t)all[i], bytes[i])) return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
 }  // namespace attn

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Mask modes. */
 typedef enum {
@@ -227,6 +227,40 @@ attn_status_t attn_fwd_ex_workspace_size(int64_t B, int64_t H, int64_t Nq, int64
 /* attn_fwd_check for attn_fwd_ex's problem (Nq queries, Nkv keys). */
 attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
                                 int32_t mask_mode, const void* params);
+
+/*
+ * attn_bwd: the backward pass of attn_fwd_ex. For the output gradient dO it
+ * writes the gradients of O = softmax(scale * Q K^T + mask) V:
+ *
+ *     dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale * dS K,  dK = scale * dS^T Q,
+ *
+ * with P = exp(scale * Q K^T + mask - LSE) recomputed from the forward's
+ * logsumexp and D the row sums of dO * O (NATTEN issue 142: the fused forward
+ * saves the logsumexp for its autograd backward).
+ *
+ * q, k, v : the forward's inputs (device, bfloat16, [B,H,Nq,d] and [B,H,Nkv,d]).
+ * o, lse  : the forward's output and logsumexp from attn_fwd_ex (lse float32
+ *           [B,H,Nq], 4-byte aligned).
+ * dout    : dO, device bfloat16 [B,H,Nq,d].
+ * dq, dk, dv : outputs, device bfloat16 shaped like q, k and v, rounded to
+ *           nearest even; disjoint from every input and from each other.
+ * mask_mode : ATTN_MASK_NONE or ATTN_MASK_CAUSAL (top-left aligned); d: 32 or 64.
+ *           Other masks and head sizes return ATTN_ERR_UNSUPPORTED.
+ * workspace : device memory of at least attn_bwd_workspace_size bytes
+ *           (B*H*Nq float32 row sums), 256-byte aligned, disjoint from the
+ *           tensors; any content; calls sharing it must not overlap.
+ * The other arguments and the error rules are those of attn_fwd_ex. Three
+ * kernels are queued on `stream`; the library allocates nothing.
+ */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
+                       int64_t Nkv, int64_t d, float scale, int32_t mask_mode, const void* params,
+                       void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_bwd needs (B * H * Nq * 4), after the argument checks
+ * of attn_bwd that need no pointer. */
+attn_status_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
+                                      int32_t mask_mode, const void* params, uint64_t* bytes);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(int32_t status);

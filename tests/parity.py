@@ -123,3 +123,90 @@ def workload_params(w: workloads.Workload):
     if w.mask == "na3d":
         return A.na3d_params(**w.na)
     return None
+
+
+# ---------------------------------------------------------------- backward
+# Per-element bound of the GPU gradients, derived from the arithmetic of attn_bwd (first order).
+# The backward recomputes P = exp(scale s - LSE) from the logsumexp it is given (off by eL, so P is
+# off by that factor per row), takes D = rowsum(dO * O) from the bf16 O it is given (off by dD_i,
+# computed exactly below), rounds dS (and P for dV) to bf16 as MFMA operands (2^-8 relative) and
+# rounds the gradients to bf16 (2^-8 relative):
+#   |d(dS)_ij| <= P_ij (eL |dP_ij - D_i| + |dD_i|) + 2^-8 |dS_ij|
+#   |d(dQ)|    <= |scale| |d(dS)| |K| + 2^-8 |dQ|,   |d(dK)| <= |scale| |d(dS)|^T |Q| + 2^-8 |dK|
+#   |d(dV)|    <= (eL + 2^-8) P^T |dO| + 2^-8 |dV|
+# The tests allow 1.25 x this bound plus 1e-4 (fp32 sums and exp2).
+BF16_U = 2.0 ** -8
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def bwd_reference(q, k, v, do, scale, mask="none", na=None, o_used=None, lse_err=2.0 ** -22):
+    """Oracle gradients and per-element tolerances (float64 arrays shaped like q, k, v) for a backward
+    given the output o_used (default: the exact output rounded to bf16) and a logsumexp within lse_err."""
+    grads = oracle.attention_backward(q, k, v, do, scale, mask, na)
+    p = oracle.probs(q, k, scale, mask, na)
+    o = oracle.attention(q, k, v, scale, mask, na)
+    o_used = bf16_round(o) if o_used is None else o_used
+    dp = do @ np.swapaxes(v, -1, -2)
+    dd = np.sum(p * dp, axis=-1, keepdims=True)
+    ds = p * (dp - dd)
+    d_delta = np.abs(np.sum(do * (o_used - o), axis=-1, keepdims=True))
+    dds = p * (lse_err * np.abs(dp - dd) + d_delta) + BF16_U * np.abs(ds)
+    tq = abs(scale) * (dds @ np.abs(k)) + BF16_U * np.abs(grads[0])
+    tk = abs(scale) * (np.swapaxes(dds, -1, -2) @ np.abs(q)) + BF16_U * np.abs(grads[1])
+    tv = (lse_err + BF16_U) * (np.swapaxes(p, -1, -2) @ np.abs(do)) + BF16_U * np.abs(grads[2])
+    return grads, tuple(1.25 * t + 1e-4 for t in (tq, tk, tv))
+
+
+def run_gpu_bwd(q, k, v, do, scale, mask_mode, o=None, lse=None):
+    """attn_bwd on the device; o and lse default to the GPU forward's (attn_fwd_ex). Returns
+    (dq, dk, dv, o, lse) on the device."""
+    import exact_attention_68_amd as A
+
+    dq_, dk_, dv_, do_ = (t.to("cuda") for t in (q, k, v, do))
+    B, H, Nq, d = dq_.shape
+    Nkv = dk_.shape[2]
+    if o is None:
+        o = torch.empty_like(dq_)
+        lse = torch.empty(B, H, Nq, dtype=torch.float32, device="cuda")
+        ws = split_workspace(B, H, Nq, d, mask_mode, None, n_kv=Nkv)
+        A.attn_fwd_ex(dq_, dk_, dv_, o, lse, scale, mask_mode, None, ws)
+    else:
+        o, lse = o.to("cuda"), lse.to("cuda")
+    wsb = torch.full((A.attn_bwd_workspace_size(B, H, Nq, Nkv, d, mask_mode),), 255, dtype=torch.uint8, device="cuda")
+    gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
+    A.attn_bwd(dq_, dk_, dv_, o, do_, lse, gq, gk, gv, scale, mask_mode, None, wsb)
+    torch.cuda.synchronize()
+    return gq, gk, gv, o, lse
+
+
+def check_bwd_case(q, k, v, do, scale, mask: str, what="", pipeline=False) -> float:
+    """GPU gradients against the oracle. By default attn_bwd gets the oracle's output (rounded to bf16)
+    and logsumexp (fp32), so the bound covers the backward alone; with pipeline=True it gets the GPU
+    forward's, and the bound takes the forward's output error and logsumexp tolerance as given."""
+    print(f"[parity-bwd] {what} B{q.shape[0]} H{q.shape[1]} Nq{q.shape[2]} Nkv{k.shape[2]} d{q.shape[3]} mask={mask} "
+          f"scale={scale} pipeline={pipeline}", flush=True)
+    qf, kf, vf, gf = (to_f64(t) for t in (q, k, v, do))
+    if pipeline:
+        gq, gk, gv, o, _ = run_gpu_bwd(q, k, v, do, scale, MASK_MODES[mask])
+        ref, tol = bwd_reference(qf, kf, vf, gf, scale, mask, o_used=to_f64(o), lse_err=6e-3)
+    else:
+        o, lse = oracle.attention(qf, kf, vf, scale, mask, return_lse=True)
+        o_b = torch.from_numpy(o.astype(np.float32)).to(torch.bfloat16)
+        lse_f = torch.from_numpy(lse.astype(np.float32))
+        gq, gk, gv, _, _ = run_gpu_bwd(q, k, v, do, scale, MASK_MODES[mask], o_b, lse_f)
+        ref, tol = bwd_reference(qf, kf, vf, gf, scale, mask, o_used=to_f64(o_b))
+    worst = 0.0
+    for name, g, r, t in zip(("dq", "dk", "dv"), (gq, gk, gv), ref, tol):
+        gv_ = to_f64(g)
+        assert np.all(np.isfinite(gv_)), f"{what}: non-finite {name}"
+        ratio = np.abs(gv_ - r) / t
+        if ratio.max() > 1.0:
+            idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+            raise AssertionError(f"{what}: {name} {int((ratio > 1).sum())} of {ratio.size} out of tolerance; worst "
+                                 f"err/tol {ratio.max():.3f} at {idx}: got {gv_[idx]}, ref {r[idx]}, tol {t[idx]}")
+        worst = max(worst, float(ratio.max()))
+    print(f"[parity-bwd] {what}: worst err/tol {worst:.3f}", flush=True)
+    return worst

@@ -31,6 +31,7 @@ def test_exports_every_declared_symbol(A):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_fwd_check",
                           "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check",
+                          "attn_bwd", "attn_bwd_workspace_size",
                           "attn_status_string", "attn_abi_version"}
     lib = A.lib()
     for n in names:
@@ -157,3 +158,35 @@ def test_host_planning_and_validation_under_sanitizers(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0 and "OK" in res.stdout, res.stdout + res.stderr
+
+
+def test_bwd_rejects_before_device_work(A):
+    """attn_bwd and attn_bwd_workspace_size check every argument before touching a device."""
+    import ctypes
+
+    lib = A.lib()
+    base = 1 << 20
+    q, k, v, o, g, lse, dq, dk, dv, ws = (base + (i << 16) for i in range(10))
+    n = ctypes.c_uint64(7)
+    assert lib.attn_bwd_workspace_size(2, 3, 100, 77, 64, 0, None, ctypes.byref(n)) == A.ATTN_OK
+    assert n.value == 2 * 3 * 100 * 4
+    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 64, 0, None, None) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 128, 0, None, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    p = ctypes.cast(ctypes.pointer(A.na2d_params(8, 8, 3, 3)), ctypes.c_void_p)
+    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 64, A.ATTN_MASK_NA2D, p, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    args = (1, 1, 64, 64, 64, 0.1, 0, None, ws, 1 << 16, None)
+    assert lib.attn_bwd(None, k, v, o, g, lse, dq, dk, dv, *args) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd(q, k, v, o, g, lse + 2, dq, dk, dv, *args) == A.ATTN_ERR_ALIGNMENT
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq + 8, dk, dv, *args) == A.ATTN_ERR_ALIGNMENT
+    assert lib.attn_bwd(q, k, v, o, g, lse, q + 64, dk, dv, *args) == A.ATTN_ERR_INVALID_ARG   # dq inside q
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dq + 64, dv, *args) == A.ATTN_ERR_INVALID_ARG  # dk inside dq
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 64, 0.1, 0, None, None, 1 << 16,
+                        None) == A.ATTN_ERR_WORKSPACE
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 64, 0.1, 0, None, ws, 255,
+                        None) == A.ATTN_ERR_WORKSPACE
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 64, 0.1, 0, None, ws + 16, 1 << 16,
+                        None) == A.ATTN_ERR_WORKSPACE
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 128, 0.1, 0, None, ws, 1 << 16,
+                        None) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 64, float("inf"), 0, None, ws, 1 << 16,
+                        None) == A.ATTN_ERR_INVALID_ARG

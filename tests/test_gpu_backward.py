@@ -1,0 +1,91 @@
+"""Parity of attn_bwd (the backward pass: gradients of Q, K and V) against the float64 CPU oracle on an
+MI355X. attn_bwd gets the oracle's output (bf16) and logsumexp (fp32), so the per-element tolerance
+(parity.bwd_reference, derived from the backward's arithmetic) covers the backward alone; the
+pipeline cases feed it the GPU forward's output and logsumexp instead."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import check_bwd_case, run_gpu_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    from exact_attention_68_amd.build import ensure_built
+
+    ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+
+
+def _inputs(B, H, Nq, Nkv, d, seed, q_gain=1.0):
+    q, k, v = workloads.make_qkv_cross(B, H, Nq, Nkv, d, seed, q_gain)
+    g = torch.Generator(device="cpu").manual_seed(seed + 1)
+    do = torch.randn(B, H, Nq, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("N", [1, 17, 100, 128, 255, 257, 320])
+def test_bwd_edge_shapes(N, mask, d):
+    q, k, v, do = _inputs(1, 2, N, N, d, 11000 + N + d)
+    check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mask, what=f"bwd N{N}")
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("Nq,Nkv", [(300, 77), (77, 300), (1, 500), (500, 1), (129, 384)])
+def test_bwd_cross_shapes(Nq, Nkv, mask, d):
+    q, k, v, do = _inputs(1, 2, Nq, Nkv, d, 11100 + Nq + Nkv + d)
+    check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mask, what=f"bwd cross {Nq}x{Nkv}")
+
+
+@pytest.mark.parametrize("scale,q_gain", [(0.0, 1.0), (-0.2, 1.0), (0.125, 2.0), (1e-3, 1.0)])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_bwd_scales(scale, q_gain, mask):
+    q, k, v, do = _inputs(2, 3, 300, 300, 64, 11200, q_gain)
+    check_bwd_case(q, k, v, do, scale, mask, what=f"bwd scale {scale} gain {q_gain}")
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_bwd_sd21_head_shape(mask):
+    """Two heads at the SD2.1 512x512 token count (N4096, d64)."""
+    q, k, v, do = _inputs(1, 2, 4096, 4096, 64, 11300)
+    check_bwd_case(q, k, v, do, 0.125, mask, what="bwd N4096")
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("N,Nkv,d", [(300, 300, 64), (257, 100, 32), (1000, 1000, 64)])
+def test_bwd_after_gpu_forward(N, Nkv, d, mask):
+    """attn_fwd_ex then attn_bwd, both on the GPU (bound with the forward's errors as inputs)."""
+    q, k, v, do = _inputs(1, 2, N, Nkv, d, 11350 + N + Nkv)
+    check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mask, what=f"bwd pipeline {N}x{Nkv}", pipeline=True)
+
+
+def test_bwd_deterministic_and_workspace_content_free():
+    """Every gradient element is written by one lane in a fixed order: repeated calls agree bit for bit,
+    whatever the workspace held."""
+    q, k, v, do = _inputs(2, 3, 700, 700, 64, 11400)
+    a = run_gpu_bwd(q, k, v, do, 0.125, 1)
+    b = run_gpu_bwd(q, k, v, do, 0.125, 1)
+    assert all(torch.equal(x, y) for x, y in zip(a[:3], b[:3]))
+
+
+def test_bwd_rejects_unsupported_and_leaves_outputs():
+    import exact_attention_68_amd as A
+
+    q, k, v, do = (t.cuda() for t in _inputs(1, 1, 64, 64, 128, 11500))
+    o = torch.zeros_like(q)
+    lse = torch.zeros(1, 1, 64, dtype=torch.float32, device="cuda")
+    gq, gk, gv = (torch.full_like(t, 3.0) for t in (q, k, v))
+    ws = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(A.AttnError) as e:
+        A.attn_bwd(q, k, v, o, do, lse, gq, gk, gv, 0.1, A.ATTN_MASK_NONE, None, ws)
+    assert e.value.status == A.ATTN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert all(torch.all(t == 3.0) for t in (gq, gk, gv))
