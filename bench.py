@@ -1,19 +1,23 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--entry E] [--lse] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--entry E] [--lse] [--backward] [--no-cpu]
 
 One step is one launch of the fused forward over one batch of the workload
 (default: SD2.1 512x512 UNet self-attention, B2 H5 N4096 d64, no mask),
 through attn_fwd_ws (keys split evenly over the resident work-groups when
 that balances the chip; --entry attn_fwd for one work-group per query tile;
 attn_fwd_ex, the default for cross-attention, also writes the logsumexp with
---lse). Inputs and the workspace are resident in HBM before timing starts.
-Prints one JSON line on stdout.
+--lse). With --backward a step is one attn_bwd call (gradients of Q, K and V
+from the forward's output and logsumexp, computed once before timing). Inputs
+and the workspace are resident in HBM before timing starts. Prints one JSON
+line on stdout.
 
 FLOP accounting (the metric of the workload): 4 Nq Nkv d per head without a
 mask, half of 4 N^2 d with the causal mask, 4 N (window cells) d per head for
-neighbourhood attention (the window-sized work). Algorithmic bytes: q, k, v
-read once and o (and the float32 logsumexp, if asked for) written once.
+neighbourhood attention (the window-sized work); the backward counts its five
+products, 10 Nq Nkv d per head (half with the causal mask). Algorithmic bytes:
+q, k, v read once and o (and the float32 logsumexp, if asked for) written once;
+the backward reads q, k, v, o, dO and the logsumexp and writes dq, dk, dv.
 """
 from __future__ import annotations
 
@@ -45,6 +49,17 @@ def flops(w: workloads.Workload) -> float:
         cells = w.na.get("kernel_d", 1) * w.na["kernel_h"] * w.na["kernel_w"]
         per_head = 4.0 * w.N * cells * w.d
     return per_head * w.B * w.H
+
+
+def backward_flops(w: workloads.Workload) -> float:
+    per_head = 10.0 * w.N * w.n_kv * w.d
+    if w.mask == "causal":
+        per_head /= 2
+    return per_head * w.B * w.H
+
+
+def backward_bytes(w: workloads.Workload) -> float:
+    return w.B * w.H * ((4.0 * w.N + 4.0 * w.n_kv) * w.d * 2 + 4.0 * w.N)
 
 
 def algorithmic_bytes(w: workloads.Workload, lse: bool = False) -> float:
@@ -138,6 +153,7 @@ def main():
     ap.add_argument("--entry", default=None, choices=["attn_fwd_ws", "attn_fwd", "attn_fwd_ex"],
                     help="C entry point (default attn_fwd_ws, attn_fwd_ex for cross-attention)")
     ap.add_argument("--lse", action="store_true", help="attn_fwd_ex also writes the logsumexp")
+    ap.add_argument("--backward", action="store_true", help="time attn_bwd (the gradients) instead of the forward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for traffic counters)")
@@ -178,6 +194,24 @@ def main():
         else:
             A.attn_fwd(dq, dk, dv, do, w.scale, mode, params, stream.cuda_stream)
 
+    if args.backward:
+        if mode not in (A.ATTN_MASK_NONE, A.ATTN_MASK_CAUSAL) or w.d not in (32, 64):
+            ap.error("the backward covers head sizes 32 and 64 without a mask or with the causal mask")
+        g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+        ddo = torch.randn(w.B, w.H, w.N, w.d, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+        lse_f = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+        nf = A.attn_fwd_ex_workspace_size(w.B, w.H, w.N, w.n_kv, w.d, mode, params)
+        wsf = torch.zeros(nf, dtype=torch.uint8, device=dev) if nf else None
+        A.attn_fwd_ex(dq, dk, dv, do, lse_f, w.scale, mode, params, wsf, stream.cuda_stream)
+        wsb = torch.zeros(A.attn_bwd_workspace_size(w.B, w.H, w.N, w.n_kv, w.d, mode, params), dtype=torch.uint8,
+                          device=dev)
+        gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+        ws = wsb
+        entry = "attn_bwd"
+
+        def step():
+            A.attn_bwd(dq, dk, dv, do, ddo, lse_f, gq, gk, gv, w.scale, mode, params, wsb, stream.cuda_stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -194,10 +228,10 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
-    F = flops(w)
+    F = backward_flops(w) if args.backward else flops(w)
     value = F * args.steps / wall / 1e12
     achieved = F / (kernel_ms * 1e-3) / 1e12
-    nbytes = algorithmic_bytes(w, args.lse)
+    nbytes = backward_bytes(w) if args.backward else algorithmic_bytes(w, args.lse)
     # neighbourhood windows and short key sequences sit below the ridge of the roofline: HBM-bound
     if w.mask in ("na2d", "na3d") or F / nbytes < RIDGE_FLOP_PER_BYTE:
         roof = {"bound": "hbm", "achieved": nbytes / (kernel_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -205,11 +239,15 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # what the event-timed step contains: the attention kernel, plus the merge kernel of a split launch
-    split = ws is not None
-    roof["kernels"] = (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
-                       else f"attn_fwd_kernel<{w.d},{w.mask}>")
+    split = ws is not None and not args.backward
+    roof["kernels"] = (f"attn_bwd_prep_kernel<{w.d}> + attn_bwd_dq_kernel<{w.d},{w.mask}> + attn_bwd_dkv_kernel<{w.d},{w.mask}>"
+                       if args.backward else
+                       (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
+                        else f"attn_fwd_kernel<{w.d},{w.mask}>"))
     roof["traffic"] = (sum(args.traffic_kib) * 1024.0 if args.traffic_kib
                        else recorded_traffic(f"{w.name}:{entry}{':lse' if args.lse else ''}"))
+    if args.backward:
+        roof["traffic"] = None  # the traffic record covers the forward kernels
 
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
@@ -225,7 +263,10 @@ def main():
     }
     if args.copy_calibration:
         copy_calibration()
-    if not args.no_cpu:
+    if args.backward:
+        line["metric"] = "attention bwd TFLOP/s (dQ, dK, dV) and % of bf16 MFMA peak"
+        line["pct_of_peak"] = 100.0 * value / PEAK_BF16_TFLOPS
+    if not args.no_cpu and not args.backward:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(line), flush=True)
 

@@ -273,7 +273,11 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float dl_lds[2][C::ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
   const int32_t Nq = a.Nq, Nkv = a.Nkv;
-  const int32_t bh = blockIdx.x / a.n_ktiles, ktile = blockIdx.x - bh * a.n_ktiles;
+  // causal: key tile 0 sees every query tile, the last one the fewest, so all heads' key tile 0
+  // go first (longest first, as the forward's causal order); otherwise head-major
+  const int32_t wg = blockIdx.x;
+  const int32_t bh = MASK == MASK_CAUSAL ? wg % a.BH : wg / a.n_ktiles;
+  const int32_t ktile = MASK == MASK_CAUSAL ? wg / a.BH : wg - bh * a.n_ktiles;
   const int32_t k0 = ktile * C::ROWS, my_k = k0 + wave * 32 + col;
   const size_t qhead = (size_t)bh * Nq, khead = (size_t)bh * Nkv;
 
