@@ -201,7 +201,13 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   a.scale = scale;
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
   if ((int64_t)a.BH * a.n_ktiles > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
-  const int32_t mask = mask_mode == ATTN_MASK_CAUSAL ? attn::MASK_CAUSAL : attn::MASK_NONE;
+  int32_t mask = mask_mode == ATTN_MASK_CAUSAL ? attn::MASK_CAUSAL : attn::MASK_NONE;
+  if (attn::is_na_mode(mask_mode)) {
+    a.na = attn::na_geom(mask_mode, params);
+    a.na_inv_w = 1.0f / (float)a.na.grid_w;
+    a.na_inv_h = 1.0f / (float)a.na.grid_h;
+    mask = attn::MASK_NA;
+  }
   const hipError_t e = attn::launch_bwd(a, (int32_t)d, mask, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -212,8 +218,8 @@ const char* attn_status_string(int32_t status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, non-finite scale, "
                                       "unknown mask mode, misplaced params, or an output overlapping an input "
                                       "or the other output)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128, and 32 or 64 with no "
-                                      "mask or the causal mask for the backward; sizes must fit 32-bit launch geometry)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128, and 32 or 64 for the "
+                                      "backward; sizes must fit 32-bit launch geometry)";
     case ATTN_ERR_PARAMS: return "inconsistent neighbourhood parameters (grid size must equal Nq and Nkv; "
                                  "kernels odd; wrap 0 or 1; dilation >= 1; (kernel-1)*dilation < size when "
                                  "wrapped, kernel*dilation <= size when clamped)";

@@ -21,7 +21,11 @@
 //                         column), query/dO tiles streamed: S = Q K^T,
 //                         dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
 // Both multiply bf16 operands on v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation; P and dS are rounded to bf16 as MFMA operands.
+// accumulation; P and dS are rounded to bf16 as MFMA operands. Masks: none,
+// causal (top-left), and the 2D/3D neighbourhood windows through an element
+// test; the dK/dV kernel visits a band of query tiles that holds every query
+// whose window reaches its keys, so the gradients of keys reached across a
+// wrapped border are summed in place.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -169,6 +173,44 @@ __device__ __forceinline__ void store_rows_scaled(uint16_t* out, int32_t row, in
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Neighbourhood windows: grid coordinates of the tokens of a tile, decoded from
+// the tile's first token (one division per tile) plus an offset below 128.
+struct TileOrigin {
+  int32_t x0, y0, z0;
+};
+
+__device__ __forceinline__ TileOrigin tile_origin(int32_t t0, const NaGeom& g) {
+  const int32_t row0 = t0 / g.grid_w, z0 = row0 / g.grid_h;
+  return TileOrigin{t0 - row0 * g.grid_w, row0 - z0 * g.grid_h, z0};
+}
+
+// For n < 2^21 the quotient (n + 0.5) / L stays at least 0.5 / L from an integer, far
+// more than the float error, so truncation is exact (n = x0 + off < grid_w + 128 here).
+__device__ __forceinline__ void token_coords(const TileOrigin& o, int32_t off, const NaGeom& g, float inv_w,
+                                             float inv_h, int32_t& z, int32_t& y, int32_t& x) {
+  const int32_t dy = (int32_t)(((float)(o.x0 + off) + 0.5f) * inv_w);
+  x = o.x0 + off - dy * g.grid_w;
+  const int32_t yy = o.y0 + dy;
+  const int32_t dz = (int32_t)(((float)yy + 0.5f) * inv_h);
+  y = yy - dz * g.grid_h;
+  z = o.z0 + dz;
+}
+
+// Whether key (zk, yk, xk) lies in the window of query (zq, yq, xq), every axis.
+__device__ __forceinline__ bool na_visible(const NaGeom& g, int32_t zq, int32_t yq, int32_t xq, int32_t zk, int32_t yk,
+                                           int32_t xk) {
+  if ((g.dil_d | g.dil_h | g.dil_w) == 1)
+    return na_axis_ok(zq, zk, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d) &
+           na_axis_ok(yq, yk, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h) &
+           na_axis_ok(xq, xk, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w);
+  return na_dil_ok(na_dil_anchor(zq, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d), zk, g.grid_d, g.kernel_d,
+                   g.rad_d, g.wrap_d, g.dil_d) &
+         na_dil_ok(na_dil_anchor(yq, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h), yk, g.grid_h, g.kernel_h,
+                   g.rad_h, g.wrap_h, g.dil_h) &
+         na_dil_ok(na_dil_anchor(xq, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w), xk, g.grid_w, g.kernel_w,
+                   g.rad_w, g.wrap_w, g.dil_w);
+}
+
 }  // namespace
 
 // D_i = sum_d dO_id O_id, one thread per query row.
@@ -219,7 +261,14 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const i32x4_t k_rsrc = head_rsrc(a.k + khead * D, head_bytes);
   const i32x4_t v_rsrc = head_rsrc(a.v + khead * D, head_bytes);
 
-  const KvRun run = kv_run(MASK, Nq, Nkv, C::ROWS, C::ROWS, q0, NaGeom{});
+  const KvRun run = kv_run(MASK, Nq, Nkv, C::ROWS, C::ROWS, q0, a.na);
+  int32_t zq = 0, yq = 0, xq = 0;  // the lane's query in the grid (neighbourhood masks)
+  if constexpr (MASK == MASK_NA) {
+    const int32_t plane = a.na.grid_h * a.na.grid_w;
+    zq = my_q / plane;
+    yq = (my_q - zq * plane) / a.na.grid_w;
+    xq = my_q - zq * plane - yq * a.na.grid_w;
+  }
   const int32_t n = run.count;
   f32x16_t dq[C::DT];
 #pragma unroll
@@ -230,6 +279,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   for (int32_t i = 0; i < n; ++i) {
     const int32_t t = kv_tile_at(run, i, a.n_ktiles);
     const int buf = i & 1;
+    TileOrigin org{0, 0, 0};
+    if constexpr (MASK == MASK_NA) org = tile_origin(t * C::ROWS, a.na);
     if (i + 1 < n) {  // the other buffer was last read before the previous barrier
       const int32_t tn = kv_tile_at(run, i + 1, a.n_ktiles);
       ld.load(k_rsrc, tn, k_lds[buf ^ 1]);
@@ -246,9 +297,15 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       f32x16_t ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int32_t key = t * C::ROWS + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int32_t off = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int32_t key = t * C::ROWS + off;
         bool ok = (key < Nkv) & (my_q < Nq);
         if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
+        if constexpr (MASK == MASK_NA) {
+          int32_t zk, yk, xk;
+          token_coords(org, off, a.na, a.na_inv_w, a.na_inv_h, zk, yk, xk);
+          ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+        }
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l2));
         ds[r] = ok ? p * (dp[r] - dlt) : 0.f;
       }
@@ -294,10 +351,19 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   const i32x4_t q_rsrc = head_rsrc(a.q + qhead * D, head_bytes);
   const i32x4_t g_rsrc = head_rsrc(a.dout + qhead * D, head_bytes);
 
-  // query tiles that see some key of this tile: all, or (causal, key j <= query i) from the
-  // tile holding query k0 on
-  const int32_t first = MASK == MASK_CAUSAL ? k0 / C::ROWS : 0;
-  const int32_t n = first < a.n_qtiles ? a.n_qtiles - first : 0;
+  // query tiles that see some key of this tile: all; (causal, key j <= query i) those from the
+  // tile holding query k0 on; for neighbourhood windows a band of them
+  KvRun qrun{0, a.n_qtiles};
+  if (MASK == MASK_CAUSAL) qrun = KvRun{k0 / C::ROWS, k0 / C::ROWS < a.n_qtiles ? a.n_qtiles - k0 / C::ROWS : 0};
+  int32_t zk = 0, yk = 0, xk = 0;  // the lane's key in the grid (neighbourhood masks)
+  if constexpr (MASK == MASK_NA) {
+    qrun = na_query_run(a.na, Nkv, C::ROWS, k0);
+    const int32_t plane = a.na.grid_h * a.na.grid_w;
+    zk = my_k / plane;
+    yk = (my_k - zk * plane) / a.na.grid_w;
+    xk = my_k - zk * plane - yk * a.na.grid_w;
+  }
+  const int32_t n = qrun.count;
 
   f32x16_t dk[C::DT], dv[C::DT];
 #pragma unroll
@@ -312,9 +378,10 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   };
   float l2n = 0.f, dln = 0.f;
   if (n > 0) {
-    ld.load(q_rsrc, first, q_lds[0]);
-    ld.load(g_rsrc, first, g_lds[0]);
-    stats(first, l2n, dln);
+    const int32_t q_first = kv_tile_at(qrun, 0, a.n_qtiles);
+    ld.load(q_rsrc, q_first, q_lds[0]);
+    ld.load(g_rsrc, q_first, g_lds[0]);
+    stats(q_first, l2n, dln);
     wait_tile_loads<0>();
     if (tid < C::ROWS) {
       l2_lds[0][tid] = l2n;
@@ -323,12 +390,15 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
     __syncthreads();
   }
   for (int32_t i = 0; i < n; ++i) {
-    const int32_t qt = first + i;
+    const int32_t qt = kv_tile_at(qrun, i, a.n_qtiles);
     const int buf = i & 1;
+    TileOrigin org{0, 0, 0};
+    if constexpr (MASK == MASK_NA) org = tile_origin(qt * C::ROWS, a.na);
     if (i + 1 < n) {  // next tile into the other buffers (last read before the previous barrier)
-      ld.load(q_rsrc, qt + 1, q_lds[buf ^ 1]);
-      ld.load(g_rsrc, qt + 1, g_lds[buf ^ 1]);
-      stats(qt + 1, l2n, dln);
+      const int32_t qn = kv_tile_at(qrun, i + 1, a.n_qtiles);
+      ld.load(q_rsrc, qn, q_lds[buf ^ 1]);
+      ld.load(g_rsrc, qn, g_lds[buf ^ 1]);
+      stats(qn, l2n, dln);
     }
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb) {
@@ -347,6 +417,11 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
           const int32_t qi = qt * C::ROWS + qr + j;
           bool ok = (qi < Nq) & (my_k < Nkv);
           if (MASK == MASK_CAUSAL) ok = ok & (my_k <= qi);
+          if constexpr (MASK == MASK_NA) {
+            int32_t zq, yq, xq;
+            token_coords(org, qr + j, a.na, a.na_inv_w, a.na_inv_h, zq, yq, xq);
+            ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+          }
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lv[j]));
           p[r] = ok ? pv : 0.f;
           ds[r] = ok ? pv * (dp[r] - dv4[j]) : 0.f;
@@ -382,9 +457,19 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_bwd_mask(const BwdArgs& a, int32_t mask, hipStream_t stream) {
+  switch (mask) {
+    case MASK_NONE: return launch_bwd_d<D, MASK_NONE>(a, stream);
+    case MASK_CAUSAL: return launch_bwd_d<D, MASK_CAUSAL>(a, stream);
+    case MASK_NA: return launch_bwd_d<D, MASK_NA>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream) {
-  if (d == 64) return mask == MASK_CAUSAL ? launch_bwd_d<64, MASK_CAUSAL>(a, stream) : launch_bwd_d<64, MASK_NONE>(a, stream);
-  if (d == 32) return mask == MASK_CAUSAL ? launch_bwd_d<32, MASK_CAUSAL>(a, stream) : launch_bwd_d<32, MASK_NONE>(a, stream);
+  if (d == 64) return launch_bwd_mask<64>(a, mask, stream);
+  if (d == 32) return launch_bwd_mask<32>(a, mask, stream);
   return hipErrorInvalidValue;
 }
 

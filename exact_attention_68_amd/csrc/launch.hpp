@@ -60,12 +60,10 @@ struct BwdArgs {
   float c;           // |scale| * log2(e)
   float scale;       // signed
   uint32_t q_sign;   // 0x80008000 when scale < 0, else 0
+  NaGeom na;         // neighbourhood geometry (neighbourhood masks only)
+  float na_inv_w;    // 1 / grid_w, rounded to float
+  float na_inv_h;    // 1 / grid_h, rounded to float
 };
-
-// Head sizes and masks the backward kernels are built for.
-constexpr bool bwd_supported(int64_t d, int32_t mask_mode) {
-  return (d == 32 || d == 64) && (mask_mode == ATTN_MASK_NONE || mask_mode == ATTN_MASK_CAUSAL);
-}
 
 // Launches the three backward kernels (D per row, dQ, dK and dV) on `stream`.
 hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream);

@@ -118,6 +118,20 @@ constexpr int32_t kv_tile_at(const KvRun& run, int32_t i, int32_t n_tiles) {
   return t >= n_tiles ? t - n_tiles : t;
 }
 
+// Backward of a neighbourhood window: the run of query tiles (BN queries each)
+// holding every query whose window reaches a key of the tile [k0, k0 + BN). It
+// is the band of kv_run with every axis taken as wrapped, of radius r on wrapped
+// axes (a wrapped window reaches the keys within r * dil of its query, both ways)
+// and kernel - 1 on clamped ones (a clamped window holds its query and spans
+// (kernel - 1) * dil cells): a superset; the element test decides.
+constexpr KvRun na_query_run(const NaGeom& g, int32_t N, int32_t BN, int32_t k0) {
+  NaGeom r = g;
+  if (!r.wrap_d) r.wrap_d = 1, r.rad_d = r.kernel_d - 1;
+  if (!r.wrap_h) r.wrap_h = 1, r.rad_h = r.kernel_h - 1;
+  if (!r.wrap_w) r.wrap_w = 1, r.rad_w = r.kernel_w - 1;
+  return kv_run(MASK_NA, N, N, BN, BN, k0, r);
+}
+
 // Does key tile t need the element mask for the query tile starting at q0?
 constexpr bool tile_needs_mask(int mask, int32_t Nkv, int32_t BN, int32_t q0, int32_t t) {
   const int32_t k_end = t * BN + BN;  // exclusive

@@ -140,14 +140,13 @@ inline attn_status_t check_workspace(const void* ws, uint64_t ws_bytes, int64_t 
   return ATTN_OK;
 }
 
-// Backward: the problem checks of the forward, then the head sizes and masks the
-// backward kernels support.
+// Backward: the problem checks of the forward, then the head sizes the backward
+// kernels support.
 inline attn_status_t check_bwd_problem(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
                                        int32_t mask_mode, const void* params) {
   const attn_status_t st = check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
   if (st != ATTN_OK) return st;
-  if (!((d == 32 || d == 64) && (mask_mode == ATTN_MASK_NONE || mask_mode == ATTN_MASK_CAUSAL)))
-    return ATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

@@ -148,6 +148,31 @@ static void check_grid_bits(const NaGeom& g, int BN) {
   else check_grid_bits_bn<4>(g);
 }
 
+// The backward's run of query tiles for a key tile: each tile once, and every query
+// whose window holds a key of the tile is in a visited tile.
+static void check_query_run(const NaGeom& g, int BN) {
+  if (!geom_valid(g)) return;
+  const int N = g.grid_d * g.grid_h * g.grid_w;
+  const int n_tiles = (int)cdiv(N, BN);
+  std::vector<std::set<int>> sees(N);  // queries that see key k
+  for (int q = 0; q < N; ++q)
+    for (int k : window_keys(g, q)) sees[k].insert(q);
+  for (int k0 = 0; k0 < N; k0 += BN) {
+    const KvRun run = na_query_run(g, N, BN, k0);
+    EXPECT(run.count >= 1 && run.count <= n_tiles, "query run count %d", run.count);
+    std::set<int> visited;
+    for (int i = 0; i < run.count; ++i) {
+      const int t = kv_tile_at(run, i, n_tiles);
+      EXPECT(t >= 0 && t < n_tiles && visited.insert(t).second, "query tile %d out of range or twice", t);
+    }
+    for (int k = k0; k < N && k < k0 + BN; ++k)
+      for (int q : sees[k])
+        EXPECT(visited.count(q / BN) == 1, "query %d sees key %d but its tile is skipped (grid %dx%dx%d k %d,%d,%d wrap %d%d%d dil %d,%d,%d)",
+               q, k, g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w,
+               g.dil_d, g.dil_h, g.dil_w);
+  }
+}
+
 static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int BN) {
   check_na_geom(geom(1, gh, gw, 1, kh, kw, 0, wh, ww, 1, 1, 1), BM, BN);
 }
@@ -368,6 +393,19 @@ int main() {
     check_na_geom(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), kBlockM, BN);
     check_na_geom(geom(16, 16, 16, 3, 3, 3, 1, 0, 1, 2, 2, 2), kBlockM, BN);
   }
+  // the backward's query runs
+  for (int gh : {1, 3, 5, 9, 17})
+    for (int gw : {2, 5, 8, 13, 40})
+      for (int kh = 1; kh <= 5; kh += 2)
+        for (int wh = 0; wh < 2; ++wh)
+          for (int ww = 0; ww < 2; ++ww)
+            for (int dil : {1, 2}) check_query_run(geom(1, gh, gw, 1, kh, 3, 0, wh, ww, 1, dil, 1), 128);
+  check_query_run(geom(4, 5, 6, 3, 3, 3, 1, 0, 1, 1, 1, 1), 128);
+  check_query_run(geom(6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2), 128);
+  check_query_run(geom(10, 9, 8, 3, 3, 3, 0, 0, 0, 3, 3, 2), 128);
+  check_query_run(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1), 128);
+  check_query_run(geom(1, 64, 64, 1, 7, 7, 0, 0, 0, 1, 1, 1), 128);
+  check_query_run(geom(1, 33, 17, 1, 9, 3, 0, 1, 1, 1, 1, 1), 128);
   // grid-window bit masks: widths 4..124 (incl. 61..65 around the 64-bit word boundary), 3D, dilation
   for (int BN : {64, 128}) {
     for (int W : {4, 5, 7, 20, 31, 33, 40, 61, 62, 63, 64, 65, 100, 124})

@@ -160,7 +160,7 @@ def bwd_reference(q, k, v, do, scale, mask="none", na=None, o_used=None, lse_err
     return grads, tuple(1.25 * t + 1e-4 for t in (tq, tk, tv))
 
 
-def run_gpu_bwd(q, k, v, do, scale, mask_mode, o=None, lse=None):
+def run_gpu_bwd(q, k, v, do, scale, mask_mode, o=None, lse=None, params=None):
     """attn_bwd on the device; o and lse default to the GPU forward's (attn_fwd_ex). Returns
     (dq, dk, dv, o, lse) on the device."""
     import exact_attention_68_amd as A
@@ -171,33 +171,35 @@ def run_gpu_bwd(q, k, v, do, scale, mask_mode, o=None, lse=None):
     if o is None:
         o = torch.empty_like(dq_)
         lse = torch.empty(B, H, Nq, dtype=torch.float32, device="cuda")
-        ws = split_workspace(B, H, Nq, d, mask_mode, None, n_kv=Nkv)
-        A.attn_fwd_ex(dq_, dk_, dv_, o, lse, scale, mask_mode, None, ws)
+        ws = split_workspace(B, H, Nq, d, mask_mode, params, n_kv=Nkv)
+        A.attn_fwd_ex(dq_, dk_, dv_, o, lse, scale, mask_mode, params, ws)
     else:
         o, lse = o.to("cuda"), lse.to("cuda")
-    wsb = torch.full((A.attn_bwd_workspace_size(B, H, Nq, Nkv, d, mask_mode),), 255, dtype=torch.uint8, device="cuda")
+    wsb = torch.full((A.attn_bwd_workspace_size(B, H, Nq, Nkv, d, mask_mode, params),), 255, dtype=torch.uint8,
+                     device="cuda")
     gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
-    A.attn_bwd(dq_, dk_, dv_, o, do_, lse, gq, gk, gv, scale, mask_mode, None, wsb)
+    A.attn_bwd(dq_, dk_, dv_, o, do_, lse, gq, gk, gv, scale, mask_mode, params, wsb)
     torch.cuda.synchronize()
     return gq, gk, gv, o, lse
 
 
-def check_bwd_case(q, k, v, do, scale, mask: str, what="", pipeline=False) -> float:
+def check_bwd_case(q, k, v, do, scale, mask: str, what="", pipeline=False, params=None) -> float:
     """GPU gradients against the oracle. By default attn_bwd gets the oracle's output (rounded to bf16)
     and logsumexp (fp32), so the bound covers the backward alone; with pipeline=True it gets the GPU
     forward's, and the bound takes the forward's output error and logsumexp tolerance as given."""
     print(f"[parity-bwd] {what} B{q.shape[0]} H{q.shape[1]} Nq{q.shape[2]} Nkv{k.shape[2]} d{q.shape[3]} mask={mask} "
           f"scale={scale} pipeline={pipeline}", flush=True)
     qf, kf, vf, gf = (to_f64(t) for t in (q, k, v, do))
+    na = oracle_na(params)
     if pipeline:
-        gq, gk, gv, o, _ = run_gpu_bwd(q, k, v, do, scale, MASK_MODES[mask])
-        ref, tol = bwd_reference(qf, kf, vf, gf, scale, mask, o_used=to_f64(o), lse_err=6e-3)
+        gq, gk, gv, o, _ = run_gpu_bwd(q, k, v, do, scale, MASK_MODES[mask], params=params)
+        ref, tol = bwd_reference(qf, kf, vf, gf, scale, mask, na, o_used=to_f64(o), lse_err=6e-3)
     else:
-        o, lse = oracle.attention(qf, kf, vf, scale, mask, return_lse=True)
+        o, lse = oracle.attention(qf, kf, vf, scale, mask, na, return_lse=True)
         o_b = torch.from_numpy(o.astype(np.float32)).to(torch.bfloat16)
         lse_f = torch.from_numpy(lse.astype(np.float32))
-        gq, gk, gv, _, _ = run_gpu_bwd(q, k, v, do, scale, MASK_MODES[mask], o_b, lse_f)
-        ref, tol = bwd_reference(qf, kf, vf, gf, scale, mask, o_used=to_f64(o_b))
+        gq, gk, gv, _, _ = run_gpu_bwd(q, k, v, do, scale, MASK_MODES[mask], o_b, lse_f, params)
+        ref, tol = bwd_reference(qf, kf, vf, gf, scale, mask, na, o_used=to_f64(o_b))
     worst = 0.0
     for name, g, r, t in zip(("dq", "dk", "dv"), (gq, gk, gv), ref, tol):
         gv_ = to_f64(g)

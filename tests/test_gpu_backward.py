@@ -67,6 +67,39 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mask, what=f"bwd pipeline {N}x{Nkv}", pipeline=True)
 
 
+# ---------------------------------------------------------------- neighbourhood windows
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("mode,geo", [
+    ("na2d", (5, 5, 3, 3, 1, 1, 1, 1)),       # the issue's 5x5 wrap example geometry
+    ("na2d", (8, 9, 5, 5, 1, 1, 1, 1)),
+    ("na2d", (7, 13, 3, 5, 0, 0, 1, 1)),      # clamped windows: not symmetric between queries and keys
+    ("na2d", (10, 6, 5, 3, 1, 0, 1, 1)),
+    ("na2d", (33, 17, 9, 3, 1, 1, 1, 1)),     # band crosses tiles and wraps
+    ("na2d", (16, 20, 3, 5, 1, 1, 2, 3)),     # dilated, wrapped
+    ("na2d", (17, 9, 5, 3, 0, 0, 3, 2)),      # dilated, clamped
+    ("na3d", (3, 5, 4, 3, 3, 3, 1, 1, 1, 1, 1, 1)),
+    ("na3d", (6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2)),
+])
+def test_bwd_neighbourhood(mode, geo, d):
+    import exact_attention_68_amd as A
+
+    params = A.na2d_params(*geo) if mode == "na2d" else A.na3d_params(*geo)
+    N = geo[0] * geo[1] * (geo[2] if mode == "na3d" else 1)
+    q, k, v, do = _inputs(1, 2, N, N, d, 11600 + N + d)
+    check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mode, what=f"bwd {mode} {geo}", params=params)
+
+
+def test_bwd_neighbourhood_workload_shape():
+    """The 64x64 7x7 wrapped window of the 2D workload (B2 H4 d32), through the GPU forward."""
+    import exact_attention_68_amd as A
+
+    w = workloads.WORKLOADS["na2d_wrap_64x64_k7"]
+    q, k, v = workloads.workload_qkv(w)
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+    do = torch.randn(w.B, w.H, w.N, w.d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    check_bwd_case(q, k, v, do, w.scale, "na2d", what="bwd na2d 64x64 k7", pipeline=True, params=A.na2d_params(**w.na))
+
+
 def test_bwd_deterministic_and_workspace_content_free():
     """Every gradient element is written by one lane in a fixed order: repeated calls agree bit for bit,
     whatever the workspace held."""
