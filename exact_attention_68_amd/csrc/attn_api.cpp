@@ -206,6 +206,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     a.na = attn::na_geom(mask_mode, params);
     a.na_inv_w = 1.0f / (float)a.na.grid_w;
     a.na_inv_h = 1.0f / (float)a.na.grid_h;
+    a.na_grid = attn::na_grid_eligible(a.na) ? 1 : 0;
     mask = attn::MASK_NA;
   }
   const hipError_t e = attn::launch_bwd(a, (int32_t)d, mask, static_cast<hipStream_t>(stream));

@@ -263,11 +263,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 
   const KvRun run = kv_run(MASK, Nq, Nkv, C::ROWS, C::ROWS, q0, a.na);
   int32_t zq = 0, yq = 0, xq = 0;  // the lane's query in the grid (neighbourhood masks)
+  GridMasks gm{};                  // its window per axis, on grids of width 4..124 (a.na_grid)
   if constexpr (MASK == MASK_NA) {
     const int32_t plane = a.na.grid_h * a.na.grid_w;
     zq = my_q / plane;
     yq = (my_q - zq * plane) / a.na.grid_w;
     xq = my_q - zq * plane - yq * a.na.grid_w;
+    if (a.na_grid) gm = na_grid_masks(zq, yq, xq, a.na);
   }
   const int32_t n = run.count;
   f32x16_t dq[C::DT];
@@ -280,7 +282,16 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     const int32_t t = kv_tile_at(run, i, a.n_ktiles);
     const int buf = i & 1;
     TileOrigin org{0, 0, 0};
-    if constexpr (MASK == MASK_NA) org = tile_origin(t * C::ROWS, a.na);
+    uint32_t bm[C::SB] = {};  // window bits of the tile's keys (a.na_grid)
+    if constexpr (MASK == MASK_NA) {
+      org = tile_origin(t * C::ROWS, a.na);
+      if (a.na_grid) {
+        uint32_t w4[C::SB];
+        na_tile_window(gm, (t * C::ROWS) / a.na.grid_w, org.x0, a.na, w4);
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) bm[sb] = lane_block_bits(w4[sb], half);
+      }
+    }
     if (i + 1 < n) {  // the other buffer was last read before the previous barrier
       const int32_t tn = kv_tile_at(run, i + 1, a.n_ktiles);
       ld.load(k_rsrc, tn, k_lds[buf ^ 1]);
@@ -302,9 +313,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
         bool ok = (key < Nkv) & (my_q < Nq);
         if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
         if constexpr (MASK == MASK_NA) {
-          int32_t zk, yk, xk;
-          token_coords(org, off, a.na, a.na_inv_w, a.na_inv_h, zk, yk, xk);
-          ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+          if (a.na_grid) {
+            ok = ok & (((bm[sb] >> r) & 1u) != 0u);
+          } else {
+            int32_t zk, yk, xk;
+            token_coords(org, off, a.na, a.na_inv_w, a.na_inv_h, zk, yk, xk);
+            ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+          }
         }
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l2));
         ds[r] = ok ? p * (dp[r] - dlt) : 0.f;
@@ -331,8 +346,9 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
   const int32_t Nq = a.Nq, Nkv = a.Nkv;
   // causal: key tile 0 sees every query tile, the last one the fewest, so all heads' key tile 0
-  // go first (longest first, as the forward's causal order); otherwise head-major
-  const int32_t wg = blockIdx.x;
+  // go first (longest first, as the forward's causal order); otherwise the key tiles of a head
+  // are kept on one XCD (xcd_contiguous), whose L2 then serves its Q and dO tiles
+  const int32_t wg = MASK == MASK_CAUSAL ? (int32_t)blockIdx.x : xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = MASK == MASK_CAUSAL ? wg % a.BH : wg / a.n_ktiles;
   const int32_t ktile = MASK == MASK_CAUSAL ? wg / a.BH : wg - bh * a.n_ktiles;
   const int32_t k0 = ktile * C::ROWS, my_k = k0 + wave * 32 + col;
@@ -356,12 +372,14 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   KvRun qrun{0, a.n_qtiles};
   if (MASK == MASK_CAUSAL) qrun = KvRun{k0 / C::ROWS, k0 / C::ROWS < a.n_qtiles ? a.n_qtiles - k0 / C::ROWS : 0};
   int32_t zk = 0, yk = 0, xk = 0;  // the lane's key in the grid (neighbourhood masks)
+  GridMasks rm{};                  // per axis, the queries whose window holds it (a.na_grid)
   if constexpr (MASK == MASK_NA) {
     qrun = na_query_run(a.na, Nkv, C::ROWS, k0);
     const int32_t plane = a.na.grid_h * a.na.grid_w;
     zk = my_k / plane;
     yk = (my_k - zk * plane) / a.na.grid_w;
     xk = my_k - zk * plane - yk * a.na.grid_w;
+    if (a.na_grid) rm = na_grid_reverse_masks(zk, yk, xk, a.na);
   }
   const int32_t n = qrun.count;
 
@@ -393,7 +411,16 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
     const int32_t qt = kv_tile_at(qrun, i, a.n_qtiles);
     const int buf = i & 1;
     TileOrigin org{0, 0, 0};
-    if constexpr (MASK == MASK_NA) org = tile_origin(qt * C::ROWS, a.na);
+    uint32_t bm[C::SB] = {};  // bits of the tile's queries whose window holds the lane's key (a.na_grid)
+    if constexpr (MASK == MASK_NA) {
+      org = tile_origin(qt * C::ROWS, a.na);
+      if (a.na_grid) {
+        uint32_t w4[C::SB];
+        na_tile_window(rm, (qt * C::ROWS) / a.na.grid_w, org.x0, a.na, w4);
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) bm[sb] = lane_block_bits(w4[sb], half);
+      }
+    }
     if (i + 1 < n) {  // next tile into the other buffers (last read before the previous barrier)
       const int32_t qn = kv_tile_at(qrun, i + 1, a.n_qtiles);
       ld.load(q_rsrc, qn, q_lds[buf ^ 1]);
@@ -418,9 +445,13 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
           bool ok = (qi < Nq) & (my_k < Nkv);
           if (MASK == MASK_CAUSAL) ok = ok & (my_k <= qi);
           if constexpr (MASK == MASK_NA) {
-            int32_t zq, yq, xq;
-            token_coords(org, qr + j, a.na, a.na_inv_w, a.na_inv_h, zq, yq, xq);
-            ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+            if (a.na_grid) {
+              ok = ok & (((bm[sb] >> r) & 1u) != 0u);
+            } else {
+              int32_t zq, yq, xq;
+              token_coords(org, qr + j, a.na, a.na_inv_w, a.na_inv_h, zq, yq, xq);
+              ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+            }
           }
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lv[j]));
           p[r] = ok ? pv : 0.f;

@@ -63,6 +63,7 @@ struct BwdArgs {
   NaGeom na;         // neighbourhood geometry (neighbourhood masks only)
   float na_inv_w;    // 1 / grid_w, rounded to float
   float na_inv_h;    // 1 / grid_h, rounded to float
+  int32_t na_grid;   // 1: per-axis window masks (na_grid_eligible), else the element test
 };
 
 // Launches the three backward kernels (D per row, dQ, dK and dV) on `stream`.

@@ -225,6 +225,35 @@ constexpr GridMasks na_grid_masks(int32_t zq, int32_t yq, int32_t xq, const NaGe
   return m;
 }
 
+// The reverse relation, for the backward: bit c of an axis mask says whether the
+// window of query coordinate c holds key coordinate x. Wrapped windows are
+// symmetric (c + dil * t = x mod L with |t| <= r), so it is the window of x itself;
+// a clamped window holds its query and spans (kernel - 1) * dil cells, so only
+// those candidates are tested.
+constexpr void na_axis_reverse_mask(int32_t x, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil,
+                                    uint64_t& lo, uint64_t& hi) {
+  if (wrap) {
+    na_axis_mask(x, len, kernel, rad, wrap, dil, lo, hi);
+    return;
+  }
+  lo = hi = 0;
+  const int32_t reach = (kernel - 1) * dil;
+  for (int32_t c = imax(x - reach, 0); c <= imin(x + reach, len - 1); ++c) {
+    if (!na_dil_ok(na_dil_anchor(c, len, kernel, rad, wrap, dil), x, len, kernel, rad, wrap, dil)) continue;
+    const uint64_t bit = 1ull << (c & 63);
+    lo |= c < 64 ? bit : 0ull;
+    hi |= c < 64 ? 0ull : bit;
+  }
+}
+
+constexpr GridMasks na_grid_reverse_masks(int32_t zk, int32_t yk, int32_t xk, const NaGeom& g) {
+  GridMasks m{};
+  na_axis_reverse_mask(xk, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w, m.x0, m.x1);
+  na_axis_reverse_mask(yk, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h, m.y0, m.y1);
+  na_axis_reverse_mask(zk, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d, m.z0, m.z1);
+  return m;
+}
+
 // Bit c of a 128-bit mask (lo, hi), c < 128.
 constexpr uint64_t bit128(uint64_t lo, uint64_t hi, int32_t c) { return ((c < 64 ? lo : hi) >> (c & 63)) & 1ull; }
 

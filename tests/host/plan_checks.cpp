@@ -142,6 +142,35 @@ static void check_grid_bits_bn(const NaGeom& g) {
   }
 }
 
+// The backward's reverse masks: for every key and query tile, bit r of each block says
+// whether that query's window holds the key.
+static void check_reverse_bits(const NaGeom& g) {
+  if (!geom_valid(g) || !na_grid_eligible(g)) return;
+  const int W = g.grid_w, plane = g.grid_h * W, N = g.grid_d * plane, BN = 128;
+  std::vector<std::set<int>> sees(N);
+  for (int q = 0; q < N; ++q)
+    for (int k : window_keys(g, q)) sees[k].insert(q);
+  for (int key = 0; key < N; ++key) {
+    const GridMasks m = na_grid_reverse_masks(key / plane, key % plane / W, key % W, g);
+    for (int t = 0; t < (int)cdiv(N, BN); ++t) {
+      const int q0 = t * BN, row0 = q0 / W;
+      uint32_t w[4];
+      na_tile_window(m, row0, q0 - row0 * W, g, w);
+      for (int half = 0; half < 2; ++half)
+        for (int sb = 0; sb < 4; ++sb) {
+          const uint32_t bits = lane_block_bits(w[sb], half);
+          for (int r = 0; r < 16; ++r) {
+            const int q = q0 + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool x = q < N && sees[key].count(q) == 1;
+            EXPECT((((bits >> r) & 1u) == 1u) == x, "reverse bits %dx%dx%d k %d,%d,%d wrap %d%d%d dil %d,%d,%d key %d query %d",
+                   g.grid_d, g.grid_h, g.grid_w, g.kernel_d, g.kernel_h, g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w,
+                   g.dil_d, g.dil_h, g.dil_w, key, q);
+          }
+        }
+    }
+  }
+}
+
 static void check_grid_bits(const NaGeom& g, int BN) {
   if (!geom_valid(g) || !na_grid_eligible(g)) return;
   if (BN == 64) check_grid_bits_bn<2>(g);
@@ -393,6 +422,14 @@ int main() {
     check_na_geom(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), kBlockM, BN);
     check_na_geom(geom(16, 16, 16, 3, 3, 3, 1, 0, 1, 2, 2, 2), kBlockM, BN);
   }
+  // the backward's reverse window masks
+  check_reverse_bits(geom(1, 7, 13, 1, 3, 5, 0, 0, 0, 1, 1, 1));
+  check_reverse_bits(geom(1, 10, 6, 1, 5, 3, 0, 1, 0, 1, 1, 1));
+  check_reverse_bits(geom(1, 17, 9, 1, 5, 3, 0, 0, 0, 1, 3, 2));
+  check_reverse_bits(geom(1, 16, 20, 1, 3, 5, 0, 1, 1, 1, 2, 3));
+  check_reverse_bits(geom(3, 5, 4, 3, 3, 3, 1, 1, 1, 1, 1, 1));
+  check_reverse_bits(geom(6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2));
+  check_reverse_bits(geom(10, 9, 8, 3, 3, 3, 0, 0, 0, 3, 3, 2));
   // the backward's query runs
   for (int gh : {1, 3, 5, 9, 17})
     for (int gw : {2, 5, 8, 13, 40})

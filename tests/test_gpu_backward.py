@@ -79,6 +79,9 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (17, 9, 5, 3, 0, 0, 3, 2)),      # dilated, clamped
     ("na3d", (3, 5, 4, 3, 3, 3, 1, 1, 1, 1, 1, 1)),
     ("na3d", (6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2)),
+    ("na2d", (40, 3, 5, 3, 1, 1, 2, 1)),      # width 3 and 200: the element test instead of the window masks
+    ("na2d", (2, 200, 1, 7, 0, 1, 1, 3)),
+    ("na3d", (2, 130, 4, 1, 5, 3, 0, 1, 1, 1, 2, 1)),   # more than 128 rows
 ])
 def test_bwd_neighbourhood(mode, geo, d):
     import exact_attention_68_amd as A
