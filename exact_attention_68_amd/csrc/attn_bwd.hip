@@ -41,6 +41,10 @@ namespace {
 template <int D>
 struct BwdCfg {
   static constexpr int ROWS = 128;  // rows of a streamed tile; a work-group holds 4 x 32 resident rows
+  // Two buffers of two streamed tiles: 64 KB of LDS at d <= 64 (two work-groups per CU),
+  // 128 KB at d = 128 (one work-group per CU, whose wavefronts then get the whole
+  // register file: the d = 128 accumulators do not fit in half of it).
+  static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROW_CHUNKS = D / 8;
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
 
 // dQ for one 128-query tile: key/value tiles through a two-buffer LDS ring.
 template <int D, int MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::WAVES_PER_EU)))
 void attn_bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][C::TILE];
@@ -336,7 +340,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 // dK and dV for one 128-key tile: query/dO tiles and their logsumexp and D values
 // through a two-buffer LDS ring.
 template <int D, int MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::WAVES_PER_EU)))
 void attn_bwd_dkv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][C::TILE];
@@ -501,6 +505,7 @@ static hipError_t launch_bwd_mask(const BwdArgs& a, int32_t mask, hipStream_t st
 hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream) {
   if (d == 64) return launch_bwd_mask<64>(a, mask, stream);
   if (d == 32) return launch_bwd_mask<32>(a, mask, stream);
+  if (d == 128) return launch_bwd_mask<128>(a, mask, stream);
   return hipErrorInvalidValue;
 }
 

@@ -140,14 +140,11 @@ inline attn_status_t check_workspace(const void* ws, uint64_t ws_bytes, int64_t 
   return ATTN_OK;
 }
 
-// Backward: the problem checks of the forward, then the head sizes the backward
-// kernels support.
+// Backward: the backward kernels take every problem the forward takes (d = 32, 64
+// or 128, every mask, Nq != Nkv).
 inline attn_status_t check_bwd_problem(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
                                        int32_t mask_mode, const void* params) {
-  const attn_status_t st = check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
-  if (st != ATTN_OK) return st;
-  if (d != 32 && d != 64) return ATTN_ERR_UNSUPPORTED;
-  return ATTN_OK;
+  return check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
 }
 
 // Backward pointers: every tensor present and aligned (lse 4 bytes, the rest 16),

@@ -245,8 +245,8 @@ attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, i
  * dq, dk, dv : outputs, device bfloat16 shaped like q, k and v, rounded to
  *           nearest even; disjoint from every input and from each other.
  * mask_mode, params : as for attn_fwd_ex (no mask, causal, 2D or 3D
- *           neighbourhood windows with wrap, clamp and dilation). d: 32 or 64;
- *           other head sizes return ATTN_ERR_UNSUPPORTED.
+ *           neighbourhood windows with wrap, clamp and dilation); d = 32, 64
+ *           or 128, as for the forward.
  * workspace : device memory of at least attn_bwd_workspace_size bytes
  *           (B*H*Nq float32 row sums), 256-byte aligned, disjoint from the
  *           tensors; any content; calls sharing it must not overlap.

@@ -171,10 +171,11 @@ def test_bwd_rejects_before_device_work(A):
     assert lib.attn_bwd_workspace_size(2, 3, 100, 77, 64, 0, None, ctypes.byref(n)) == A.ATTN_OK
     assert n.value == 2 * 3 * 100 * 4
     assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 64, 0, None, None) == A.ATTN_ERR_INVALID_ARG
-    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 128, 0, None, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 96, 0, None, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 128, 0, None, ctypes.byref(n)) == A.ATTN_OK
     p = ctypes.cast(ctypes.pointer(A.na2d_params(8, 8, 3, 3)), ctypes.c_void_p)
     assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 64, A.ATTN_MASK_NA2D, p, ctypes.byref(n)) == A.ATTN_OK
-    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 128, A.ATTN_MASK_NA2D, p, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_bwd_workspace_size(1, 1, 64, 64, 96, A.ATTN_MASK_NA2D, p, ctypes.byref(n)) == A.ATTN_ERR_UNSUPPORTED
     args = (1, 1, 64, 64, 64, 0.1, 0, None, ws, 1 << 16, None)
     assert lib.attn_bwd(None, k, v, o, g, lse, dq, dk, dv, *args) == A.ATTN_ERR_INVALID_ARG
     assert lib.attn_bwd(q, k, v, o, g, lse + 2, dq, dk, dv, *args) == A.ATTN_ERR_ALIGNMENT
@@ -187,7 +188,7 @@ def test_bwd_rejects_before_device_work(A):
                         None) == A.ATTN_ERR_WORKSPACE
     assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 64, 0.1, 0, None, ws + 16, 1 << 16,
                         None) == A.ATTN_ERR_WORKSPACE
-    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 128, 0.1, 0, None, ws, 1 << 16,
+    assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 96, 0.1, 0, None, ws, 1 << 16,
                         None) == A.ATTN_ERR_UNSUPPORTED
     assert lib.attn_bwd(q, k, v, o, g, lse, dq, dk, dv, 1, 1, 64, 64, 64, float("inf"), 0, None, ws, 1 << 16,
                         None) == A.ATTN_ERR_INVALID_ARG

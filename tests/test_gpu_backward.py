@@ -29,7 +29,7 @@ def _inputs(B, H, Nq, Nkv, d, seed, q_gain=1.0):
     return q, k, v, do
 
 
-@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 @pytest.mark.parametrize("N", [1, 17, 100, 128, 255, 257, 320])
 def test_bwd_edge_shapes(N, mask, d):
@@ -37,7 +37,7 @@ def test_bwd_edge_shapes(N, mask, d):
     check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mask, what=f"bwd N{N}")
 
 
-@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 @pytest.mark.parametrize("Nq,Nkv", [(300, 77), (77, 300), (1, 500), (500, 1), (129, 384)])
 def test_bwd_cross_shapes(Nq, Nkv, mask, d):
@@ -60,7 +60,14 @@ def test_bwd_sd21_head_shape(mask):
 
 
 @pytest.mark.parametrize("mask", ["none", "causal"])
-@pytest.mark.parametrize("N,Nkv,d", [(300, 300, 64), (257, 100, 32), (1000, 1000, 64)])
+def test_bwd_d128_head_shape(mask):
+    """One head of the d = 128 workload's size (N4096, d128)."""
+    q, k, v, do = _inputs(1, 1, 4096, 4096, 128, 11320)
+    check_bwd_case(q, k, v, do, 1 / math.sqrt(128), mask, what="bwd N4096 d128")
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("N,Nkv,d", [(300, 300, 64), (257, 100, 32), (1000, 1000, 64), (700, 700, 128)])
 def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     """attn_fwd_ex then attn_bwd, both on the GPU (bound with the forward's errors as inputs)."""
     q, k, v, do = _inputs(1, 2, N, Nkv, d, 11350 + N + Nkv)
@@ -68,7 +75,7 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
 
 
 # ---------------------------------------------------------------- neighbourhood windows
-@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("mode,geo", [
     ("na2d", (5, 5, 3, 3, 1, 1, 1, 1)),       # the issue's 5x5 wrap example geometry
     ("na2d", (8, 9, 5, 5, 1, 1, 1, 1)),
@@ -115,7 +122,7 @@ def test_bwd_deterministic_and_workspace_content_free():
 def test_bwd_rejects_unsupported_and_leaves_outputs():
     import exact_attention_68_amd as A
 
-    q, k, v, do = (t.cuda() for t in _inputs(1, 1, 64, 64, 128, 11500))
+    q, k, v, do = (t.cuda() for t in _inputs(1, 1, 64, 64, 96, 11500))
     o = torch.zeros_like(q)
     lse = torch.zeros(1, 1, 64, dtype=torch.float32, device="cuda")
     gq, gk, gv = (torch.full_like(t, 3.0) for t in (q, k, v))
