@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn.h"
 #include "kernel_common.hpp"
 #include "launch.hpp"
@@ -305,33 +307,52 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       wait_tile_loads<0>();
     }
     __syncthreads();
+    // A hidden score enters the exponent as -inf (P = 0, dS = 0 for any scale, 0 included).
+    // Rows past Nq need no test: their Q and dO fragments are zero, so dS = 1 * (0 - 0).
+    // Keys past Nkv do (K = 0 there, but P * (0 - D) could overflow), as do causal
+    // diagonal tiles and every window tile; other tiles take the body without any test,
+    // chosen per tile (uniform): a per-element select of the product itself compiles
+    // into a branch around each exponential.
+    auto tile_body = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb) {
-      const f32x16_t s = block_product<D>(k_lds[buf], sb, col, half, swz, qf);
-      const f32x16_t dp = block_product<D>(v_lds[buf], sb, col, half, swz, gf);
-      f32x16_t ds;
+      for (int sb = 0; sb < C::SB; ++sb) {
+        const f32x16_t s = block_product<D>(k_lds[buf], sb, col, half, swz, qf);
+        const f32x16_t dp = block_product<D>(v_lds[buf], sb, col, half, swz, gf);
+        f32x16_t ds;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t off = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int32_t key = t * C::ROWS + off;
-        bool ok = (key < Nkv) & (my_q < Nq);
-        if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
-        if constexpr (MASK == MASK_NA) {
-          if (a.na_grid) {
-            ok = ok & (((bm[sb] >> r) & 1u) != 0u);
-          } else {
-            int32_t zk, yk, xk;
-            token_coords(org, off, a.na, a.na_inv_w, a.na_inv_h, zk, yk, xk);
-            ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+        for (int r = 0; r < 16; ++r) {
+          float add = -l2;
+          if constexpr (MASKED) {
+            const int32_t off = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int32_t key = t * C::ROWS + off;
+            bool ok = key < Nkv;
+            if (MASK == MASK_CAUSAL) ok = ok & (key <= my_q);
+            if constexpr (MASK == MASK_NA) {
+              if (a.na_grid) {
+                ok = ok & (((bm[sb] >> r) & 1u) != 0u);
+              } else {
+                int32_t zk, yk, xk;
+                token_coords(org, off, a.na, a.na_inv_w, a.na_inv_h, zk, yk, xk);
+                ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+              }
+            }
+            add = ok ? add : -INFINITY;
           }
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, add));
+          ds[r] = p * (dp[r] - dlt);
         }
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l2));
-        ds[r] = ok ? p * (dp[r] - dlt) : 0.f;
+        bf16x8_t dsb[2];
+        to_bf16_operand(ds, dsb);
+        block_transpose_product<D>(k_lds[buf], sb, v_row, v_off, dsb, dq);
       }
-      bf16x8_t dsb[2];
-      to_bf16_operand(ds, dsb);
-      block_transpose_product<D>(k_lds[buf], sb, v_row, v_off, dsb, dq);
-    }
+    };
+    bool masked = MASK == MASK_NA || (t + 1) * C::ROWS > Nkv;
+    if (MASK == MASK_CAUSAL) masked = masked || t * C::ROWS + C::ROWS - 1 > q0;
+    if (masked)
+      tile_body(std::true_type{});
+    else
+      tile_body(std::false_type{});
     __syncthreads();  // every wavefront is done with this buffer before it is refilled
   }
   store_rows_scaled<D>(a.dq + qhead * D, my_q, Nq, half, dq, a.scale);
@@ -431,43 +452,60 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
       ld.load(g_rsrc, qn, g_lds[buf ^ 1]);
       stats(qn, l2n, dln);
     }
+    // As in the dQ kernel, a hidden score enters the exponent as -inf. Queries past Nq
+    // need no test (their logsumexp is stored as +inf, so P = 0), nor do keys past Nkv
+    // (their columns of dK and dV are never stored); causal tiles that hold a query
+    // before a key and every window tile take the masked body, chosen per tile.
+    auto tile_body = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb) {
-      const f32x16_t s = block_product<D>(q_lds[buf], sb, col, half, swz, kf);
-      const f32x16_t dp = block_product<D>(g_lds[buf], sb, col, half, swz, vf);
-      f32x16_t p, ds;
+      for (int sb = 0; sb < C::SB; ++sb) {
+        const f32x16_t s = block_product<D>(q_lds[buf], sb, col, half, swz, kf);
+        const f32x16_t dp = block_product<D>(g_lds[buf], sb, col, half, swz, vf);
+        f32x16_t p, ds;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qr = sb * 32 + 8 * g4 + 4 * half;  // first of the 4 queries of this group
-        const float4 l4 = *reinterpret_cast<const float4*>(&l2_lds[buf][qr]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][qr]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qr = sb * 32 + 8 * g4 + 4 * half;  // first of the 4 queries of this group
+          const float4 l4 = *reinterpret_cast<const float4*>(&l2_lds[buf][qr]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][qr]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g4 + j;
-          const int32_t qi = qt * C::ROWS + qr + j;
-          bool ok = (qi < Nq) & (my_k < Nkv);
-          if (MASK == MASK_CAUSAL) ok = ok & (my_k <= qi);
-          if constexpr (MASK == MASK_NA) {
-            if (a.na_grid) {
-              ok = ok & (((bm[sb] >> r) & 1u) != 0u);
-            } else {
-              int32_t zq, yq, xq;
-              token_coords(org, qr + j, a.na, a.na_inv_w, a.na_inv_h, zq, yq, xq);
-              ok = ok & na_visible(a.na, zq, yq, xq, zk, yk, xk);
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * g4 + j;
+            float add = -lv[j];
+            if constexpr (MASKED) {
+              const int32_t qi = qt * C::ROWS + qr + j;
+              bool ok = true;
+              if (MASK == MASK_CAUSAL) ok = my_k <= qi;
+              if constexpr (MASK == MASK_NA) {
+                if (a.na_grid) {
+                  ok = ((bm[sb] >> r) & 1u) != 0u;
+                } else {
+                  int32_t zq, yq, xq;
+                  token_coords(org, qr + j, a.na, a.na_inv_w, a.na_inv_h, zq, yq, xq);
+                  ok = na_visible(a.na, zq, yq, xq, zk, yk, xk);
+                }
+              }
+              add = ok ? add : -INFINITY;
             }
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, add));
+            p[r] = pv;
+            ds[r] = pv * (dp[r] - dv4[j]);
           }
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lv[j]));
-          p[r] = ok ? pv : 0.f;
-          ds[r] = ok ? pv * (dp[r] - dv4[j]) : 0.f;
         }
+        bf16x8_t pb[2], dsb[2];
+        to_bf16_operand(p, pb);
+        to_bf16_operand(ds, dsb);
+        block_transpose_product<D>(g_lds[buf], sb, v_row, v_off, pb, dv);
+        block_transpose_product<D>(q_lds[buf], sb, v_row, v_off, dsb, dk);
       }
-      bf16x8_t pb[2], dsb[2];
-      to_bf16_operand(p, pb);
-      to_bf16_operand(ds, dsb);
-      block_transpose_product<D>(g_lds[buf], sb, v_row, v_off, pb, dv);
-      block_transpose_product<D>(q_lds[buf], sb, v_row, v_off, dsb, dk);
-    }
+    };
+    bool masked = MASK == MASK_NA;
+    if (MASK == MASK_CAUSAL) masked = qt * C::ROWS < k0 + C::ROWS - 1;
+    if (masked)
+      tile_body(std::true_type{});
+    else
+      tile_body(std::false_type{});
     wait_tile_loads<0>();
     if (i + 1 < n && tid < C::ROWS) {
       l2_lds[buf ^ 1][tid] = l2n;
