@@ -46,6 +46,7 @@
 #include "launch.hpp"
 #include "tile_plan.hpp"
 
+
 namespace attn {
 
 template <int D>
@@ -529,7 +530,6 @@ void attn_fwd_kernel(KernelArgs a) {
     u32x4_t kf[TOT];
     bf16x8_t vf[TOT];
     uint32_t pw[SB][2][4];  // new probabilities, two bf16 per word
-    float psum0 = 0.f, psum1 = 0.f;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     auto issue_read = [&](auto slot_c) {
@@ -551,6 +551,49 @@ void attn_fwd_kernel(KernelArgs a) {
       }
     };
 
+    // Softmax pieces (two scores each) run as three stages in consecutive slots,
+    // so that no slot holds a chain of dependent VALU operations (each would wait
+    // for the previous one's result): A = the exponents' arguments (fma), B = the
+    // exponentials (and the window mask), C = the bf16 pack. Piece q starts
+    // in slot GS + q * VSLOTS / NPAIR, after its block's S^T group; stages falling
+    // past the last slot run after it. An empty asm pins each stage to its slot:
+    // without a use there, IR passes sink the arithmetic below every MFMA.
+    float xa[NPAIR][2];  // stage A results
+    float pb[NPAIR][2];  // stage B results
+    auto pieces_at = [&](auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      static_for<NPAIR>([&](auto q_c) {
+        constexpr int q = decltype(q_c)::value;
+        constexpr int a = GS + (q * VSLOTS) / NPAIR;
+        constexpr int b2 = q / 8, pp = q % 8;
+        if constexpr (a == slot) {
+          float x0 = __builtin_fmaf(s[b2][2 * pp], c, -m_run);
+          float x1 = __builtin_fmaf(s[b2][2 * pp + 1], c, -m_run);
+          asm volatile("" : "+v"(x0), "+v"(x1));
+          xa[q][0] = x0;
+          xa[q][1] = x1;
+        }
+        if constexpr (a + 1 == slot) {
+          float p0 = __builtin_amdgcn_exp2f(xa[q][0]);
+          float p1 = __builtin_amdgcn_exp2f(xa[q][1]);
+          if constexpr (BITS) {
+            // signed one-bit extract: all ones where the key is in the window, else 0
+            p0 = __uint_as_float(__float_as_uint(p0) & (uint32_t)__builtin_amdgcn_sbfe((int)bm[b2], 2 * pp, 1));
+            p1 = __uint_as_float(__float_as_uint(p1) & (uint32_t)__builtin_amdgcn_sbfe((int)bm[b2], 2 * pp + 1, 1));
+          }
+          asm volatile("" : "+v"(p0), "+v"(p1));
+          pb[q][0] = p0;
+          pb[q][1] = p1;
+        }
+        if constexpr (a + 2 == slot) {
+          const bf16x2_t pp2 = {(__bf16)pb[q][0], (__bf16)pb[q][1]};
+          uint32_t pk = __builtin_bit_cast(uint32_t, pp2);
+          asm volatile("" : "+v"(pk));
+          pw[b2][pp / 4][pp % 4] = pk;
+        }
+      });
+    };
+
     static_for<PF>([&](auto slot_c) { issue_read(slot_c); });
     static_for<TOT>([&](auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
@@ -569,37 +612,30 @@ void attn_fwd_kernel(KernelArgs a) {
         if constexpr (li < C::LOADS) ld.load_part(k_rsrc, tk, k_dst, li);
         else ld.load_part(v_rsrc, tv, v_dst, li - C::LOADS);
       }
-      // softmax pieces assigned to this slot
-      static_for<NPAIR>([&](auto q_c) {
-        constexpr int q = decltype(q_c)::value;
-        if constexpr (slot >= GS && GS + (q * VSLOTS) / NPAIR == slot) {
-          constexpr int b2 = q / 8, pp = q % 8;
-          const float s0 = s[b2][2 * pp], s1 = s[b2][2 * pp + 1];
-          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
-          if constexpr (BITS) {
-            // signed one-bit extract: all ones where the key is in the window, else 0
-            p0 = __uint_as_float(__float_as_uint(p0) & (uint32_t)__builtin_amdgcn_sbfe((int)bm[b2], 2 * pp, 1));
-            p1 = __uint_as_float(__float_as_uint(p1) & (uint32_t)__builtin_amdgcn_sbfe((int)bm[b2], 2 * pp + 1, 1));
-          }
-          const bf16x2_t pp2 = {(__bf16)p0, (__bf16)p1};
-          float& acc = (pp & 1) ? psum1 : psum0;
-          acc = __builtin_amdgcn_fdot2_f32_bf16(pp2, ones, acc, false);
-          // pin this piece to its slot: without a use here, IR passes sink the
-          // arithmetic to the end of the step, below every MFMA
-          uint32_t pk = __builtin_bit_cast(uint32_t, pp2);
-          asm volatile("" : "+v"(pk), "+v"(acc));
-          pw[b2][pp / 4][pp % 4] = pk;
-        }
-      });
+      pieces_at(slot_c);  // softmax stages assigned to this slot
       __builtin_amdgcn_sched_barrier(0);
     });
+    pieces_at(std::integral_constant<int, TOT>{});
+    __builtin_amdgcn_sched_barrier(0);
+    pieces_at(std::integral_constant<int, TOT + 1>{});
+    // Row sum of the rounded probabilities. v_dot2c_f32_bf16 does not run beside a
+    // matrix instruction: the first one after an MFMA waits for the matrix core to
+    // drain (about half an MFMA), later ones issue at the normal rate. One batch per
+    // step, after the last MFMA, pays that wait once instead of once per slot.
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    static_for<NPAIR>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      constexpr int b2 = q / 8, pp = q % 8;
+      ps[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[b2][pp / 4][pp % 4]), ones,
+                                                 ps[q & 3], false);
+    });
+    const float psum = (ps[0] + ps[2]) + (ps[1] + ps[3]);
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
         pn[sb][kb2] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[sb][kb2][0], pw[sb][kb2][1], pw[sb][kb2][2], pw[sb][kb2][3]});
-    finish_step(psum0 + psum1, s, false, pn, bm, bits_tag);
+    finish_step(psum, s, false, pn, bm, bits_tag);
   };
 
   // Step for a key tile of a neighbourhood grid that has no bit-mask form
