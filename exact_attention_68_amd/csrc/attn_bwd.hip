@@ -179,6 +179,12 @@ __device__ __forceinline__ void store_rows_scaled(uint16_t* out, int32_t row, in
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Whether a tile's 32-row blocks run as a two-stage pipeline (next block's S and
+// dP products before this block's softmax arithmetic): only where the extra two
+// accumulators fit the registers without spilling.
+template <int D>
+constexpr bool kPipelineBlocks = D == 32;
+
 // Neighbourhood windows: grid coordinates of the tokens of a tile, decoded from
 // the tile's first token (one division per tile) plus an offset below 128.
 struct TileOrigin {
@@ -315,10 +321,30 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     // into a branch around each exponential.
     auto tile_body = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
+      // At d = 32 a two-stage pipeline over the 32-key blocks: the next block's S
+      // and dP products are issued before this block's exponentials, so the matrix
+      // core has independent work while the VALU runs. At d = 64 and 128 the extra
+      // accumulators do not fit the register budget (they spill), so blocks run in order.
+      constexpr bool PIPE = kPipelineBlocks<D>;
+      f32x16_t s_nx{}, dp_nx{};
+      if constexpr (PIPE) {
+        s_nx = block_product<D>(k_lds[buf], 0, col, half, swz, qf);
+        dp_nx = block_product<D>(v_lds[buf], 0, col, half, swz, gf);
+      }
 #pragma unroll
       for (int sb = 0; sb < C::SB; ++sb) {
-        const f32x16_t s = block_product<D>(k_lds[buf], sb, col, half, swz, qf);
-        const f32x16_t dp = block_product<D>(v_lds[buf], sb, col, half, swz, gf);
+        f32x16_t s, dp;
+        if constexpr (PIPE) {
+          s = s_nx;
+          dp = dp_nx;
+          if (sb + 1 < C::SB) {
+            s_nx = block_product<D>(k_lds[buf], sb + 1, col, half, swz, qf);
+            dp_nx = block_product<D>(v_lds[buf], sb + 1, col, half, swz, gf);
+          }
+        } else {
+          s = block_product<D>(k_lds[buf], sb, col, half, swz, qf);
+          dp = block_product<D>(v_lds[buf], sb, col, half, swz, gf);
+        }
         f32x16_t ds;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -458,10 +484,27 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
     // before a key and every window tile take the masked body, chosen per tile.
     auto tile_body = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
+      // Two-stage pipeline over the 32-query blocks at d = 32, as in the dQ kernel.
+      constexpr bool PIPE = kPipelineBlocks<D>;
+      f32x16_t s_nx{}, dp_nx{};
+      if constexpr (PIPE) {
+        s_nx = block_product<D>(q_lds[buf], 0, col, half, swz, kf);
+        dp_nx = block_product<D>(g_lds[buf], 0, col, half, swz, vf);
+      }
 #pragma unroll
       for (int sb = 0; sb < C::SB; ++sb) {
-        const f32x16_t s = block_product<D>(q_lds[buf], sb, col, half, swz, kf);
-        const f32x16_t dp = block_product<D>(g_lds[buf], sb, col, half, swz, vf);
+        f32x16_t s, dp;
+        if constexpr (PIPE) {
+          s = s_nx;
+          dp = dp_nx;
+          if (sb + 1 < C::SB) {
+            s_nx = block_product<D>(q_lds[buf], sb + 1, col, half, swz, kf);
+            dp_nx = block_product<D>(g_lds[buf], sb + 1, col, half, swz, vf);
+          }
+        } else {
+          s = block_product<D>(q_lds[buf], sb, col, half, swz, kf);
+          dp = block_product<D>(g_lds[buf], sb, col, half, swz, vf);
+        }
         f32x16_t p, ds;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
