@@ -241,7 +241,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     # what the event-timed step contains: the attention kernel, plus the merge kernel of a split launch
     split = ws is not None and not args.backward
-    roof["kernels"] = (f"attn_bwd_prep_kernel<{w.d}> + attn_bwd_dq_kernel<{w.d},{w.mask}> + attn_bwd_dkv_kernel<{w.d},{w.mask}>"
+    roof["kernels"] = (f"attn_bwd_dq_kernel<{w.d},{w.mask}> + attn_bwd_dkv_kernel<{w.d},{w.mask}>"
                        if args.backward else
                        (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
                         else f"attn_fwd_kernel<{w.d},{w.mask}>"))

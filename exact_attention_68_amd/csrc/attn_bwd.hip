@@ -9,10 +9,11 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three kernels on the caller's stream:
-//   attn_bwd_prep_kernel  D per query row into the workspace (fp32);
+// Two kernels on the caller's stream:
 //   attn_bwd_dq_kernel    one work-group per 128-query tile (4 wavefronts x 32
-//                         queries), key/value tiles streamed through LDS:
+//                         queries); first D of its queries (fp32, also left in
+//                         the workspace for the next kernel), then key/value
+//                         tiles streamed through LDS:
 //                         S^T = K Q^T, dP^T = V dO^T (the forward's S^T layout,
 //                         one query per lane column), dS^T, then dQ^T += K^T dS^T
 //                         (the forward's O^T += V^T P^T layout, K read through
@@ -225,25 +226,23 @@ __device__ __forceinline__ bool na_visible(const NaGeom& g, int32_t zq, int32_t 
 
 }  // namespace
 
-// D_i = sum_d dO_id O_id, one thread per query row.
+// This lane's share of D = sum_d dO_d O_d for its row: the fragments hold
+// d = 16kb + 8*half + 0..7 (bf16, widened exactly); the two half-waves hold the
+// two halves of d, combined by the caller.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= (int64_t)a.BH * a.Nq) return;
-  const uint16_t* o = a.o + row * D;
-  const uint16_t* g = a.dout + row * D;
+__device__ __forceinline__ float row_delta_part(const bf16x8_t (&o)[D / 16], const bf16x8_t (&g)[D / 16]) {
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(o + c);
-    const u32x4_t y = *reinterpret_cast<const u32x4_t*>(g + c);
+  for (int kb = 0; kb < D / 16; ++kb) {
+    const u32x4_t x = __builtin_bit_cast(u32x4_t, o[kb]);
+    const u32x4_t y = __builtin_bit_cast(u32x4_t, g[kb]);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       acc += __uint_as_float(x[w] << 16) * __uint_as_float(y[w] << 16);
       acc += __uint_as_float(x[w] & 0xffff0000u) * __uint_as_float(y[w] & 0xffff0000u);
     }
   }
-  a.delta[row] = acc;
+  return acc;
 }
 
 // dQ for one 128-query tile: key/value tiles through a two-buffer LDS ring.
@@ -263,7 +262,15 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   row_fragment<D>(a.q + qhead * D, my_q, Nq, a.q_sign, half, qf);
   row_fragment<D>(a.dout + qhead * D, my_q, Nq, 0u, half, gf);
   const float l2 = my_q < Nq ? a.lse[qhead + my_q] * kLog2e : 0.f;
-  const float dlt = my_q < Nq ? a.delta[qhead + my_q] : 0.f;
+  // D of the lane's query from its O and dO rows; the dK/dV kernel, which runs
+  // after this one on the same stream, reads it from the workspace
+  float dlt;
+  {
+    bf16x8_t of[C::KB];
+    row_fragment<D>(a.o + qhead * D, my_q, Nq, 0u, half, of);
+    dlt = swap_halves_sum(row_delta_part<D>(of, gf));
+    if (my_q < Nq && half == 0) a.delta[qhead + my_q] = dlt;
+  }
 
   int v_row[2], v_off[2][C::DT];
   transpose_offsets<D>(lane, half, v_row, v_off);
@@ -562,12 +569,8 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
 
 template <int D, int MASK>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.BH * a.Nq;
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3(a.BH * a.n_qtiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, MASK>), dim3(a.BH * a.n_ktiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
   return hipGetLastError();
