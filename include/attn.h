@@ -250,8 +250,9 @@ attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, i
  * workspace : device memory of at least attn_bwd_workspace_size bytes
  *           (B*H*Nq float32 row sums), 256-byte aligned, disjoint from the
  *           tensors; any content; calls sharing it must not overlap.
- * The other arguments and the error rules are those of attn_fwd_ex. Three
- * kernels are queued on `stream`; the library allocates nothing.
+ * The other arguments and the error rules are those of attn_fwd_ex. Two
+ * kernels are queued on `stream` (the first also leaves D in the workspace for
+ * the second); the library allocates nothing.
  */
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
