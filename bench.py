@@ -74,14 +74,15 @@ RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 KERNEL_SOURCES = ["attn_fwd.hip", "kernel_common.hpp", "launch.hpp", "tile_plan.hpp"]
+BWD_KERNEL_SOURCES = ["attn_bwd.hip", "kernel_common.hpp", "launch.hpp", "tile_plan.hpp"]
 
 
-def recorded_traffic(name: str):
+def recorded_traffic(name: str, sources=KERNEL_SOURCES):
     """Calibrated HBM bytes of one launch from profiles/traffic.txt, if taken on the current kernel sources."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "exact_attention_68_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     digest = h.hexdigest()[:16]
@@ -248,7 +249,7 @@ def main():
     roof["traffic"] = (sum(args.traffic_kib) * 1024.0 if args.traffic_kib
                        else recorded_traffic(f"{w.name}:{entry}{':lse' if args.lse else ''}"))
     if args.backward:
-        roof["traffic"] = None  # the traffic record covers the forward kernels
+        roof["traffic"] = recorded_traffic(f"{w.name}:attn_bwd", BWD_KERNEL_SOURCES)
 
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
