@@ -62,10 +62,10 @@ class AttnError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_attention_68_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m exact_attention_68_amd.build`")
+    lib = ctypes.CDLL(path)
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp, vp]
     lib.attn_fwd.restype = i32

@@ -2,8 +2,11 @@
 
     python -m exact_attention_68_amd.build
 
-Compiles the C ABI (csrc/attn_api.cpp) and the kernels (csrc/attn_fwd.hip)
-into exact_attention_68_amd/libattn.so. Every call compiles.
+Compiles the C ABI (csrc/attn_api.cpp) and the kernels (csrc/attn_fwd.hip,
+csrc/attn_bwd.hip) into exact_attention_68_amd/libattn.so, and the same sources
+with ATTN_SERIAL_TILES=1 into libattn_serial.so: the race check of the tile
+rings (every tile load awaited before any tile is read), which the race tests
+compare bit for bit against the pipelined library. Every call compiles both.
 """
 from __future__ import annotations
 
@@ -17,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
+LIB_SERIAL = os.path.join(PKG, "libattn_serial.so")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
 HEADERS = ["kernel_common.hpp", "launch.hpp", "tile_plan.hpp", "validate.hpp"]
@@ -40,17 +44,49 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile libattn.so; returns its path. Raises RuntimeError on a failed build."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
-    _check_kernel_stubs(tmp)
-    os.replace(tmp, LIB)
+    """Compile libattn.so and libattn_serial.so; returns the path of libattn.so. Each source is
+    compiled to an object in its own hipcc process (all at once), then each library is linked.
+    Raises RuntimeError on a failed build."""
+    import tempfile
+
+    work = tempfile.mkdtemp(prefix="attn_build_")
+    try:
+        compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+        jobs = {}  # object path -> command
+        for src in SOURCES:
+            variants = [False] if src.endswith(".cpp") else [False, True]  # the C ABI holds no kernels
+            for serial in variants:
+                obj = os.path.join(work, src + (".serial" if serial else "") + ".o")
+                jobs[obj] = [hipcc(), *compile_flags, *(["-DATTN_SERIAL_TILES=1"] if serial else []), "-I", INCLUDE,
+                             "-c", os.path.join(CSRC, src), "-o", obj]
+        _run_all(list(jobs.values()), verbose)
+        links = []
+        for out, serial in ((LIB, False), (LIB_SERIAL, True)):
+            objs = [o for o in jobs if (".serial" in o) == serial or o.endswith(".cpp.o")]
+            links.append([hipcc(), *HIPCC_FLAGS, *objs, "-o", out + ".tmp"])
+        _run_all(links, verbose)
+        for out in (LIB, LIB_SERIAL):
+            _check_kernel_stubs(out + ".tmp")
+            os.replace(out + ".tmp", out)
+    finally:
+        shutil.rmtree(work, ignore_errors=True)
     return LIB
+
+
+def _run_all(cmds: list, verbose: bool) -> None:
+    """Run the commands at once; raise with every failure's stderr."""
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    failed = []
+    for cmd, proc in procs:
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            failed.append(f"hipcc failed ({proc.returncode}): {' '.join(cmd[-3:])}\n{err}")
+    if failed:
+        raise RuntimeError("\n".join(failed))
 
 
 def _check_kernel_stubs(path: str) -> None:
@@ -66,8 +102,8 @@ def _check_kernel_stubs(path: str) -> None:
 
 
 def ensure_built() -> str:
-    """Build only when no library exists yet (tests, smoke check and bench use this)."""
-    if not os.path.exists(LIB):
+    """Build only when a library does not exist yet (tests, smoke check and bench use this)."""
+    if not os.path.exists(LIB) or not os.path.exists(LIB_SERIAL):
         build_library()
     return LIB
 

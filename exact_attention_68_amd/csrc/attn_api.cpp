@@ -219,8 +219,9 @@ const char* attn_status_string(int32_t status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, non-finite scale, "
                                       "unknown mask mode, misplaced params, or an output overlapping an input "
                                       "or the other output)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128, and 32 or 64 for the "
-                                      "backward; sizes must fit 32-bit launch geometry)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size must be 32, 64 or 128; sizes must fit "
+                                      "32-bit launch geometry, and one head's K and V rows (the backward: also "
+                                      "Q and dO rows) at most 2^31 - 1 bytes)";
     case ATTN_ERR_PARAMS: return "inconsistent neighbourhood parameters (grid size must equal Nq and Nkv; "
                                  "kernels odd; wrap 0 or 1; dilation >= 1; (kernel-1)*dilation < size when "
                                  "wrapped, kernel*dilation <= size when clamped)";

@@ -77,7 +77,8 @@ struct RowTileLoader {
   }
 
   __device__ __forceinline__ void load(i32x4_t src, int32_t tile, const uint16_t* lds_tile) const {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile * (C::ROWS * D * 2));
+    // byte offset of the tile in the head, below 2^31 (one head's rows fit a 32-bit record count)
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile * (uint32_t)(C::ROWS * D * 2));
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + wave * 1024);
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) dma_lds16(src, base + j * C::WAVES * 1024, voff[j], soff);
@@ -311,7 +312,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
         for (int sb = 0; sb < C::SB; ++sb) bm[sb] = lane_block_bits(w4[sb], half);
       }
     }
-    if (i + 1 < n) {  // the other buffer was last read before the previous barrier
+    if (!kSerialTiles && i + 1 < n) {  // the other buffer was last read before the previous barrier
       const int32_t tn = kv_tile_at(run, i + 1, a.n_ktiles);
       ld.load(k_rsrc, tn, k_lds[buf ^ 1]);
       ld.load(v_rsrc, tn, v_lds[buf ^ 1]);
@@ -386,6 +387,11 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       tile_body(std::true_type{});
     else
       tile_body(std::false_type{});
+    if (kSerialTiles && i + 1 < n) {  // race check: the next tile's loads only after this tile's compute
+      const int32_t tn = kv_tile_at(run, i + 1, a.n_ktiles);
+      ld.load(k_rsrc, tn, k_lds[buf ^ 1]);
+      ld.load(v_rsrc, tn, v_lds[buf ^ 1]);
+    }
     __syncthreads();  // every wavefront is done with this buffer before it is refilled
   }
   store_rows_scaled<D>(a.dq + qhead * D, my_q, Nq, half, dq, a.scale);
@@ -479,12 +485,15 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
         for (int sb = 0; sb < C::SB; ++sb) bm[sb] = lane_block_bits(w4[sb], half);
       }
     }
-    if (i + 1 < n) {  // next tile into the other buffers (last read before the previous barrier)
-      const int32_t qn = kv_tile_at(qrun, i + 1, a.n_qtiles);
-      ld.load(q_rsrc, qn, q_lds[buf ^ 1]);
-      ld.load(g_rsrc, qn, g_lds[buf ^ 1]);
-      stats(qn, l2n, dln);
-    }
+    auto next_loads = [&]() {
+      if (i + 1 < n) {  // next tile into the other buffers (last read before the previous barrier)
+        const int32_t qn = kv_tile_at(qrun, i + 1, a.n_qtiles);
+        ld.load(q_rsrc, qn, q_lds[buf ^ 1]);
+        ld.load(g_rsrc, qn, g_lds[buf ^ 1]);
+        stats(qn, l2n, dln);
+      }
+    };
+    if constexpr (!kSerialTiles) next_loads();
     // As in the dQ kernel, a hidden score enters the exponent as -inf. Queries past Nq
     // need no test (their logsumexp is stored as +inf, so P = 0), nor do keys past Nkv
     // (their columns of dK and dV are never stored); causal tiles that hold a query
@@ -556,6 +565,7 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
       tile_body(std::true_type{});
     else
       tile_body(std::false_type{});
+    if constexpr (kSerialTiles) next_loads();  // race check: loads only after this tile's compute
     wait_tile_loads<0>();
     if (i + 1 < n && tid < C::ROWS) {
       l2_lds[buf ^ 1][tid] = l2n;

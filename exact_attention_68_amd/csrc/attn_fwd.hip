@@ -92,13 +92,13 @@ struct TileLoader {
 
   // One of the LOADS 16-byte loads of a tile (lets a step spread its loads out).
   __device__ __forceinline__ void load_part(i32x4_t src, int32_t tile, const uint16_t* lds_tile, int j) const {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile * (C::BN * D * 2));
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile * (uint32_t)(C::BN * D * 2));
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + wave * 1024);
     dma_lds16(src, base + j * C::WAVES * 1024, voff[j], soff);
   }
 
   __device__ __forceinline__ void load(i32x4_t src, int32_t tile, const uint16_t* lds_tile) const {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile * (C::BN * D * 2));
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile * (uint32_t)(C::BN * D * 2));
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + wave * 1024);
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) dma_lds16(src, base + j * C::WAVES * 1024, voff[j], soff);
@@ -189,7 +189,8 @@ void attn_fwd_kernel(KernelArgs a) {
 
   // One query tile of head bh against the key tiles of `run`: leaves the
   // unnormalised output (O^T rows of the lane's query), the reference maximum
-  // and the lane's row sum. No LDS DMA is in flight on return.
+  // and the lane's row sum. No LDS DMA is in flight on return (the clamped refills
+  // past the run are awaited at its end).
   auto segment = [&](const int32_t bh, const int32_t qtile, const KvRun run, f32x16_t (&oacc)[DT], float& m_run,
                      float& l_run) {
   const int32_t q0 = qtile * C::BM;
@@ -435,7 +436,7 @@ void attn_fwd_kernel(KernelArgs a) {
       ld.load(k_rsrc, run_tile(i), k_lds[i]);
       ld.load(v_rsrc, run_tile(i - 1), v_lds[i - 1]);
     }
-    wait_tile_loads<C::LOADS_AHEAD + 2 * C::LOADS>();  // K of tile 0
+    wait_tile_loads<kSerialTiles ? 0 : C::LOADS_AHEAD + 2 * C::LOADS>();  // K of tile 0
     __syncthreads();
     f32x16_t s[SB];
     qk_tile(k_lds[0], s);
@@ -450,7 +451,7 @@ void attn_fwd_kernel(KernelArgs a) {
     const float mx = swap_halves_max(lane_max(s));
     m_run = mx == -INFINITY ? -FLT_MAX : mx * c;  // finite sentinel: never inf - inf
     l_run = exp_tile(s, m_run, masked, p);
-    wait_tile_loads<C::LOADS_AHEAD>();  // K of tile 1 and V of tile 0
+    wait_tile_loads<kSerialTiles ? 0 : C::LOADS_AHEAD>();  // K of tile 1 and V of tile 0
     __syncthreads();  // ... published, and every wavefront has read K of tile 0 before its buffer is refilled
   }
 
@@ -479,7 +480,7 @@ void attn_fwd_kernel(KernelArgs a) {
       psum = exp_tile(s, m_run, masked, pn);
     }
     l_run += psum;
-    wait_tile_loads<C::LOADS_AHEAD>();  // K of tile j + 2 and V of tile j + 1
+    wait_tile_loads<kSerialTiles ? 0 : C::LOADS_AHEAD>();  // K of tile j + 2 and V of tile j + 1
     __syncthreads();
   };
 
@@ -607,7 +608,7 @@ void attn_fwd_kernel(KernelArgs a) {
       }
       // next tiles' loads, one every other slot in the first half of the step: issued
       // in one burst they back up the CU's path to LDS and stall the issuing wave
-      if constexpr (slot % 2 == 0 && slot / 2 < 2 * C::LOADS) {
+      if constexpr (!kSerialTiles && slot % 2 == 0 && slot / 2 < 2 * C::LOADS) {
         constexpr int li = slot / 2;
         if constexpr (li < C::LOADS) ld.load_part(k_rsrc, tk, k_dst, li);
         else ld.load_part(v_rsrc, tv, v_dst, li - C::LOADS);
@@ -635,6 +636,10 @@ void attn_fwd_kernel(KernelArgs a) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
         pn[sb][kb2] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[sb][kb2][0], pw[sb][kb2][1], pw[sb][kb2][2], pw[sb][kb2][3]});
+    if constexpr (kSerialTiles) {  // race check: this step's loads only after its compute
+      ld.load(k_rsrc, tk, k_dst);
+      ld.load(v_rsrc, tv, v_dst);
+    }
     finish_step(psum, s, false, pn, bm, bits_tag);
   };
 
@@ -642,8 +647,11 @@ void attn_fwd_kernel(KernelArgs a) {
   // (every tile needs the element predicate): plain order.
   auto step_masked = [&](int32_t j) {
     const int32_t t1 = kv_tile_at(run, j + 1, n_kv);
-    ld.load(k_rsrc, run_tile(j + S), k_lds[j & (S - 1)]);
-    ld.load(v_rsrc, run_tile(j + S - 1), v_lds[(j + S - 1) & (S - 1)]);
+    auto loads = [&]() {
+      ld.load(k_rsrc, run_tile(j + S), k_lds[j & (S - 1)]);
+      ld.load(v_rsrc, run_tile(j + S - 1), v_lds[(j + S - 1) & (S - 1)]);
+    };
+    if constexpr (!kSerialTiles) loads();
     f32x16_t s[SB];
     qk_tile(k_lds[(j + 1) & (S - 1)], s);
     pv_tile(v_lds[j & (S - 1)], p, oacc);
@@ -651,6 +659,7 @@ void attn_fwd_kernel(KernelArgs a) {
     bf16x8_t pn[SB][2];
     const float psum = exp_tile(s, m_run, true, pn);
     const uint32_t no_bits[SB] = {};
+    if constexpr (kSerialTiles) loads();  // race check: loads only after the step's compute
     finish_step(psum, s, true, pn, no_bits, std::false_type{});
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
@@ -693,6 +702,9 @@ void attn_fwd_kernel(KernelArgs a) {
 
   // ---- last tile's product with V
   pv_tile(v_lds[(n - 1) & (S - 1)], p, oacc);
+  // refills issued past the end of the run (up to STAGES - 2 steps' worth at d = 32)
+  // must land before the work-group's LDS is released
+  wait_tile_loads<0>();
   };
 
   // Delayed division and store of query tile qtile of head bh: lane holds d = 32dt + 8(r/4) + 4*half + r%4.

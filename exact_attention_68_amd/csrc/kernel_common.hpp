@@ -113,6 +113,17 @@ __device__ __forceinline__ void dma_lds16(i32x4_t rsrc, uint32_t lds, uint32_t v
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) { return (uint32_t)(uintptr_t)(lptr_t)p; }
 
+// Race check of the hand-managed tile rings. Built with ATTN_SERIAL_TILES=1, every
+// kernel issues each tile load only after the computation of its step and waits
+// for all of this wavefront's loads (vmcnt(0)) before the barrier that publishes
+// them: no load is in flight while any tile is read. The arithmetic is unchanged,
+// so that build must agree bit for bit with the pipelined one; a wait count or
+// barrier that let a step read a tile before it landed would show as a mismatch.
+#ifndef ATTN_SERIAL_TILES
+#define ATTN_SERIAL_TILES 0
+#endif
+constexpr bool kSerialTiles = ATTN_SERIAL_TILES != 0;
+
 // Wait until at most N of this wavefront's tile loads are still in flight (loads
 // complete in issue order). Every step issues the same number of loads, so a
 // fixed count names exactly the tiles the next step reads.

@@ -66,7 +66,8 @@ struct BwdArgs {
   int32_t na_grid;   // 1: per-axis window masks (na_grid_eligible), else the element test
 };
 
-// Launches the three backward kernels (D per row, dQ, dK and dV) on `stream`.
+// Launches the two backward kernels on `stream`: dQ (which also forms D = rowsum(dO * O)
+// in the workspace), then dK and dV.
 hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream);
 
 // Launches the kernel for head size d (32, 64 or 128) and kernel mask `mask`

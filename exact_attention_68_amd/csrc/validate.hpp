@@ -141,10 +141,14 @@ inline attn_status_t check_workspace(const void* ws, uint64_t ws_bytes, int64_t 
 }
 
 // Backward: the backward kernels take every problem the forward takes (d = 32, 64
-// or 128, every mask, Nq != Nkv).
+// or 128, every mask, Nq != Nkv). The dK/dV kernel also streams one head's Q and
+// dO rows through a 32-bit buffer record count, so Nq * d * 2 bytes must fit too.
 inline attn_status_t check_bwd_problem(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
                                        int32_t mask_mode, const void* params) {
-  return check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
+  const attn_status_t st = check_problem(B, H, Nq, Nkv, d, scale, mask_mode, params);
+  if (st != ATTN_OK) return st;
+  if (Nq * d * 2 > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
 }
 
 // Backward pointers: every tensor present and aligned (lse 4 bytes, the rest 16),

@@ -313,6 +313,11 @@ static void check_validation() {
   EXPECT(check_problem(2, 5, 0, 4096, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "Nq=0");
   EXPECT(check_problem(2, 5, 4096, 0, 64, 0.125f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "Nkv=0");
   EXPECT(check_problem(2, 5, 64, 64, 96, 0.125f, 0, nullptr) == ATTN_ERR_UNSUPPORTED, "d=96");
+  // one head's Q and dO rows pass a 32-bit buffer record count in the backward only
+  EXPECT(check_problem(1, 1, 33554432, 64, 64, 0.125f, 0, nullptr) == ATTN_OK, "forward: Nq * d * 2 = 2^32");
+  EXPECT(check_bwd_problem(1, 1, 33554432, 64, 64, 0.125f, 0, nullptr) == ATTN_ERR_UNSUPPORTED,
+         "backward: Nq * d * 2 = 2^32");
+  EXPECT(check_bwd_problem(1, 1, 16777215, 64, 64, 0.125f, 0, nullptr) == ATTN_OK, "backward: Nq * d * 2 < 2^31");
   EXPECT(check_problem(2, 5, 64, 64, 64, 1.0f / 0.0f, 0, nullptr) == ATTN_ERR_INVALID_ARG, "inf scale");
   EXPECT(check_problem(2, 5, 64, 64, 64, 0.1f, 4, nullptr) == ATTN_ERR_INVALID_ARG, "mode 4");
   EXPECT(check_problem(2, 5, 64, 64, 64, 0.1f, ATTN_MASK_CAUSAL, &p) == ATTN_ERR_INVALID_ARG, "params with causal");
