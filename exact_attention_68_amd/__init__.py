@@ -29,6 +29,7 @@ ATTN_ERR_PARAMS = 3
 ATTN_ERR_ALIGNMENT = 4
 ATTN_ERR_HIP = 5
 ATTN_ERR_WORKSPACE = 6
+ATTN_ERR_SCRATCH = 7
 
 
 class attn_na2d_params_t(ctypes.Structure):
@@ -81,6 +82,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_ex_workspace_size.restype = i32
     lib.attn_fwd_ex_check.argtypes = [i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_ex_check.restype = i32
+    lib.attn_fwd_ex_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, vp, vp]
+    lib.attn_fwd_ex_static.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, vp, vp,
                              ctypes.c_uint64, vp]
     lib.attn_bwd.restype = i32
@@ -223,6 +226,25 @@ def attn_fwd_ex(q, k, v, o, lse=None, scale=1.0, mask_mode=ATTN_MASK_NONE, param
                            _stream_handle(stream, q.device))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_fwd_ex")
+
+
+def attn_fwd_ex_static(q, k, v, o, lse=None, scale=1.0, mask_mode=ATTN_MASK_NONE, params=None, stream=None) -> None:
+    """attn_fwd_ex with the library's static device scratch as its workspace: allocates nothing.
+    Calls that overlap on one device race for the scratch. See include/attn.h."""
+    import torch
+
+    B, H, Nq, Nkv, d = _check_tensors(q, k, v, o, same_n=False)
+    lse_ptr = None
+    if lse is not None:
+        if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda:
+            raise TypeError("lse must be a float32 CUDA tensor")
+        if not lse.is_contiguous() or tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be a contiguous [B, H, Nq] tensor")
+        lse_ptr = lse.data_ptr()
+    rc = lib().attn_fwd_ex_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr, B, H, Nq, Nkv, d,
+                                  float(scale), int(mask_mode), _params_ptr(params), _stream_handle(stream, q.device))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_ex_static")
 
 
 def attn_bwd_workspace_size(B, H, Nq, Nkv, d, mask_mode=ATTN_MASK_NONE, params=None) -> int:

@@ -10,6 +10,8 @@
 #include "tile_plan.hpp"
 #include "validate.hpp"
 
+static_assert(ATTN_STATIC_SCRATCH_BYTES == attn::kStaticScratchBytes, "header and library agree on the scratch size");
+
 namespace {
 
 // CU count of the current device, cached per device.
@@ -163,6 +165,25 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   return run_with_workspace(p, workspace, workspace_bytes, stream);
 }
 
+attn_status_t attn_fwd_ex_static(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                 int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale, int32_t mask_mode,
+                                 const void* params, void* stream) {
+  const attn::Problem p{q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask_mode, params};
+  attn_status_t st = attn::check_problem(p);
+  if (st != ATTN_OK) return st;
+  st = attn::check_pointers(p);
+  if (st != ATTN_OK) return st;
+  int32_t cus = 0;
+  st = device_cus(&cus);
+  if (st != ATTN_OK) return st;
+  const attn::SplitPlan plan = plan_for(p.B, p.H, p.Nq, p.Nkv, p.d, p.mask, cus);
+  const int64_t need = attn::split_workspace_bytes(plan, p.d);
+  if (need > attn::kStaticScratchBytes) return ATTN_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (need > 0 && attn::static_scratch(&scratch) != hipSuccess) return ATTN_ERR_HIP;
+  return run_fwd(p, &plan, scratch, stream);
+}
+
 attn_status_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int32_t mask_mode,
                                       const void* params, uint64_t* bytes) {
   if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
@@ -228,6 +249,8 @@ const char* attn_status_string(int32_t status) {
     case ATTN_ERR_ALIGNMENT: return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_HIP: return "HIP runtime error (no device, or a failed query or launch)";
     case ATTN_ERR_WORKSPACE: return "workspace missing, too small, not 256-byte aligned, or overlapping a tensor";
+    case ATTN_ERR_SCRATCH: return "attn_fwd_ex_static: the problem's split needs more than the library's static "
+                                  "device scratch (ATTN_STATIC_SCRATCH_BYTES); use attn_fwd_ex with a workspace";
     default: return "unknown status";
   }
 }

@@ -38,6 +38,7 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -862,6 +863,31 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
     case MASK_NA_GRID: return launch_one<D, MASK_NA_GRID, false>(a, n_wg, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The split workspace of attn_fwd_ex_static: one array per device, kept until the
+// process ends and shared by every call on that device (calls that overlap on one
+// device race for it). It needs no initial content.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void* addr[kDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // host code sees `scratch` only as a stand-in: the device address comes from the runtime
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream) {

@@ -38,6 +38,14 @@ constexpr int64_t split_workspace_bytes(const SplitPlan& p, int64_t d) {
   return p.rem > 0 ? (int64_t)p.slots() * part_slot_bytes(d) : 0;
 }
 
+// Bytes of the device scratch of attn_fwd_ex_static: the split workspace of the largest
+// plan on a device of up to 256 CUs (at most one part slot per CU, d = 128 slots).
+constexpr int64_t kStaticScratchBytes = 256 * part_slot_bytes(128);
+
+// Device address of this device's static scratch (file-scope __device__ array,
+// looked up once per device with hipGetSymbolAddress and cached).
+hipError_t static_scratch(void** ptr);
+
 // Keys per key/value tile of the kernel for head size d: 128 for d = 32 and 64,
 // 64 for d = 128 (the same 16 KB of LDS per K or V tile).
 constexpr int32_t tile_keys(int64_t d) { return d == 128 ? 64 : 128; }

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Mask modes. */
 typedef enum {
@@ -99,9 +99,11 @@ typedef enum {
     ATTN_ERR_ALIGNMENT = 4,   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error (no device, a failed
                                  device query, or a failed launch) */
-    ATTN_ERR_WORKSPACE = 6    /* attn_fwd_ws: workspace NULL, smaller than
+    ATTN_ERR_WORKSPACE = 6,   /* attn_fwd_ws: workspace NULL, smaller than
                                  attn_fwd_workspace_size, not 256-byte aligned, or
                                  overlapping q, k, v or o */
+    ATTN_ERR_SCRATCH = 7      /* attn_fwd_ex_static: the problem's split needs more than
+                                 ATTN_STATIC_SCRATCH_BYTES */
 } attn_status_t;
 
 /*
@@ -227,6 +229,25 @@ attn_status_t attn_fwd_ex_workspace_size(int64_t B, int64_t H, int64_t Nq, int64
 /* attn_fwd_check for attn_fwd_ex's problem (Nq queries, Nkv keys). */
 attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
                                 int32_t mask_mode, const void* params);
+
+/*
+ * attn_fwd_ex_static: attn_fwd_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid it).
+ * The same computation, kernels and results as attn_fwd_ex, but the split
+ * workspace is a static device array inside the library (one per device, of
+ * ATTN_STATIC_SCRATCH_BYTES, held until the process ends) instead of a caller
+ * buffer; no call allocates or frees memory. The array needs no initial content
+ * and keeps the last call's parts. Every call on a device shares that device's
+ * array: calls that overlap on one device (concurrent streams, or host threads
+ * with the same device current) race and give undefined outputs; order them on
+ * one stream. Problems whose split needs more than the array (none on devices of
+ * up to 256 CUs) fail with ATTN_ERR_SCRATCH before any device work; other errors
+ * are those of attn_fwd_ex.
+ */
+#define ATTN_STATIC_SCRATCH_BYTES 17301504  /* 256 part slots of the d = 128 kernel */
+attn_status_t attn_fwd_ex_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
+                                 int32_t mask_mode, const void* params, void* stream);
 
 /*
  * attn_bwd: the backward pass of attn_fwd_ex. For the output gradient dO it

@@ -30,7 +30,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol(A):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_fwd_check",
-                          "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check",
+                          "attn_fwd_ex", "attn_fwd_ex_workspace_size", "attn_fwd_ex_check", "attn_fwd_ex_static",
                           "attn_bwd", "attn_bwd_workspace_size",
                           "attn_status_string", "attn_abi_version"}
     lib = A.lib()
@@ -45,11 +45,11 @@ def test_abi_version_matches_header(A):
 
 def test_status_strings(A):
     seen = set()
-    for code in range(7):
+    for code in range(8):
         s = A.attn_status_string(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert A.attn_status_string(99) == "unknown status"
     assert A.attn_status_string(-1) == "unknown status"
 
