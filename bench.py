@@ -12,6 +12,13 @@ from the forward's output and logsumexp, computed once before timing). Inputs
 and the workspace are resident in HBM before timing starts. Prints one JSON
 line on stdout.
 
+Before timing, the run measures its own workload under rocprofv3 in child
+processes (this script with --child, placed after `--`): a kernel trace (the
+per-dispatch durations; their median per step is reported beside the HIP-event
+time), a counter pass for the matrix cores (mfma_util) and FETCH_SIZE and
+WRITE_SIZE passes scaled by a plain 256 MiB device copy (roofline.traffic and
+hbm_gbs). --no-prof skips them; a pass that fails leaves its fields null.
+
 FLOP accounting (the metric of the workload): 4 Nq Nkv d per head without a
 mask, half of 4 N^2 d with the causal mask, 4 N (window cells) d per head for
 neighbourhood attention (the window-sized work); the backward counts its five
@@ -72,31 +79,6 @@ def algorithmic_bytes(w: workloads.Workload, lse: bool = False) -> float:
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
-KERNEL_SOURCES = ["attn_fwd.hip", "kernel_common.hpp", "launch.hpp", "tile_plan.hpp"]
-BWD_KERNEL_SOURCES = ["attn_bwd.hip", "kernel_common.hpp", "launch.hpp", "tile_plan.hpp"]
-
-
-def recorded_traffic(name: str, sources=KERNEL_SOURCES):
-    """Calibrated HBM bytes of one launch from profiles/traffic.txt, if taken on the current kernel sources."""
-    import hashlib
-
-    h = hashlib.sha256()
-    for f in sources:
-        with open(os.path.join(ROOT, "exact_attention_68_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    digest = h.hexdigest()[:16]
-    try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
-    except OSError:
-        return None
-    for ln in lines:
-        parts = ln.split()
-        if len(parts) == 4 and not ln.startswith("#") and parts[0] == name and parts[1] == digest:
-            return (float(parts[2]) + float(parts[3])) * 1024.0
-    return None
-
-
 def mask_mode(A, w):
     return {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na2d": A.ATTN_MASK_NA2D,
             "na3d": A.ATTN_MASK_NA3D}[w.mask]
@@ -138,6 +120,155 @@ def cpu_baseline(w: workloads.Workload, q, k, v, budget_s: float = 12.0) -> dict
                       f"float64 NumPy, S materialised per head) in {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
 
 
+# ---------------------------------------------------------------- live profiler passes
+# The default run measures its own workload under rocprofv3 in child processes (the
+# program itself after `--`, never a relaunch of this process), before this process
+# touches the GPU: a kernel trace (per-dispatch durations, median over steps, as the
+# headline's cross-check of the HIP-event time), one counter pass for the matrix
+# cores (SQ_VALU_MFMA_BUSY_CYCLES against GRBM_GUI_ACTIVE) and one each for
+# FETCH_SIZE and WRITE_SIZE, scaled by a plain device copy of known size in the same
+# run. Each field states its source; a pass that fails leaves its fields null.
+PROF_TIMEOUT_S = 180
+XCD_CUS = 32  # CUs per XCD on MI355X (GRBM_GUI_ACTIVE is summed over the XCDs)
+
+
+def _child_cmd(args, steps: int, warmup: int, calibrate: bool = False) -> list:
+    cmd = [sys.executable, os.path.abspath(__file__), "--child", "--no-cpu", "--workload", args.workload,
+           "--steps", str(steps), "--warmup", str(warmup)]
+    if args.entry:
+        cmd += ["--entry", args.entry]
+    if args.lse:
+        cmd.append("--lse")
+    if args.backward:
+        cmd.append("--backward")
+    if calibrate:
+        cmd.append("--copy-calibration")
+    return cmd
+
+
+def _rocprof(prof_args: list, child: list, out_dir: str):
+    """Run rocprofv3 <prof_args> -d out_dir -o run -- child; returns the list of its csv files, or
+    None. rocprofv3 may exit non-zero after a complete run (its own teardown); the files decide."""
+    import glob
+    import signal
+    import subprocess
+
+    cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", out_dir, "-o", "run", "--", *child]
+    env = dict(os.environ, TMPDIR="/tmp")
+    try:
+        proc = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True, cwd="/tmp",
+                                env=env, start_new_session=True)
+        try:
+            _, err = proc.communicate(timeout=PROF_TIMEOUT_S)
+        except subprocess.TimeoutExpired:
+            os.killpg(proc.pid, signal.SIGKILL)
+            proc.communicate()
+            print(f"[bench] rocprofv3 {' '.join(prof_args)}: timed out", file=sys.stderr, flush=True)
+            return None
+    except OSError as e:
+        print(f"[bench] rocprofv3 not runnable: {e}", file=sys.stderr, flush=True)
+        return None
+    files = glob.glob(os.path.join(out_dir, "**", "*.csv"), recursive=True)
+    if not files:
+        print(f"[bench] rocprofv3 {' '.join(prof_args)}: no output (rc {proc.returncode}): {err[-400:]}",
+              file=sys.stderr, flush=True)
+        return None
+    return files
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return None if n == 0 else (xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2]))
+
+
+def _counter_rows(files):
+    """{dispatch id: (kernel name, {counter: value})} from rocprofv3 counter-collection csv files."""
+    import csv
+
+    out = {}
+    for f in files:
+        if not f.endswith("counter_collection.csv"):
+            continue
+        for row in csv.DictReader(open(f)):
+            did = (f, row.get("Dispatch_Id"))
+            name, ctr = out.setdefault(did, (row.get("Kernel_Name", ""), {}))
+            ctr[row["Counter_Name"]] = ctr.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return out
+
+
+def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
+    """The profiler passes of one workload; returns the fields of the bench line."""
+    import csv
+    import shutil
+    import tempfile
+
+    res = {"kernel_trace": None, "mfma_util": None, "traffic_bytes": None}
+    if shutil.which("rocprofv3") is None:
+        return res
+    work = tempfile.mkdtemp(prefix="attn_bench_prof_")
+    try:
+        # kernel trace: 30 timed calls after 5 warm-up calls; the last 30 calls' dispatches
+        files = _rocprof(["--kernel-trace"], _child_cmd(args, 30, 5), os.path.join(work, "trace"))
+        if files:
+            rows = []
+            for f in files:
+                if f.endswith("kernel_trace.csv"):
+                    rows += [r for r in csv.DictReader(open(f)) if "attn_" in r.get("Kernel_Name", "")]
+            rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+            rows = rows[-30 * steps_per_call_kernels:]
+            per_kernel = {}
+            for r in rows:
+                short = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("attn::", "")
+                per_kernel.setdefault(short, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            steps = [sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                         for r in rows[i:i + steps_per_call_kernels])
+                     for i in range(0, len(rows) - steps_per_call_kernels + 1, steps_per_call_kernels)]
+            if steps:
+                res["kernel_trace"] = {
+                    "step_us_median": _median(steps), "steps": len(steps),
+                    "kernels": {k: {"median_us": _median(v), "calls": len(v)} for k, v in per_kernel.items()},
+                    "source": "rocprofv3 --kernel-trace of this run (child process), median over steps"}
+        # matrix-core busy cycles of the dominant kernel, per dispatch
+        files = _rocprof(["--pmc", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+                         _child_cmd(args, 5, 2), os.path.join(work, "mfma"))
+        if files:
+            utils = []
+            for name, ctr in _counter_rows(files).values():
+                if "attn_fwd_kernel" in name or "attn_bwd_dkv" in name:
+                    xcds = max(1, cus // XCD_CUS)
+                    cycles = ctr.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+                    if cycles > 0:
+                        utils.append(ctr.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * cus) / cycles)
+            if utils:
+                res["mfma_util"] = _median(utils)
+        # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) in separate passes, each scaled by
+        # what the counter reads for a plain device copy of 256 MiB in the same run
+        traffic = 0.0
+        for ctr_name in ("FETCH_SIZE", "WRITE_SIZE"):
+            files = _rocprof(["--pmc", ctr_name], _child_cmd(args, 5, 2, calibrate=True),
+                             os.path.join(work, ctr_name))
+            if not files:
+                traffic = None
+                break
+            att, calib = {}, []
+            for name, ctr in _counter_rows(files).values():
+                if "attn_" in name:
+                    att.setdefault(name.split("(")[0], []).append(ctr.get(ctr_name, 0.0))
+                elif "copy" in name.lower():
+                    calib.append(ctr.get(ctr_name, 0.0))
+            if not att or not calib:
+                traffic = None
+                break
+            factor = (256 << 10) / _median(calib)  # KiB moved per KiB counted
+            traffic += sum(_median(v) for v in att.values()) * 1024.0 * factor
+            res[f"{ctr_name.lower()}_factor"] = factor
+        res["traffic_bytes"] = traffic
+    finally:
+        shutil.rmtree(work, ignore_errors=True)
+    return res
+
+
 def copy_calibration(nbytes: int = 256 << 20, reps: int = 3) -> None:
     """A plain device-to-device copy of known size, for scaling memory-traffic counters."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
@@ -163,6 +294,9 @@ def main():
                     help="also run a plain 256 MiB device copy (reference for traffic counters)")
     ap.add_argument("--traffic-kib", type=float, nargs=2, metavar=("FETCH", "WRITE"), default=None,
                     help="FETCH_SIZE and WRITE_SIZE of one launch in KiB, already scaled by the copy calibration")
+    ap.add_argument("--no-prof", action="store_true",
+                    help="skip the live rocprofv3 passes (kernel trace, MFMA busy, HBM traffic)")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)  # a profiled pass of the parent
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -214,6 +348,15 @@ def main():
         def step():
             A.attn_bwd(dq, dk, dv, do, ddo, lse_f, gq, gk, gv, w.scale, mode, params, wsb, stream.cuda_stream)
 
+    prof = None
+    if not args.child and not args.no_prof:
+        split_call = ws is not None and not args.backward
+        kernels_per_call = 2 if (args.backward or split_call) else 1
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        print(f"[bench] {w.name}: rocprofv3 passes (kernel trace, MFMA busy, FETCH_SIZE, WRITE_SIZE)", file=sys.stderr,
+              flush=True)
+        prof = live_profile(args, kernels_per_call, cus)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -246,10 +389,15 @@ def main():
                        if args.backward else
                        (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
                         else f"attn_fwd_kernel<{w.d},{w.mask}>"))
-    roof["traffic"] = (sum(args.traffic_kib) * 1024.0 if args.traffic_kib
-                       else recorded_traffic(f"{w.name}:{entry}{':lse' if args.lse else ''}"))
-    if args.backward:
-        roof["traffic"] = recorded_traffic(f"{w.name}:attn_bwd", BWD_KERNEL_SOURCES)
+    # HBM bytes of one step, from this run's FETCH_SIZE and WRITE_SIZE passes (or given on the command line)
+    roof["traffic"] = None
+    if prof and prof.get("traffic_bytes"):
+        roof["traffic"] = prof["traffic_bytes"]
+        roof["traffic_source"] = ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE passes of this run, per dispatch, "
+                                  "scaled by a 256 MiB device copy in the same pass")
+    elif args.traffic_kib:
+        roof["traffic"] = sum(args.traffic_kib) * 1024.0
+        roof["traffic_source"] = "--traffic-kib"
 
     line = {
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
@@ -263,6 +411,16 @@ def main():
                    "workspace_bytes": 0 if ws is None else ws.numel()},
         "roofline": roof,
     }
+    # matrix-core utilisation and HBM bandwidth (spec item 4), from the live passes
+    line["mfma_util"] = prof.get("mfma_util") if prof else None
+    line["mfma_util_source"] = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES / (4 x CUs) / (GRBM_GUI_ACTIVE / XCDs) of "
+                                "the attention kernel, median over dispatches" if line["mfma_util"] is not None
+                                else None)
+    line["hbm_gbs"] = roof["traffic"] / (kernel_ms * 1e-3) / 1e9 if roof["traffic"] else None
+    if prof and prof.get("kernel_trace"):
+        kt = prof["kernel_trace"]
+        line["kernel_trace"] = kt
+        line["kernel_trace_tflops"] = F / (kt["step_us_median"] * 1e-6) / 1e12
     if args.copy_calibration:
         copy_calibration()
     if args.backward:
