@@ -10,7 +10,9 @@ attn_fwd_ex, the default for cross-attention, also writes the logsumexp with
 --lse). With --backward a step is one attn_bwd call (gradients of Q, K and V
 from the forward's output and logsumexp, computed once before timing). Inputs
 and the workspace are resident in HBM before timing starts. Prints one JSON
-line on stdout.
+line on stdout. Before the warm-up steps the step is repeated, untimed, for
+--spinup-ms (300 ms by default; reported as "spinup"): timed right after idle,
+a few milliseconds of work run while the GPU's clocks are still ramping up.
 
 Before timing, the run measures its own workload under rocprofv3 in child
 processes (this script with --child, placed after `--`): a kernel trace (the
@@ -132,9 +134,9 @@ PROF_TIMEOUT_S = 180
 XCD_CUS = 32  # CUs per XCD on MI355X (GRBM_GUI_ACTIVE is summed over the XCDs)
 
 
-def _child_cmd(args, steps: int, warmup: int, calibrate: bool = False) -> list:
+def _child_cmd(args, steps: int, warmup: int, calibrate: bool = False, spinup: bool = False) -> list:
     cmd = [sys.executable, os.path.abspath(__file__), "--child", "--no-cpu", "--workload", args.workload,
-           "--steps", str(steps), "--warmup", str(warmup)]
+           "--steps", str(steps), "--warmup", str(warmup), "--spinup-ms", str(args.spinup_ms if spinup else 0)]
     if args.entry:
         cmd += ["--entry", args.entry]
     if args.lse:
@@ -204,17 +206,21 @@ def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
     import tempfile
 
     res = {"kernel_trace": None, "mfma_util": None, "traffic_bytes": None}
+    # the kernels of one step (the backward run also holds the one forward call made before timing)
+    step_kernel = ("attn_bwd_",) if args.backward else ("attn_fwd_kernel", "attn_merge_kernel")
+    main_kernel = "attn_bwd_dkv" if args.backward else "attn_fwd_kernel"
     if shutil.which("rocprofv3") is None:
         return res
     work = tempfile.mkdtemp(prefix="attn_bench_prof_")
     try:
-        # kernel trace: 30 timed calls after 5 warm-up calls; the last 30 calls' dispatches
-        files = _rocprof(["--kernel-trace"], _child_cmd(args, 30, 5), os.path.join(work, "trace"))
+        # kernel trace: 30 timed calls after the clock spin-up and 5 warm-up calls; the last 30 calls' dispatches
+        files = _rocprof(["--kernel-trace"], _child_cmd(args, 30, 5, spinup=True), os.path.join(work, "trace"))
         if files:
             rows = []
             for f in files:
                 if f.endswith("kernel_trace.csv"):
-                    rows += [r for r in csv.DictReader(open(f)) if "attn_" in r.get("Kernel_Name", "")]
+                    rows += [r for r in csv.DictReader(open(f))
+                             if any(k in r.get("Kernel_Name", "") for k in step_kernel)]
             rows.sort(key=lambda r: int(r["Start_Timestamp"]))
             rows = rows[-30 * steps_per_call_kernels:]
             per_kernel = {}
@@ -235,7 +241,7 @@ def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
         if files:
             utils = []
             for name, ctr in _counter_rows(files).values():
-                if "attn_fwd_kernel" in name or "attn_bwd_dkv" in name:
+                if main_kernel in name:
                     xcds = max(1, cus // XCD_CUS)
                     cycles = ctr.get("GRBM_GUI_ACTIVE", 0.0) / xcds
                     if cycles > 0:
@@ -253,7 +259,7 @@ def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
                 break
             att, calib = {}, []
             for name, ctr in _counter_rows(files).values():
-                if "attn_" in name:
+                if any(k in name for k in step_kernel):
                     att.setdefault(name.split("(")[0], []).append(ctr.get(ctr_name, 0.0))
                 elif "copy" in name.lower():
                     calib.append(ctr.get(ctr_name, 0.0))
@@ -263,6 +269,9 @@ def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
             factor = (256 << 10) / _median(calib)  # KiB moved per KiB counted
             traffic += sum(_median(v) for v in att.values()) * 1024.0 * factor
             res[f"{ctr_name.lower()}_factor"] = factor
+            for name, v in att.items():
+                short = name.replace("void ", "").replace("attn::", "")
+                res.setdefault("traffic_kernels", {}).setdefault(short, {})[ctr_name] = _median(v) * 1024.0 * factor
         res["traffic_bytes"] = traffic
     finally:
         shutil.rmtree(work, ignore_errors=True)
@@ -296,6 +305,9 @@ def main():
                     help="FETCH_SIZE and WRITE_SIZE of one launch in KiB, already scaled by the copy calibration")
     ap.add_argument("--no-prof", action="store_true",
                     help="skip the live rocprofv3 passes (kernel trace, MFMA busy, HBM traffic)")
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="before the warm-up steps, repeat the step for this long so that the GPU's clocks "
+                         "leave their idle state (0: none)")
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)  # a profiled pass of the parent
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -357,6 +369,16 @@ def main():
               flush=True)
         prof = live_profile(args, kernels_per_call, cus)
 
+    # Clock spin-up: the GPU leaves idle at reduced clocks and needs some tens of milliseconds of
+    # load to reach its steady state; a step of 50-200 us timed over a few milliseconds right after
+    # idle measures that ramp, not the kernels. The step is repeated (untimed) for spinup_ms first.
+    spin_calls, t_spin = 0, time.perf_counter()
+    while args.spinup_ms > 0 and (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        for _ in range(16):
+            step()
+        spin_calls += 16
+        torch.cuda.synchronize()
+    spin_ms = (time.perf_counter() - t_spin) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -395,6 +417,7 @@ def main():
         roof["traffic"] = prof["traffic_bytes"]
         roof["traffic_source"] = ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE passes of this run, per dispatch, "
                                   "scaled by a 256 MiB device copy in the same pass")
+        roof["traffic_kernels"] = prof.get("traffic_kernels")
     elif args.traffic_kib:
         roof["traffic"] = sum(args.traffic_kib) * 1024.0
         roof["traffic_source"] = "--traffic-kib"
@@ -403,6 +426,7 @@ def main():
         "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak, SD2.1 B2 H5 N4096 d64",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "spinup": {"ms": spin_ms, "calls": spin_calls},
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "kernel_us": kernel_ms * 1e3,

@@ -64,6 +64,11 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   a.BH = (int32_t)(p.B * p.H);
   a.n_qtiles = (int32_t)attn::cdiv(p.Nq, attn::kBlockM);
   a.n_kvtiles = (int32_t)attn::cdiv(p.Nkv, attn::tile_keys(p.d));
+  // causal forward: every head in one superblock, longest first over the whole grid. Head
+  // groups sized to the XCDs' slots (the backward's order) measured 7 % slower on the causal
+  // B4 H16 N2048 d64 problem: fewer L2 misses, but the long and short items no longer pair
+  // up as evenly on the CUs.
+  a.causal_group = (int32_t)attn::cdiv(a.BH, 8);
   // exp(x) = 2^(x log2 e): the kernel works in base 2 with the scale folded in
   a.c = (float)(fabs((double)p.scale) * 1.4426950408889634);
   a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
@@ -222,6 +227,11 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   a.scale = scale;
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
   if ((int64_t)a.BH * a.n_ktiles > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  int32_t cus = 0;
+  st = device_cus(&cus);
+  if (st != ATTN_OK) return st;
+  a.group_q = attn::causal_group(a.n_qtiles, cus, attn::bwd_wgs_per_cu(d));
+  a.group_k = attn::causal_group(a.n_ktiles, cus, attn::bwd_wgs_per_cu(d));
   int32_t mask = mask_mode == ATTN_MASK_CAUSAL ? attn::MASK_CAUSAL : attn::MASK_NONE;
   if (attn::is_na_mode(mask_mode)) {
     a.na = attn::na_geom(mask_mode, params);

@@ -255,7 +255,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][C::TILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
   const int32_t Nq = a.Nq, Nkv = a.Nkv;
-  const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH);
+  const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH, a.group_q);
   const int32_t q0 = w.qtile * C::ROWS, my_q = q0 + wave * 32 + col;
   const size_t qhead = (size_t)w.bh * Nq, khead = (size_t)w.bh * Nkv;
 
@@ -409,12 +409,19 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float dl_lds[2][C::ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
   const int32_t Nq = a.Nq, Nkv = a.Nkv;
-  // causal: key tile 0 sees every query tile, the last one the fewest, so all heads' key tile 0
-  // go first (longest first, as the forward's causal order); otherwise the key tiles of a head
-  // are kept on one XCD (xcd_contiguous), whose L2 then serves its Q and dO tiles
-  const int32_t wg = MASK == MASK_CAUSAL ? (int32_t)blockIdx.x : xcd_contiguous(blockIdx.x, gridDim.x);
-  const int32_t bh = MASK == MASK_CAUSAL ? wg % a.BH : wg / a.n_ktiles;
-  const int32_t ktile = MASK == MASK_CAUSAL ? wg / a.BH : wg - bh * a.n_ktiles;
+  // causal: key tile 0 sees every query tile, the last one the fewest, so they go longest
+  // first in head groups (causal_item, as the forward's causal order); otherwise the key tiles
+  // of a head are kept on one XCD (xcd_contiguous), whose L2 then serves its Q and dO tiles
+  int32_t bh, ktile;
+  if constexpr (MASK == MASK_CAUSAL) {
+    const RankedItem r = causal_item(blockIdx.x, a.n_ktiles, a.BH, a.group_k);
+    bh = r.bh;
+    ktile = r.rank;
+  } else {
+    const int32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    bh = wg / a.n_ktiles;
+    ktile = wg - bh * a.n_ktiles;
+  }
   const int32_t k0 = ktile * C::ROWS, my_k = k0 + wave * 32 + col;
   const size_t qhead = (size_t)bh * Nq, khead = (size_t)bh * Nkv;
 
@@ -494,6 +501,7 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
       }
     };
     if constexpr (!kSerialTiles) next_loads();
+    const int32_t kd = my_k - qt * C::ROWS;  // causal: the lane's key sees the tile's queries from kd on
     // As in the dQ kernel, a hidden score enters the exponent as -inf. Queries past Nq
     // need no test (their logsumexp is stored as +inf, so P = 0), nor do keys past Nkv
     // (their columns of dK and dV are never stored); causal tiles that hold a query
@@ -533,9 +541,8 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
             const int r = 4 * g4 + j;
             float add = -lv[j];
             if constexpr (MASKED) {
-              const int32_t qi = qt * C::ROWS + qr + j;
               bool ok = true;
-              if (MASK == MASK_CAUSAL) ok = my_k <= qi;
+              if (MASK == MASK_CAUSAL) ok = kd <= qr + j;
               if constexpr (MASK == MASK_NA) {
                 if (a.na_grid) {
                   ok = ((bm[sb] >> r) & 1u) != 0u;
@@ -559,8 +566,7 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
         block_transpose_product<D>(q_lds[buf], sb, v_row, v_off, dsb, dk);
       }
     };
-    bool masked = MASK == MASK_NA;
-    if (MASK == MASK_CAUSAL) masked = qt * C::ROWS < k0 + C::ROWS - 1;
+    bool masked = MASK != MASK_NONE;
     if (masked)
       tile_body(std::true_type{});
     else
@@ -576,6 +582,10 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   store_rows_scaled<D>(a.dk + khead * D, my_k, Nkv, half, dk, a.scale);
   store_rows_scaled<D>(a.dv + khead * D, my_k, Nkv, half, dv, 1.0f);
 }
+
+static_assert(BwdCfg<32>::WAVES_PER_EU == bwd_wgs_per_cu(32) && BwdCfg<64>::WAVES_PER_EU == bwd_wgs_per_cu(64) &&
+                  BwdCfg<128>::WAVES_PER_EU == bwd_wgs_per_cu(128),
+              "one wavefront per SIMD per work-group: waves per SIMD = work-groups per CU");
 
 template <int D, int MASK>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {

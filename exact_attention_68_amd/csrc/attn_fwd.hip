@@ -736,7 +736,7 @@ void attn_fwd_kernel(KernelArgs a) {
   f32x16_t oacc[DT];
   float m_run, l_run;
   if constexpr (!SPLIT) {
-    const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH);
+    const WorkItem w = work_item(MASK, blockIdx.x, gridDim.x, a.n_qtiles, a.BH, a.causal_group);
     segment(w.bh, w.qtile, kv_run(MASK, Nq, Nkv, C::BM, C::BN, w.qtile * C::BM, a.na), oacc, m_run, l_run);
     store_rows(w.bh, w.qtile, oacc, m_run, l_run);
   } else {

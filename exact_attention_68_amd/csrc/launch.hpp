@@ -30,6 +30,7 @@ struct KernelArgs {
   float* ws_parts;      // rem * parts slots of part_slot_bytes(d)
   int32_t split_full;   // whole-tile work-groups
   int32_t split_parts;  // parts per split tile
+  int32_t causal_group; // causal: heads per XCD dispatched together (causal_item)
 };
 
 // Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
@@ -45,6 +46,10 @@ constexpr int64_t kStaticScratchBytes = 256 * part_slot_bytes(128);
 // Device address of this device's static scratch (file-scope __device__ array,
 // looked up once per device with hipGetSymbolAddress and cached).
 hipError_t static_scratch(void** ptr);
+
+// Work-groups of the backward kernels resident per CU: two at d <= 64 and one at d = 128
+// (their register and LDS budgets). The causal dispatch order sizes its head groups with it.
+constexpr int32_t bwd_wgs_per_cu(int64_t d) { return d == 128 ? 1 : 2; }
 
 // Keys per key/value tile of the kernel for head size d: 128 for d = 32 and 64,
 // 64 for d = 128 (the same 16 KB of LDS per K or V tile).
@@ -72,6 +77,8 @@ struct BwdArgs {
   float na_inv_w;    // 1 / grid_w, rounded to float
   float na_inv_h;    // 1 / grid_h, rounded to float
   int32_t na_grid;   // 1: per-axis window masks (na_grid_eligible), else the element test
+  int32_t group_q;   // causal: heads per XCD dispatched together by the dQ kernel (causal_group)
+  int32_t group_k;   // and by the dK/dV kernel
 };
 
 // Launches the two backward kernels on `stream`: dQ (which also forms D = rowsum(dO * O)

@@ -358,10 +358,7 @@ constexpr uint32_t limit_bits(int32_t lim) {
 // Work-groups are dispatched round-robin over the 8 XCDs of the chip, each
 // with its own L2. For equal-length work items the remap gives each XCD a
 // contiguous block of logical items, so the query tiles of one head (which
-// share its K and V) land on the same L2. Causal items differ in length, so
-// they keep the dispatch order, longest first with all heads of one tile
-// index together; round-robin then spreads long and short items evenly over
-// the XCDs (and keeps a head on one XCD when B*H is a multiple of 8).
+// share its K and V) land on the same L2.
 struct WorkItem {
   int32_t bh, qtile;
 };
@@ -373,8 +370,41 @@ constexpr int32_t xcd_contiguous(int32_t wg, int32_t n) {
   return wg < per_xcd * 8 ? (wg % 8) * per_xcd + wg / 8 : wg;
 }
 
-constexpr WorkItem work_item(int mask, int32_t wg, int32_t n_wg, int32_t n_qtiles, int32_t BH) {
-  if (mask == MASK_CAUSAL) return WorkItem{wg % BH, n_qtiles - 1 - wg / BH};
+// Causal items differ in length: query tile t of the forward (and of the dQ
+// kernel) sees t + 1 key tiles, key tile t of the dK/dV kernel is seen by
+// n - t query tiles. They are dispatched longest first (rank 0 = longest) in
+// superblocks of 8 * group heads; within a superblock the order is rank major,
+// head minor. Round-robin dispatch then keeps head h on XCD h % 8 (in every
+// superblock whose head count is a multiple of 8) and spreads long and short
+// items evenly over the XCDs. `group` heads per XCD are chosen so that their
+// items fill the XCD's resident work-group slots (causal_group): the streamed
+// tiles of only those heads share its L2 at a time, and the next superblock's
+// longest items take the slots that the current one's shortest items free first.
+struct RankedItem {
+  int32_t bh, rank;
+};
+
+constexpr RankedItem causal_item(int32_t wg, int32_t n_tiles, int32_t BH, int32_t group) {
+  const int32_t span = 8 * group;              // heads per superblock
+  const int32_t per_block = span * n_tiles;    // items per superblock
+  const int32_t blk = wg / per_block;
+  const int32_t idx = wg - blk * per_block;
+  const int32_t heads = BH - blk * span < span ? BH - blk * span : span;  // the last may hold fewer
+  return RankedItem{blk * span + idx % heads, idx / heads};
+}
+
+// Heads per XCD whose n_tiles items fill its resident slots (cus / 8 CUs, wgs_per_cu
+// work-groups each); at least 1.
+constexpr int32_t causal_group(int32_t n_tiles, int32_t cus, int32_t wgs_per_cu) {
+  const int32_t slots = cus / 8 * wgs_per_cu;
+  return n_tiles > 0 && slots / n_tiles > 1 ? slots / n_tiles : 1;
+}
+
+constexpr WorkItem work_item(int mask, int32_t wg, int32_t n_wg, int32_t n_qtiles, int32_t BH, int32_t group) {
+  if (mask == MASK_CAUSAL) {
+    const RankedItem r = causal_item(wg, n_qtiles, BH, group);
+    return WorkItem{r.bh, n_qtiles - 1 - r.rank};
+  }
   const int32_t logical = xcd_contiguous(wg, n_wg);
   return WorkItem{logical / n_qtiles, logical % n_qtiles};
 }

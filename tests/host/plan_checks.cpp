@@ -1,5 +1,6 @@
 // Host-only checks of the launch planning and argument validation shared with the kernels.
 // Built with g++ and sanitizers by tests/test_abi.py; prints "OK" and exits 0 when every check holds.
+#include <algorithm>
 #include <cstdio>
 #include <set>
 #include <vector>
@@ -224,13 +225,28 @@ static void check_causal(int Nq, int Nkv, int BM, int BN) {
   }
 }
 
-static void check_work_items(int mask, int BH, int n_qtiles) {
+static void check_work_items(int mask, int BH, int n_qtiles, int group) {
   const int n_wg = BH * n_qtiles;
-  std::vector<int> seen(n_wg, 0);
+  std::vector<int> seen(n_wg, 0), xcd_of_head(BH, -1);
   for (int wg = 0; wg < n_wg; ++wg) {
-    const WorkItem w = work_item(mask, wg, n_wg, n_qtiles, BH);
+    const WorkItem w = work_item(mask, wg, n_wg, n_qtiles, BH, group);
     EXPECT(w.bh >= 0 && w.bh < BH && w.qtile >= 0 && w.qtile < n_qtiles, "work item out of range");
     if (w.bh >= 0 && w.bh < BH && w.qtile >= 0 && w.qtile < n_qtiles) seen[w.bh * n_qtiles + w.qtile]++;
+    if (mask == MASK_CAUSAL) {
+      // superblocks of 8 * group heads: inside one, longest (highest query tile) first; and a
+      // superblock with a multiple of 8 heads keeps each head on one XCD (wg % 8)
+      const int span = 8 * group, blk = wg / (span * n_qtiles);
+      const int heads = std::min(span, BH - blk * span);
+      EXPECT(w.bh / span == blk, "causal item %d leaves its superblock", wg);
+      if (wg > 0 && (wg - 1) / (span * n_qtiles) == blk) {
+        const WorkItem prev = work_item(mask, wg - 1, n_wg, n_qtiles, BH, group);
+        EXPECT(prev.qtile >= w.qtile, "causal items not longest first at %d", wg);
+      }
+      if (heads % 8 == 0 && w.bh >= 0 && w.bh < BH) {
+        if (xcd_of_head[w.bh] < 0) xcd_of_head[w.bh] = wg % 8;
+        EXPECT(xcd_of_head[w.bh] == wg % 8, "head %d spread over XCDs", w.bh);
+      }
+    }
   }
   for (int i = 0; i < n_wg; ++i) EXPECT(seen[i] == 1, "work item %d covered %d times", i, seen[i]);
 }
@@ -462,8 +478,13 @@ int main() {
     check_grid_bits(geom(70, 2, 4, 5, 1, 1, 1, 0, 0, 3, 1, 1), BN);   // 70 planes
   }
   for (int mask : {MASK_NONE, MASK_CAUSAL})
-    for (int BH : {1, 3, 8, 10, 64})
-      for (int nq : {1, 2, 7, 32, 72}) check_work_items(mask, BH, nq);
+    for (int BH : {1, 3, 8, 10, 64, 80})
+      for (int nq : {1, 2, 7, 16, 32, 72})
+        for (int group : {1, 2, 4, 64}) check_work_items(mask, BH, nq, group);
+  EXPECT(causal_group(16, 256, 2) == 4, "N 2048 at d 64: 4 heads x 16 tiles fill an XCD's 64 slots");
+  EXPECT(causal_group(16, 256, 1) == 2 && causal_group(64, 256, 2) == 1 && causal_group(1, 256, 2) == 64,
+         "causal groups at d 128, long sequences and one tile");
+  EXPECT(causal_group(40, 256, 2) == 1 && causal_group(0, 256, 2) == 1, "causal group at least 1");
   // split plans: the sizes of the unmasked workloads and small or odd shapes
   EXPECT(split_plan(MASK_NONE, 320, 32, 256).rem == 64 && split_plan(MASK_NONE, 320, 32, 256).parts == 4,
          "B2 H5 N4096: 256 whole tiles, 64 tiles in 4 parts");
