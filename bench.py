@@ -207,8 +207,8 @@ def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
 
     res = {"kernel_trace": None, "mfma_util": None, "traffic_bytes": None}
     # the kernels of one step (the backward run also holds the one forward call made before timing)
-    step_kernel = ("attn_bwd_",) if args.backward else ("attn_fwd_kernel", "attn_merge_kernel")
-    main_kernel = "attn_bwd_dkv" if args.backward else "attn_fwd_kernel"
+    step_kernel = ("attn_bwd_",) if args.backward else ("attn_fwd_", "attn_merge_kernel")
+    main_kernel = "attn_bwd_dkv" if args.backward else "attn_fwd_"
     if shutil.which("rocprofv3") is None:
         return res
     work = tempfile.mkdtemp(prefix="attn_bench_prof_")
@@ -411,6 +411,8 @@ def main():
                        if args.backward else
                        (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
                         else f"attn_fwd_kernel<{w.d},{w.mask}>"))
+    if prof and prof.get("kernel_trace"):  # the names the kernel trace recorded
+        roof["kernels"] = " + ".join(prof["kernel_trace"]["kernels"])
     # HBM bytes of one step, from this run's FETCH_SIZE and WRITE_SIZE passes (or given on the command line)
     roof["traffic"] = None
     if prof and prof.get("traffic_bytes"):

@@ -40,13 +40,19 @@ attn::SplitPlan plan_for(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t 
   return attn::split_plan(mask_mode, n_tiles, (int32_t)attn::cdiv(Nkv, attn::tile_keys(d)), cus);
 }
 
-// Kernel mask kind for a checked problem: the block-masked neighbourhood kernel
-// for undilated 2D windows on grids of width 32, 64, 96 or 128; the grid-mask
-// kernel for other grids of width 4..124 with rows and planes <= 128; the element
-// predicate for the rest.
+// Kernel mask kind for a checked problem: the patch kernel for undilated 2D
+// windows whose patch bands fit it (na_patch_eligible, d = 32 or 64); the
+// block-masked neighbourhood kernel for other undilated 2D windows on grids of
+// width 32, 64, 96 or 128; the grid-mask kernel for other grids of width 4..124
+// with rows and planes <= 128; the element predicate for the rest.
 int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
   if (p.mask == ATTN_MASK_NONE) return attn::MASK_NONE;
   if (p.mask == ATTN_MASK_CAUSAL) return attn::MASK_CAUSAL;
+  const int32_t patch_rows = attn::patch_lds_rows(p.d);
+  if (patch_rows > 0 && attn::na_patch_eligible(g, patch_rows)) {
+    const int64_t patches = p.B * p.H * attn::cdiv(g.grid_h, attn::kPatchRows) * attn::cdiv(g.grid_w, attn::kPatchCols);
+    if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
+  }
   const bool blocks = g.grid_d == 1 && g.dil_h == 1 && g.dil_w == 1 && g.grid_w % 32 == 0 && g.grid_w <= 128;
   if (blocks) return attn::MASK_NA_BLOCKS;
   return attn::na_grid_eligible(g) ? attn::MASK_NA_GRID : attn::MASK_NA;
@@ -81,6 +87,11 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   mask = kernel_mask(p, a.na);
   a.na_phases = mask == attn::MASK_NA_BLOCKS ? a.na.grid_w / 32 : 0;
   int32_t n_wg = a.BH * a.n_qtiles, rem = 0;
+  if (mask == attn::MASK_NA_PATCH) {
+    a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
+    a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kPatchRows);
+    n_wg = a.BH * a.patch_nx * a.patch_ny;
+  }
   if (split != nullptr && split->rem > 0) {
     a.ws_parts = static_cast<float*>(workspace);
     a.split_full = split->full;

@@ -754,6 +754,298 @@ void attn_fwd_kernel(KernelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Neighbourhood windows by query patches (MASK_NA_PATCH, na_patch_eligible).
+//
+// One work-group per patch of 8 x 16 queries of one head. It copies the patch's
+// key rectangle (a band of key rows times a band of at most 32 columns, see
+// na_patch_bands) into LDS once, one 32-key block per key row, and waits for it
+// once; query wavefront w then holds the 32 queries of patch rows 2w and 2w + 1
+// (lane column col: row col / 16, column col % 16) and runs over the key rows of
+// its own two rows' band, four blocks per step. The arithmetic per step is that of
+// the tile kernel (scores on the matrix core, window bits, P = 2^(c s - m) against
+// a reference maximum set by the part's first step and moved only past the 2^20
+// row-sum guard, O += P V, delayed division). At d = 32 every query wavefront has
+// a second wavefront on its SIMD that takes the odd steps of the same queries
+// (two parts); the parts meet once at the end, where the second leaves its
+// output, maximum and row sums in LDS and the first combines them exactly (the
+// rescaling by 2^(m_i - m) of the running-softmax paragraph of PhotoRoom's
+// xformers post) and stores.
+template <int D>
+struct PatchCfg {
+  // key rows (32 keys each) of the K and of the V rectangle in LDS: 80 KB in all at
+  // d = 32 (two work-groups per CU), 136 KB at d = 64
+  static constexpr int ROWS = D == 32 ? 20 : 17;
+  static constexpr int PARTS = D == 32 ? 2 : 1;  // wavefronts per query wavefront (step parity)
+  static constexpr int THREADS = 256 * PARTS;
+  static constexpr int ROW_CHUNKS = D / 8;
+  static constexpr int CHUNKS = ROWS * kPatchKeyCols * ROW_CHUNKS;  // 16-byte chunks per rectangle
+  static_assert(CHUNKS % THREADS == 0, "the copy runs in whole rounds of the work-group's lanes");
+  static constexpr int ELEMS = CHUNKS * 8;
+  static constexpr int MERGE = PARTS > 1 ? 4 * (D / 32 * 16 + 2) * 64 : 1;  // floats: second part's O, m, l
+};
+static_assert(PatchCfg<32>::ROWS == patch_lds_rows(32) && PatchCfg<64>::ROWS == patch_lds_rows(64),
+              "host eligibility and kernel LDS must agree");
+
+template <int D>
+__global__ __launch_bounds__(PatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_na_patch_kernel(KernelArgs a) {
+  using P = PatchCfg<D>;
+  constexpr int KB = D / 16, DT = D / 32, SB = 4, RC = D / 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[P::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[P::ELEMS];
+  __shared__ float merge_lds[P::MERGE];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave8 & 3, part = wave8 >> 2;  // query wavefront, step parity
+  const NaGeom& g = a.na;
+  const int32_t H = g.grid_h, W = g.grid_w, N = a.Nq;
+  const float c = a.c;
+
+  // patches row-major within a head, heads kept on one XCD (xcd_contiguous)
+  const int32_t per_head = a.patch_ny * a.patch_nx;
+  const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int32_t bh = item / per_head, pidx = item - bh * per_head;
+  const int32_t py = pidx / a.patch_nx;
+  const int32_t y0 = py * kPatchRows, x0 = (pidx - py * a.patch_nx) * kPatchCols;
+  const PatchBands pb = na_patch_bands(y0, x0, g);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+
+  // ---- the lane's query (loaded first, used after the rectangle has landed)
+  const int32_t qy = y0 + 2 * wave + (col >> 4), qx = x0 + (col & 15);
+  const bool q_ok = qy < H && qx < W;
+  const int32_t my_q = qy * W + qx;
+  // every lane loads (a query outside the grid reads query 0 and zeroes it after the wait)
+  const int32_t q_row = q_ok ? my_q : 0;
+  u32x4_t qraw[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    qraw[kb] = *reinterpret_cast<const u32x4_t*>(a.q + head + (size_t)q_row * D + kb * 16 + half * 8);
+
+  // ---- the key rectangle: LDS chunk p holds chunk (p % RC) ^ swizzle of key p / RC,
+  // key = 32 r + x: row band cell r, column band cell x. Rows past the band (up to 3
+  // are read by a wavefront's last step) and columns past the column band read as
+  // zero (an offset past the head) and are masked.
+  {
+    const i32x4_t k_rsrc = head_rsrc(a.k + head, head_bytes);
+    const i32x4_t v_rsrc = head_rsrc(a.v + head, head_bytes);
+    const uint32_t k_base = __builtin_amdgcn_readfirstlane(lds_addr(k_lds) + wave8 * 1024);
+    const uint32_t v_base = __builtin_amdgcn_readfirstlane(lds_addr(v_lds) + wave8 * 1024);
+    const int32_t n_loads = (int32_t)cdiv((int64_t)(pb.rows.count + 3) * kPatchKeyCols * RC, P::THREADS);
+    for (int32_t j = 0; j < n_loads; ++j) {
+      const int32_t p = j * P::THREADS + tid;
+      const int32_t key = p / RC, r = key / kPatchKeyCols, x = key % kPatchKeyCols;
+      const int32_t chunk = (p % RC) ^ chunk_swizzle<D>(key);
+      uint32_t voff = head_bytes;
+      if (r < pb.rows.count && x < pb.cols.count) {
+        int32_t ky = pb.rows.start + r, kx = pb.cols.start + x;
+        ky -= ky >= H ? H : 0;  // both start inside the axis and span at most its length
+        kx -= kx >= W ? W : 0;
+        voff = (uint32_t)(ky * W + kx) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
+      }
+      dma_lds16(k_rsrc, k_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
+      dma_lds16(v_rsrc, v_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
+    }
+    wait_tile_loads<0>();
+    __syncthreads();  // the rectangle is read-only from here on
+  }
+  // a query wavefront below the grid (last patch row of a ragged grid) has no work; with two
+  // parts it still meets the other part at the end
+  const bool rows_in = y0 + 2 * wave < H;
+  if (P::PARTS == 1 && !rows_in) return;
+
+  bf16x8_t qf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    u32x4_t x = qraw[kb];
+    asm volatile("" : "+v"(x));  // keeps the wait for Q after the rectangle's copy has been issued
+    x ^= a.q_sign;               // negative scale: flip Q's sign bits, use |scale|
+    qf[kb] = __builtin_bit_cast(bf16x8_t, q_ok ? x : u32x4_t{0, 0, 0, 0});
+  }
+
+  // ---- this wavefront's key rows: the band of its two query rows, a run of the patch's band
+  const int32_t wy0 = imin(y0 + 2 * wave, H - 1);
+  const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, 1);
+  int32_t off = wb.start - pb.rows.start;
+  off += off < 0 ? H : 0;
+  const int32_t n_steps = rows_in ? (wb.count + SB - 1) / SB : 0;
+
+  // The window along an axis is `kernel` consecutive cells from win_start (mod the
+  // axis length when wrapped); in band cells it starts lo cells into the band. Window
+  // bits of the lane's column: bit x for column band cell x (a wrapped window on an
+  // axis no longer than the band runs past the band's end and continues at cell 0).
+  // Element e of a 32-key block of the lane holds cell 8 (e / 4) + 4 half + e % 4.
+  auto win_start = [](int32_t c, int32_t len, int32_t kernel, int32_t rad, int32_t wrap) {
+    return wrap ? c - rad : iclamp(c - rad, 0, len - kernel);
+  };
+  int32_t lo_x = win_start(qx, W, g.kernel_w, g.rad_w, g.wrap_w) - pb.cols.start;
+  lo_x += lo_x < 0 ? W : 0;
+  uint64_t cm64 = ((1ull << g.kernel_w) - 1ull) << lo_x;
+  cm64 |= cm64 >> pb.cols.count;  // the wrapped tail (cols.count = W here), else bits past 32 only
+  const uint32_t cm = (uint32_t)cm64 & (uint32_t)((1ull << pb.cols.count) - 1ull);
+  int32_t lo_y = win_start(qy, H, g.kernel_h, g.rad_h, g.wrap_h) - pb.rows.start;  // < H: the band holds the window
+  lo_y += lo_y < 0 ? H : 0;
+  uint32_t cm16 = 0;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) cm16 |= ((cm >> (8 * g4 + 4 * half)) & 0xFu) << (4 * g4);
+  cm16 = q_ok ? cm16 : 0u;
+
+  // LDS read offsets of the transposing V read (as in the tile kernel)
+  const int k_swz = chunk_swizzle<D>(col);
+  int v_row[2], v_off[2][DT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v_row[h] = h * 8 + half * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      v_off[h][dt] = (((dcol >> 3) ^ chunk_swizzle<D>(v_row[h])) << 3) + (dcol & 7);
+    }
+  }
+
+  f32x16_t oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
+  float m_run = -FLT_MAX, l_run = 0.f;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (int32_t st = part; st < n_steps; st += P::PARTS) {
+    const int32_t r0 = off + SB * st;  // first band row of the step (r0 + 3 < pb.rows.count + 3)
+    const uint16_t* ks = k_lds + r0 * kPatchKeyCols * D;
+    const uint16_t* vs = v_lds + r0 * kPatchKeyCols * D;
+    // S^T = K Q^T: lane holds keys 32 sb + 8 (e / 4) + 4 half + e % 4 of its query
+    f32x16_t s[SB];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(ks + (sb * 32 + col) * D + (((2 * kb + half) ^ k_swz) << 3));
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qf[kb], s[sb], 0, 0, 0);
+      }
+    // window: the block's key row within this wavefront's band and the query's row window
+    uint32_t bm[SB];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      const bool rok = SB * st + sb < wb.count && (uint32_t)(r0 + sb - lo_y) < (uint32_t)g.kernel_h;
+      bm[sb] = rok ? cm16 : 0u;
+    }
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[sb][e] = ((bm[sb] >> e) & 1u) ? s[sb][e] : -INFINITY;
+    if (st == part) {  // the part's reference maximum (every query sees a key of step 0)
+      float mx = s[0][0];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
+      mx = swap_halves_max(mx);
+      m_run = mx == -INFINITY ? -FLT_MAX : mx * c;
+    }
+    // P = 2^(c s - m) rounded to bfloat16, the lane's sum of the rounded values
+    bf16x8_t p[SB][2];
+    auto probs = [&]() {
+      float psum = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float s0 = s[sb][kb2 * 8 + e], s1 = s[sb][kb2 * 8 + e + 1];
+            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
+            p0 = s0 == -INFINITY ? 0.f : p0;
+            p1 = s1 == -INFINITY ? 0.f : p1;
+            const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+            p[sb][kb2][e] = pp[0];
+            p[sb][kb2][e + 1] = pp[1];
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+          }
+      return psum;
+    };
+    float psum = probs();
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {  // rare: a row's maximum moved far up
+      float mx = s[0][0];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
+      mx = swap_halves_max(mx);
+      const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
+      const float m_new = fmaxf(m_run, cand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      l_run *= alpha;
+      psum = probs();
+    }
+    l_run += psum;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int row0 = sb * 32 + kb2 * 16;
+          u32x2_t x[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4*)((lds_u16*)vs + (row0 + v_row[h]) * D + v_off[h][dt])));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[sb][kb2], oacc[dt], 0, 0, 0);
+        }
+  }
+
+  if constexpr (P::PARTS > 1) {
+    // the second part leaves O, m and l (per lane, in lane order); the first combines
+    constexpr int F = DT * 16 + 2;
+    float* slot = merge_lds + wave * F * 64 + lane;
+    if (part == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) slot[(dt * 16 + e) * 64] = oacc[dt][e];
+      slot[(F - 2) * 64] = m_run;
+      slot[(F - 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (part == 1 || !rows_in) return;
+    const float m1 = slot[(F - 2) * 64], l1 = slot[(F - 1) * 64];
+    const float m_new = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_new), a1 = __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[dt][e] = oacc[dt][e] * a0 + slot[(dt * 16 + e) * 64] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m_new;
+  }
+
+  // ---- delayed division and store (lane `col` of the first half-wave also writes the logsumexp)
+  const float l_tot = swap_halves_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (q_ok) {
+    uint16_t* __restrict__ oh = a.o + head;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4_t ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(oacc[dt][g4 * 4 + e] * inv);
+        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2_t, ob);
+      }
+    if (a.lse != nullptr && half == 0) a.lse[(size_t)bh * N + my_q] = row_lse(m_run, l_tot);
+  }
+}
+
 // Second kernel of a split launch: one wavefront per (split tile, wavefront
 // slice of the tile, half of the head dimension at d = 128). It reads every
 // part's maximum and row sum, rescales all parts to the largest maximum, sums
@@ -861,6 +1153,12 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
     case MASK_NA: return launch_one<D, MASK_NA, false>(a, n_wg, stream);
     case MASK_NA_BLOCKS: return launch_one<D, MASK_NA_BLOCKS, false>(a, n_wg, stream);
     case MASK_NA_GRID: return launch_one<D, MASK_NA_GRID, false>(a, n_wg, stream);
+    case MASK_NA_PATCH:
+      if constexpr (D == 32 || D == 64) {
+        hipLaunchKernelGGL((attn_fwd_na_patch_kernel<D>), dim3(n_wg), dim3(PatchCfg<D>::THREADS), 0, stream, a);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,6 +31,7 @@ struct KernelArgs {
   int32_t split_full;   // whole-tile work-groups
   int32_t split_parts;  // parts per split tile
   int32_t causal_group; // causal: heads per XCD dispatched together (causal_item)
+  int32_t patch_nx, patch_ny;  // MASK_NA_PATCH: patches per grid row and per grid column
 };
 
 // Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
@@ -46,6 +47,10 @@ constexpr int64_t kStaticScratchBytes = 256 * part_slot_bytes(128);
 // Device address of this device's static scratch (file-scope __device__ array,
 // looked up once per device with hipGetSymbolAddress and cached).
 hipError_t static_scratch(void** ptr);
+
+// Key rows (32 keys each) the patch kernel of 2D neighbourhood windows keeps in LDS for
+// head size d (0: no patch kernel at that size).
+constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 20 : d == 64 ? 17 : 0; }
 
 // Work-groups of the backward kernels resident per CU: two at d <= 64 and one at d = 128
 // (their register and LDS budgets). The causal dispatch order sizes its head groups with it.

@@ -29,9 +29,13 @@ namespace attn {
 // dilation (an element predicate). The bit-mask kinds cover the common grids:
 // MASK_NA_BLOCKS the 2D, undilated window on grids whose width is a multiple of
 // 32 (at most 128); MASK_NA_GRID any window on grids of width 4..124 whose
-// height and depth are at most 128 (na_grid_eligible).
-enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3, MASK_NA_GRID = 4 };
-constexpr bool is_na(int mask) { return mask == MASK_NA || mask == MASK_NA_BLOCKS || mask == MASK_NA_GRID; }
+// height and depth are at most 128 (na_grid_eligible). MASK_NA_PATCH, a kernel of
+// its own, takes 2D undilated windows whose patch bands fit its LDS
+// (na_patch_eligible) in query patches instead of query tiles.
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3, MASK_NA_GRID = 4, MASK_NA_PATCH = 5 };
+constexpr bool is_na(int mask) {
+  return mask == MASK_NA || mask == MASK_NA_BLOCKS || mask == MASK_NA_GRID || mask == MASK_NA_PATCH;
+}
 
 // Neighbourhood geometry in the form the kernel uses. Token n sits at depth
 // z = n / (grid_h * grid_w), row y and column x of its plane (row-major); a 2D
@@ -340,6 +344,49 @@ constexpr void na_col_bits(int32_t cq, int32_t half, int32_t W, int32_t kernel, 
       bits[ph >> 1] |= nib << ((ph & 1) * 16 + 4 * g);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Query patches of 2D neighbourhood windows (MASK_NA_PATCH).
+//
+// A query tile of consecutive tokens spans whole grid rows, so its wavefronts
+// score every key of the rows their windows reach, most of them outside every
+// window (a 32-query run of one row against 64-column rows: 38 of 64 columns
+// hold some window cell, and the tile's band of rows is the union over its two
+// query rows). A patch of 8 rows x 16 columns instead reaches a band of rows
+// (na_band over its rows) times a band of at most 32 columns (na_band over its
+// columns). The work-group copies that rectangle into LDS once, each key row of
+// it as one 32-key block (its column band, padded to 32 with keys read as zero
+// and masked); wavefront w, holding patch rows 2w and 2w + 1, then scores only
+// the key rows of its own rows' band, four blocks per step.
+constexpr int32_t kPatchRows = 8, kPatchCols = 16, kPatchKeyCols = 32;
+
+struct PatchBands {
+  Band rows, cols;
+};
+
+constexpr PatchBands na_patch_bands(int32_t y0, int32_t x0, const NaGeom& g) {
+  return PatchBands{na_band(y0, imin(y0 + kPatchRows, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, 1),
+                    na_band(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, 1)};
+}
+
+// The most key rows and columns any patch's bands hold.
+constexpr int32_t na_patch_max_rows(const NaGeom& g) {
+  return imin(g.wrap_h ? kPatchRows + 2 * g.rad_h : kPatchRows - 1 + g.kernel_h, g.grid_h);
+}
+constexpr int32_t na_patch_max_cols(const NaGeom& g) {
+  return imin(g.wrap_w ? kPatchCols + 2 * g.rad_w : kPatchCols - 1 + g.kernel_w, g.grid_w);
+}
+
+// One plane, undilated; every column band within one 32-key block; a wrapped row
+// band shorter than the axis (so the band of a wavefront's two rows is one run
+// of its work-group's band); and the band's rows, plus the 3 rows a wavefront's
+// last step of four may read past them, within the kernel's `lds_rows`.
+constexpr bool na_patch_eligible(const NaGeom& g, int32_t lds_rows) {
+  if (g.grid_d != 1 || g.dil_h != 1 || g.dil_w != 1) return false;
+  if (na_patch_max_cols(g) > kPatchKeyCols) return false;
+  if (g.wrap_h && kPatchRows + 2 * g.rad_h >= g.grid_h) return false;
+  return na_patch_max_rows(g) + 3 <= lds_rows;
 }
 
 // 16-bit mask of the accumulator elements of one 32-key block that a lane keeps

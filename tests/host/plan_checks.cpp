@@ -207,6 +207,77 @@ static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int
   check_na_geom(geom(1, gh, gw, 1, kh, kw, 0, wh, ww, 1, 1, 1), BM, BN);
 }
 
+// The patch kernel (MASK_NA_PATCH) as it walks its LDS rectangle: for every patch,
+// wavefront and lane, the cells it marks visible are exactly the query's window
+// (enumerated independently), each once; the rectangle fits the kernel's LDS rows;
+// every step's four blocks lie inside them; and the first step holds a visible key
+// of every query (it sets the reference maximum).
+static int check_patch(const NaGeom& g, int lds_rows) {
+  if (!na_patch_eligible(g, lds_rows)) return 0;
+  const int H = g.grid_h, W = g.grid_w;
+  for (int y0 = 0; y0 < H; y0 += kPatchRows)
+    for (int x0 = 0; x0 < W; x0 += kPatchCols) {
+      const PatchBands pb = na_patch_bands(y0, x0, g);
+      EXPECT(pb.cols.count >= 1 && pb.cols.count <= kPatchKeyCols && pb.rows.count >= 1 && pb.rows.count + 3 <= lds_rows,
+             "patch bands %d x %d (grid %dx%d k %d,%d wrap %d%d)", pb.rows.count, pb.cols.count, H, W, g.kernel_h,
+             g.kernel_w, g.wrap_h, g.wrap_w);
+      for (int w = 0; w < 4; ++w) {
+        const int wy0 = y0 + 2 * w;
+        if (wy0 >= H) continue;
+        const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, 1);
+        int off = wb.start - pb.rows.start;
+        off += off < 0 ? H : 0;
+        const int n_steps = (wb.count + 3) / 4;
+        EXPECT(off >= 0 && off + wb.count <= pb.rows.count && off + 4 * n_steps <= pb.rows.count + 3,
+               "wave band off %d count %d of %d rows", off, wb.count, pb.rows.count);
+        for (int col = 0; col < 32; ++col) {
+          const int qy = wy0 + col / 16, qx = x0 + col % 16;
+          if (qy >= H || qx >= W) continue;
+          // the kernel's window bits: kernel-long runs of band cells from lo_x and lo_y
+          auto win_start = [](int c, int len, int kernel, int rad, int wrap) {
+            return wrap ? c - rad : iclamp(c - rad, 0, len - kernel);
+          };
+          int lo_x = win_start(qx, W, g.kernel_w, g.rad_w, g.wrap_w) - pb.cols.start;
+          lo_x += lo_x < 0 ? W : 0;
+          uint64_t cm64 = ((1ull << g.kernel_w) - 1ull) << lo_x;
+          cm64 |= cm64 >> pb.cols.count;
+          const uint32_t cm = (uint32_t)cm64 & (uint32_t)((1ull << pb.cols.count) - 1ull);
+          int lo_y = win_start(qy, H, g.kernel_h, g.rad_h, g.wrap_h) - pb.rows.start;
+          lo_y += lo_y < 0 ? H : 0;
+          EXPECT(lo_x >= 0 && lo_x < 64 - g.kernel_w && lo_y >= 0 && lo_y < H, "window offsets %d %d", lo_x, lo_y);
+          std::vector<int> seen;
+          bool first_step = false;
+          for (int st = 0; st < n_steps; ++st)
+            for (int sb = 0; sb < 4; ++sb) {
+              const int r = off + 4 * st + sb;
+              int ky = pb.rows.start + r;
+              ky -= ky >= H ? H : 0;
+              const bool rok = 4 * st + sb < wb.count && (unsigned)(r - lo_y) < (unsigned)g.kernel_h;
+              for (int x = 0; x < kPatchKeyCols; ++x) {
+                int kx = pb.cols.start + x;
+                kx -= kx >= W ? W : 0;
+                if (rok && ((cm >> x) & 1u)) {
+                  EXPECT(r < pb.rows.count && x < pb.cols.count && ky >= 0 && ky < H && kx >= 0 && kx < W,
+                         "visible cell outside the rectangle");
+                  seen.push_back(ky * W + kx);
+                  first_step = first_step || st == 0;
+                }
+              }
+            }
+          std::set<int> want;
+          for (int yc : axis_cells(qy, H, g.kernel_h, g.wrap_h, 1))
+            for (int xc : axis_cells(qx, W, g.kernel_w, g.wrap_w, 1)) want.insert(yc * W + xc);
+          const std::set<int> got(seen.begin(), seen.end());
+          EXPECT(got.size() == seen.size() && got == want,
+                 "patch window of query (%d,%d): %zu cells (%zu distinct), want %zu (grid %dx%d k %d,%d wrap %d%d)", qy, qx,
+                 seen.size(), got.size(), want.size(), H, W, g.kernel_h, g.kernel_w, g.wrap_h, g.wrap_w);
+          EXPECT(first_step, "query (%d,%d) sees no key in its first step", qy, qx);
+        }
+      }
+    }
+  return 1;
+}
+
 static void check_causal(int Nq, int Nkv, int BM, int BN) {
   const int n_tiles = (int)cdiv(Nkv, BN);
   for (int q0 = 0; q0 < Nq; q0 += BM) {
@@ -476,6 +547,27 @@ int main() {
     check_grid_bits(geom(3, 4, 20, 3, 3, 5, 1, 1, 0, 1, 1, 3), BN);
     check_grid_bits(geom(2, 66, 4, 1, 5, 3, 0, 1, 1, 1, 9, 1), BN);   // 66 rows: row bits in the upper word
     check_grid_bits(geom(70, 2, 4, 5, 1, 1, 1, 0, 0, 3, 1, 1), BN);   // 70 planes
+  }
+  {
+    // patch kernel: grids, windows and wrap flags around the limits of na_patch_eligible
+    int eligible = 0, tried = 0;
+    for (int H : {7, 11, 17, 33, 64})
+      for (int W : {9, 17, 32, 33, 64})
+        for (int k : {1, 3, 7, 9, 13, 17, 19})
+          for (int wh = 0; wh < 2; ++wh)
+            for (int ww = 0; ww < 2; ++ww)
+              for (int lds_rows : {17, 20}) {
+                const NaGeom g = geom(1, H, W, 1, k, k == 1 ? 3 : k - 2, 0, wh, ww, 1, 1, 1);
+                if (!geom_valid(g)) continue;
+                ++tried;
+                eligible += check_patch(g, lds_rows);
+              }
+    EXPECT(eligible > 100 && eligible < tried, "patch eligibility covers %d of %d shapes", eligible, tried);
+    const NaGeom c4 = geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1);
+    EXPECT(na_patch_eligible(c4, 20) && na_patch_eligible(c4, 17), "64x64 grid, 7x7 wrapped window takes the patch kernel");
+    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 20), "dilated windows do not");
+    EXPECT(!na_patch_eligible(geom(4, 20, 20, 3, 5, 5, 1, 1, 1, 1, 1, 1), 20), "3D windows do not");
+    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 19, 0, 1, 1, 1, 1, 1), 20), "19 columns wide: the band passes 32");
   }
   for (int mask : {MASK_NONE, MASK_CAUSAL})
     for (int BH : {1, 3, 8, 10, 64, 80})
