@@ -14,13 +14,26 @@
  * tensors in bfloat16), with the 1/sqrt(d) scale and the -inf causal mask of
  * "Profiling in PyTorch" part 3 (section "Deconstructing Naive Attention"),
  * and the wrap-around 2D neighbourhood window requested in NATTEN issue 142
- * ("circular windowed attention", the 5x5 kernel_size=3 example).
+ * (a window that wraps circularly at the grid's edges; its 5x5 grid, kernel
+ * size 3 example).
  *
  * The N x N score matrix is never written to memory: scores are produced
  * tile by tile, reduced with a running row maximum and row sum, and divided
  * once after the product with V (NKI tutorial, section "Softmax
  * implementation"; PhotoRoom's xformers post, the running-softmax
  * paragraph).
+ *
+ * Types at the boundary: every `stream` argument is a `void*` that holds a
+ * hipStream_t (NULL = the default stream), so that this header needs no HIP
+ * include; functions return attn_status_t; attn_status_string takes an
+ * int32_t so that any integer, including a code this version does not know,
+ * can be passed to it.
+ *
+ * State: the library keeps no per-call state. It caches two read-only facts
+ * per device the first time a call needs them (the CU count, used to plan
+ * the remainder split and the causal dispatch order, and the device address
+ * of attn_fwd_ex_static's scratch array); the caches are filled under a lock
+ * or an atomic store and never change afterwards.
  */
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H
@@ -125,8 +138,9 @@ typedef enum {
  * stream  : a hipStream_t (NULL = the default stream).
  *
  * The caller owns all memory. The library allocates nothing, keeps no state
- * between calls, never synchronises and is safe to call concurrently on
- * different streams. Exactly one kernel is launched per call.
+ * between calls (beyond the per-device caches above), never synchronises and
+ * is safe to call concurrently on different streams. Exactly one kernel is
+ * launched per call.
  *
  * Returns ATTN_OK after the launch is queued. Argument errors are detected
  * before any device work and leave o untouched. ATTN_ERR_HIP reports a

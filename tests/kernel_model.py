@@ -62,7 +62,9 @@ def model_head(q, k, v, scale: float, allow=None, bn: int = 128, first_tile: int
     """Modelled kernel output (float32 values of bfloat16) of one head: q (Nq, d), k, v (Nkv, d)
     holding bfloat16 values. allow: bool (Nq, Nkv) or None. Tiles are visited circularly from
     first_tile. p_format "bf16" is the kernel's; "fp16" models float16 probabilities and values
-    (values scaled by 2^-8 into float16 range, probabilities kept below 2^15)."""
+    (values scaled by 2^-8 into float16 range, probabilities kept below 2^15); "bf16x2" models P
+    split into a bfloat16 high part and a bfloat16 remainder (two products with V, both parts in
+    the row sum)."""
     q = np.asarray(q, np.float32)
     k = np.asarray(k, np.float32)
     v = np.asarray(v, np.float32)
@@ -77,6 +79,8 @@ def model_head(q, k, v, scale: float, allow=None, bn: int = 128, first_tile: int
         round_p, vv, v_scale, safe = to_bf16, v, np.float32(1.0), SAFE_SUM
     elif p_format == "fp16":
         round_p, vv, v_scale, safe = to_fp16, to_fp16(v * np.float32(2.0 ** -8)), np.float32(2.0 ** 8), np.float32(2.0 ** 15)
+    elif p_format == "bf16x2":  # P as the sum of two bfloat16 parts (P V as two products)
+        round_p, vv, v_scale, safe = (lambda x: to_bf16(x) + to_bf16(x - to_bf16(x))), v, np.float32(1.0), SAFE_SUM
     else:
         raise ValueError(p_format)
     n_tiles = -(-Nkv // bn)

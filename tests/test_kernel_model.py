@@ -41,7 +41,7 @@ def _ratios(B, H, N, d, seed, scale, q_gain=1.0, mask="none", na=None, bn=128, p
     got = model_forward(qf, kf, vf, scale, allow, bn=bn, p_format=p_format)
     ref = oracle.attention(qf, kf, vf, scale, mask, na)
     p = oracle.probs(qf, kf, scale, mask, na)
-    u_p = U_FP16 if p_format == "fp16" else 2.0 ** -8
+    u_p = {"fp16": U_FP16, "bf16x2": 2.0 ** -16}.get(p_format, 2.0 ** -8)
     worst_ns, worst_derived = 0.0, 0.0
     for b in range(B):
         for h in range(H):
@@ -71,8 +71,12 @@ def test_sharp_rows_within_derived_bound(scale, q_gain, seed, exceeds, mask):
 
 
 @pytest.mark.parametrize("scale,q_gain,seed", [(0.125, 4.0, 2003), (1.0, 1.0, 2000), (0.125, 4.0, 2001)])
-def test_fp16_probabilities_meet_north_star(scale, q_gain, seed):
-    worst_ns, _ = _ratios(2, 3, 300, 64, seed, scale, q_gain, p_format="fp16")
+@pytest.mark.parametrize("p_format", ["fp16", "bf16x2"])
+def test_wider_probabilities_meet_north_star(scale, q_gain, seed, p_format):
+    """Either float16 probabilities and values, or P kept as two bfloat16 parts (the variant
+    timed on the GPU at 0.56-0.73x of the kernel's throughput), bring the sharp rows inside the
+    spec bound: the output's own bfloat16 rounding is then the main error."""
+    worst_ns, _ = _ratios(2, 3, 300, 64, seed, scale, q_gain, p_format=p_format)
     assert worst_ns < 0.85, worst_ns
 
 
