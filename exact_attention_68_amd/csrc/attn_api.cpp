@@ -41,7 +41,8 @@ attn::SplitPlan plan_for(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t 
 }
 
 // Kernel mask kind for a checked problem: the patch kernel for undilated 2D
-// windows whose patch bands fit it (na_patch_eligible, d = 32 or 64); the
+// windows whose patch bands fit it (na_patch_eligible, d = 32 or 64); the row
+// kernel for other windows on grids at most 32 wide (na_rows_eligible, d = 32); the
 // block-masked neighbourhood kernel for other undilated 2D windows on grids of
 // width 32, 64, 96 or 128; the grid-mask kernel for other grids of width 4..124
 // with rows and planes <= 128; the element predicate for the rest.
@@ -52,6 +53,11 @@ int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
   if (patch_rows > 0 && attn::na_patch_eligible(g, patch_rows)) {
     const int64_t patches = p.B * p.H * attn::cdiv(g.grid_h, attn::kPatchRows) * attn::cdiv(g.grid_w, attn::kPatchCols);
     if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
+  }
+  const int32_t rows_rows = attn::rows_lds_rows(p.d);
+  if (rows_rows > 0 && attn::na_rows_eligible(g, rows_rows)) {
+    const int64_t groups = p.B * p.H * (int64_t)g.grid_d * attn::cdiv(g.grid_h, attn::kRowsGroup);
+    if (groups <= INT32_MAX) return attn::MASK_NA_ROWS;
   }
   const bool blocks = g.grid_d == 1 && g.dil_h == 1 && g.dil_w == 1 && g.grid_w % 32 == 0 && g.grid_w <= 128;
   if (blocks) return attn::MASK_NA_BLOCKS;
@@ -91,6 +97,11 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
     a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
     a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kPatchRows);
     n_wg = a.BH * a.patch_nx * a.patch_ny;
+  }
+  if (mask == attn::MASK_NA_ROWS) {
+    a.patch_nx = 1;
+    a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kRowsGroup);
+    n_wg = a.BH * a.na.grid_d * a.patch_ny;
   }
   if (split != nullptr && split->rem > 0) {
     a.ws_parts = static_cast<float*>(workspace);

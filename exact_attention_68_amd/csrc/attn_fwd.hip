@@ -771,6 +771,107 @@ void attn_fwd_kernel(KernelArgs a) {
 // output, maximum and row sums in LDS and the first combines them exactly (the
 // rescaling by 2^(m_i - m) of the running-softmax paragraph of PhotoRoom's
 // xformers post) and stores.
+// One step of a neighbourhood walk over key rows held in LDS (the patch and row
+// kernels): the first nblk (1..4, uniform) of four 32-key blocks, block b at kb[b]
+// and vb[b] (32 rows of D elements, swizzled as the tile rings). Element e of a
+// block is key 8 (e / 4) + 4 half + e % 4. The window: a block whose key row is in
+// the lane's window (live[b]) takes the lane's per-element bias over the row's
+// columns (0 for a visible key, -inf for a hidden one); every key of another block
+// is hidden. The window enters as the addend of the exponent's fma, so a hidden key
+// gives 2^-inf = 0 with no test (also at scale 0: the addend is -inf, not the
+// product). On the walk's first step (first)
+// the reference maximum m_run is c times the largest visible score; P = 2^(c s -
+// m_run) is rounded to bfloat16 and the lane's sum of the rounded values kept,
+// redone against a new maximum past the 2^20 row-sum guard (the tile kernel's
+// rule); O^T += V^T P^T. Blocks past nblk cost nothing.
+template <int D>
+__device__ __forceinline__ void window_step(const uint16_t* const (&kb)[4], const uint16_t* const (&vb)[4],
+                                            const bool (&live)[4], const float (&bias)[16], int nblk, bool first,
+                                            const bf16x8_t (&qf)[D / 16], float c, int col, int half, int k_swz,
+                                            const int (&v_row)[2], const int (&v_off)[2][D / 32],
+                                            f32x16_t (&oacc)[D / 32], float& m_run, float& l_run) {
+  constexpr int KB = D / 16, DT = D / 32, SB = 4;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // S^T = K Q^T: lane holds keys 8 (e / 4) + 4 half + e % 4 of each block, for its query
+  f32x16_t s[SB];
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+#pragma unroll
+  for (int kb_ = 0; kb_ < KB; ++kb_)
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      if (sb >= nblk) continue;
+      const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(kb[sb] + col * D + (((2 * kb_ + half) ^ k_swz) << 3));
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qf[kb_], s[sb], 0, 0, 0);
+    }
+  // c * (largest visible score), -FLT_MAX when there is none (a finite sentinel)
+  auto row_max = [&]() {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (sb >= nblk) continue;
+        mx = fmaxf(mx, live[sb] ? __builtin_fmaf(s[sb][e], c, bias[e]) : -INFINITY);
+      }
+    mx = swap_halves_max(mx);
+    return mx == -INFINITY ? -FLT_MAX : mx;
+  };
+  if (first) m_run = row_max();
+  bf16x8_t p[SB][2];
+  auto probs = [&]() {
+    float nb[16];  // the exponent's addend per element of a live block
+#pragma unroll
+    for (int e = 0; e < 16; ++e) nb[e] = bias[e] - m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          if (sb >= nblk) continue;
+          const int e0 = kb2 * 8 + e, e1 = e0 + 1;
+          const float a0 = live[sb] ? nb[e0] : -INFINITY;
+          const float a1 = live[sb] ? nb[e1] : -INFINITY;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][e0], c, a0));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][e1], c, a1));
+          const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+          p[sb][kb2][e] = pp[0];
+          p[sb][kb2][e + 1] = pp[1];
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+        }
+    return psum;
+  };
+  float psum = probs();
+  if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {  // rare: a row's maximum moved far up
+    const float m_new = fmaxf(m_run, row_max());
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    l_run *= alpha;
+    psum = probs();
+  }
+  l_run += psum;
+  // O^T += V^T P^T
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        if (sb >= nblk) continue;
+        u32x2_t x[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (lds_s16x4*)((lds_u16*)vb[sb] + (kb2 * 16 + v_row[h]) * D + v_off[h][dt])));
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[sb][kb2], oacc[dt], 0, 0, 0);
+      }
+}
+
 template <int D>
 struct PatchCfg {
   // key rows (32 keys each) of the K and of the V rectangle in LDS: 80 KB in all at
@@ -908,99 +1009,22 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
   float m_run = -FLT_MAX, l_run = 0.f;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float bias[16];  // the lane's column window as an addend: 0 in the window, -inf outside
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bias[e] = ((cm16 >> e) & 1u) ? 0.f : -INFINITY;
 
   for (int32_t st = part; st < n_steps; st += P::PARTS) {
     const int32_t r0 = off + SB * st;  // first band row of the step (r0 + 3 < pb.rows.count + 3)
-    const uint16_t* ks = k_lds + r0 * kPatchKeyCols * D;
-    const uint16_t* vs = v_lds + r0 * kPatchKeyCols * D;
-    // S^T = K Q^T: lane holds keys 32 sb + 8 (e / 4) + 4 half + e % 4 of its query
-    f32x16_t s[SB];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(ks + (sb * 32 + col) * D + (((2 * kb + half) ^ k_swz) << 3));
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qf[kb], s[sb], 0, 0, 0);
-      }
-    // window: the block's key row within this wavefront's band and the query's row window
-    uint32_t bm[SB];
+    const uint16_t* kb[SB];
+    const uint16_t* vb[SB];
+    bool live[SB];  // the block's key row within this wavefront's band and the query's row window
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
-      const bool rok = SB * st + sb < wb.count && (uint32_t)(r0 + sb - lo_y) < (uint32_t)g.kernel_h;
-      bm[sb] = rok ? cm16 : 0u;
+      kb[sb] = k_lds + (r0 + sb) * kPatchKeyCols * D;
+      vb[sb] = v_lds + (r0 + sb) * kPatchKeyCols * D;
+      live[sb] = SB * st + sb < wb.count && (uint32_t)(r0 + sb - lo_y) < (uint32_t)g.kernel_h;
     }
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[sb][e] = ((bm[sb] >> e) & 1u) ? s[sb][e] : -INFINITY;
-    if (st == part) {  // the part's reference maximum (every query sees a key of step 0)
-      float mx = s[0][0];
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
-      mx = swap_halves_max(mx);
-      m_run = mx == -INFINITY ? -FLT_MAX : mx * c;
-    }
-    // P = 2^(c s - m) rounded to bfloat16, the lane's sum of the rounded values
-    bf16x8_t p[SB][2];
-    auto probs = [&]() {
-      float psum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float s0 = s[sb][kb2 * 8 + e], s1 = s[sb][kb2 * 8 + e + 1];
-            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_run));
-            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_run));
-            p0 = s0 == -INFINITY ? 0.f : p0;
-            p1 = s1 == -INFINITY ? 0.f : p1;
-            const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
-            p[sb][kb2][e] = pp[0];
-            p[sb][kb2][e + 1] = pp[1];
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-          }
-      return psum;
-    };
-    float psum = probs();
-    if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {  // rare: a row's maximum moved far up
-      float mx = s[0][0];
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
-      mx = swap_halves_max(mx);
-      const float cand = mx == -INFINITY ? -FLT_MAX : mx * c;
-      const float m_new = fmaxf(m_run, cand);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      l_run *= alpha;
-      psum = probs();
-    }
-    l_run += psum;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int row0 = sb * 32 + kb2 * 16;
-          u32x2_t x[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                   (lds_s16x4*)((lds_u16*)vs + (row0 + v_row[h]) * D + v_off[h][dt])));
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[sb][kb2], oacc[dt], 0, 0, 0);
-        }
+    window_step<D>(kb, vb, live, bias, SB, st == part, qf, c, col, half, k_swz, v_row, v_off, oacc, m_run, l_run);
   }
 
   if constexpr (P::PARTS > 1) {
@@ -1026,6 +1050,198 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
       for (int e = 0; e < 16; ++e) oacc[dt][e] = oacc[dt][e] * a0 + slot[(dt * 16 + e) * 64] * a1;
     l_run = l_run * a0 + l1 * a1;
     m_run = m_new;
+  }
+
+  // ---- delayed division and store (lane `col` of the first half-wave also writes the logsumexp)
+  const float l_tot = swap_halves_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (q_ok) {
+    uint16_t* __restrict__ oh = a.o + head;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4_t ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(oacc[dt][g4 * 4 + e] * inv);
+        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g4 * 8 + half * 4) = __builtin_bit_cast(u32x2_t, ob);
+      }
+    if (a.lse != nullptr && half == 0) a.lse[(size_t)bh * N + my_q] = row_lse(m_run, l_tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Neighbourhood windows on grids at most 32 wide by grid rows (MASK_NA_ROWS,
+// na_rows_eligible): wavefront w of a work-group holds grid row y0 + w of plane z
+// (lane column = grid column). The planes the windows reach stream through two LDS
+// stages; a stage holds the work-group's band of key rows of one plane, each row
+// as one 32-key block. A wavefront's window over a stage is uniform in its rows
+// (the key row is in or out for every lane) and the lane's own column bits inside
+// a block, so each wavefront runs over just its visible rows, four per step
+// (window_step), with the lane's column bits as the block mask.
+template <int D>
+struct RowsCfg {
+  static constexpr int ROWS = 10;  // key rows per stage: 20 KB of K or V at d = 32
+  static constexpr int ROW_CHUNKS = D / 8;
+  static constexpr int CHUNKS = ROWS * 32 * ROW_CHUNKS;  // 16-byte chunks of a stage of K (or V)
+  static_assert(CHUNKS % 256 == 0, "a stage is copied in whole rounds of 256 lanes");
+  static constexpr int LOADS = CHUNKS / 256;  // per lane, stage and tensor
+  static constexpr int ELEMS = CHUNKS * 8;
+};
+static_assert(RowsCfg<32>::ROWS == rows_lds_rows(32), "host eligibility and kernel LDS must agree");
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_na_rows_kernel(KernelArgs a) {
+  using R = RowsCfg<D>;
+  constexpr int KB = D / 16, DT = D / 32, SB = 4, RC = D / 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][R::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][R::ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const NaGeom& g = a.na;
+  const int32_t H = g.grid_h, W = g.grid_w, N = a.Nq;
+  const float c = a.c;
+
+  // (head, plane, group of 4 rows), the items of one head kept on one XCD
+  const int32_t groups = a.patch_ny, per_head = g.grid_d * groups;
+  const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int32_t bh = item / per_head, rest = item - bh * per_head;
+  const int32_t z = rest / groups, y0 = (rest - z * groups) * kRowsGroup;
+  const int32_t y = y0 + wave;  // this wavefront's grid row
+  const bool row_in = y < H;
+  const bool q_ok = row_in && col < W;
+  const int32_t my_q = (z * H + y) * W + col;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+
+  // ---- the lane's query, loaded first; used after the first stage has landed
+  const int32_t q_row = q_ok ? my_q : 0;
+  u32x4_t qraw[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    qraw[kb] = *reinterpret_cast<const u32x4_t*>(a.q + head + (size_t)q_row * D + kb * 16 + half * 8);
+
+  const Band bz = na_band(z, z, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+  const Band by = na_rows_band(y0, g);  // by.count <= R::ROWS
+  // Planes are visited from the work-group's own plane (always in its window, so its
+  // stage can be requested before any mask is built) through the band, circularly.
+  int32_t i_own = z - bz.start;
+  i_own += i_own < 0 ? g.grid_d : 0;
+  auto plane_at = [&](int32_t j) {  // plane of the j-th band cell visited
+    int32_t i = i_own + j;
+    i -= i >= bz.count ? bz.count : 0;
+    const int32_t zk = bz.start + i;
+    return zk >= g.grid_d ? zk - g.grid_d : zk;
+  };
+
+  // ---- a stage: the band rows of one plane; LDS chunk p holds chunk (p % RC) ^ swizzle of
+  // key p / RC = 32 r + x (band row r, column x); columns past W and rows past the band
+  // read as zero (an offset past the head)
+  const i32x4_t k_rsrc = head_rsrc(a.k + head, head_bytes);
+  const i32x4_t v_rsrc = head_rsrc(a.v + head, head_bytes);
+  auto load_stage = [&](int32_t zk, int stage) {
+    const uint32_t k_base = __builtin_amdgcn_readfirstlane(lds_addr(k_lds[stage]) + wave * 1024);
+    const uint32_t v_base = __builtin_amdgcn_readfirstlane(lds_addr(v_lds[stage]) + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < R::LOADS; ++j) {
+      const int32_t p = j * 256 + tid;
+      const int32_t key = p / RC, r = key / 32, x = key % 32;
+      const int32_t chunk = (p % RC) ^ chunk_swizzle<D>(key);
+      uint32_t voff = head_bytes;
+      if (r < by.count && x < W) {
+        int32_t yk = by.start + r;
+        yk -= yk >= H ? H : 0;
+        voff = (uint32_t)((zk * H + yk) * W + x) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
+      }
+      dma_lds16(k_rsrc, k_base + (uint32_t)j * 4096u, voff, 0u);
+      dma_lds16(v_rsrc, v_base + (uint32_t)j * 4096u, voff, 0u);
+    }
+  };
+
+  load_stage(z, 0);
+
+  // window masks per axis (rows and planes are the same for every lane of a wavefront)
+  const GridMasks gm = na_grid_masks(z, imin(y, H - 1), imin(col, W - 1), g);
+  // the lane's columns (bit x of the low word, x < W <= 32) as a per-element bias: 0 for a
+  // key in the window, -inf for the rest (and for a lane outside the grid)
+  const uint32_t cm16 = q_ok ? lane_block_bits((uint32_t)gm.x0, half) : 0u;
+  float bias[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bias[e] = ((cm16 >> e) & 1u) ? 0.f : -INFINITY;
+  uint32_t rows_vis = 0;  // bit r: band row r in this wavefront's row window
+  for (int32_t r = 0; r < by.count; ++r) {
+    int32_t yk = by.start + r;
+    yk -= yk >= H ? H : 0;
+    rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, yk) << r;
+  }
+  rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
+  const int n_vis = __builtin_popcount(rows_vis);
+  auto next_plane = [&](int32_t j) {  // first visit from j whose plane is in the window (uniform)
+    while (j < bz.count && __builtin_amdgcn_readfirstlane((int)bit128(gm.z0, gm.z1, plane_at(j))) == 0) ++j;
+    return j;
+  };
+
+  // LDS read offsets (as in the tile kernel)
+  const int k_swz = chunk_swizzle<D>(col);
+  int v_row[2], v_off[2][DT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v_row[h] = h * 8 + half * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dcol = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      v_off[h][dt] = (((dcol >> 3) ^ chunk_swizzle<D>(v_row[h])) << 3) + (dcol & 7);
+    }
+  }
+
+  f32x16_t oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
+  float m_run = -FLT_MAX, l_run = 0.f;
+  bf16x8_t qf[KB];
+  bool first = true;  // the walk's first step sets the reference maximum: any visible row
+                      // holds a visible key of every query of the row (its column window)
+  for (int32_t i = 0, it = 0, stage = 0; i < bz.count; ++it, stage ^= 1) {
+    const int32_t i_next = next_plane(i + 1);
+    const bool more = i_next < bz.count;
+    // the next plane's rows go into the other stage (last read before the previous barrier);
+    // on the first pass they are issued after the wait, so that Q's wait does not take them in
+    if (it > 0 && more) load_stage(plane_at(i_next), stage ^ 1);
+    if (it > 0 && more)
+      wait_tile_loads<2 * R::LOADS>();
+    else
+      wait_tile_loads<0>();
+    __syncthreads();
+    if (it == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4_t x = qraw[kb];
+        asm volatile("" : "+v"(x));  // keeps the wait for Q after the first stage's copy has been issued
+        x ^= a.q_sign;               // negative scale: flip Q's sign bits, use |scale|
+        qf[kb] = __builtin_bit_cast(bf16x8_t, q_ok ? x : u32x4_t{0, 0, 0, 0});
+      }
+      if (more) load_stage(plane_at(i_next), stage ^ 1);
+    }
+    // this wavefront's visible rows of the stage, four per step (the last step takes the rest)
+    uint32_t rem = rows_vis;
+    for (int left = n_vis; left > 0; left -= SB) {
+      const uint16_t* kb[SB];
+      const uint16_t* vb[SB];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int32_t r = rem != 0u ? __builtin_ctz(rem) : 0;
+        rem &= rem - 1u;
+        kb[sb] = k_lds[stage] + r * 32 * D;
+        vb[sb] = v_lds[stage] + r * 32 * D;
+      }
+      const bool live[SB] = {true, true, true, true};  // visible rows only (and the lane's columns)
+      window_step<D>(kb, vb, live, bias, left < SB ? left : SB, first, qf, c, col, half, k_swz, v_row, v_off, oacc,
+                     m_run, l_run);
+      first = false;
+    }
+    __syncthreads();  // every wavefront is done with this stage before it is refilled
+    i = i_next;
   }
 
   // ---- delayed division and store (lane `col` of the first half-wave also writes the logsumexp)
@@ -1156,6 +1372,12 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
     case MASK_NA_PATCH:
       if constexpr (D == 32 || D == 64) {
         hipLaunchKernelGGL((attn_fwd_na_patch_kernel<D>), dim3(n_wg), dim3(PatchCfg<D>::THREADS), 0, stream, a);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    case MASK_NA_ROWS:
+      if constexpr (D == 32) {
+        hipLaunchKernelGGL((attn_fwd_na_rows_kernel<D>), dim3(n_wg), dim3(256), 0, stream, a);
         return hipGetLastError();
       }
       return hipErrorInvalidValue;

@@ -31,7 +31,8 @@ struct KernelArgs {
   int32_t split_full;   // whole-tile work-groups
   int32_t split_parts;  // parts per split tile
   int32_t causal_group; // causal: heads per XCD dispatched together (causal_item)
-  int32_t patch_nx, patch_ny;  // MASK_NA_PATCH: patches per grid row and per grid column
+  int32_t patch_nx, patch_ny;  // MASK_NA_PATCH: patches per grid row and per grid column;
+                               // MASK_NA_ROWS: patch_ny groups of rows per plane
 };
 
 // Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
@@ -51,6 +52,9 @@ hipError_t static_scratch(void** ptr);
 // Key rows (32 keys each) the patch kernel of 2D neighbourhood windows keeps in LDS for
 // head size d (0: no patch kernel at that size).
 constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 20 : d == 64 ? 17 : 0; }
+
+// Key rows per LDS stage of the row kernel of narrow grids for head size d (0: none).
+constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : 0; }
 
 // Work-groups of the backward kernels resident per CU: two at d <= 64 and one at d = 128
 // (their register and LDS budgets). The causal dispatch order sizes its head groups with it.

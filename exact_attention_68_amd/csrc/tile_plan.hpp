@@ -29,12 +29,16 @@ namespace attn {
 // dilation (an element predicate). The bit-mask kinds cover the common grids:
 // MASK_NA_BLOCKS the 2D, undilated window on grids whose width is a multiple of
 // 32 (at most 128); MASK_NA_GRID any window on grids of width 4..124 whose
-// height and depth are at most 128 (na_grid_eligible). MASK_NA_PATCH, a kernel of
-// its own, takes 2D undilated windows whose patch bands fit its LDS
-// (na_patch_eligible) in query patches instead of query tiles.
-enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3, MASK_NA_GRID = 4, MASK_NA_PATCH = 5 };
+// height and depth are at most 128 (na_grid_eligible). Two kernels of their own
+// take most windows instead of query tiles: MASK_NA_PATCH 2D undilated windows in
+// query patches (na_patch_eligible), MASK_NA_ROWS any window on grids at most 32
+// wide in grid rows (na_rows_eligible).
+enum : int {
+  MASK_NONE = 0, MASK_CAUSAL = 1, MASK_NA = 2, MASK_NA_BLOCKS = 3, MASK_NA_GRID = 4, MASK_NA_PATCH = 5, MASK_NA_ROWS = 6
+};
 constexpr bool is_na(int mask) {
-  return mask == MASK_NA || mask == MASK_NA_BLOCKS || mask == MASK_NA_GRID || mask == MASK_NA_PATCH;
+  return mask == MASK_NA || mask == MASK_NA_BLOCKS || mask == MASK_NA_GRID || mask == MASK_NA_PATCH ||
+         mask == MASK_NA_ROWS;
 }
 
 // Neighbourhood geometry in the form the kernel uses. Token n sits at depth
@@ -387,6 +391,33 @@ constexpr bool na_patch_eligible(const NaGeom& g, int32_t lds_rows) {
   if (na_patch_max_cols(g) > kPatchKeyCols) return false;
   if (g.wrap_h && kPatchRows + 2 * g.rad_h >= g.grid_h) return false;
   return na_patch_max_rows(g) + 3 <= lds_rows;
+}
+
+// ---------------------------------------------------------------------------
+// Grid rows of narrow grids (MASK_NA_ROWS).
+//
+// On a grid at most 32 wide, a wavefront holds one grid row of queries (lane column
+// = grid column; lanes past the width idle) and a work-group 4 consecutive rows of
+// one plane. Every key row is then one 32-key block (its columns, padded with keys
+// read as zero), so a query's window bits in any block are its own column bits, and
+// whether a key row (plane, row) lies in the window is the same for every lane of a
+// wavefront. The work-group streams the planes its windows reach (na_band of its
+// plane) through two LDS stages, each the band of key rows of its 4 rows (na_band
+// of those rows); each wavefront scores only its own visible rows of a stage.
+constexpr int32_t kRowsGroup = 4;
+
+constexpr Band na_rows_band(int32_t y0, const NaGeom& g) {
+  return na_band(y0, imin(y0 + kRowsGroup, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+}
+
+// At most 32 columns (one block per key row), axes of at most 128 cells (the
+// 128-bit window masks), and every group's band of rows within the kernel's
+// `lds_rows` rows per stage.
+constexpr bool na_rows_eligible(const NaGeom& g, int32_t lds_rows) {
+  if (g.grid_w > 32 || g.grid_h > 128 || g.grid_d > 128) return false;
+  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kRowsGroup)
+    if (na_rows_band(y0, g).count > lds_rows) return false;
+  return true;
 }
 
 // 16-bit mask of the accumulator elements of one 32-key block that a lane keeps

@@ -278,6 +278,50 @@ static int check_patch(const NaGeom& g, int lds_rows) {
   return 1;
 }
 
+// The row kernel (MASK_NA_ROWS) as it walks its stages: for every plane, group of
+// rows, wavefront and lane, the cells it marks visible (visible planes of the plane
+// band, visible rows of the group's row band, the lane's column bits) are exactly the
+// query's window, each once; every group's row band fits the stage.
+static int check_rows(const NaGeom& g, int lds_rows) {
+  if (!na_rows_eligible(g, lds_rows)) return 0;
+  const int H = g.grid_h, W = g.grid_w, D = g.grid_d;
+  for (int z = 0; z < D; ++z)
+    for (int y0 = 0; y0 < H; y0 += kRowsGroup) {
+      const Band bz = na_band(z, z, D, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+      const Band by = na_rows_band(y0, g);
+      EXPECT(by.count >= 1 && by.count <= lds_rows && bz.count >= 1 && bz.count <= D, "rows bands %d, %d", by.count,
+             bz.count);
+      for (int w = 0; w < kRowsGroup; ++w) {
+        const int y = y0 + w;
+        if (y >= H) continue;
+        for (int x = 0; x < W; ++x) {
+          const GridMasks gm = na_grid_masks(z, y, x, g);
+          std::vector<int> seen;
+          for (int i = 0; i < bz.count; ++i) {
+            const int zk = (bz.start + i) % D;
+            if (!bit128(gm.z0, gm.z1, zk)) continue;
+            for (int r = 0; r < by.count; ++r) {
+              const int yk = (by.start + r) % H;
+              if (!bit128(gm.y0, gm.y1, yk)) continue;
+              for (int xk = 0; xk < 32; ++xk)
+                if ((((uint32_t)gm.x0 >> xk) & 1u) != 0) {
+                  EXPECT(xk < W, "column bit past the grid width");
+                  seen.push_back((zk * H + yk) * W + xk);
+                }
+            }
+          }
+          const int q = (z * H + y) * W + x;
+          const std::set<int> want = window_keys(g, q), got(seen.begin(), seen.end());
+          EXPECT(got.size() == seen.size() && got == want,
+                 "rows window of query %d: %zu cells (%zu distinct), want %zu (grid %dx%dx%d k %d,%d,%d wrap %d%d%d "
+                 "dil %d,%d,%d)", q, seen.size(), got.size(), want.size(), D, H, W, g.kernel_d, g.kernel_h,
+                 g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w, g.dil_d, g.dil_h, g.dil_w);
+        }
+      }
+    }
+  return 1;
+}
+
 static void check_causal(int Nq, int Nkv, int BM, int BN) {
   const int n_tiles = (int)cdiv(Nkv, BN);
   for (int q0 = 0; q0 < Nq; q0 += BM) {
@@ -568,6 +612,25 @@ int main() {
     EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 20), "dilated windows do not");
     EXPECT(!na_patch_eligible(geom(4, 20, 20, 3, 5, 5, 1, 1, 1, 1, 1, 1), 20), "3D windows do not");
     EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 19, 0, 1, 1, 1, 1, 1), 20), "19 columns wide: the band passes 32");
+  }
+  {
+    // row kernel: narrow 2D and 3D grids, wrap and clamp per axis, dilation
+    int eligible = 0, tried = 0;
+    for (int D : {1, 5})
+      for (int H : {4, 9, 20})
+        for (int W : {7, 20, 32})
+          for (int k : {1, 3, 5})
+            for (int dil : {1, 2})
+              for (int wrap = 0; wrap < 8; ++wrap) {
+                const NaGeom g = geom(D, H, W, D == 1 ? 1 : k, k, k == 1 ? 3 : k, (wrap >> 2) & 1, (wrap >> 1) & 1,
+                                      wrap & 1, D == 1 ? 1 : dil, dil, 1);
+                if (!geom_valid(g)) continue;
+                ++tried;
+                eligible += check_rows(g, 10);
+              }
+    EXPECT(eligible > 100 && eligible < tried, "row-kernel eligibility covers %d of %d shapes", eligible, tried);
+    EXPECT(na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), 10), "20x20x20, 5x5x5 window takes the row kernel");
+    EXPECT(!na_rows_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1), 10), "64 wide does not");
   }
   for (int mask : {MASK_NONE, MASK_CAUSAL})
     for (int BH : {1, 3, 8, 10, 64, 80})
