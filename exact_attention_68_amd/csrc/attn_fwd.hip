@@ -874,9 +874,9 @@ __device__ __forceinline__ void window_step(const uint16_t* const (&kb)[4], cons
 
 template <int D>
 struct PatchCfg {
-  // key rows (32 keys each) of the K and of the V rectangle in LDS: 80 KB in all at
-  // d = 32 (two work-groups per CU), 136 KB at d = 64
-  static constexpr int ROWS = D == 32 ? 20 : 17;
+  // key rows (32 keys each) of the K and of the V rectangle in LDS: 96 KB in all at
+  // d = 32 (114 KB with the two parts' merge area), 136 KB at d = 64
+  static constexpr int ROWS = D == 32 ? 24 : 17;
   static constexpr int PARTS = D == 32 ? 2 : 1;  // wavefronts per query wavefront (step parity)
   static constexpr int THREADS = 256 * PARTS;
   static constexpr int ROW_CHUNKS = D / 8;
@@ -967,26 +967,37 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
 
   // ---- this wavefront's key rows: the band of its two query rows, a run of the patch's band
   const int32_t wy0 = imin(y0 + 2 * wave, H - 1);
-  const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, 1);
+  const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
   int32_t off = wb.start - pb.rows.start;
   off += off < 0 ? H : 0;
   const int32_t n_steps = rows_in ? (wb.count + SB - 1) / SB : 0;
 
-  // The window along an axis is `kernel` consecutive cells from win_start (mod the
-  // axis length when wrapped); in band cells it starts lo cells into the band. Window
-  // bits of the lane's column: bit x for column band cell x (a wrapped window on an
-  // axis no longer than the band runs past the band's end and continues at cell 0).
-  // Element e of a 32-key block of the lane holds cell 8 (e / 4) + 4 half + e % 4.
-  auto win_start = [](int32_t c, int32_t len, int32_t kernel, int32_t rad, int32_t wrap) {
-    return wrap ? c - rad : iclamp(c - rad, 0, len - kernel);
+  // The window along an axis is `kernel` cells `dil` apart from its first cell (the
+  // query's coordinate less rad * dil when wrapped, its anchor when clamped: na_dil_ok;
+  // mod the axis length when wrapped); in band cells it starts lo cells into the band.
+  // Window bits of the lane's column: bit x for column band cell x (a wrapped window on
+  // an axis no longer than the band runs past the band's end and continues at cell 0);
+  // of its row: bit r for band row r. Element e of a 32-key block of the lane holds
+  // column cell 8 (e / 4) + 4 half + e % 4.
+  auto win_first = [](int32_t c, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil) {
+    if (wrap) return c - rad * dil;
+    return dil == 1 ? iclamp(c - rad, 0, len - kernel) : na_dil_anchor(c, len, kernel, rad, wrap, dil);
   };
-  int32_t lo_x = win_start(qx, W, g.kernel_w, g.rad_w, g.wrap_w) - pb.cols.start;
+  // kernel cells dil apart from bit lo (below bit 64): one run of bits when undilated
+  auto cells = [](int32_t lo, int32_t kernel, int32_t dil) -> uint64_t {
+    if (dil == 1) return ((uint64_t{1} << kernel) - 1u) << lo;
+    uint64_t m = 0;
+    for (int32_t t = 0; t < kernel; ++t) m |= uint64_t{1} << (lo + dil * t);
+    return m;
+  };
+  int32_t lo_x = win_first(qx, W, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w) - pb.cols.start;
   lo_x += lo_x < 0 ? W : 0;
-  uint64_t cm64 = ((1ull << g.kernel_w) - 1ull) << lo_x;
+  uint64_t cm64 = cells(lo_x, g.kernel_w, g.dil_w);
   cm64 |= cm64 >> pb.cols.count;  // the wrapped tail (cols.count = W here), else bits past 32 only
   const uint32_t cm = (uint32_t)cm64 & (uint32_t)((1ull << pb.cols.count) - 1ull);
-  int32_t lo_y = win_start(qy, H, g.kernel_h, g.rad_h, g.wrap_h) - pb.rows.start;  // < H: the band holds the window
+  int32_t lo_y = win_first(qy, H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h) - pb.rows.start;  // the band holds the window
   lo_y += lo_y < 0 ? H : 0;
+  const uint32_t rows_w = (uint32_t)cells(lo_y, g.kernel_h, g.dil_h);  // below the band's count (< 32)
   uint32_t cm16 = 0;
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) cm16 |= ((cm >> (8 * g4 + 4 * half)) & 0xFu) << (4 * g4);
@@ -1022,7 +1033,7 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
     for (int sb = 0; sb < SB; ++sb) {
       kb[sb] = k_lds + (r0 + sb) * kPatchKeyCols * D;
       vb[sb] = v_lds + (r0 + sb) * kPatchKeyCols * D;
-      live[sb] = SB * st + sb < wb.count && (uint32_t)(r0 + sb - lo_y) < (uint32_t)g.kernel_h;
+      live[sb] = ((rows_w >> (r0 + sb)) & 1u) != 0u;
     }
     window_step<D>(kb, vb, live, bias, SB, st == part, qf, c, col, half, k_swz, v_row, v_off, oacc, m_run, l_run);
   }

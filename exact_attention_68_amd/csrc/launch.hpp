@@ -51,7 +51,7 @@ hipError_t static_scratch(void** ptr);
 
 // Key rows (32 keys each) the patch kernel of 2D neighbourhood windows keeps in LDS for
 // head size d (0: no patch kernel at that size).
-constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 20 : d == 64 ? 17 : 0; }
+constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 24 : d == 64 ? 17 : 0; }
 
 // Key rows per LDS stage of the row kernel of narrow grids for head size d (0: none).
 constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : 0; }

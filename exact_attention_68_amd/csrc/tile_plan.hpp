@@ -351,7 +351,7 @@ constexpr void na_col_bits(int32_t cq, int32_t half, int32_t W, int32_t kernel, 
 }
 
 // ---------------------------------------------------------------------------
-// Query patches of 2D neighbourhood windows (MASK_NA_PATCH).
+// Query patches of 2D neighbourhood windows (MASK_NA_PATCH), dilated or not.
 //
 // A query tile of consecutive tokens spans whole grid rows, so its wavefronts
 // score every key of the rows their windows reach, most of them outside every
@@ -370,27 +370,24 @@ struct PatchBands {
 };
 
 constexpr PatchBands na_patch_bands(int32_t y0, int32_t x0, const NaGeom& g) {
-  return PatchBands{na_band(y0, imin(y0 + kPatchRows, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, 1),
-                    na_band(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, 1)};
+  return PatchBands{
+      na_band(y0, imin(y0 + kPatchRows, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h),
+      na_band(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w)};
 }
 
-// The most key rows and columns any patch's bands hold.
-constexpr int32_t na_patch_max_rows(const NaGeom& g) {
-  return imin(g.wrap_h ? kPatchRows + 2 * g.rad_h : kPatchRows - 1 + g.kernel_h, g.grid_h);
-}
-constexpr int32_t na_patch_max_cols(const NaGeom& g) {
-  return imin(g.wrap_w ? kPatchCols + 2 * g.rad_w : kPatchCols - 1 + g.kernel_w, g.grid_w);
-}
-
-// One plane, undilated; every column band within one 32-key block; a wrapped row
-// band shorter than the axis (so the band of a wavefront's two rows is one run
-// of its work-group's band); and the band's rows, plus the 3 rows a wavefront's
-// last step of four may read past them, within the kernel's `lds_rows`.
+// One plane; every column band within one 32-key block; a wrapped row band shorter
+// than the axis (so the band of a wavefront's two rows is one run of its
+// work-group's band); and every row band, plus the 3 rows a wavefront's last step
+// of four may read past it, within the kernel's `lds_rows`.
 constexpr bool na_patch_eligible(const NaGeom& g, int32_t lds_rows) {
-  if (g.grid_d != 1 || g.dil_h != 1 || g.dil_w != 1) return false;
-  if (na_patch_max_cols(g) > kPatchKeyCols) return false;
-  if (g.wrap_h && kPatchRows + 2 * g.rad_h >= g.grid_h) return false;
-  return na_patch_max_rows(g) + 3 <= lds_rows;
+  if (g.grid_d != 1) return false;
+  for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols)
+    if (na_patch_bands(0, x0, g).cols.count > kPatchKeyCols) return false;
+  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kPatchRows) {
+    const Band rows = na_patch_bands(y0, 0, g).rows;
+    if (rows.count + 3 > lds_rows || (g.wrap_h && rows.count >= g.grid_h)) return false;
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------------------

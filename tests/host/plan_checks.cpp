@@ -224,7 +224,7 @@ static int check_patch(const NaGeom& g, int lds_rows) {
       for (int w = 0; w < 4; ++w) {
         const int wy0 = y0 + 2 * w;
         if (wy0 >= H) continue;
-        const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, 1);
+        const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
         int off = wb.start - pb.rows.start;
         off += off < 0 ? H : 0;
         const int n_steps = (wb.count + 3) / 4;
@@ -233,18 +233,22 @@ static int check_patch(const NaGeom& g, int lds_rows) {
         for (int col = 0; col < 32; ++col) {
           const int qy = wy0 + col / 16, qx = x0 + col % 16;
           if (qy >= H || qx >= W) continue;
-          // the kernel's window bits: kernel-long runs of band cells from lo_x and lo_y
-          auto win_start = [](int c, int len, int kernel, int rad, int wrap) {
-            return wrap ? c - rad : iclamp(c - rad, 0, len - kernel);
+          // the kernel's window bits: kernel cells dil apart from lo_x and lo_y in band cells
+          auto win_first = [](int c, int len, int kernel, int rad, int wrap, int dil) {
+            return wrap ? c - rad * dil : na_dil_anchor(c, len, kernel, rad, wrap, dil);
           };
-          int lo_x = win_start(qx, W, g.kernel_w, g.rad_w, g.wrap_w) - pb.cols.start;
+          int lo_x = win_first(qx, W, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w) - pb.cols.start;
           lo_x += lo_x < 0 ? W : 0;
-          uint64_t cm64 = ((1ull << g.kernel_w) - 1ull) << lo_x;
+          EXPECT(lo_x >= 0 && lo_x + g.dil_w * (g.kernel_w - 1) < 64, "column window offset %d", lo_x);
+          uint64_t cm64 = 0;
+          for (int t = 0; t < g.kernel_w; ++t) cm64 |= 1ull << (lo_x + g.dil_w * t);
           cm64 |= cm64 >> pb.cols.count;
           const uint32_t cm = (uint32_t)cm64 & (uint32_t)((1ull << pb.cols.count) - 1ull);
-          int lo_y = win_start(qy, H, g.kernel_h, g.rad_h, g.wrap_h) - pb.rows.start;
+          int lo_y = win_first(qy, H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h) - pb.rows.start;
           lo_y += lo_y < 0 ? H : 0;
-          EXPECT(lo_x >= 0 && lo_x < 64 - g.kernel_w && lo_y >= 0 && lo_y < H, "window offsets %d %d", lo_x, lo_y);
+          EXPECT(lo_y >= 0 && lo_y + g.dil_h * (g.kernel_h - 1) < pb.rows.count, "row window offset %d", lo_y);
+          uint32_t rows_w = 0;
+          for (int t = 0; t < g.kernel_h; ++t) rows_w |= 1u << (lo_y + g.dil_h * t);
           std::vector<int> seen;
           bool first_step = false;
           for (int st = 0; st < n_steps; ++st)
@@ -252,7 +256,7 @@ static int check_patch(const NaGeom& g, int lds_rows) {
               const int r = off + 4 * st + sb;
               int ky = pb.rows.start + r;
               ky -= ky >= H ? H : 0;
-              const bool rok = 4 * st + sb < wb.count && (unsigned)(r - lo_y) < (unsigned)g.kernel_h;
+              const bool rok = ((rows_w >> r) & 1u) != 0u;
               for (int x = 0; x < kPatchKeyCols; ++x) {
                 int kx = pb.cols.start + x;
                 kx -= kx >= W ? W : 0;
@@ -265,13 +269,14 @@ static int check_patch(const NaGeom& g, int lds_rows) {
               }
             }
           std::set<int> want;
-          for (int yc : axis_cells(qy, H, g.kernel_h, g.wrap_h, 1))
-            for (int xc : axis_cells(qx, W, g.kernel_w, g.wrap_w, 1)) want.insert(yc * W + xc);
+          for (int yc : axis_cells(qy, H, g.kernel_h, g.wrap_h, g.dil_h))
+            for (int xc : axis_cells(qx, W, g.kernel_w, g.wrap_w, g.dil_w)) want.insert(yc * W + xc);
           const std::set<int> got(seen.begin(), seen.end());
           EXPECT(got.size() == seen.size() && got == want,
                  "patch window of query (%d,%d): %zu cells (%zu distinct), want %zu (grid %dx%d k %d,%d wrap %d%d)", qy, qx,
                  seen.size(), got.size(), want.size(), H, W, g.kernel_h, g.kernel_w, g.wrap_h, g.wrap_w);
-          EXPECT(first_step, "query (%d,%d) sees no key in its first step", qy, qx);
+          // the first step sets the reference maximum; dilated clamped windows may leave it to the guard
+          if (g.dil_h == 1) EXPECT(first_step, "query (%d,%d) sees no key in its first step", qy, qx);
         }
       }
     }
@@ -600,18 +605,20 @@ int main() {
         for (int k : {1, 3, 7, 9, 13, 17, 19})
           for (int wh = 0; wh < 2; ++wh)
             for (int ww = 0; ww < 2; ++ww)
-              for (int lds_rows : {17, 20}) {
-                const NaGeom g = geom(1, H, W, 1, k, k == 1 ? 3 : k - 2, 0, wh, ww, 1, 1, 1);
+              for (int lds_rows : {17, 24}) {
+                const int dil = (k + wh + ww) % 3 == 0 ? 2 : 1;  // a third of the shapes dilated
+                const NaGeom g = geom(1, H, W, 1, k, k == 1 ? 3 : k - 2, 0, wh, ww, 1, dil, dil);
                 if (!geom_valid(g)) continue;
                 ++tried;
                 eligible += check_patch(g, lds_rows);
               }
     EXPECT(eligible > 100 && eligible < tried, "patch eligibility covers %d of %d shapes", eligible, tried);
     const NaGeom c4 = geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1);
-    EXPECT(na_patch_eligible(c4, 20) && na_patch_eligible(c4, 17), "64x64 grid, 7x7 wrapped window takes the patch kernel");
-    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 20), "dilated windows do not");
-    EXPECT(!na_patch_eligible(geom(4, 20, 20, 3, 5, 5, 1, 1, 1, 1, 1, 1), 20), "3D windows do not");
-    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 19, 0, 1, 1, 1, 1, 1), 20), "19 columns wide: the band passes 32");
+    EXPECT(na_patch_eligible(c4, 24) && na_patch_eligible(c4, 17), "64x64 grid, 7x7 wrapped window takes the patch kernel");
+    EXPECT(na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 24), "and with dilation 2 (20 band rows)");
+    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 17), "not in 17 rows");
+    EXPECT(!na_patch_eligible(geom(4, 20, 20, 3, 5, 5, 1, 1, 1, 1, 1, 1), 24), "3D windows do not");
+    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 19, 0, 1, 1, 1, 1, 1), 24), "19 columns wide: the band passes 32");
   }
   {
     // row kernel: narrow 2D and 3D grids, wrap and clamp per axis, dilation
