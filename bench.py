@@ -207,7 +207,7 @@ def live_profile(args, steps_per_call_kernels: int, cus: int) -> dict:
 
     res = {"kernel_trace": None, "mfma_util": None, "traffic_bytes": None}
     # the kernels of one step (the backward run also holds the one forward call made before timing)
-    step_kernel = ("attn_bwd_",) if args.backward else ("attn_fwd_", "attn_merge_kernel")
+    step_kernel = ("attn_bwd_",) if args.backward else ("attn_fwd_", "attn_split_clear_kernel")
     main_kernel = "attn_bwd_dkv" if args.backward else "attn_fwd_"
     if shutil.which("rocprofv3") is None:
         return res
@@ -405,11 +405,11 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # what the event-timed step contains: the attention kernel, plus the merge kernel of a split launch
+    # what the event-timed step contains: the attention kernel, after the counter clear of a split launch
     split = ws is not None and not args.backward
     roof["kernels"] = (f"attn_bwd_dq_kernel<{w.d},{w.mask}> + attn_bwd_dkv_kernel<{w.d},{w.mask}>"
                        if args.backward else
-                       (f"attn_fwd_kernel<{w.d},none,split> + attn_merge_kernel" if split
+                       (f"attn_split_clear_kernel + attn_fwd_kernel<{w.d},none,split>" if split
                         else f"attn_fwd_kernel<{w.d},{w.mask}>"))
     if prof and prof.get("kernel_trace"):  # the names the kernel trace recorded
         roof["kernels"] = " + ".join(prof["kernel_trace"]["kernels"])

@@ -105,6 +105,8 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   }
   if (split != nullptr && split->rem > 0) {
     a.ws_parts = static_cast<float*>(workspace);
+    a.split_count = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) +
+                                                (int64_t)split->slots() * attn::part_slot_bytes(p.d));
     a.split_full = split->full;
     a.split_parts = split->parts;
     n_wg = split->groups();

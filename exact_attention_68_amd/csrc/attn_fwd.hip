@@ -13,8 +13,8 @@
 // 128 tokens (64 at d = 128) stream through LDS rings (2 tiles deep at d = 64
 // and 128, 4 at d = 32) shared by the 4 wavefronts; later tiles' global loads are in flight while
 // the current tile is computed. An unmasked launch may instead run a round of
-// whole tiles plus key-range parts of the remaining tiles, merged by a second
-// small kernel (remainder split, tile_plan.hpp).
+// whole tiles plus key-range parts of the remaining tiles, each tile's parts
+// merged by the last of them to finish (remainder split, tile_plan.hpp).
 //
 // Per key tile and wavefront:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS (A operand), Q held
@@ -137,18 +137,101 @@ static_assert(PartSlot<128>::FLOATS * 4 == part_slot_bytes(128) && PartSlot<64>:
                   PartSlot<32>::FLOATS * 4 == part_slot_bytes(32),
               "workspace slot size and kernel layout must agree");
 
+// A part's slot is written and read with device-coherent accesses (the sc1
+// cache policy: stores write through the XCD's L2, loads read past it), so the
+// parts of a tile meet across XCDs without a writeback or invalidation of a
+// whole L2 (the agent-scope fences, which measured 1.25x slower on SD2.1-512).
+constexpr int kCoherent = 16;  // buffer cache-policy bit sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int D>
 __device__ __forceinline__ void write_part(float* slot, int wave, int lane, const f32x16_t (&o)[D / 32], float m,
                                            float l) {
+  const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slot, PartSlot<D>::FLOATS * 4);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float4 x = make_float4(o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]);
-      *reinterpret_cast<float4*>(slot + (((wave * (D / 32) + dt) * 4 + g) * 64 + lane) * 4) = x;
+      const u32x4_t x = {__float_as_uint(o[dt][4 * g]), __float_as_uint(o[dt][4 * g + 1]),
+                         __float_as_uint(o[dt][4 * g + 2]), __float_as_uint(o[dt][4 * g + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(x, rs, (((wave * (D / 32) + dt) * 4 + g) * 64 + lane) * 16, 0, kCoherent);
     }
-  slot[PartSlot<D>::M + wave * 64 + lane] = m;
-  slot[PartSlot<D>::L + wave * 64 + lane] = l;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs, (PartSlot<D>::M + wave * 64 + lane) * 4, 0, kCoherent);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs, (PartSlot<D>::L + wave * 64 + lane) * 4, 0, kCoherent);
+}
+
+// Combines the parts of split tile r and stores the tile (run by the work-group
+// of its last part to finish). Wavefront w takes the tile's rows 32 w .. 32 w +
+// 31 with the lanes of write_part. Every part is rescaled to the largest of the
+// parts' maxima and the parts are summed in part order, so the result does not
+// depend on which part finished last; then the division by the row sum and the
+// bfloat16 store of a whole tile. Parts are read one at a time (the registers
+// hold one part's rows and the sums).
+template <int D>
+__device__ __forceinline__ void merge_parts(const KernelArgs& a, int32_t r, int wave, int lane) {
+  constexpr int DT = D / 32;
+  constexpr uint32_t SLOT = PartSlot<D>::FLOATS * 4;  // bytes
+  const int col = lane & 31, half = lane >> 5;
+  const int32_t parts = a.split_parts;
+  const __amdgpu_buffer_rsrc_t rs = slot_rsrc(a.ws_parts + (size_t)r * parts * PartSlot<D>::FLOATS, parts * SLOT);
+  const uint32_t row = (wave * 64 + lane) * 4;
+  float m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, PartSlot<D>::M * 4 + row, 0, kCoherent));
+  for (int32_t p = 1; p < parts; ++p)
+    m = fmaxf(m, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, p * SLOT + PartSlot<D>::M * 4 + row, 0,
+                                                                      kCoherent)));
+  float l = 0.f;
+  float o[DT][16];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  for (int32_t p = 0; p < parts; ++p) {
+    u32x4_t x[DT][4];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        x[dt][g] = __builtin_amdgcn_raw_buffer_load_b128(rs, p * SLOT + (((wave * DT + dt) * 4 + g) * 64 + lane) * 16,
+                                                         0, kCoherent);
+    const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, p * SLOT + PartSlot<D>::M * 4 + row, 0,
+                                                                          kCoherent));
+    const float lp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, p * SLOT + PartSlot<D>::L * 4 + row, 0,
+                                                                          kCoherent));
+    const float w = __builtin_amdgcn_exp2f(mp - m);
+    l += w * lp;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[dt][4 * g + e] += w * __uint_as_float(x[dt][g][e]);
+  }
+  const int32_t tile = a.split_full + r;
+  const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
+  const int32_t my_q = qtile * Cfg<D>::BM + wave * 32 + col;
+  const float l_tot = swap_halves_sum(l);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (my_q < a.Nq) {
+    if (a.lse != nullptr && half == 0) a.lse[(size_t)bh * a.Nq + my_q] = row_lse(m, l_tot);
+    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)a.Nq * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[dt][g * 4 + e] * inv);
+        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + dt * 32 + g * 8 + half * 4) = __builtin_bit_cast(u32x2_t, ob);
+      }
+  }
+}
+
+// Zeroes the arrival counters of a split launch (queued just before it).
+__global__ __launch_bounds__(256) void attn_split_clear_kernel(uint32_t* count, int32_t n) {
+  for (int32_t i = threadIdx.x; i < n; i += 256) count[i] = 0u;
 }
 
 template <int D, int MASK, bool SPLIT>
@@ -743,14 +826,33 @@ void attn_fwd_kernel(KernelArgs a) {
     // Remainder split (unmasked problems): whole tiles first, XCD-contiguous so
     // the tiles of one head share an L2; then the parts of the split tiles,
     // each of which leaves its partial result in its own workspace slot.
+    // The parts are XCD-contiguous too, so a tile's parts (and its merge) share an L2.
     const int32_t full = a.split_full, parts = a.split_parts;
     const bool whole = (int32_t)blockIdx.x < full;
-    const int32_t slot = blockIdx.x - full;  // part slot (parts only)
-    const int32_t tile = whole ? xcd_contiguous(blockIdx.x, full) : full + slot / parts;
+    const int32_t slot = whole ? 0 : xcd_contiguous(blockIdx.x - full, gridDim.x - full);  // parts only
+    const int32_t r = slot / parts;  // split tile (parts only)
+    const int32_t tile = whole ? xcd_contiguous(blockIdx.x, full) : full + r;
     const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
     segment(bh, qtile, whole ? KvRun{0, n_kv} : part_run(n_kv, parts, slot % parts), oacc, m_run, l_run);
-    if (whole) store_rows(bh, qtile, oacc, m_run, l_run);
-    else write_part<D>(a.ws_parts + (size_t)slot * PartSlot<D>::FLOATS, wave, lane, oacc, m_run, l_run);
+    if (whole) {
+      store_rows(bh, qtile, oacc, m_run, l_run);
+      return;
+    }
+    write_part<D>(a.ws_parts + (size_t)slot * PartSlot<D>::FLOATS, wave, lane, oacc, m_run, l_run);
+    // The tile's last part to finish merges it. Every wavefront waits until
+    // its write-through slot stores have completed; then the work-group counts
+    // one arrival on the tile's counter (an agent-scope atomic; the counters
+    // are zeroed by the clear kernel queued before this one). The work-group
+    // that brings the count to `parts` comes after every part's completed
+    // stores, and reads the slots past its L2 (merge_parts).
+    __shared__ uint32_t last_part;
+    wait_tile_loads<0>();  // vmcnt(0): this wavefront's slot stores are done
+    __syncthreads();
+    if (tid == 0)
+      last_part = __hip_atomic_fetch_add(a.split_count + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)parts - 1;
+    __syncthreads();
+    if (last_part) merge_parts<D>(a, r, wave, lane);
   }
 }
 
@@ -1273,82 +1375,6 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
   }
 }
 
-// Second kernel of a split launch: one wavefront per (split tile, wavefront
-// slice of the tile, half of the head dimension at d = 128). It reads every
-// part's maximum and row sum, rescales all parts to the largest maximum, sums
-// them in part order (so the result does not depend on timing) and writes the
-// rows. The parts were written by the previous kernel on the same stream, so
-// plain loads see them.
-template <int D>
-constexpr int kMergeSlices = D == 128 ? 2 : 1;  // d-slices per wavefront slice (keeps the loads in registers)
-
-template <int D, int PARTS>
-__global__ __launch_bounds__(64) void attn_merge_kernel(KernelArgs a) {
-  constexpr int DS = kMergeSlices<D>;
-  constexpr int DT = D / 32, DTB = DT / DS;
-  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
-  const int32_t ds = blockIdx.x % DS, rw = blockIdx.x / DS;
-  const int32_t r = rw >> 2, wave = rw & 3;
-  const float* slots = a.ws_parts + (size_t)r * PARTS * PartSlot<D>::FLOATS;
-  // every load is unconditional, so all parts are in flight together
-  float mp[PARTS], lp[PARTS];
-  float4 x[PARTS][DTB][4];
-#pragma unroll
-  for (int p = 0; p < PARTS; ++p) {
-    const float* slot = slots + (size_t)p * PartSlot<D>::FLOATS;
-    mp[p] = slot[PartSlot<D>::M + wave * 64 + lane];
-    lp[p] = slot[PartSlot<D>::L + wave * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < DTB; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        x[p][i][g] =
-            *reinterpret_cast<const float4*>(slot + (((wave * DT + ds * DTB + i) * 4 + g) * 64 + lane) * 4);
-  }
-  float m = mp[0];
-#pragma unroll
-  for (int p = 1; p < PARTS; ++p) m = fmaxf(m, mp[p]);
-  float l = 0.f;
-  float o[DTB][16];
-#pragma unroll
-  for (int i = 0; i < DTB; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-#pragma unroll
-  for (int p = 0; p < PARTS; ++p) {
-    const float w = __builtin_amdgcn_exp2f(mp[p] - m);
-    l += w * lp[p];
-#pragma unroll
-    for (int i = 0; i < DTB; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        o[i][4 * g] += w * x[p][i][g].x;
-        o[i][4 * g + 1] += w * x[p][i][g].y;
-        o[i][4 * g + 2] += w * x[p][i][g].z;
-        o[i][4 * g + 3] += w * x[p][i][g].w;
-      }
-  }
-  const int32_t tile = a.split_full + r;
-  const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
-  const int32_t my_q = qtile * Cfg<D>::BM + wave * 32 + col;
-  const float l_tot = swap_halves_sum(l);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_q < a.Nq) {
-    if (a.lse != nullptr && half == 0 && ds == 0) a.lse[(size_t)bh * a.Nq + my_q] = row_lse(m, l_tot);
-    uint16_t* __restrict__ oh = a.o + (size_t)bh * (size_t)a.Nq * D;
-#pragma unroll
-    for (int i = 0; i < DTB; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4_t ob;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)(o[i][g * 4 + e] * inv);
-        *reinterpret_cast<u32x2_t*>(oh + (size_t)my_q * D + (ds * DTB + i) * 32 + g * 8 + half * 4) =
-            __builtin_bit_cast(u32x2_t, ob);
-      }
-  }
-}
-
 template <int D, int MASK, bool SPLIT>
 static hipError_t launch_one(const KernelArgs& a, int32_t n_wg, hipStream_t stream) {
   hipLaunchKernelGGL((attn_fwd_kernel<D, MASK, SPLIT>), dim3(n_wg), dim3(Cfg<D>::THREADS), 0, stream, a);
@@ -1357,22 +1383,11 @@ static hipError_t launch_one(const KernelArgs& a, int32_t n_wg, hipStream_t stre
 
 template <int D>
 static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream) {
-  if (a.ws_parts != nullptr) {  // remainder split, no mask
-    const hipError_t e = launch_one<D, MASK_NONE, true>(a, n_wg, stream);
+  if (a.ws_parts != nullptr) {  // remainder split, no mask: the counters, then the parts' kernel
+    hipLaunchKernelGGL(attn_split_clear_kernel, dim3(1), dim3(256), 0, stream, a.split_count, rem);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid(rem * Cfg<D>::WAVES * kMergeSlices<D>), block(64);
-    static_assert(kMaxParts == 8, "one merge kernel per part count");
-    switch (a.split_parts) {
-      case 2: hipLaunchKernelGGL((attn_merge_kernel<D, 2>), grid, block, 0, stream, a); break;
-      case 3: hipLaunchKernelGGL((attn_merge_kernel<D, 3>), grid, block, 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((attn_merge_kernel<D, 4>), grid, block, 0, stream, a); break;
-      case 5: hipLaunchKernelGGL((attn_merge_kernel<D, 5>), grid, block, 0, stream, a); break;
-      case 6: hipLaunchKernelGGL((attn_merge_kernel<D, 6>), grid, block, 0, stream, a); break;
-      case 7: hipLaunchKernelGGL((attn_merge_kernel<D, 7>), grid, block, 0, stream, a); break;
-      case 8: hipLaunchKernelGGL((attn_merge_kernel<D, 8>), grid, block, 0, stream, a); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return launch_one<D, MASK_NONE, true>(a, n_wg, stream);
   }
   switch (mask) {
     case MASK_NONE: return launch_one<D, MASK_NONE, false>(a, n_wg, stream);

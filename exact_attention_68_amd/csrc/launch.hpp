@@ -27,7 +27,8 @@ struct KernelArgs {
   float na_inv_h;     // 1 / grid_h, rounded to float
   int32_t na_phases;  // grid_w / 32 for the block-masked kernel, else 0
   // remainder split (SplitPlan; ws_parts null = one work-group per query tile)
-  float* ws_parts;      // rem * parts slots of part_slot_bytes(d)
+  float* ws_parts;       // rem * parts slots of part_slot_bytes(d)
+  uint32_t* split_count; // rem arrival counters (after the slots), zeroed before the launch
   int32_t split_full;   // whole-tile work-groups
   int32_t split_parts;  // parts per split tile
   int32_t causal_group; // causal: heads per XCD dispatched together (causal_item)
@@ -37,13 +38,16 @@ struct KernelArgs {
 
 // Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
 constexpr int64_t part_slot_bytes(int64_t d) { return (4 * (d / 32) * 4 * 64 * 4 + 2 * 4 * 64) * 4; }
+// Bytes of the arrival counters of `rem` split tiles (one 32-bit word each, whole 256-byte lines).
+constexpr int64_t split_count_bytes(int64_t rem) { return (rem * 4 + 255) / 256 * 256; }
 constexpr int64_t split_workspace_bytes(const SplitPlan& p, int64_t d) {
-  return p.rem > 0 ? (int64_t)p.slots() * part_slot_bytes(d) : 0;
+  return p.rem > 0 ? (int64_t)p.slots() * part_slot_bytes(d) + split_count_bytes(p.rem) : 0;
 }
 
 // Bytes of the device scratch of attn_fwd_ex_static: the split workspace of the largest
-// plan on a device of up to 256 CUs (at most one part slot per CU, d = 128 slots).
-constexpr int64_t kStaticScratchBytes = 256 * part_slot_bytes(128);
+// plan on a device of up to 256 CUs (at most one part slot per CU, d = 128 slots, and
+// fewer than 256 split tiles).
+constexpr int64_t kStaticScratchBytes = 256 * part_slot_bytes(128) + split_count_bytes(256);
 
 // Device address of this device's static scratch (file-scope __device__ array,
 // looked up once per device with hipGetSymbolAddress and cached).
@@ -95,9 +99,10 @@ struct BwdArgs {
 hipError_t launch_bwd(const BwdArgs& a, int32_t d, int32_t mask, hipStream_t stream);
 
 // Launches the kernel for head size d (32, 64 or 128) and kernel mask `mask`
-// (MASK_*). With a.ws_parts set (unmasked problems only), n_wg = full + rem *
-// parts work-groups run the whole tiles and the parts, and a second kernel of
-// rem work-groups merges the parts, both on `stream`.
+// (MASK_*). With a.ws_parts set (unmasked problems only), a one-work-group
+// kernel zeroes the rem arrival counters, then n_wg = full + rem * parts
+// work-groups run the whole tiles and the parts (each tile's last part merges
+// it), both on `stream`.
 hipError_t launch_fwd(const KernelArgs& a, int32_t d, int32_t mask, int32_t n_wg, int32_t rem, hipStream_t stream);
 
 }  // namespace attn

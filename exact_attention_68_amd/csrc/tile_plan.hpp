@@ -495,15 +495,16 @@ constexpr WorkItem work_item(int mask, int32_t wg, int32_t n_wg, int32_t n_qtile
 // work-group of its own that sits beside a whole-tile work-group on some CU.
 // With rem * parts close to the CU count every CU then does about the same
 // work. A part ends in a partial result (the unnormalised output rows, the
-// running maximum and the row sums over its keys); a second, small kernel
-// combines the parts of each tile exactly (the rescaling by 2^(m_i - m) of the
+// running maximum and the row sums over its keys) in a workspace slot; the
+// work-group of the tile's last part to finish (an arrival counter per split
+// tile) combines the parts exactly (the rescaling by 2^(m_i - m) of the
 // running-softmax paragraph of PhotoRoom's xformers post, applied across
-// parts) and writes it.
+// parts) and writes the tile, while whole tiles are still running.
 //
 // Tiles are numbered head-major (tile = bh * n_qtiles + qtile). Work-group g <
-// full takes a whole tile; work-group full + r * parts + p takes part p of tile
-// full + r, which covers key tiles [p * n_kv / parts, (p + 1) * n_kv / parts)
-// and writes workspace slot r * parts + p.
+// full takes a whole tile; the other work-groups take the rem * parts part
+// slots (XCD-contiguous), slot r * parts + p being part p of tile full + r,
+// which covers key tiles [p * n_kv / parts, (p + 1) * n_kv / parts).
 struct SplitPlan {
   int32_t full;   // whole tiles (work-groups 0 .. full - 1)
   int32_t rem;    // split tiles; 0 = no split

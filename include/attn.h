@@ -161,10 +161,13 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
  * problems of fewer than two tiles per CU, this entry point keeps one
  * work-group per tile for a whole round of tiles and cuts each remaining
  * tile along its keys into parts that run beside them, so every CU does
- * about the same work; a second, small kernel on the same stream combines
- * the parts of each such tile exactly (the running-softmax rescaling of
- * PhotoRoom's xformers post, running-softmax paragraph, applied between
- * parts). The result equals attn_fwd's up to floating-point summation order.
+ * about the same work; the last part of each such tile to finish combines
+ * the parts exactly (the running-softmax rescaling of PhotoRoom's xformers
+ * post, running-softmax paragraph, applied between parts) and stores the
+ * tile. The parts meet through one arrival counter per split tile in the
+ * workspace, which a one-work-group kernel queued on the same stream just
+ * before zeroes. The result equals attn_fwd's up to floating-point summation
+ * order, and does not depend on which part finishes last.
  * Other problems (causal and neighbourhood masks, tile counts that fill
  * the chip for two or more rounds, or that would cut a tile into parts of
  * fewer than 2 key tiles) run exactly as attn_fwd with one kernel, and the
@@ -179,8 +182,9 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,
  * workspace_bytes : its size in bytes.
  *
  * The size depends on the current device (its CU count) and the head size;
- * it is at most the CU count x 18, 34 or 66 KB for d = 32, 64 or 128 (about
- * 8.9 MB at d = 64 on an MI355X). Returns the codes of attn_fwd, and
+ * it is at most the CU count x 18, 34 or 66 KB for d = 32, 64 or 128, plus
+ * 4 bytes per split tile rounded up to 256 (about 8.9 MB at d = 64 on an
+ * MI355X). Returns the codes of attn_fwd, and
  * ATTN_ERR_WORKSPACE for a workspace that does not meet the above; all
  * argument errors are detected before any device work.
  * The library still allocates nothing.
@@ -258,7 +262,7 @@ attn_status_t attn_fwd_ex_check(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, i
  * up to 256 CUs) fail with ATTN_ERR_SCRATCH before any device work; other errors
  * are those of attn_fwd_ex.
  */
-#define ATTN_STATIC_SCRATCH_BYTES 17301504  /* 256 part slots of the d = 128 kernel */
+#define ATTN_STATIC_SCRATCH_BYTES 17302528  /* 256 part slots of the d = 128 kernel + 256 counters */
 attn_status_t attn_fwd_ex_static(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
                                  int32_t mask_mode, const void* params, void* stream);

@@ -4,9 +4,10 @@ torch.profiler (no relaunch, no second process).
 The fused forward is one kernel: the score matrix never reaches memory and nothing
 is copied or cleared on the device ("Profiling in PyTorch", the efficient SDPA
 backend: one fused kernel per forward; and the in-place masked_fill_ section: an
-out-of-place mask costs an extra Memcpy kernel). attn_fwd_ws / attn_fwd_ex add the
-merge kernel only when they split key ranges; attn_bwd is two kernels (dQ, then dK
-and dV).
+out-of-place mask costs an extra Memcpy kernel). attn_fwd_ws / attn_fwd_ex queue a
+one-work-group kernel that zeroes the split tiles' arrival counters before the
+attention kernel only when they split key ranges (the parts are merged inside the
+attention kernel); attn_bwd is two kernels (dQ, then dK and dV).
 """
 import pytest
 import torch
@@ -62,8 +63,8 @@ def test_attn_fwd_is_one_kernel(mask):
 
 @pytest.mark.parametrize("N,expect", [(4096, 2), (1000, 2), (9216, 1)])
 def test_attn_fwd_ws_dispatches(N, expect):
-    """SD2.1-512 (320 query tiles) and a 1000-token problem split (attention + merge); SD2.1-768
-    (720 tiles, more than two per CU) does not."""
+    """SD2.1-512 (320 query tiles) and a 1000-token problem split (counter clear + attention);
+    SD2.1-768 (720 tiles, more than two per CU) does not."""
     import exact_attention_68_amd as A
 
     B, H, d = (2, 5, 64) if N != 1000 else (1, 2, 64)
@@ -73,7 +74,9 @@ def test_attn_fwd_ws_dispatches(N, expect):
     kernels, others = _split(_dispatches(lambda: A.attn_fwd_ws(q, k, v, o, 0.125, A.ATTN_MASK_NONE, None, ws)))
     assert len(kernels) == expect, kernels
     if expect == 2:
-        assert "attn_fwd_kernel" in kernels[0] and "attn_merge_kernel" in kernels[1], kernels
+        assert "attn_split_clear_kernel" in kernels[0] and "attn_fwd_kernel" in kernels[1], kernels
+    else:
+        assert "attn_fwd_kernel" in kernels[0], kernels
     assert others == [], others
 
 
