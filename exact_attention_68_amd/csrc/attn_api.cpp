@@ -263,6 +263,11 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     a.na_inv_h = 1.0f / (float)a.na.grid_h;
     a.na_grid = attn::na_grid_eligible(a.na) ? 1 : 0;
     mask = attn::MASK_NA;
+    const int32_t dq_lds = attn::bwd_dq_rows_lds(d), dkv_lds = attn::bwd_dkv_rows_lds(d);
+    a.row_groups = (int32_t)attn::cdiv(a.na.grid_h, attn::kRowsGroup);
+    const bool groups_fit = (int64_t)a.BH * a.na.grid_d * a.row_groups <= INT32_MAX;
+    a.dq_rows = groups_fit && dq_lds > 0 && attn::na_rows_eligible(a.na, dq_lds) ? 1 : 0;
+    a.dkv_rows = groups_fit && dkv_lds > 0 && attn::na_rows_reverse_eligible(a.na, dkv_lds) ? 1 : 0;
   }
   const hipError_t e = attn::launch_bwd(a, (int32_t)d, mask, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

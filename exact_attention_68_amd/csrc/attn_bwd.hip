@@ -583,16 +583,373 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   store_rows_scaled<D>(a.dv + khead * D, my_k, Nkv, half, dv, 1.0f);
 }
 
+// ---------------------------------------------------------------------------
+// Neighbourhood windows on grids at most 32 wide (na_rows_eligible,
+// na_rows_reverse_eligible): the forward row kernel's layout. A work-group holds
+// 4 rows of one plane, a wavefront one row and a lane one column (lanes past the
+// width idle); the band rows of each plane that the work-group's windows reach
+// stream through two LDS stages (32 tokens per row, columns past the width read
+// as zero); each wavefront visits only its own visible rows, in order, and the
+// window test inside a row is the lane's per-element addend of the exponent (-inf
+// for a hidden pair). A visible row is one 32-row block of the tile kernels'
+// products. Stage ring: wait for this stage, barrier (which also frees the other
+// stage), issue the next stage, compute.
+
+// ROWS rows of 32 tokens of D elements, copied in whole rounds of 256 lanes.
+template <int D, int ROWS_>
+struct RowStage {
+  static constexpr int ROWS = ROWS_;
+  static constexpr int RC = D / 8;  // 16-byte chunks per token
+  static constexpr int CHUNKS = ROWS * 32 * RC;
+  static_assert(ROWS > 0 && CHUNKS % 256 == 0, "a stage is copied in whole rounds of 256 lanes");
+  static constexpr int LOADS = CHUNKS / 256;  // per lane, stage and tensor
+  static constexpr int ELEMS = CHUNKS * 8;
+};
+
+// Copies rows [by.start, by.start + by.count) (mod H) of plane z of two tensors of
+// one head into a stage each: LDS chunk p holds chunk (p % RC) ^ swizzle of token
+// p / RC = 32 r + x (band row r, column x), the tile layout; columns past W and
+// rows past the band read as zero (an offset past the head).
+template <int D, int ROWS>
+__device__ __forceinline__ void load_row_stage(i32x4_t ra, i32x4_t rb, const uint16_t* la, const uint16_t* lb,
+                                               int32_t z, Band by, int32_t H, int32_t W, uint32_t head_bytes,
+                                               int wave, int tid) {
+  using R = RowStage<D, ROWS>;
+  const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds_addr(la) + wave * 1024);
+  const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds_addr(lb) + wave * 1024);
+#pragma unroll
+  for (int j = 0; j < R::LOADS; ++j) {
+    const int32_t p = j * 256 + tid;
+    const int32_t tok = p / R::RC, r = tok / 32, x = tok % 32;
+    const int32_t chunk = (p % R::RC) ^ chunk_swizzle<D>(tok);
+    uint32_t voff = head_bytes;
+    if (r < by.count && x < W) {
+      int32_t y = by.start + r;
+      y -= y >= H ? H : 0;
+      voff = (uint32_t)((z * H + y) * W + x) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
+    }
+    dma_lds16(ra, a_base + (uint32_t)j * 4096u, voff, 0u);
+    dma_lds16(rb, b_base + (uint32_t)j * 4096u, voff, 0u);
+  }
+}
+
+// The band cell of plane index j of a walk that starts at the work-group's own
+// plane and runs through the band circularly.
+__device__ __forceinline__ int32_t band_plane(const Band& bz, int32_t i_own, int32_t j, int32_t len) {
+  int32_t i = i_own + j;
+  i -= i >= bz.count ? bz.count : 0;
+  const int32_t c = bz.start + i;
+  return c >= len ? c - len : c;
+}
+
+// dQ by query rows: per visible key row (32 keys) S^T = K Q^T, dP^T = V dO^T,
+// P = 2^(c s - lse2) (hidden keys 0), dS = P (dP - D), dQ^T += K^T dS^T; also
+// forms D of its queries for the dK/dV kernel, as the tile kernel does.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dq_rows_kernel(BwdArgs a) {
+  using R = RowStage<D, bwd_dq_rows_lds(D)>;
+  constexpr int KB = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][R::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][R::ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const NaGeom& g = a.na;
+  const int32_t H = g.grid_h, W = g.grid_w, N = a.Nq;
+
+  // (head, plane, group of 4 rows), the items of one head kept on one XCD
+  const int32_t groups = a.row_groups, per_head = g.grid_d * groups;
+  const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int32_t bh = item / per_head, rest = item - bh * per_head;
+  const int32_t z = rest / groups, y0 = (rest - z * groups) * kRowsGroup;
+  const int32_t y = y0 + wave;  // this wavefront's grid row
+  const bool row_in = y < H;
+  const bool q_ok = row_in && col < W;
+  const int32_t my_q = (z * H + y) * W + col;
+  const int32_t q_row = q_ok ? my_q : N;  // past the last row: zero fragments, no store
+  const size_t head = (size_t)bh * (size_t)N;
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+
+  const Band bz = na_band(z, z, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+  const Band by = na_rows_band(y0, g);  // by.count <= R::ROWS
+  int32_t i_own = z - bz.start;  // the own plane is in its windows: its stage goes first
+  i_own += i_own < 0 ? g.grid_d : 0;
+  const i32x4_t k_rsrc = head_rsrc(a.k + head * D, head_bytes);
+  const i32x4_t v_rsrc = head_rsrc(a.v + head * D, head_bytes);
+  load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[0], v_lds[0], z, by, H, W, head_bytes, wave, tid);
+
+  // scale < 0: Q's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
+  bf16x8_t qf[KB], gf[KB];
+  row_fragment<D>(a.q + head * D, q_row, N, a.q_sign, half, qf);
+  row_fragment<D>(a.dout + head * D, q_row, N, 0u, half, gf);
+
+  // window per axis; the lane's columns as the exponent's addend: -lse2 for a key
+  // in the window, -inf for the rest (and for a lane outside the grid)
+  const GridMasks gm = na_grid_masks(z, imin(y, H - 1), imin(col, W - 1), g);
+  const float l2 = q_ok ? a.lse[head + my_q] * kLog2e : 0.f;
+  const uint32_t cm16 = q_ok ? lane_block_bits((uint32_t)gm.x0, half) : 0u;
+  float add[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) add[e] = ((cm16 >> e) & 1u) ? -l2 : -INFINITY;
+  uint32_t rows_vis = 0;  // bit r: band row r in this wavefront's row window
+  for (int32_t r = 0; r < by.count; ++r) {
+    int32_t yk = by.start + r;
+    yk -= yk >= H ? H : 0;
+    rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, yk) << r;
+  }
+  rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
+  auto next_plane = [&](int32_t j) {  // first visit from j whose plane is in the window (uniform)
+    while (j < bz.count &&
+           __builtin_amdgcn_readfirstlane((int)bit128(gm.z0, gm.z1, band_plane(bz, i_own, j, g.grid_d))) == 0)
+      ++j;
+    return j;
+  };
+
+  float dlt;
+  {
+    bf16x8_t of[KB];
+    row_fragment<D>(a.o + head * D, q_row, N, 0u, half, of);
+    dlt = swap_halves_sum(row_delta_part<D>(of, gf));
+    if (q_ok && half == 0) a.delta[head + my_q] = dlt;
+  }
+
+  int v_row[2], v_off[2][DT];
+  transpose_offsets<D>(lane, half, v_row, v_off);
+  const int swz = chunk_swizzle<D>(col);
+  f32x16_t dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16_t{};
+
+  for (int32_t i = 0, stage = 0; i < bz.count; stage ^= 1) {
+    const int32_t i_next = next_plane(i + 1);
+    const bool more = i_next < bz.count;
+    wait_tile_loads<0>();  // this stage has landed
+    __syncthreads();       // published; the other stage was last read before this barrier
+    if (!kSerialTiles && more)
+      load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[stage ^ 1], v_lds[stage ^ 1],
+                                 band_plane(bz, i_own, i_next, g.grid_d), by, H, W, head_bytes, wave, tid);
+    // the wavefront's visible rows of the stage, in order: the next row's products are
+    // issued before this row's exponentials
+    const uint16_t* ks = k_lds[stage];
+    const uint16_t* vs = v_lds[stage];
+    uint32_t rem = rows_vis;
+    if (rem != 0u) {
+      int32_t r = __builtin_ctz(rem);
+      f32x16_t s_nx = block_product<D>(ks + r * 32 * D, 0, col, half, swz, qf);
+      f32x16_t dp_nx = block_product<D>(vs + r * 32 * D, 0, col, half, swz, gf);
+      while (true) {
+        const f32x16_t s = s_nx, dp = dp_nx;
+        const int32_t rc = r;
+        rem &= rem - 1u;
+        const bool nxt = rem != 0u;
+        if (nxt) {
+          r = __builtin_ctz(rem);
+          s_nx = block_product<D>(ks + r * 32 * D, 0, col, half, swz, qf);
+          dp_nx = block_product<D>(vs + r * 32 * D, 0, col, half, swz, gf);
+        }
+        f32x16_t ds;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, add[e]));
+          ds[e] = p * (dp[e] - dlt);
+        }
+        bf16x8_t dsb[2];
+        to_bf16_operand(ds, dsb);
+        block_transpose_product<D>(ks + rc * 32 * D, 0, v_row, v_off, dsb, dq);
+        if (!nxt) break;
+      }
+    }
+    if (kSerialTiles && more)  // race check: the next stage's loads only after this stage's compute
+      load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[stage ^ 1], v_lds[stage ^ 1],
+                                 band_plane(bz, i_own, i_next, g.grid_d), by, H, W, head_bytes, wave, tid);
+    i = i_next;
+  }
+  store_rows_scaled<D>(a.dq + head * D, q_row, N, half, dq, a.scale);
+}
+
+// dK and dV by key rows: a work-group holds 4 key rows of one plane and streams
+// the query rows whose windows reach them (na_band_reverse per axis, the key's
+// reverse window masks deciding); per visible query row (32 queries) S = Q K^T,
+// dP = dO V^T, P = 2^(c s - lse2) (hidden pairs 0), dS = P (dP - D), dV^T +=
+// dO^T P, dK^T += Q^T dS. Each stage also holds its queries' lse2 and D.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dkv_rows_kernel(BwdArgs a) {
+  using R = RowStage<D, bwd_dkv_rows_lds(D)>;
+  constexpr int KB = D / 16, DT = D / 32, TOK = R::ROWS * 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][R::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds[2][R::ELEMS];
+  __shared__ __attribute__((aligned(16))) float l2_lds[2][TOK];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][TOK];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const NaGeom& g = a.na;
+  const int32_t H = g.grid_h, W = g.grid_w, N = a.Nkv;
+
+  const int32_t groups = a.row_groups, per_head = g.grid_d * groups;
+  const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int32_t bh = item / per_head, rest = item - bh * per_head;
+  const int32_t z = rest / groups, y0 = (rest - z * groups) * kRowsGroup;
+  const int32_t y = y0 + wave;  // this wavefront's key row
+  const bool row_in = y < H;
+  const bool k_ok = row_in && col < W;
+  const int32_t my_k = (z * H + y) * W + col;
+  const int32_t k_row = k_ok ? my_k : N;
+  const size_t head = (size_t)bh * (size_t)N;
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+
+  const Band bz = na_band_reverse(z, z, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+  const Band by = na_rows_reverse_band(y0, g);  // by.count <= R::ROWS
+  int32_t i_own = z - bz.start;  // a key's own plane sees it: its stage goes first
+  i_own += i_own < 0 ? g.grid_d : 0;
+  const i32x4_t q_rsrc = head_rsrc(a.q + head * D, head_bytes);
+  const i32x4_t g_rsrc = head_rsrc(a.dout + head * D, head_bytes);
+  // lse2 and D of the stage's tokens (thread t < TOK: token t = 32 r + x), +inf and 0
+  // past the band and the width (P = 0 there)
+  auto stats = [&](int32_t zq, float& l2v, float& dlv) {
+    l2v = INFINITY;
+    dlv = 0.f;
+    const int32_t r = tid / 32, x = tid % 32;
+    if (tid < TOK && r < by.count && x < W) {
+      int32_t yq = by.start + r;
+      yq -= yq >= H ? H : 0;
+      const int32_t qi = (zq * H + yq) * W + x;
+      l2v = a.lse[head + qi] * kLog2e;
+      dlv = a.delta[head + qi];
+    }
+  };
+  load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[0], g_lds[0], z, by, H, W, head_bytes, wave, tid);
+  float l2n, dln;
+  stats(z, l2n, dln);
+
+  // scale < 0: K's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
+  bf16x8_t kf[KB], vf[KB];
+  row_fragment<D>(a.k + head * D, k_row, N, a.q_sign, half, kf);
+  row_fragment<D>(a.v + head * D, k_row, N, 0u, half, vf);
+
+  // per axis, the queries whose window holds the lane's key; its query columns as a
+  // per-element bias (0 or -inf; -inf for every query of a lane outside the grid)
+  const GridMasks rm = na_grid_reverse_masks(z, imin(y, H - 1), imin(col, W - 1), g);
+  const uint32_t cm16 = k_ok ? lane_block_bits((uint32_t)rm.x0, half) : 0u;
+  float bias[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bias[e] = ((cm16 >> e) & 1u) ? 0.f : -INFINITY;
+  uint32_t rows_vis = 0;  // bit r: band query row r reaches this wavefront's key row
+  for (int32_t r = 0; r < by.count; ++r) {
+    int32_t yq = by.start + r;
+    yq -= yq >= H ? H : 0;
+    rows_vis |= (uint32_t)bit128(rm.y0, rm.y1, yq) << r;
+  }
+  rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
+  auto next_plane = [&](int32_t j) {
+    while (j < bz.count &&
+           __builtin_amdgcn_readfirstlane((int)bit128(rm.z0, rm.z1, band_plane(bz, i_own, j, g.grid_d))) == 0)
+      ++j;
+    return j;
+  };
+
+  int v_row[2], v_off[2][DT];
+  transpose_offsets<D>(lane, half, v_row, v_off);
+  const int swz = chunk_swizzle<D>(col);
+  f32x16_t dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16_t{};
+
+  if (tid < TOK) {  // the first stage's statistics (published by the loop's first barrier)
+    l2_lds[0][tid] = l2n;
+    dl_lds[0][tid] = dln;
+  }
+  for (int32_t i = 0, stage = 0; i < bz.count; stage ^= 1) {
+    const int32_t i_next = next_plane(i + 1);
+    const bool more = i_next < bz.count;
+    const int32_t z_next = more ? band_plane(bz, i_own, i_next, g.grid_d) : 0;
+    wait_tile_loads<0>();
+    __syncthreads();
+    if (!kSerialTiles && more) {
+      load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[stage ^ 1], g_lds[stage ^ 1], z_next, by, H, W, head_bytes,
+                                 wave, tid);
+      stats(z_next, l2n, dln);
+    }
+    const uint16_t* qs = q_lds[stage];
+    const uint16_t* gs = g_lds[stage];
+    uint32_t rem = rows_vis;
+    if (rem != 0u) {
+      int32_t r = __builtin_ctz(rem);
+      f32x16_t s_nx = block_product<D>(qs + r * 32 * D, 0, col, half, swz, kf);
+      f32x16_t dp_nx = block_product<D>(gs + r * 32 * D, 0, col, half, swz, vf);
+      while (true) {
+        const f32x16_t s = s_nx, dp = dp_nx;
+        const int32_t rc = r;
+        rem &= rem - 1u;
+        const bool nxt = rem != 0u;
+        if (nxt) {
+          r = __builtin_ctz(rem);
+          s_nx = block_product<D>(qs + r * 32 * D, 0, col, half, swz, kf);
+          dp_nx = block_product<D>(gs + r * 32 * D, 0, col, half, swz, vf);
+        }
+        f32x16_t p, ds;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qr = rc * 32 + 8 * g4 + 4 * half;  // first of the 4 queries of this group
+          const float4 l4 = *reinterpret_cast<const float4*>(&l2_lds[stage][qr]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[stage][qr]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * g4 + j;
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, bias[e] - lv[j]));
+            p[e] = pv;
+            ds[e] = pv * (dp[e] - dv4[j]);
+          }
+        }
+        bf16x8_t pb[2], dsb[2];
+        to_bf16_operand(p, pb);
+        to_bf16_operand(ds, dsb);
+        block_transpose_product<D>(gs + rc * 32 * D, 0, v_row, v_off, pb, dv);
+        block_transpose_product<D>(qs + rc * 32 * D, 0, v_row, v_off, dsb, dk);
+        if (!nxt) break;
+      }
+    }
+    if (kSerialTiles && more) {  // race check: the next stage's loads only after this stage's compute
+      load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[stage ^ 1], g_lds[stage ^ 1], z_next, by, H, W, head_bytes,
+                                 wave, tid);
+      stats(z_next, l2n, dln);
+    }
+    if (more && tid < TOK) {  // the other stage's statistics were last read before this step's barrier
+      l2_lds[stage ^ 1][tid] = l2n;
+      dl_lds[stage ^ 1][tid] = dln;
+    }
+    i = i_next;
+  }
+  store_rows_scaled<D>(a.dk + head * D, k_row, N, half, dk, a.scale);
+  store_rows_scaled<D>(a.dv + head * D, k_row, N, half, dv, 1.0f);
+}
+
 static_assert(BwdCfg<32>::WAVES_PER_EU == bwd_wgs_per_cu(32) && BwdCfg<64>::WAVES_PER_EU == bwd_wgs_per_cu(64) &&
                   BwdCfg<128>::WAVES_PER_EU == bwd_wgs_per_cu(128),
               "one wavefront per SIMD per work-group: waves per SIMD = work-groups per CU");
 
 template <int D, int MASK>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3(a.BH * a.n_qtiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
+  bool dq_rows = false, dkv_rows = false;
+  if constexpr (MASK == MASK_NA && D == 32) {
+    dq_rows = a.dq_rows != 0;
+    dkv_rows = a.dkv_rows != 0;
+  }
+  const dim3 rows_grid(dq_rows || dkv_rows ? a.BH * a.na.grid_d * a.row_groups : 1);
+  if constexpr (MASK == MASK_NA && D == 32) {
+    if (dq_rows) hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+  }
+  if (!dq_rows)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3(a.BH * a.n_qtiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, MASK>), dim3(a.BH * a.n_ktiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
+  if constexpr (MASK == MASK_NA && D == 32) {
+    if (dkv_rows) hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+  }
+  if (!dkv_rows)
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, MASK>), dim3(a.BH * a.n_ktiles), dim3(BwdCfg<D>::THREADS), 0, stream,
+                       a);
   return hipGetLastError();
 }
 

@@ -92,7 +92,16 @@ struct BwdArgs {
   int32_t na_grid;   // 1: per-axis window masks (na_grid_eligible), else the element test
   int32_t group_q;   // causal: heads per XCD dispatched together by the dQ kernel (causal_group)
   int32_t group_k;   // and by the dK/dV kernel
+  // neighbourhood windows on grids at most 32 wide: the row kernels (1) or the tile kernels (0)
+  int32_t dq_rows;   // dQ by query rows (na_rows_eligible with bwd_dq_rows_lds(d))
+  int32_t dkv_rows;  // dK/dV by key rows (na_rows_reverse_eligible with bwd_dkv_rows_lds(d))
+  int32_t row_groups;  // groups of kRowsGroup rows per plane (either row kernel)
 };
+
+// Key rows per LDS stage of the dQ row kernel and query rows per stage of the dK/dV
+// row kernel for head size d (0: no row kernel at that size).
+constexpr int32_t bwd_dq_rows_lds(int64_t d) { return d == 32 ? 10 : 0; }
+constexpr int32_t bwd_dkv_rows_lds(int64_t d) { return d == 32 ? 8 : 0; }
 
 // Launches the two backward kernels on `stream`: dQ (which also forms D = rowsum(dO * O)
 // in the workspace), then dK and dV.

@@ -417,6 +417,43 @@ constexpr bool na_rows_eligible(const NaGeom& g, int32_t lds_rows) {
   return true;
 }
 
+// Backward of the row kernel: the same grids, with key rows in the wavefronts
+// (dK and dV of 4 key rows of one plane per work-group) and the queries whose
+// windows reach them streamed. Along one axis, the query coordinates whose window
+// holds some key coordinate in [c0, c1]: a wrapped window is symmetric (query c
+// sees key c' iff key c sees query c'), so it is na_band itself; a clamped window
+// of dilation 1 starts at s(c) = clamp(c - rad, 0, len - kernel), non-decreasing,
+// so the queries form one run from the first with s(c) + kernel > c0 to the last
+// with s(c) <= c1; a clamped dilated window holds its query and spans (kernel - 1)
+// * dil cells, so a run of that reach around [c0, c1] holds them (a superset; the
+// per-axis reverse masks decide).
+constexpr Band na_band_reverse(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
+                               int32_t dil) {
+  if (wrap) return na_band(c0, c1, len, kernel, rad, wrap, dil);
+  if (dil == 1) {
+    const int32_t first = c0 - kernel + 1 <= 0 ? 0 : c0 - kernel + 1 + rad;
+    const int32_t last = c1 >= len - kernel ? len - 1 : c1 + rad;
+    return Band{first, last - first + 1};
+  }
+  const int32_t reach = (kernel - 1) * dil;
+  const int32_t s = imax(c0 - reach, 0), e = imin(c1 + reach, len - 1);
+  return Band{s, e - s + 1};
+}
+
+// Query rows of one plane whose windows reach the key rows [y0, y0 + kRowsGroup).
+constexpr Band na_rows_reverse_band(int32_t y0, const NaGeom& g) {
+  return na_band_reverse(y0, imin(y0 + kRowsGroup, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+}
+
+// The dK/dV row kernel's condition: na_rows_eligible's grid limits, and every
+// group's band of query rows within `lds_rows` rows per stage.
+constexpr bool na_rows_reverse_eligible(const NaGeom& g, int32_t lds_rows) {
+  if (g.grid_w > 32 || g.grid_h > 128 || g.grid_d > 128) return false;
+  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kRowsGroup)
+    if (na_rows_reverse_band(y0, g).count > lds_rows) return false;
+  return true;
+}
+
 // 16-bit mask of the accumulator elements of one 32-key block that a lane keeps
 // when the keys it may see end at `lim` keys past the lane's first key of the
 // block: element r holds key offset 8 * (r / 4) + r % 4, kept iff <= lim (so

@@ -327,6 +327,57 @@ static int check_rows(const NaGeom& g, int lds_rows) {
   return 1;
 }
 
+// The dK/dV row kernel as it walks its stages: for every key plane, group of key
+// rows, wavefront and lane, the query cells it marks (visible planes of the reverse
+// plane band, visible rows of the group's reverse row band, the lane's query-column
+// bits, all from the key's reverse masks) are exactly the queries whose window holds
+// the key, each once; every group's reverse row band fits the stage.
+static int check_rows_reverse(const NaGeom& g, int lds_rows) {
+  if (!na_rows_reverse_eligible(g, lds_rows)) return 0;
+  const int H = g.grid_h, W = g.grid_w, D = g.grid_d, N = D * H * W;
+  std::vector<std::set<int>> seers(N);
+  for (int q = 0; q < N; ++q)
+    for (int k : window_keys(g, q)) seers[k].insert(q);
+  for (int z = 0; z < D; ++z)
+    for (int y0 = 0; y0 < H; y0 += kRowsGroup) {
+      const Band bz = na_band_reverse(z, z, D, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+      const Band by = na_rows_reverse_band(y0, g);
+      EXPECT(by.count >= 1 && by.count <= lds_rows && bz.count >= 1 && bz.count <= D, "reverse bands %d, %d",
+             by.count, bz.count);
+      int own = z - bz.start;
+      own += own < 0 ? D : 0;
+      EXPECT(own >= 0 && own < bz.count, "the key plane %d lies in its reverse band", z);
+      for (int w = 0; w < kRowsGroup; ++w) {
+        const int y = y0 + w;
+        if (y >= H) continue;
+        for (int x = 0; x < W; ++x) {
+          const GridMasks rm = na_grid_reverse_masks(z, y, x, g);
+          std::vector<int> seen;
+          for (int i = 0; i < bz.count; ++i) {
+            const int zq = (bz.start + i) % D;
+            if (!bit128(rm.z0, rm.z1, zq)) continue;
+            for (int r = 0; r < by.count; ++r) {
+              const int yq = (by.start + r) % H;
+              if (!bit128(rm.y0, rm.y1, yq)) continue;
+              for (int xq = 0; xq < 32; ++xq)
+                if ((((uint32_t)rm.x0 >> xq) & 1u) != 0) {
+                  EXPECT(xq < W, "query column bit past the grid width");
+                  seen.push_back((zq * H + yq) * W + xq);
+                }
+            }
+          }
+          const int k = (z * H + y) * W + x;
+          const std::set<int> got(seen.begin(), seen.end());
+          EXPECT(got.size() == seen.size() && got == seers[k],
+                 "reverse rows of key %d: %zu cells (%zu distinct), want %zu (grid %dx%dx%d k %d,%d,%d wrap %d%d%d "
+                 "dil %d,%d,%d)", k, seen.size(), got.size(), seers[k].size(), D, H, W, g.kernel_d, g.kernel_h,
+                 g.kernel_w, g.wrap_d, g.wrap_h, g.wrap_w, g.dil_d, g.dil_h, g.dil_w);
+        }
+      }
+    }
+  return 1;
+}
+
 static void check_causal(int Nq, int Nkv, int BM, int BN) {
   const int n_tiles = (int)cdiv(Nkv, BN);
   for (int q0 = 0; q0 < Nq; q0 += BM) {
@@ -622,7 +673,7 @@ int main() {
   }
   {
     // row kernel: narrow 2D and 3D grids, wrap and clamp per axis, dilation
-    int eligible = 0, tried = 0;
+    int eligible = 0, eligible_rev = 0, tried = 0;
     for (int D : {1, 5})
       for (int H : {4, 9, 20})
         for (int W : {7, 20, 32})
@@ -634,8 +685,44 @@ int main() {
                 if (!geom_valid(g)) continue;
                 ++tried;
                 eligible += check_rows(g, 10);
+                eligible_rev += check_rows_reverse(g, 8);
               }
     EXPECT(eligible > 100 && eligible < tried, "row-kernel eligibility covers %d of %d shapes", eligible, tried);
+    EXPECT(eligible_rev > 80 && eligible_rev < eligible, "dK/dV row-kernel eligibility covers %d of %d shapes",
+           eligible_rev, tried);
+    EXPECT(na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), 8),
+           "20x20x20, 5x5x5 window: dK/dV by key rows");
+    EXPECT(!na_rows_reverse_eligible(geom(1, 20, 20, 1, 5, 5, 1, 0, 0, 1, 1, 1), 8),
+           "clamped 5-row windows near a border: 10 query rows reach the key rows 4..7");
+    // the reverse band of one clamped axis against brute force, every coordinate range
+    for (int len : {1, 2, 5, 9, 20})
+      for (int kernel : {1, 3, 5, 7})
+        for (int dil : {1, 2, 3})
+          for (int wrap : {0, 1}) {
+            const NaGeom ax = geom(1, 1, len, 1, 1, kernel, 0, 0, wrap, 1, 1, dil);
+            if (!geom_valid(ax)) continue;
+            for (int c0 = 0; c0 < len; ++c0)
+              for (int c1 = c0; c1 < len && c1 < c0 + 4; ++c1) {
+                const Band b = na_band_reverse(c0, c1, len, kernel, ax.rad_w, wrap, dil);
+                EXPECT(b.count >= 1 && b.count <= len && b.start >= 0 && b.start < len, "reverse band in range");
+                for (int q = 0; q < len; ++q)
+                  for (int k = c0; k <= c1; ++k) {
+                    const bool sees = na_dil_ok(na_dil_anchor(q, len, kernel, ax.rad_w, wrap, dil), k, len, kernel,
+                                                ax.rad_w, wrap, dil);
+                    const int off = ((q - b.start) % len + len) % len;
+                    EXPECT(!sees || off < b.count, "query %d sees key %d outside the reverse band (len %d k %d dil %d "
+                           "wrap %d)", q, k, len, kernel, dil, wrap);
+                  }
+                if (!wrap && dil == 1) {  // exact: its ends are seers
+                  bool first = false, last = false;
+                  for (int k = c0; k <= c1; ++k) {
+                    first |= na_axis_ok(b.start, k, len, kernel, ax.rad_w, 0);
+                    last |= na_axis_ok(b.start + b.count - 1, k, len, kernel, ax.rad_w, 0);
+                  }
+                  EXPECT(first && last, "clamped reverse band [%d, +%d) is tight", b.start, b.count);
+                }
+              }
+          }
     EXPECT(na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), 10), "20x20x20, 5x5x5 window takes the row kernel");
     EXPECT(!na_rows_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1), 10), "64 wide does not");
   }

@@ -89,6 +89,15 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (40, 3, 5, 3, 1, 1, 2, 1)),      # width 3 and 200: the element test instead of the window masks
     ("na2d", (2, 200, 1, 7, 0, 1, 1, 3)),
     ("na3d", (2, 130, 4, 1, 5, 3, 0, 1, 1, 1, 2, 1)),   # more than 128 rows
+    # at d = 32 these take the row kernels (grids at most 32 wide): dQ by query rows, dK/dV by key
+    # rows over the queries whose windows reach them
+    ("na3d", (8, 8, 8, 5, 5, 5, 1, 1, 0, 1, 1, 1)),     # the 3D workload's window: wrapped planes and rows
+    ("na3d", (5, 9, 20, 3, 5, 5, 0, 1, 1, 1, 1, 1)),    # clamped planes, 9 rows (a partial group)
+    ("na3d", (4, 6, 32, 3, 3, 7, 1, 0, 0, 1, 1, 1)),    # 32 wide, clamped rows and columns
+    ("na2d", (12, 31, 3, 7, 0, 0, 1, 1)),               # clamped both ways: reverse bands near the borders
+    ("na2d", (20, 32, 5, 5, 0, 1, 1, 1)),               # clamped 5-row windows: dK/dV back on the tile kernel
+    ("na2d", (16, 20, 3, 5, 1, 0, 2, 2)),               # dilated rows and columns
+    ("na2d", (9, 1, 3, 1, 1, 0, 1, 1)),                 # one column
 ])
 def test_bwd_neighbourhood(mode, geo, d):
     import exact_attention_68_amd as A

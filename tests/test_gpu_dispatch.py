@@ -110,3 +110,29 @@ def test_attn_bwd_is_two_kernels():
     assert len(kernels) == 2, kernels
     assert "attn_bwd_dq_kernel" in kernels[0] and "attn_bwd_dkv_kernel" in kernels[1], kernels
     assert others == [], others
+
+
+@pytest.mark.parametrize("name,dq,dkv", [
+    ("na3d_wrap_20x20x20_k5", "attn_bwd_dq_rows_kernel", "attn_bwd_dkv_rows_kernel"),
+    ("na2d_wrap_64x64_k7", "attn_bwd_dq_kernel", "attn_bwd_dkv_kernel"),
+])
+def test_attn_bwd_neighbourhood_kernels(name, dq, dkv):
+    """Grids at most 32 wide take the row kernels (dQ by query rows, dK/dV by key rows); wider grids
+    the tile kernels."""
+    import exact_attention_68_amd as A
+
+    w = workloads.WORKLOADS[name]
+    q, k, v = (t.cuda() for t in workloads.workload_qkv(w))
+    mode = A.ATTN_MASK_NA3D if w.mask == "na3d" else A.ATTN_MASK_NA2D
+    params = A.na3d_params(**w.na) if w.mask == "na3d" else A.na2d_params(**w.na)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    A.attn_fwd_ex(q, k, v, o, lse, w.scale, mode, params)
+    do = torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16)
+    ws = torch.empty(A.attn_bwd_workspace_size(w.B, w.H, w.N, w.N, w.d, mode, params), dtype=torch.uint8,
+                     device="cuda")
+    grads = [torch.empty_like(t) for t in (q, k, v)]
+    kernels, others = _split(_dispatches(lambda: A.attn_bwd(q, k, v, o, do, lse, *grads, w.scale, mode, params, ws)))
+    assert len(kernels) == 2 and dq in kernels[0] and dkv in kernels[1], kernels
+    assert others == [], others
+

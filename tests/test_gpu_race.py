@@ -101,25 +101,28 @@ def test_d32_four_stage_rings_equal_serial(libs, mask):
         assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
 
 
-@pytest.mark.parametrize("mask,d", [("none", 64), ("causal", 64), ("none", 128)])
+@pytest.mark.parametrize("mask,d", [("none", 64), ("causal", 64), ("none", 128), ("na3d", 32)])
 def test_backward_pipelined_equals_serial(libs, mask, d):
+    """The tile kernels, and at "na3d" (a 10x10x10 volume, 5x5x5 window) the row kernels' two-stage rings."""
     import exact_attention_68_amd as A
 
     piped, serial = libs
-    B, H, N = 1, 4, 2000
+    B, H, N = (1, 4, 2000) if mask != "na3d" else (2, 2, 1000)
     q, k, v = (t.cuda() for t in workloads.make_qkv(B, H, N, d, 88))
     g = torch.Generator(device="cpu").manual_seed(89)
     do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda()
-    mode = A.ATTN_MASK_CAUSAL if mask == "causal" else A.ATTN_MASK_NONE
-    o, lse = _fwd(piped, q, k, v, mode, d ** -0.5, None, "attn_fwd_ex", True)
+    mode = {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL, "na3d": A.ATTN_MASK_NA3D}[mask]
+    params = A.na3d_params(10, 10, 10, 5, 5, 5, 1, 1, 0) if mask == "na3d" else None
+    pp = A._params_ptr(params)
+    o, lse = _fwd(piped, q, k, v, mode, d ** -0.5, params, "attn_fwd_ex", True)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    nws = A.attn_bwd_workspace_size(B, H, N, N, d, mode)
+    nws = A.attn_bwd_workspace_size(B, H, N, N, d, mode, params)
 
     def grads(lib):
         ws = torch.full((nws,), 255, dtype=torch.uint8, device="cuda")
         out = [torch.full_like(t, float("nan")) for t in (q, k, v)]
         rc = lib.attn_bwd(_p(q), _p(k), _p(v), _p(o), _p(do), _p(lse), *[_p(t) for t in out], B, H, N, N, d,
-                          d ** -0.5, mode, None, _p(ws), nws, stream)
+                          d ** -0.5, mode, pp, _p(ws), nws, stream)
         assert rc == 0, rc
         torch.cuda.synchronize()
         return out
