@@ -268,6 +268,13 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     const bool groups_fit = (int64_t)a.BH * a.na.grid_d * a.row_groups <= INT32_MAX;
     a.dq_rows = groups_fit && dq_lds > 0 && attn::na_rows_eligible(a.na, dq_lds) ? 1 : 0;
     a.dkv_rows = groups_fit && dkv_lds > 0 && attn::na_rows_reverse_eligible(a.na, dkv_lds) ? 1 : 0;
+    // wider single-plane grids: the patch kernels (the row kernels keep the narrow ones)
+    const int32_t patch_lds = attn::bwd_patch_lds(d);
+    a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
+    a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kPatchRows);
+    const bool patches_fit = (int64_t)a.BH * a.patch_nx * a.patch_ny <= INT32_MAX;
+    a.dq_patch = !a.dq_rows && patches_fit && attn::na_patch_bwd_eligible(a.na, patch_lds, false) ? 1 : 0;
+    a.dkv_patch = !a.dkv_rows && patches_fit && attn::na_patch_bwd_eligible(a.na, patch_lds, true) ? 1 : 0;
   }
   const hipError_t e = attn::launch_bwd(a, (int32_t)d, mask, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

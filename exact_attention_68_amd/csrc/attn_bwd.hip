@@ -925,29 +925,347 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
   store_rows_scaled<D>(a.dv + head * D, k_row, N, half, dv, 1.0f);
 }
 
+// ---------------------------------------------------------------------------
+// Neighbourhood windows of one plane by 8 x 16 patches (na_patch_bwd_eligible),
+// the forward patch kernel's layout: the dQ kernel holds a patch of queries and
+// copies the key rectangle its windows reach (K and V) into LDS once; the dK/dV
+// kernel holds a patch of keys and copies the rectangle of queries whose windows
+// reach them (Q, dO and their lse2 and D). Wavefront w holds the patch's rows 2w
+// and 2w + 1 (lane column col: row col / 16, column col % 16) and walks the band
+// rows of those two rows in the rectangle; each query wavefront has a second
+// wavefront on its SIMD that takes every other row (two parts, summed at the end
+// through LDS). Window bits per lane: its columns over the rectangle's column
+// cells (an exponent addend per element) and its rows over the rectangle's rows.
+
+template <int D>
+struct BwdPatchCfg {
+  static constexpr int ROWS = bwd_patch_lds(D);  // rows of 32 tokens per rectangle
+  static constexpr int PARTS = 2;
+  static constexpr int THREADS = 256 * PARTS;
+  static constexpr int RC = D / 8;
+  static constexpr int CHUNKS = ROWS * kPatchKeyCols * RC;
+  static_assert(ROWS > 0 && CHUNKS % THREADS == 0, "the copy runs in whole rounds of the work-group's lanes");
+  static constexpr int ELEMS = CHUNKS * 8;
+};
+
+// Copies the rectangle (rows x cols band cells, each mod its axis) of two tensors of
+// one head into LDS: chunk p holds chunk (p % RC) ^ swizzle of token p / RC = 32 r +
+// x (row cell r, column cell x); columns past the column band read as zero.
+template <int D>
+__device__ __forceinline__ void load_patch_rect(i32x4_t ra, i32x4_t rb, const uint16_t* la, const uint16_t* lb,
+                                                const PatchBands& pb, int32_t H, int32_t W, uint32_t head_bytes,
+                                                int wave8, int tid) {
+  using P = BwdPatchCfg<D>;
+  const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds_addr(la) + wave8 * 1024);
+  const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds_addr(lb) + wave8 * 1024);
+  const int32_t n_loads = (int32_t)cdiv((int64_t)pb.rows.count * kPatchKeyCols * P::RC, P::THREADS);
+  for (int32_t j = 0; j < n_loads; ++j) {
+    const int32_t p = j * P::THREADS + tid;
+    const int32_t tok = p / P::RC, r = tok / kPatchKeyCols, x = tok % kPatchKeyCols;
+    const int32_t chunk = (p % P::RC) ^ chunk_swizzle<D>(tok);
+    uint32_t voff = head_bytes;
+    if (r < pb.rows.count && x < pb.cols.count) {
+      int32_t ty = pb.rows.start + r, tx = pb.cols.start + x;
+      ty -= ty >= H ? H : 0;  // both start inside the axis and span at most its length
+      tx -= tx >= W ? W : 0;
+      voff = (uint32_t)(ty * W + tx) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
+    }
+    dma_lds16(ra, a_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
+    dma_lds16(rb, b_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
+  }
+}
+
+// The lane's column bits of a 32-token block, in accumulator element order.
+__device__ __forceinline__ uint32_t block_elem_bits(uint32_t cm, int half) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) m |= ((cm >> (8 * g4 + 4 * half)) & 0xFu) << (4 * g4);
+  return m;
+}
+
+// dQ by query patches; also forms D of its queries for the dK/dV kernel.
+template <int D>
+__global__ __launch_bounds__(BwdPatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dq_patch_kernel(BwdArgs a) {
+  using P = BwdPatchCfg<D>;
+  constexpr int KB = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[P::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[P::ELEMS];
+  __shared__ float merge_lds[4 * DT * 16 * 64];  // the second part's dQ
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave8 & 3, part = wave8 >> 2;
+  const NaGeom& g = a.na;
+  const int32_t H = g.grid_h, W = g.grid_w, N = a.Nq;
+
+  const int32_t per_head = a.patch_ny * a.patch_nx;
+  const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int32_t bh = item / per_head, pidx = item - bh * per_head;
+  const int32_t py = pidx / a.patch_nx;
+  const int32_t y0 = py * kPatchRows, x0 = (pidx - py * a.patch_nx) * kPatchCols;
+  const PatchBands pb = na_patch_bands(y0, x0, g);
+  const size_t head = (size_t)bh * (size_t)N;
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+  load_patch_rect<D>(head_rsrc(a.k + head * D, head_bytes), head_rsrc(a.v + head * D, head_bytes), k_lds, v_lds, pb,
+                     H, W, head_bytes, wave8, tid);
+
+  const int32_t qy = y0 + 2 * wave + (col >> 4), qx = x0 + (col & 15);
+  const bool q_ok = qy < H && qx < W;
+  const int32_t my_q = qy * W + qx;
+  const int32_t q_row = q_ok ? my_q : N;
+  bf16x8_t qf[KB], gf[KB];
+  row_fragment<D>(a.q + head * D, q_row, N, a.q_sign, half, qf);
+  row_fragment<D>(a.dout + head * D, q_row, N, 0u, half, gf);
+  const float l2 = q_ok ? a.lse[head + my_q] * kLog2e : 0.f;
+  float dlt;
+  {
+    bf16x8_t of[KB];
+    row_fragment<D>(a.o + head * D, q_row, N, 0u, half, of);
+    dlt = swap_halves_sum(row_delta_part<D>(of, gf));
+    if (part == 0 && q_ok && half == 0) a.delta[head + my_q] = dlt;
+  }
+  // window bits: key column cells of the rectangle, key rows of the rectangle
+  const int32_t cy = imin(qy, H - 1), cx = imin(qx, W - 1);
+  const uint32_t cm = block_elem_bits(band_window_bits(cx, pb.cols, W, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w, false),
+                                      half);
+  const uint32_t rows_w = band_window_bits(cy, pb.rows, H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h, false);
+  float add[16];  // -lse2 for a key column in the window, -inf otherwise (and for a lane outside the grid)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) add[e] = q_ok && ((cm >> e) & 1u) ? -l2 : -INFINITY;
+  // this wavefront's rows: the band of its two query rows, a run of the rectangle's band
+  const bool rows_in = y0 + 2 * wave < H;
+  const int32_t wy0 = imin(y0 + 2 * wave, H - 1);
+  const Band wb = na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+  int32_t off = wb.start - pb.rows.start;
+  off += off < 0 ? H : 0;
+  const int32_t end = rows_in ? off + wb.count : 0;
+
+  int v_row[2], v_off[2][DT];
+  transpose_offsets<D>(lane, half, v_row, v_off);
+  const int swz = chunk_swizzle<D>(col);
+  f32x16_t dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16_t{};
+
+  wait_tile_loads<0>();
+  __syncthreads();  // the rectangle is read-only from here on
+  // rows off + part, off + part + 2, ... that some lane of the wavefront sees
+  auto next_row = [&](int32_t r) {
+    while (r < end && __builtin_amdgcn_ballot_w64(((rows_w >> r) & 1u) != 0u) == 0) r += P::PARTS;
+    return r;
+  };
+  int32_t r = next_row(off + part);
+  if (r < end) {
+    f32x16_t s_nx = block_product<D>(k_lds + r * 32 * D, 0, col, half, swz, qf);
+    f32x16_t dp_nx = block_product<D>(v_lds + r * 32 * D, 0, col, half, swz, gf);
+    while (true) {
+      const f32x16_t s = s_nx, dp = dp_nx;
+      const int32_t rc = r;
+      r = next_row(r + P::PARTS);
+      const bool nxt = r < end;
+      if (nxt) {
+        s_nx = block_product<D>(k_lds + r * 32 * D, 0, col, half, swz, qf);
+        dp_nx = block_product<D>(v_lds + r * 32 * D, 0, col, half, swz, gf);
+      }
+      const bool live = ((rows_w >> rc) & 1u) != 0u;
+      f32x16_t ds;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, live ? add[e] : -INFINITY));
+        ds[e] = p * (dp[e] - dlt);
+      }
+      bf16x8_t dsb[2];
+      to_bf16_operand(ds, dsb);
+      block_transpose_product<D>(k_lds + rc * 32 * D, 0, v_row, v_off, dsb, dq);
+      if (!nxt) break;
+    }
+  }
+  // the second part's sums join the first's (lane order), which stores
+  float* slot = merge_lds + wave * DT * 16 * 64 + lane;
+  if (part == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) slot[(dt * 16 + e) * 64] = dq[dt][e];
+  }
+  __syncthreads();
+  if (part == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[dt][e] += slot[(dt * 16 + e) * 64];
+  store_rows_scaled<D>(a.dq + head * D, q_row, N, half, dq, a.scale);
+}
+
+// dK and dV by key patches over the rectangle of queries whose windows reach them.
+template <int D>
+__global__ __launch_bounds__(BwdPatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dkv_patch_kernel(BwdArgs a) {
+  using P = BwdPatchCfg<D>;
+  constexpr int KB = D / 16, DT = D / 32, TOK = P::ROWS * kPatchKeyCols;
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[P::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds[P::ELEMS];
+  __shared__ __attribute__((aligned(16))) float l2_lds[TOK];
+  __shared__ __attribute__((aligned(16))) float dl_lds[TOK];
+  __shared__ float merge_lds[4 * 2 * DT * 16 * 64];  // the second part's dK and dV
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave8 & 3, part = wave8 >> 2;
+  const NaGeom& g = a.na;
+  const int32_t H = g.grid_h, W = g.grid_w, N = a.Nkv;
+
+  const int32_t per_head = a.patch_ny * a.patch_nx;
+  const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int32_t bh = item / per_head, pidx = item - bh * per_head;
+  const int32_t py = pidx / a.patch_nx;
+  const int32_t y0 = py * kPatchRows, x0 = (pidx - py * a.patch_nx) * kPatchCols;
+  const PatchBands pb = na_patch_reverse_bands(y0, x0, g);
+  const size_t head = (size_t)bh * (size_t)N;
+  const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
+  load_patch_rect<D>(head_rsrc(a.q + head * D, head_bytes), head_rsrc(a.dout + head * D, head_bytes), q_lds, g_lds,
+                     pb, H, W, head_bytes, wave8, tid);
+  // lse2 and D of the rectangle's queries (+inf and 0 past its bands: P = 0 there)
+  for (int32_t t = tid; t < TOK; t += P::THREADS) {
+    const int32_t r = t / kPatchKeyCols, x = t % kPatchKeyCols;
+    float l2v = INFINITY, dlv = 0.f;
+    if (r < pb.rows.count && x < pb.cols.count) {
+      int32_t ty = pb.rows.start + r, tx = pb.cols.start + x;
+      ty -= ty >= H ? H : 0;
+      tx -= tx >= W ? W : 0;
+      const int32_t qi = ty * W + tx;
+      l2v = a.lse[head + qi] * kLog2e;
+      dlv = a.delta[head + qi];
+    }
+    l2_lds[t] = l2v;
+    dl_lds[t] = dlv;
+  }
+
+  const int32_t ky = y0 + 2 * wave + (col >> 4), kx = x0 + (col & 15);
+  const bool k_ok = ky < H && kx < W;
+  const int32_t my_k = ky * W + kx;
+  const int32_t k_row = k_ok ? my_k : N;
+  // scale < 0: K's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
+  bf16x8_t kf[KB], vf[KB];
+  row_fragment<D>(a.k + head * D, k_row, N, a.q_sign, half, kf);
+  row_fragment<D>(a.v + head * D, k_row, N, 0u, half, vf);
+  // window bits: the rectangle's query columns and rows whose windows hold the lane's key
+  const int32_t cy = imin(ky, H - 1), cx = imin(kx, W - 1);
+  const uint32_t cm = block_elem_bits(band_window_bits(cx, pb.cols, W, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w, true),
+                                      half);
+  const uint32_t rows_w = band_window_bits(cy, pb.rows, H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h, true);
+  float bias[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bias[e] = k_ok && ((cm >> e) & 1u) ? 0.f : -INFINITY;
+  const bool rows_in = y0 + 2 * wave < H;
+  const int32_t wy0 = imin(y0 + 2 * wave, H - 1);
+  const Band wb = na_band_reverse(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+  int32_t off = wb.start - pb.rows.start;
+  off += off < 0 ? H : 0;
+  const int32_t end = rows_in ? off + wb.count : 0;
+
+  int v_row[2], v_off[2][DT];
+  transpose_offsets<D>(lane, half, v_row, v_off);
+  const int swz = chunk_swizzle<D>(col);
+  f32x16_t dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16_t{};
+
+  wait_tile_loads<0>();
+  __syncthreads();  // the rectangle and its statistics are read-only from here on
+  auto next_row = [&](int32_t r) {
+    while (r < end && __builtin_amdgcn_ballot_w64(((rows_w >> r) & 1u) != 0u) == 0) r += P::PARTS;
+    return r;
+  };
+  int32_t r = next_row(off + part);
+  if (r < end) {
+    f32x16_t s_nx = block_product<D>(q_lds + r * 32 * D, 0, col, half, swz, kf);
+    f32x16_t dp_nx = block_product<D>(g_lds + r * 32 * D, 0, col, half, swz, vf);
+    while (true) {
+      const f32x16_t s = s_nx, dp = dp_nx;
+      const int32_t rc = r;
+      r = next_row(r + P::PARTS);
+      const bool nxt = r < end;
+      if (nxt) {
+        s_nx = block_product<D>(q_lds + r * 32 * D, 0, col, half, swz, kf);
+        dp_nx = block_product<D>(g_lds + r * 32 * D, 0, col, half, swz, vf);
+      }
+      const bool live = ((rows_w >> rc) & 1u) != 0u;
+      f32x16_t p, ds;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qr = rc * 32 + 8 * g4 + 4 * half;  // first of the 4 queries of this group
+        const float4 l4 = *reinterpret_cast<const float4*>(&l2_lds[qr]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[qr]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * g4 + j;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, live ? bias[e] - lv[j] : -INFINITY));
+          p[e] = pv;
+          ds[e] = pv * (dp[e] - dv4[j]);
+        }
+      }
+      bf16x8_t pb2[2], dsb[2];
+      to_bf16_operand(p, pb2);
+      to_bf16_operand(ds, dsb);
+      block_transpose_product<D>(g_lds + rc * 32 * D, 0, v_row, v_off, pb2, dv);
+      block_transpose_product<D>(q_lds + rc * 32 * D, 0, v_row, v_off, dsb, dk);
+      if (!nxt) break;
+    }
+  }
+  float* slot = merge_lds + wave * 2 * DT * 16 * 64 + lane;
+  if (part == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        slot[(dt * 16 + e) * 64] = dk[dt][e];
+        slot[((DT + dt) * 16 + e) * 64] = dv[dt][e];
+      }
+  }
+  __syncthreads();
+  if (part == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[dt][e] += slot[(dt * 16 + e) * 64];
+      dv[dt][e] += slot[((DT + dt) * 16 + e) * 64];
+    }
+  store_rows_scaled<D>(a.dk + head * D, k_row, N, half, dk, a.scale);
+  store_rows_scaled<D>(a.dv + head * D, k_row, N, half, dv, 1.0f);
+}
+
 static_assert(BwdCfg<32>::WAVES_PER_EU == bwd_wgs_per_cu(32) && BwdCfg<64>::WAVES_PER_EU == bwd_wgs_per_cu(64) &&
                   BwdCfg<128>::WAVES_PER_EU == bwd_wgs_per_cu(128),
               "one wavefront per SIMD per work-group: waves per SIMD = work-groups per CU");
 
 template <int D, int MASK>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  bool dq_rows = false, dkv_rows = false;
+  bool dq_rows = false, dkv_rows = false, dq_patch = false, dkv_patch = false;
   if constexpr (MASK == MASK_NA && D == 32) {
     dq_rows = a.dq_rows != 0;
     dkv_rows = a.dkv_rows != 0;
+    dq_patch = !dq_rows && a.dq_patch != 0;
+    dkv_patch = !dkv_rows && a.dkv_patch != 0;
   }
   const dim3 rows_grid(dq_rows || dkv_rows ? a.BH * a.na.grid_d * a.row_groups : 1);
+  const dim3 patch_grid(dq_patch || dkv_patch ? a.BH * a.patch_nx * a.patch_ny : 1);
   if constexpr (MASK == MASK_NA && D == 32) {
     if (dq_rows) hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+    if (dq_patch)
+      hipLaunchKernelGGL((attn_bwd_dq_patch_kernel<D>), patch_grid, dim3(BwdPatchCfg<D>::THREADS), 0, stream, a);
   }
-  if (!dq_rows)
+  if (!dq_rows && !dq_patch)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3(a.BH * a.n_qtiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (MASK == MASK_NA && D == 32) {
     if (dkv_rows) hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+    if (dkv_patch)
+      hipLaunchKernelGGL((attn_bwd_dkv_patch_kernel<D>), patch_grid, dim3(BwdPatchCfg<D>::THREADS), 0, stream, a);
   }
-  if (!dkv_rows)
+  if (!dkv_rows && !dkv_patch)
     hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, MASK>), dim3(a.BH * a.n_ktiles), dim3(BwdCfg<D>::THREADS), 0, stream,
                        a);
   return hipGetLastError();

@@ -96,12 +96,19 @@ struct BwdArgs {
   int32_t dq_rows;   // dQ by query rows (na_rows_eligible with bwd_dq_rows_lds(d))
   int32_t dkv_rows;  // dK/dV by key rows (na_rows_reverse_eligible with bwd_dkv_rows_lds(d))
   int32_t row_groups;  // groups of kRowsGroup rows per plane (either row kernel)
+  // neighbourhood windows of one plane whose bands fit 32 columns: the patch kernels
+  int32_t dq_patch;    // dQ by 8 x 16 query patches (na_patch_bwd_eligible, forward bands)
+  int32_t dkv_patch;   // dK/dV by 8 x 16 key patches (reverse bands)
+  int32_t patch_nx, patch_ny;  // patches per grid row and per grid column
 };
 
 // Key rows per LDS stage of the dQ row kernel and query rows per stage of the dK/dV
 // row kernel for head size d (0: no row kernel at that size).
 constexpr int32_t bwd_dq_rows_lds(int64_t d) { return d == 32 ? 10 : 0; }
 constexpr int32_t bwd_dkv_rows_lds(int64_t d) { return d == 32 ? 8 : 0; }
+
+// Rows (of 32 tokens) of the LDS rectangles of the backward patch kernels for head size d.
+constexpr int32_t bwd_patch_lds(int64_t d) { return d == 32 ? 24 : 0; }
 
 // Launches the two backward kernels on `stream`: dQ (which also forms D = rowsum(dO * O)
 // in the workspace), then dK and dV.

@@ -89,6 +89,27 @@ constexpr Band na_band(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int3
   return Band{s, e - s + 1};
 }
 
+// Along one axis, the query coordinates whose window holds some key coordinate in
+// [c0, c1]: a wrapped window is symmetric (query c sees key c' iff key c sees
+// query c'), so it is na_band itself; a clamped window of dilation 1 starts at
+// s(c) = clamp(c - rad, 0, len - kernel), non-decreasing, so the queries form one
+// run from the first with s(c) + kernel > c0 to the last with s(c) <= c1; a
+// clamped dilated window holds its query and spans (kernel - 1) * dil cells, so a
+// run of that reach around [c0, c1] holds them (a superset; the per-axis reverse
+// masks decide).
+constexpr Band na_band_reverse(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
+                               int32_t dil) {
+  if (wrap) return na_band(c0, c1, len, kernel, rad, wrap, dil);
+  if (dil == 1) {
+    const int32_t first = c0 - kernel + 1 <= 0 ? 0 : c0 - kernel + 1 + rad;
+    const int32_t last = c1 >= len - kernel ? len - 1 : c1 + rad;
+    return Band{first, last - first + 1};
+  }
+  const int32_t reach = (kernel - 1) * dil;
+  const int32_t s = imax(c0 - reach, 0), e = imin(c1 + reach, len - 1);
+  return Band{s, e - s + 1};
+}
+
 constexpr KvRun kv_run(int mask, int32_t Nq, int32_t Nkv, int32_t BM, int32_t BN, int32_t q0, const NaGeom& g) {
   const int32_t n_tiles = (int32_t)cdiv(Nkv, BN);
   const int32_t q_last = imin(q0 + BM, Nq) - 1;
@@ -390,6 +411,50 @@ constexpr bool na_patch_eligible(const NaGeom& g, int32_t lds_rows) {
   return true;
 }
 
+// Backward of the patch kernel: dK and dV of an 8 x 16 patch of keys over the
+// rectangle of queries whose windows reach them (na_band_reverse per axis).
+constexpr PatchBands na_patch_reverse_bands(int32_t y0, int32_t x0, const NaGeom& g) {
+  return PatchBands{
+      na_band_reverse(y0, imin(y0 + kPatchRows, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h),
+      na_band_reverse(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w)};
+}
+
+// Bits over the cells of band b (start, mod len; count <= 32) of one axis for the
+// coordinate c of a lane: bit i set iff the pair is in the window, with the lane as
+// the query and cell i as the key (reverse = false) or the other way round.
+constexpr uint32_t band_window_bits(int32_t c, Band b, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
+                                    int32_t dil, bool reverse) {
+  const int32_t anchor = na_dil_anchor(c, len, kernel, rad, wrap, dil);
+  uint32_t m = 0;
+  for (int32_t i = 0; i < b.count; ++i) {
+    int32_t x = b.start + i;
+    x -= x >= len ? len : 0;
+    const bool ok = reverse ? na_dil_ok(na_dil_anchor(x, len, kernel, rad, wrap, dil), c, len, kernel, rad, wrap, dil)
+                            : na_dil_ok(anchor, x, len, kernel, rad, wrap, dil);
+    m |= (uint32_t)ok << i;
+  }
+  return m;
+}
+
+// The backward patch kernels' condition, for the key rectangles of the dQ kernel
+// (reverse = false) or the query rectangles of the dK/dV kernel (reverse = true):
+// one plane; every column band within one 32-token block; a wrapped row band
+// shorter than the axis (so a wavefront's band is one run of its work-group's);
+// every row band within `lds_rows`. Both kernels walk only their wavefront's band
+// rows, so no rows past a band are read.
+constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool reverse) {
+  if (g.grid_d != 1 || lds_rows <= 0) return false;
+  for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols) {
+    const PatchBands b = reverse ? na_patch_reverse_bands(0, x0, g) : na_patch_bands(0, x0, g);
+    if (b.cols.count > kPatchKeyCols) return false;
+  }
+  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kPatchRows) {
+    const Band rows = (reverse ? na_patch_reverse_bands(y0, 0, g) : na_patch_bands(y0, 0, g)).rows;
+    if (rows.count > lds_rows || (g.wrap_h && rows.count >= g.grid_h)) return false;
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Grid rows of narrow grids (MASK_NA_ROWS).
 //
@@ -419,28 +484,8 @@ constexpr bool na_rows_eligible(const NaGeom& g, int32_t lds_rows) {
 
 // Backward of the row kernel: the same grids, with key rows in the wavefronts
 // (dK and dV of 4 key rows of one plane per work-group) and the queries whose
-// windows reach them streamed. Along one axis, the query coordinates whose window
-// holds some key coordinate in [c0, c1]: a wrapped window is symmetric (query c
-// sees key c' iff key c sees query c'), so it is na_band itself; a clamped window
-// of dilation 1 starts at s(c) = clamp(c - rad, 0, len - kernel), non-decreasing,
-// so the queries form one run from the first with s(c) + kernel > c0 to the last
-// with s(c) <= c1; a clamped dilated window holds its query and spans (kernel - 1)
-// * dil cells, so a run of that reach around [c0, c1] holds them (a superset; the
-// per-axis reverse masks decide).
-constexpr Band na_band_reverse(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
-                               int32_t dil) {
-  if (wrap) return na_band(c0, c1, len, kernel, rad, wrap, dil);
-  if (dil == 1) {
-    const int32_t first = c0 - kernel + 1 <= 0 ? 0 : c0 - kernel + 1 + rad;
-    const int32_t last = c1 >= len - kernel ? len - 1 : c1 + rad;
-    return Band{first, last - first + 1};
-  }
-  const int32_t reach = (kernel - 1) * dil;
-  const int32_t s = imax(c0 - reach, 0), e = imin(c1 + reach, len - 1);
-  return Band{s, e - s + 1};
-}
-
-// Query rows of one plane whose windows reach the key rows [y0, y0 + kRowsGroup).
+// windows reach them streamed (na_band_reverse per axis): the query rows of one
+// plane whose windows reach the key rows [y0, y0 + kRowsGroup).
 constexpr Band na_rows_reverse_band(int32_t y0, const NaGeom& g) {
   return na_band_reverse(y0, imin(y0 + kRowsGroup, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
 }

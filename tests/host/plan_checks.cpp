@@ -378,6 +378,58 @@ static int check_rows_reverse(const NaGeom& g, int lds_rows) {
   return 1;
 }
 
+// The backward patch kernels as they walk their rectangles: for every patch, wavefront
+// and lane (a query of the dQ kernel, reverse = false; a key of the dK/dV kernel), the
+// cells it marks (its wavefront's band rows of the rectangle whose row bit is set, its
+// column bits) are exactly its window (the queries that see its key), each once, and
+// every rectangle fits `lds_rows` rows of 32 tokens.
+static int check_patch_bwd(const NaGeom& g, int lds_rows, bool reverse) {
+  if (!na_patch_bwd_eligible(g, lds_rows, reverse)) return 0;
+  const int H = g.grid_h, W = g.grid_w, N = H * W;
+  std::vector<std::vector<int>> want(N);  // sorted, distinct
+  for (int q = 0; q < N; ++q)
+    for (int k : window_keys(g, q)) {
+      if (reverse) want[k].push_back(q);  // q ascending: sorted
+      else want[q].push_back(k);          // from a set: sorted
+    }
+  for (int y0 = 0; y0 < H; y0 += kPatchRows)
+    for (int x0 = 0; x0 < W; x0 += kPatchCols) {
+      const PatchBands pb = reverse ? na_patch_reverse_bands(y0, x0, g) : na_patch_bands(y0, x0, g);
+      EXPECT(pb.rows.count >= 1 && pb.rows.count <= lds_rows && pb.cols.count >= 1 && pb.cols.count <= kPatchKeyCols,
+             "patch rectangle %d x %d", pb.rows.count, pb.cols.count);
+      for (int w = 0; w < 4; ++w) {
+        if (y0 + 2 * w >= H) continue;
+        const int wy0 = y0 + 2 * w;
+        const Band wb = reverse ? na_band_reverse(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h)
+                                : na_band(wy0, imin(wy0 + 1, H - 1), H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+        int off = wb.start - pb.rows.start;
+        off += off < 0 ? H : 0;
+        EXPECT(off >= 0 && off + wb.count <= pb.rows.count, "wavefront band [%d, +%d) inside the rectangle's %d rows",
+               off, wb.count, pb.rows.count);
+        for (int c = 0; c < 32; ++c) {
+          const int cy = wy0 + (c >> 4), cx = x0 + (c & 15);
+          if (cy >= H || cx >= W) continue;
+          const uint32_t cm = band_window_bits(cx, pb.cols, W, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w, reverse);
+          const uint32_t rows_w = band_window_bits(cy, pb.rows, H, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h, reverse);
+          std::vector<int> seen;
+          for (int r = off; r < off + wb.count; ++r) {
+            if (!((rows_w >> r) & 1u)) continue;
+            const int ty = (pb.rows.start + r) % H;
+            for (int x = 0; x < pb.cols.count; ++x)
+              if ((cm >> x) & 1u) seen.push_back(ty * W + (pb.cols.start + x) % W);
+          }
+          const int me = cy * W + cx;
+          std::sort(seen.begin(), seen.end());
+          EXPECT(seen == want[me],  // equal sorted lists: the same cells, each once
+                 "%s patch cells of token %d: %zu, want %zu (grid %dx%d k %d,%d wrap %d%d dil %d,%d)",
+                 reverse ? "dK/dV" : "dQ", me, seen.size(), want[me].size(), H, W, g.kernel_h, g.kernel_w, g.wrap_h,
+                 g.wrap_w, g.dil_h, g.dil_w);
+        }
+      }
+    }
+  return 1;
+}
+
 static void check_causal(int Nq, int Nkv, int BM, int BN) {
   const int n_tiles = (int)cdiv(Nkv, BN);
   for (int q0 = 0; q0 < Nq; q0 += BM) {
@@ -650,7 +702,7 @@ int main() {
   }
   {
     // patch kernel: grids, windows and wrap flags around the limits of na_patch_eligible
-    int eligible = 0, tried = 0;
+    int eligible = 0, tried = 0, bwd_dq = 0, bwd_dkv = 0;
     for (int H : {7, 11, 17, 33, 64})
       for (int W : {9, 17, 32, 33, 64})
         for (int k : {1, 3, 7, 9, 13, 17, 19})
@@ -662,8 +714,17 @@ int main() {
                 if (!geom_valid(g)) continue;
                 ++tried;
                 eligible += check_patch(g, lds_rows);
+                if (lds_rows == 24 && (H + W + k) % 2 == 0) {  // half of the shapes: the ASan run stays short
+                  bwd_dq += check_patch_bwd(g, 24, false);
+                  bwd_dkv += check_patch_bwd(g, 24, true);
+                }
               }
     EXPECT(eligible > 100 && eligible < tried, "patch eligibility covers %d of %d shapes", eligible, tried);
+    EXPECT(bwd_dq > 40 && bwd_dkv > 30 && bwd_dkv <= tried, "backward patch eligibility: dQ %d, dK/dV %d of %d",
+           bwd_dq, bwd_dkv, tried);
+    EXPECT(na_patch_bwd_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1), 24, false) &&
+               na_patch_bwd_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1), 24, true),
+           "64x64 grid, 7x7 wrapped window: both backward patch kernels");
     const NaGeom c4 = geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1);
     EXPECT(na_patch_eligible(c4, 24) && na_patch_eligible(c4, 17), "64x64 grid, 7x7 wrapped window takes the patch kernel");
     EXPECT(na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 24), "and with dilation 2 (20 band rows)");

@@ -114,11 +114,11 @@ def test_attn_bwd_is_two_kernels():
 
 @pytest.mark.parametrize("name,dq,dkv", [
     ("na3d_wrap_20x20x20_k5", "attn_bwd_dq_rows_kernel", "attn_bwd_dkv_rows_kernel"),
-    ("na2d_wrap_64x64_k7", "attn_bwd_dq_kernel", "attn_bwd_dkv_kernel"),
+    ("na2d_wrap_64x64_k7", "attn_bwd_dq_patch_kernel", "attn_bwd_dkv_patch_kernel"),
 ])
 def test_attn_bwd_neighbourhood_kernels(name, dq, dkv):
-    """Grids at most 32 wide take the row kernels (dQ by query rows, dK/dV by key rows); wider grids
-    the tile kernels."""
+    """Grids at most 32 wide take the row kernels (dQ by query rows, dK/dV by key rows); wider grids of
+    one plane the patch kernels (8 x 16 patches over LDS rectangles)."""
     import exact_attention_68_amd as A
 
     w = workloads.WORKLOADS[name]
