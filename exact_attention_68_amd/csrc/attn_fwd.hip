@@ -826,11 +826,16 @@ void attn_fwd_kernel(KernelArgs a) {
     // Remainder split (unmasked problems): whole tiles first, XCD-contiguous so
     // the tiles of one head share an L2; then the parts of the split tiles,
     // each of which leaves its partial result in its own workspace slot.
-    // The parts are XCD-contiguous too, so a tile's parts (and its merge) share an L2.
+    // The parts are numbered part-major (all tiles' part 0, then part 1, ...) and
+    // taken XCD-contiguously, so an XCD holds one key range of consecutive tiles,
+    // mostly of one head: each key range of a head is fetched into one L2, not
+    // into every L2 that holds some part of its tiles.
     const int32_t full = a.split_full, parts = a.split_parts;
     const bool whole = (int32_t)blockIdx.x < full;
-    const int32_t slot = whole ? 0 : xcd_contiguous(blockIdx.x - full, gridDim.x - full);  // parts only
-    const int32_t r = slot / parts;  // split tile (parts only)
+    const int32_t rem = (gridDim.x - full) / parts;
+    const int32_t j = whole ? 0 : xcd_contiguous(blockIdx.x - full, gridDim.x - full);  // parts only
+    const int32_t r = whole ? 0 : j % rem;                // split tile
+    const int32_t slot = whole ? 0 : r * parts + j / rem;  // its slot: part j / rem of tile r
     const int32_t tile = whole ? xcd_contiguous(blockIdx.x, full) : full + r;
     const int32_t bh = tile / a.n_qtiles, qtile = tile - bh * a.n_qtiles;
     segment(bh, qtile, whole ? KvRun{0, n_kv} : part_run(n_kv, parts, slot % parts), oacc, m_run, l_run);

@@ -584,9 +584,10 @@ constexpr WorkItem work_item(int mask, int32_t wg, int32_t n_wg, int32_t n_qtile
 // parts) and writes the tile, while whole tiles are still running.
 //
 // Tiles are numbered head-major (tile = bh * n_qtiles + qtile). Work-group g <
-// full takes a whole tile; the other work-groups take the rem * parts part
-// slots (XCD-contiguous), slot r * parts + p being part p of tile full + r,
-// which covers key tiles [p * n_kv / parts, (p + 1) * n_kv / parts).
+// full takes a whole tile; the other work-groups take the rem * parts parts in
+// part-major order, XCD-contiguously (an XCD holds one key range of consecutive
+// tiles). Part p of tile full + r covers key tiles [p * n_kv / parts, (p + 1) *
+// n_kv / parts) and writes workspace slot r * parts + p.
 struct SplitPlan {
   int32_t full;   // whole tiles (work-groups 0 .. full - 1)
   int32_t rem;    // split tiles; 0 = no split
