@@ -102,6 +102,35 @@ def test_split_deterministic():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+def test_split_concurrent_streams_own_workspaces():
+    """Two streams, each with its own workspace, run split launches at the same time: a split tile's
+    parts meet through the arrival counters of their own workspace only, so both streams' outputs equal
+    the serial ones bit for bit (a counter shared across calls would merge a tile early or never)."""
+    import exact_attention_68_amd as A
+
+    B, H, N, d = 2, 5, 4096, 64
+    ins = [[t.cuda() for t in _qkv(B, H, N, d, 8250 + i)] for i in range(2)]
+    wss = [split_workspace(B, H, N, d, A.ATTN_MASK_NONE) for _ in range(2)]
+    assert all(ws is not None for ws in wss)
+    ref = []
+    for (q, k, v), ws in zip(ins, wss):
+        o = torch.empty_like(q)
+        A.attn_fwd_ws(q, k, v, o, 0.125, A.ATTN_MASK_NONE, None, ws)
+        ref.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(ins[i][0]) for _ in range(8)] for i in range(2)]
+    for it in range(8):  # interleaved launches: the two streams' kernels overlap on the device
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                q, k, v = ins[i]
+                A.attn_fwd_ws(q, k, v, outs[i][it], 0.125, A.ATTN_MASK_NONE, None, wss[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for it in range(8):
+            assert torch.equal(outs[i][it], ref[i]), f"stream {i}, call {it} differs from the serial output"
+
+
 def test_split_workspace_reused_across_shapes():
     """One workspace, sized for the largest problem, serves other sizes and head sizes in turn."""
     import exact_attention_68_amd as A
