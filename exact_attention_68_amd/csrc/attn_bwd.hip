@@ -940,7 +940,10 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
 template <int D>
 struct BwdPatchCfg {
   static constexpr int ROWS = bwd_patch_lds(D);  // rows of 32 tokens per rectangle
-  static constexpr int PARTS = 2;
+  // d = 32: two wavefronts per SIMD (the parts); d = 64: the rectangles take 136-140 KB,
+  // so one work-group of one wavefront per SIMD, which then gets the whole register file
+  static constexpr int PARTS = D == 32 ? 2 : 1;
+  static constexpr int WAVES_PER_EU = PARTS;
   static constexpr int THREADS = 256 * PARTS;
   static constexpr int RC = D / 8;
   static constexpr int CHUNKS = ROWS * kPatchKeyCols * RC;
@@ -985,13 +988,13 @@ __device__ __forceinline__ uint32_t block_elem_bits(uint32_t cm, int half) {
 
 // dQ by query patches; also forms D of its queries for the dK/dV kernel.
 template <int D>
-__global__ __launch_bounds__(BwdPatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(BwdPatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(BwdPatchCfg<D>::WAVES_PER_EU)))
 void attn_bwd_dq_patch_kernel(BwdArgs a) {
   using P = BwdPatchCfg<D>;
   constexpr int KB = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[P::ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[P::ELEMS];
-  __shared__ float merge_lds[4 * DT * 16 * 64];  // the second part's dQ
+  __shared__ float merge_lds[P::PARTS > 1 ? 4 * DT * 16 * 64 : 1];  // the second part's dQ
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave = wave8 & 3, part = wave8 >> 2;
@@ -1080,26 +1083,27 @@ void attn_bwd_dq_patch_kernel(BwdArgs a) {
       if (!nxt) break;
     }
   }
-  // the second part's sums join the first's (lane order), which stores
-  float* slot = merge_lds + wave * DT * 16 * 64 + lane;
-  if (part == 1) {
+  if constexpr (P::PARTS > 1) {  // the second part's sums join the first's (lane order), which stores
+    float* slot = merge_lds + wave * DT * 16 * 64 + lane;
+    if (part == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) slot[(dt * 16 + e) * 64] = dq[dt][e];
+    }
+    __syncthreads();
+    if (part == 1) return;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) slot[(dt * 16 + e) * 64] = dq[dt][e];
+      for (int e = 0; e < 16; ++e) dq[dt][e] += slot[(dt * 16 + e) * 64];
   }
-  __syncthreads();
-  if (part == 1) return;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dq[dt][e] += slot[(dt * 16 + e) * 64];
   store_rows_scaled<D>(a.dq + head * D, q_row, N, half, dq, a.scale);
 }
 
 // dK and dV by key patches over the rectangle of queries whose windows reach them.
 template <int D>
-__global__ __launch_bounds__(BwdPatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(BwdPatchCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(BwdPatchCfg<D>::WAVES_PER_EU)))
 void attn_bwd_dkv_patch_kernel(BwdArgs a) {
   using P = BwdPatchCfg<D>;
   constexpr int KB = D / 16, DT = D / 32, TOK = P::ROWS * kPatchKeyCols;
@@ -1107,7 +1111,7 @@ void attn_bwd_dkv_patch_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds[P::ELEMS];
   __shared__ __attribute__((aligned(16))) float l2_lds[TOK];
   __shared__ __attribute__((aligned(16))) float dl_lds[TOK];
-  __shared__ float merge_lds[4 * 2 * DT * 16 * 64];  // the second part's dK and dV
+  __shared__ float merge_lds[P::PARTS > 1 ? 4 * 2 * DT * 16 * 64 : 1];  // the second part's dK and dV
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave = wave8 & 3, part = wave8 >> 2;
@@ -1213,25 +1217,27 @@ void attn_bwd_dkv_patch_kernel(BwdArgs a) {
       if (!nxt) break;
     }
   }
-  float* slot = merge_lds + wave * 2 * DT * 16 * 64 + lane;
-  if (part == 1) {
+  if constexpr (P::PARTS > 1) {
+    float* slot = merge_lds + wave * 2 * DT * 16 * 64 + lane;
+    if (part == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          slot[(dt * 16 + e) * 64] = dk[dt][e];
+          slot[((DT + dt) * 16 + e) * 64] = dv[dt][e];
+        }
+    }
+    __syncthreads();
+    if (part == 1) return;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        slot[(dt * 16 + e) * 64] = dk[dt][e];
-        slot[((DT + dt) * 16 + e) * 64] = dv[dt][e];
+        dk[dt][e] += slot[(dt * 16 + e) * 64];
+        dv[dt][e] += slot[((DT + dt) * 16 + e) * 64];
       }
   }
-  __syncthreads();
-  if (part == 1) return;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dk[dt][e] += slot[(dt * 16 + e) * 64];
-      dv[dt][e] += slot[((DT + dt) * 16 + e) * 64];
-    }
   store_rows_scaled<D>(a.dk + head * D, k_row, N, half, dk, a.scale);
   store_rows_scaled<D>(a.dv + head * D, k_row, N, half, dv, 1.0f);
 }
@@ -1246,6 +1252,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   if constexpr (MASK == MASK_NA && D == 32) {
     dq_rows = a.dq_rows != 0;
     dkv_rows = a.dkv_rows != 0;
+  }
+  if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     dq_patch = !dq_rows && a.dq_patch != 0;
     dkv_patch = !dkv_rows && a.dkv_patch != 0;
   }
@@ -1253,6 +1261,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const dim3 patch_grid(dq_patch || dkv_patch ? a.BH * a.patch_nx * a.patch_ny : 1);
   if constexpr (MASK == MASK_NA && D == 32) {
     if (dq_rows) hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+  }
+  if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     if (dq_patch)
       hipLaunchKernelGGL((attn_bwd_dq_patch_kernel<D>), patch_grid, dim3(BwdPatchCfg<D>::THREADS), 0, stream, a);
   }
@@ -1262,6 +1272,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if constexpr (MASK == MASK_NA && D == 32) {
     if (dkv_rows) hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+  }
+  if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     if (dkv_patch)
       hipLaunchKernelGGL((attn_bwd_dkv_patch_kernel<D>), patch_grid, dim3(BwdPatchCfg<D>::THREADS), 0, stream, a);
   }

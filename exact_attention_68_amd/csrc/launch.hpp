@@ -108,7 +108,7 @@ constexpr int32_t bwd_dq_rows_lds(int64_t d) { return d == 32 ? 10 : 0; }
 constexpr int32_t bwd_dkv_rows_lds(int64_t d) { return d == 32 ? 8 : 0; }
 
 // Rows (of 32 tokens) of the LDS rectangles of the backward patch kernels for head size d.
-constexpr int32_t bwd_patch_lds(int64_t d) { return d == 32 ? 24 : 0; }
+constexpr int32_t bwd_patch_lds(int64_t d) { return d == 32 ? 24 : d == 64 ? 17 : 0; }
 
 // Launches the two backward kernels on `stream`: dQ (which also forms D = rowsum(dO * O)
 // in the workspace), then dK and dV.

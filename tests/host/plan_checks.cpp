@@ -714,9 +714,10 @@ int main() {
                 if (!geom_valid(g)) continue;
                 ++tried;
                 eligible += check_patch(g, lds_rows);
-                if (lds_rows == 24 && (H + W + k) % 2 == 0) {  // half of the shapes: the ASan run stays short
-                  bwd_dq += check_patch_bwd(g, 24, false);
-                  bwd_dkv += check_patch_bwd(g, 24, true);
+                // each shape once, at one of the two rectangle sizes (d = 32: 24 rows, d = 64: 17)
+                if ((H + W + k + lds_rows) % 2 == 0) {
+                  bwd_dq += check_patch_bwd(g, lds_rows, false);
+                  bwd_dkv += check_patch_bwd(g, lds_rows, true);
                 }
               }
     EXPECT(eligible > 100 && eligible < tried, "patch eligibility covers %d of %d shapes", eligible, tried);

@@ -98,7 +98,7 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (20, 32, 5, 5, 0, 1, 1, 1)),               # clamped 5-row windows: dK/dV back on the tile kernel
     ("na2d", (16, 20, 3, 5, 1, 0, 2, 2)),               # dilated rows and columns
     ("na2d", (9, 1, 3, 1, 1, 0, 1, 1)),                 # one column
-    # wider single-plane grids at d = 32: the patch kernels (8 x 16 patches over LDS rectangles)
+    # wider single-plane grids at d = 32 and 64: the patch kernels (8 x 16 patches over LDS rectangles)
     ("na2d", (20, 40, 5, 5, 1, 1, 1, 1)),
     ("na2d", (17, 48, 7, 3, 0, 0, 1, 1)),               # clamped: reverse rectangles near the borders
     ("na2d", (24, 36, 3, 7, 1, 0, 2, 1)),               # dilated rows, clamped columns
