@@ -646,7 +646,7 @@ __device__ __forceinline__ int32_t band_plane(const Band& bz, int32_t i_own, int
 // P = 2^(c s - lse2) (hidden keys 0), dS = P (dP - D), dQ^T += K^T dS^T; also
 // forms D of its queries for the dK/dV kernel, as the tile kernel does.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 ? 2 : 1)))
 void attn_bwd_dq_rows_kernel(BwdArgs a) {
   using R = RowStage<D, bwd_dq_rows_lds(D)>;
   constexpr int KB = D / 16, DT = D / 32;
@@ -773,7 +773,7 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
 // dP = dO V^T, P = 2^(c s - lse2) (hidden pairs 0), dS = P (dP - D), dV^T +=
 // dO^T P, dK^T += Q^T dS. Each stage also holds its queries' lse2 and D.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 ? 2 : 1)))
 void attn_bwd_dkv_rows_kernel(BwdArgs a) {
   using R = RowStage<D, bwd_dkv_rows_lds(D)>;
   constexpr int KB = D / 16, DT = D / 32, TOK = R::ROWS * 32;
@@ -1249,7 +1249,7 @@ static_assert(BwdCfg<32>::WAVES_PER_EU == bwd_wgs_per_cu(32) && BwdCfg<64>::WAVE
 template <int D, int MASK>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   bool dq_rows = false, dkv_rows = false, dq_patch = false, dkv_patch = false;
-  if constexpr (MASK == MASK_NA && D == 32) {
+  if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     dq_rows = a.dq_rows != 0;
     dkv_rows = a.dkv_rows != 0;
   }
@@ -1259,7 +1259,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   }
   const dim3 rows_grid(dq_rows || dkv_rows ? a.BH * a.na.grid_d * a.row_groups : 1);
   const dim3 patch_grid(dq_patch || dkv_patch ? a.BH * a.patch_nx * a.patch_ny : 1);
-  if constexpr (MASK == MASK_NA && D == 32) {
+  if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     if (dq_rows) hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
   }
   if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
@@ -1270,7 +1270,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3(a.BH * a.n_qtiles), dim3(BwdCfg<D>::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (MASK == MASK_NA && D == 32) {
+  if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     if (dkv_rows) hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
   }
   if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {

@@ -58,6 +58,7 @@ hipError_t static_scratch(void** ptr);
 constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 24 : d == 64 ? 17 : 0; }
 
 // Key rows per LDS stage of the row kernel of narrow grids for head size d (0: none).
+// (d = 64 with 8-row stages, one wavefront per SIMD, ran 0.89x the tile kernel on the 20x20x20 volume.)
 constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : 0; }
 
 // Work-groups of the backward kernels resident per CU: two at d <= 64 and one at d = 128
@@ -104,8 +105,8 @@ struct BwdArgs {
 
 // Key rows per LDS stage of the dQ row kernel and query rows per stage of the dK/dV
 // row kernel for head size d (0: no row kernel at that size).
-constexpr int32_t bwd_dq_rows_lds(int64_t d) { return d == 32 ? 10 : 0; }
-constexpr int32_t bwd_dkv_rows_lds(int64_t d) { return d == 32 ? 8 : 0; }
+constexpr int32_t bwd_dq_rows_lds(int64_t d) { return d == 32 ? 10 : d == 64 ? 8 : 0; }
+constexpr int32_t bwd_dkv_rows_lds(int64_t d) { return d == 32 || d == 64 ? 8 : 0; }
 
 // Rows (of 32 tokens) of the LDS rectangles of the backward patch kernels for head size d.
 constexpr int32_t bwd_patch_lds(int64_t d) { return d == 32 ? 24 : d == 64 ? 17 : 0; }

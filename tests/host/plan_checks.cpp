@@ -747,6 +747,7 @@ int main() {
                 if (!geom_valid(g)) continue;
                 ++tried;
                 eligible += check_rows(g, 10);
+                if (W % 2 == 1) check_rows(g, 8);  // the backward dQ row kernel's stages at d = 64
                 eligible_rev += check_rows_reverse(g, 8);
               }
     EXPECT(eligible > 100 && eligible < tried, "row-kernel eligibility covers %d of %d shapes", eligible, tried);
