@@ -979,6 +979,88 @@ __device__ __forceinline__ void window_step(const uint16_t* const (&kb)[4], cons
       }
 }
 
+// The same walk one key row (32-key block) at a time, for the row and patch
+// kernels: the scores of the next visible row are issued on the matrix core
+// before the current row's exponentials (row_scores), and row_update takes one
+// row's softmax and P V. The row is in the lane's window (live) or hidden for
+// it; inside it the lane's column bias decides. A lane's reference maximum is
+// set by the first row that holds a visible key for it (m_run starts at the
+// sentinel -FLT_MAX; a lane outside the grid starts at 0 and never sees one) and
+// moved only past the 2^20 row-sum guard, per row.
+template <int D>
+__device__ __forceinline__ f32x16_t row_scores(const uint16_t* krow, const bf16x8_t (&qf)[D / 16], int col, int half,
+                                               int k_swz) {
+  f32x16_t s = f32x16_t{};
+#pragma unroll
+  for (int kb_ = 0; kb_ < D / 16; ++kb_) {
+    const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(krow + col * D + (((2 * kb_ + half) ^ k_swz) << 3));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qf[kb_], s, 0, 0, 0);
+  }
+  return s;
+}
+
+template <int D>
+__device__ __forceinline__ void row_update(const f32x16_t& s, const uint16_t* vrow, const float (&bias)[16],
+                                           bool live, float c, const int (&v_row)[2], const int (&v_off)[2][D / 32],
+                                           f32x16_t (&oacc)[D / 32], float& m_run, float& l_run) {
+  constexpr int DT = D / 32;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto row_max = [&]() {  // c * (largest visible score of the row), -FLT_MAX when there is none
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, live ? __builtin_fmaf(s[e], c, bias[e]) : -INFINITY);
+    mx = swap_halves_max(mx);
+    return mx == -INFINITY ? -FLT_MAX : mx;
+  };
+  if (__builtin_amdgcn_ballot_w64(m_run == -FLT_MAX)) {  // some lane has seen no visible key yet
+    const float mx = row_max();
+    m_run = m_run == -FLT_MAX ? mx : m_run;
+  }
+  bf16x8_t p[2];
+  auto probs = [&]() {
+    float nb[16];  // the exponent's addend: bias - m for a row in the window, -inf otherwise
+#pragma unroll
+    for (int e = 0; e < 16; ++e) nb[e] = live ? bias[e] - m_run : -INFINITY;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int e0 = kb2 * 8 + e, e1 = e0 + 1;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e0], c, nb[e0]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e1], c, nb[e1]));
+        const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+        p[kb2][e] = pp[0];
+        p[kb2][e + 1] = pp[1];
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+      }
+    return psum;
+  };
+  float psum = probs();
+  if (__builtin_amdgcn_ballot_w64(!(psum <= kSafeSum))) {  // rare: a row's maximum moved far up
+    const float m_new = fmaxf(m_run, row_max());
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    l_run *= alpha;
+    psum = probs();
+  }
+  l_run += psum;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x2_t x[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        x[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                               (lds_s16x4*)((lds_u16*)vrow + (kb2 * 16 + v_row[h]) * D + v_off[h][dt])));
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0][0], x[0][1], x[1][0], x[1][1]});
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[kb2], oacc[dt], 0, 0, 0);
+    }
+}
+
 template <int D>
 struct PatchCfg {
   // key rows (32 keys each) of the K and of the V rectangle in LDS: 96 KB in all at
@@ -1131,6 +1213,9 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) bias[e] = ((cm16 >> e) & 1u) ? 0.f : -INFINITY;
 
+  // four key rows per step (window_step): with a wavefront's few rows per part, the four
+  // blocks' independent products keep the matrix core busier than a row-by-row walk
+  // (row_update), which ran 0.78-0.93x here
   for (int32_t st = part; st < n_steps; st += P::PARTS) {
     const int32_t r0 = off + SB * st;  // first band row of the step (r0 + 3 < pb.rows.count + 3)
     const uint16_t* kb[SB];
@@ -1195,8 +1280,10 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
 // stages; a stage holds the work-group's band of key rows of one plane, each row
 // as one 32-key block. A wavefront's window over a stage is uniform in its rows
 // (the key row is in or out for every lane) and the lane's own column bits inside
-// a block, so each wavefront runs over just its visible rows, four per step
-// (window_step), with the lane's column bits as the block mask.
+// a block, so each wavefront runs over just its visible rows, one at a time with
+// the next row's scores issued before this row's exponentials (row_scores,
+// row_update), with the lane's column bits as the exponent's addend. (Four rows per
+// step through window_step, with no overlap between steps, ran 0.75x.)
 template <int D>
 struct RowsCfg {
   static constexpr int ROWS = 10;  // key rows per stage: 20 KB of K or V at d = 32
@@ -1212,7 +1299,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_na_rows_kernel(KernelArgs a) {
   using R = RowsCfg<D>;
-  constexpr int KB = D / 16, DT = D / 32, SB = 4, RC = D / 8;
+  constexpr int KB = D / 16, DT = D / 32, RC = D / 8;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][R::ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][R::ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -1294,7 +1381,6 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
     rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, yk) << r;
   }
   rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
-  const int n_vis = __builtin_popcount(rows_vis);
   auto next_plane = [&](int32_t j) {  // first visit from j whose plane is in the window (uniform)
     while (j < bz.count && __builtin_amdgcn_readfirstlane((int)bit128(gm.z0, gm.z1, plane_at(j))) == 0) ++j;
     return j;
@@ -1316,10 +1402,8 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
   f32x16_t oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16_t{};
-  float m_run = -FLT_MAX, l_run = 0.f;
+  float m_run = q_ok ? -FLT_MAX : 0.f, l_run = 0.f;  // row_update sets a lane's maximum at its first visible key
   bf16x8_t qf[KB];
-  bool first = true;  // the walk's first step sets the reference maximum: any visible row
-                      // holds a visible key of every query of the row (its column window)
   for (int32_t i = 0, it = 0, stage = 0; i < bz.count; ++it, stage ^= 1) {
     const int32_t i_next = next_plane(i + 1);
     const bool more = i_next < bz.count;
@@ -1341,22 +1425,26 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
       }
       if (more) load_stage(plane_at(i_next), stage ^ 1);
     }
-    // this wavefront's visible rows of the stage, four per step (the last step takes the rest)
+    // this wavefront's visible rows of the stage, in order, one at a time: the next row's
+    // scores are issued before this row's exponentials
+    const uint16_t* ks = k_lds[stage];
+    const uint16_t* vs = v_lds[stage];
     uint32_t rem = rows_vis;
-    for (int left = n_vis; left > 0; left -= SB) {
-      const uint16_t* kb[SB];
-      const uint16_t* vb[SB];
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        const int32_t r = rem != 0u ? __builtin_ctz(rem) : 0;
+    if (rem != 0u) {
+      int32_t r = __builtin_ctz(rem);
+      f32x16_t s_nx = row_scores<D>(ks + r * 32 * D, qf, col, half, k_swz);
+      while (true) {
+        const f32x16_t s = s_nx;
+        const int32_t rc = r;
         rem &= rem - 1u;
-        kb[sb] = k_lds[stage] + r * 32 * D;
-        vb[sb] = v_lds[stage] + r * 32 * D;
+        const bool nxt = rem != 0u;
+        if (nxt) {
+          r = __builtin_ctz(rem);
+          s_nx = row_scores<D>(ks + r * 32 * D, qf, col, half, k_swz);
+        }
+        row_update<D>(s, vs + rc * 32 * D, bias, true, c, v_row, v_off, oacc, m_run, l_run);
+        if (!nxt) break;
       }
-      const bool live[SB] = {true, true, true, true};  // visible rows only (and the lane's columns)
-      window_step<D>(kb, vb, live, bias, left < SB ? left : SB, first, qf, c, col, half, k_swz, v_row, v_off, oacc,
-                     m_run, l_run);
-      first = false;
     }
     __syncthreads();  // every wavefront is done with this stage before it is refilled
     i = i_next;
