@@ -224,6 +224,27 @@ def test_rescale_path_planted_keys(mask, entry):
     check_case(q.to(torch.bfloat16), k.to(torch.bfloat16), v, 0.25, mask, what="planted keys", entry=entry)
 
 
+@pytest.mark.parametrize("mode,geo", [
+    ("na3d", (8, 8, 8, 5, 5, 5, 1, 0, 1, 1, 1, 1)),   # the row kernel (a grid 8 wide)
+    ("na2d", (24, 48, 7, 7, 0, 1, 1, 1)),             # the patch kernel
+])
+def test_rescale_path_planted_keys_windows(mode, geo):
+    """Keys whose scores climb by about 30 (base 2) from one grid row to the next (rows clamped, so
+    a walk meets them in rising order): the row kernel's walk and the patch kernel's steps move the
+    reference maximum past the 2^20 row-sum guard again and again."""
+    import exact_attention_68_amd as A
+
+    params = A.na3d_params(*geo) if mode == "na3d" else A.na2d_params(*geo)
+    H, W = (geo[1], geo[2]) if mode == "na3d" else (geo[0], geo[1])
+    N = geo[0] * geo[1] * (geo[2] if mode == "na3d" else 1)
+    q, k, v = _qkv(1, 2, N, 32, 8600)
+    q = q.float().abs() + 0.5                                # positive queries
+    y = (torch.arange(N) // W) % H                           # each key's grid row
+    k = (k.float().abs() + 0.25) * (1.0 + 2.0 * y).view(1, 1, N, 1)
+    check_case(q.to(torch.bfloat16), k.to(torch.bfloat16), v, 0.25, mode, params, what=f"planted keys {mode}",
+               entry="attn_fwd_ex")
+
+
 # ---------------------------------------------------------------- 2D neighbourhood
 def test_na2d_issue_example_5x5():
     """NATTEN issue 142: q = k = 1, v one-hot at the top-left pixel, 5x5 grid, kernel 3, wrap."""
