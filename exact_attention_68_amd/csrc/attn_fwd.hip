@@ -878,8 +878,8 @@ void attn_fwd_kernel(KernelArgs a) {
 // output, maximum and row sums in LDS and the first combines them exactly (the
 // rescaling by 2^(m_i - m) of the running-softmax paragraph of PhotoRoom's
 // xformers post) and stores.
-// One step of a neighbourhood walk over key rows held in LDS (the patch and row
-// kernels): the first nblk (1..4, uniform) of four 32-key blocks, block b at kb[b]
+// One step of a neighbourhood walk over key rows held in LDS (the patch kernel):
+// the first nblk (1..4, uniform) of four 32-key blocks, block b at kb[b]
 // and vb[b] (32 rows of D elements, swizzled as the tile rings). Element e of a
 // block is key 8 (e / 4) + 4 half + e % 4. The window: a block whose key row is in
 // the lane's window (live[b]) takes the lane's per-element bias over the row's
