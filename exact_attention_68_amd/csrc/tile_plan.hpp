@@ -189,6 +189,7 @@ constexpr bool na_axis_ok(int32_t cq, int32_t ck, int32_t len, int32_t kernel, i
 // and L_g is the length of the sub-grid of cells congruent to g.
 constexpr int32_t na_dil_anchor(int32_t cq, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil) {
   if (wrap) return cq;
+  if (dil == 1) return iclamp(cq - rad, 0, len - kernel);  // the same, without the divisions
   const int32_t g = cq % dil;
   const int32_t sub_len = (len - 1 - g) / dil + 1;
   return g + dil * iclamp(cq / dil - rad, 0, sub_len - kernel);
@@ -204,9 +205,11 @@ constexpr bool na_dil_ok(int32_t anchor, int32_t ck, int32_t len, int32_t kernel
     f += f < 0 ? len : 0;          // forward distance in [0, len)
     const int32_t b = len - f;     // backward distance in (0, len]
     const int32_t reach = rad * dil;
+    if (dil == 1) return f <= reach || b <= reach;  // every distance is a multiple of 1
     return (f <= reach && f % dil == 0) || (b <= reach && b % dil == 0);
   }
   const int32_t off = ck - anchor;
+  if (dil == 1) return (uint32_t)off <= (uint32_t)(kernel - 1);
   return (uint32_t)off <= (uint32_t)((kernel - 1) * dil) && off % dil == 0;
 }
 
@@ -239,7 +242,10 @@ constexpr void na_axis_mask(int32_t c, int32_t len, int32_t kernel, int32_t rad,
   lo = hi = 0;
   const int32_t anchor = na_dil_anchor(c, len, kernel, rad, wrap, dil);
   for (int32_t t = 0; t < kernel; ++t) {
-    const int32_t cell = wrap ? imod(c + dil * (t - rad), len) : anchor + dil * t;
+    // wrapped: c + dil (t - rad) lies in (-len, 2 len) since (kernel - 1) dil < len
+    int32_t cell = wrap ? c + dil * (t - rad) : anchor + dil * t;
+    cell += cell < 0 ? len : 0;
+    cell -= cell >= len ? len : 0;
     const uint64_t bit = 1ull << (cell & 63);
     lo |= cell < 64 ? bit : 0ull;
     hi |= cell < 64 ? 0ull : bit;
@@ -424,8 +430,17 @@ constexpr PatchBands na_patch_reverse_bands(int32_t y0, int32_t x0, const NaGeom
 // the query and cell i as the key (reverse = false) or the other way round.
 constexpr uint32_t band_window_bits(int32_t c, Band b, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
                                     int32_t dil, bool reverse) {
-  const int32_t anchor = na_dil_anchor(c, len, kernel, rad, wrap, dil);
   uint32_t m = 0;
+  if (dil == 1) {  // the undilated predicate: compares only (the dilated one divides by dil)
+    for (int32_t i = 0; i < b.count; ++i) {
+      int32_t x = b.start + i;
+      x -= x >= len ? len : 0;
+      const bool ok = reverse ? na_axis_ok(x, c, len, kernel, rad, wrap) : na_axis_ok(c, x, len, kernel, rad, wrap);
+      m |= (uint32_t)ok << i;
+    }
+    return m;
+  }
+  const int32_t anchor = na_dil_anchor(c, len, kernel, rad, wrap, dil);
   for (int32_t i = 0; i < b.count; ++i) {
     int32_t x = b.start + i;
     x -= x >= len ? len : 0;
