@@ -44,7 +44,10 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+/* 6: the split workspace of attn_fwd_ws / attn_fwd_ex also holds one arrival
+ * counter per split tile (its size grew by at most 1 KB), and ATTN_STATIC_SCRATCH_BYTES
+ * with it; signatures are unchanged. */
+#define ATTN_ABI_VERSION 6
 
 /* Mask modes. */
 typedef enum {
