@@ -113,6 +113,22 @@ def test_bwd_neighbourhood(mode, geo, d):
     check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mode, what=f"bwd {mode} {geo}", params=params)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1e-3])
+@pytest.mark.parametrize("mode,geo", [
+    ("na3d", (6, 7, 9, 3, 5, 3, 1, 1, 0, 1, 1, 1)),   # the row kernels
+    ("na2d", (20, 40, 5, 7, 1, 0, 1, 1)),             # the patch kernels
+])
+def test_bwd_neighbourhood_scales(mode, geo, scale):
+    """Scale 0 (every visible key weighs the same), a negative scale (the flipped sign bits of K in the
+    dK/dV kernels, of Q in the dQ kernels) and a tiny one, through the row and patch kernels at d = 32."""
+    import exact_attention_68_amd as A
+
+    params = A.na2d_params(*geo) if mode == "na2d" else A.na3d_params(*geo)
+    N = geo[0] * geo[1] * (geo[2] if mode == "na3d" else 1)
+    q, k, v, do = _inputs(1, 2, N, N, 32, 11700 + N)
+    check_bwd_case(q, k, v, do, scale, mode, what=f"bwd {mode} {geo} scale {scale}", params=params)
+
+
 def test_bwd_neighbourhood_workload_shape():
     """The 64x64 7x7 wrapped window of the 2D workload (B2 H4 d32), through the GPU forward."""
     import exact_attention_68_amd as A

@@ -131,6 +131,18 @@ def test_na3d_shapes(geo, d):
     check_case(q, k, v, 1 / math.sqrt(d), "na3d", A.na3d_params(*geo), what=f"na3d {geo}", entry=EX)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1e-3])
+def test_na3d_row_kernel_scales(scale):
+    """Scale 0, a negative scale and a tiny one through the row kernel's walk (d = 32, a grid 9 wide):
+    each lane's reference maximum is set at its first visible key whatever the scale."""
+    import exact_attention_68_amd as A
+
+    geo = (6, 7, 9, 3, 5, 3, 1, 1, 0, 1, 1, 1)
+    N = geo[0] * geo[1] * geo[2]
+    q, k, v = _qkv(1, 2, N, N, 32, 9700 + N)
+    check_case(q, k, v, scale, "na3d", A.na3d_params(*geo), what=f"na3d rows scale {scale}", entry=EX)
+
+
 # ---------------------------------------------------------------- dilated 2D windows
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("gh,gw,kh,kw,wh,ww,dh,dw", [
