@@ -95,7 +95,7 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na3d", (5, 9, 20, 3, 5, 5, 0, 1, 1, 1, 1, 1)),    # clamped planes, 9 rows (a partial group)
     ("na3d", (4, 6, 32, 3, 3, 7, 1, 0, 0, 1, 1, 1)),    # 32 wide, clamped rows and columns
     ("na2d", (12, 31, 3, 7, 0, 0, 1, 1)),               # clamped both ways: reverse bands near the borders
-    ("na2d", (20, 32, 5, 5, 0, 1, 1, 1)),               # clamped 5-row windows: dK/dV back on the tile kernel
+    ("na2d", (20, 32, 5, 5, 0, 1, 1, 1)),               # clamped 5-row windows: dK/dV on the patch kernel (reverse row bands past 8)
     ("na2d", (16, 20, 3, 5, 1, 0, 2, 2)),               # dilated rows and columns
     ("na2d", (9, 1, 3, 1, 1, 0, 1, 1)),                 # one column
     # wider single-plane grids at d = 32 and 64: the patch kernels (8 x 16 patches over LDS rectangles)
