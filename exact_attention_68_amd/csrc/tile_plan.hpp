@@ -440,13 +440,24 @@ constexpr uint32_t band_window_bits(int32_t c, Band b, int32_t len, int32_t kern
     }
     return m;
   }
-  const int32_t anchor = na_dil_anchor(c, len, kernel, rad, wrap, dil);
-  for (int32_t i = 0; i < b.count; ++i) {
+  if (wrap || !reverse) {
+    // the window's kernel cells, dil apart (a wrapped window is symmetric, so also its reverse),
+    // placed at their offsets in the band; no cell repeats ((kernel - 1) * dil < len)
+    const int32_t first = wrap ? c - rad * dil : na_dil_anchor(c, len, kernel, rad, wrap, dil);
+    for (int32_t t = 0; t < kernel; ++t) {
+      int32_t cell = first + dil * t;  // within (-len, 2 len)
+      cell += cell < 0 ? len : 0;
+      cell -= cell >= len ? len : 0;
+      int32_t i = cell - b.start;
+      i += i < 0 ? len : 0;
+      m |= i < b.count ? uint32_t{1} << i : 0u;
+    }
+    return m;
+  }
+  for (int32_t i = 0; i < b.count; ++i) {  // clamped and dilated, the queries that see cell c
     int32_t x = b.start + i;
     x -= x >= len ? len : 0;
-    const bool ok = reverse ? na_dil_ok(na_dil_anchor(x, len, kernel, rad, wrap, dil), c, len, kernel, rad, wrap, dil)
-                            : na_dil_ok(anchor, x, len, kernel, rad, wrap, dil);
-    m |= (uint32_t)ok << i;
+    m |= (uint32_t)na_dil_ok(na_dil_anchor(x, len, kernel, rad, wrap, dil), c, len, kernel, rad, wrap, dil) << i;
   }
   return m;
 }
