@@ -77,40 +77,37 @@ constexpr Band na_band(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int3
     if (count >= len) return Band{0, len};
     return Band{imod(c0 - rad * dil, len), count};
   }
-  if (dil == 1) {
-    // clamped windows start at clamp(c - r, 0, L - k), a non-decreasing function of c
-    const int32_t s0 = iclamp(c0 - rad, 0, len - kernel);
-    const int32_t s1 = iclamp(c1 - rad, 0, len - kernel);
-    return Band{s0, s1 + kernel - s0};
-  }
-  // a clamped dilated window holds its query's cell and spans (kernel - 1) * dil cells
-  const int32_t reach = (kernel - 1) * dil;
-  const int32_t s = imax(c0 - reach, 0), e = imin(c1 + reach, len - 1);
+  // Clamped: the window of c is c - rad dil ... c + rad dil, pushed inwards near the
+  // ends (na_dil_anchor). A window pushed back from the far end still starts at or
+  // after len - kernel dil (its last cell is its sub-grid's, within dil of the end),
+  // one pushed from the near end ends at or before kernel dil - 1 (its first cell is
+  // its sub-grid's, below dil). Exact at dil = 1, where the window starts at
+  // clamp(c - rad, 0, len - kernel), a non-decreasing function of c.
+  const int32_t s = imax(0, imin(c0 - rad * dil, len - kernel * dil));
+  const int32_t e = imin(len - 1, imax(c1 + rad * dil, kernel * dil - 1));
   return Band{s, e - s + 1};
 }
 
 // Along one axis, the query coordinates whose window holds some key coordinate in
 // [c0, c1]: a wrapped window is symmetric (query c sees key c' iff key c sees
-// query c'), so it is na_band itself; a clamped window of dilation 1 starts at
-// s(c) = clamp(c - rad, 0, len - kernel), non-decreasing, so the queries form one
-// run from the first with s(c) + kernel > c0 to the last with s(c) <= c1; a
-// clamped dilated window holds its query and spans (kernel - 1) * dil cells, so a
-// run of that reach around [c0, c1] holds them (a superset; the per-axis reverse
-// masks decide).
+// query c'), so it is na_band itself. On a clamped axis the queries of key x share
+// its residue mod dil and, on that sub-grid, run from x's sub-coordinate less rad
+// to it plus rad, except that the first kernel cells of the sub-grid are seen from
+// its first cell on (by the windows pushed inwards) and its last kernel cells up to
+// its last: so the queries of keys at or past kernel dil start within rad dil
+// before them, and those of keys before len - kernel dil end within rad dil after
+// them. Exact at dil = 1 (the window start clamp(c - rad, 0, len - kernel) is
+// non-decreasing in c); a superset by less than dil cells at each end otherwise.
 constexpr Band na_band_reverse(int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap,
                                int32_t dil) {
   if (wrap) return na_band(c0, c1, len, kernel, rad, wrap, dil);
-  if (dil == 1) {
-    const int32_t first = c0 - kernel + 1 <= 0 ? 0 : c0 - kernel + 1 + rad;
-    const int32_t last = c1 >= len - kernel ? len - 1 : c1 + rad;
-    return Band{first, last - first + 1};
-  }
-  const int32_t reach = (kernel - 1) * dil;
-  const int32_t s = imax(c0 - reach, 0), e = imin(c1 + reach, len - 1);
-  return Band{s, e - s + 1};
+  const int32_t first = c0 >= kernel * dil ? c0 - rad * dil : 0;
+  const int32_t last = c1 < len - kernel * dil ? c1 + rad * dil : len - 1;
+  return Band{first, last - first + 1};
 }
 
-constexpr KvRun kv_run(int mask, int32_t Nq, int32_t Nkv, int32_t BM, int32_t BN, int32_t q0, const NaGeom& g) {
+constexpr KvRun kv_run(int mask, int32_t Nq, int32_t Nkv, int32_t BM, int32_t BN, int32_t q0, const NaGeom& g,
+                       bool reverse = false) {
   const int32_t n_tiles = (int32_t)cdiv(Nkv, BN);
   const int32_t q_last = imin(q0 + BM, Nq) - 1;
   if (mask == MASK_CAUSAL) return KvRun{0, imin(q_last / BN + 1, n_tiles)};
@@ -118,11 +115,14 @@ constexpr KvRun kv_run(int mask, int32_t Nq, int32_t Nkv, int32_t BM, int32_t BN
   const int32_t N = Nkv;  // = Nq for the neighbourhood masks
   const int32_t plane = g.grid_h * g.grid_w;
   const int32_t z0 = q0 / plane, z1 = q_last / plane;
-  const Band bz = na_band(z0, z1, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
+  auto band = [reverse](int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil) {
+    return reverse ? na_band_reverse(c0, c1, len, kernel, rad, wrap, dil) : na_band(c0, c1, len, kernel, rad, wrap, dil);
+  };
+  const Band bz = band(z0, z1, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
   int32_t tok_start = bz.start * plane, tok_len = bz.count * plane;
   if (bz.count == 1) {  // one plane (then z0 = z1): narrow it to the band of rows
-    const Band by = na_band((q0 - z0 * plane) / g.grid_w, (q_last - z1 * plane) / g.grid_w, g.grid_h, g.kernel_h,
-                            g.rad_h, g.wrap_h, g.dil_h);
+    const Band by = band((q0 - z0 * plane) / g.grid_w, (q_last - z1 * plane) / g.grid_w, g.grid_h, g.kernel_h,
+                         g.rad_h, g.wrap_h, g.dil_h);
     // a row band that wraps inside one plane of several is not one run of tokens
     if (g.grid_d == 1 || by.start + by.count <= g.grid_h) {
       tok_start += by.start * g.grid_w;
@@ -148,17 +148,11 @@ constexpr int32_t kv_tile_at(const KvRun& run, int32_t i, int32_t n_tiles) {
 }
 
 // Backward of a neighbourhood window: the run of query tiles (BN queries each)
-// holding every query whose window reaches a key of the tile [k0, k0 + BN). It
-// is the band of kv_run with every axis taken as wrapped, of radius r on wrapped
-// axes (a wrapped window reaches the keys within r * dil of its query, both ways)
-// and kernel - 1 on clamped ones (a clamped window holds its query and spans
-// (kernel - 1) * dil cells): a superset; the element test decides.
+// holding every query whose window reaches a key of the tile [k0, k0 + BN), from
+// the reverse bands (na_band_reverse) of the tile's keys; the element test decides
+// within it.
 constexpr KvRun na_query_run(const NaGeom& g, int32_t N, int32_t BN, int32_t k0) {
-  NaGeom r = g;
-  if (!r.wrap_d) r.wrap_d = 1, r.rad_d = r.kernel_d - 1;
-  if (!r.wrap_h) r.wrap_h = 1, r.rad_h = r.kernel_h - 1;
-  if (!r.wrap_w) r.wrap_w = 1, r.rad_w = r.kernel_w - 1;
-  return kv_run(MASK_NA, N, N, BN, BN, k0, r);
+  return kv_run(MASK_NA, N, N, BN, BN, k0, g, true);
 }
 
 // Does key tile t need the element mask for the query tile starting at q0?
@@ -260,11 +254,21 @@ constexpr GridMasks na_grid_masks(int32_t zq, int32_t yq, int32_t xq, const NaGe
   return m;
 }
 
+// On a clamped axis the queries whose window holds key coordinate x share x's
+// residue mod dil (na_dil_anchor takes the window inside that sub-grid of congruent
+// cells) and, on the sub-grid, form the undilated reverse run of x's sub-grid
+// coordinate: queries start, start + dil, ..., count of them.
+constexpr Band na_clamped_reverse_run(int32_t x, int32_t len, int32_t kernel, int32_t rad, int32_t dil) {
+  if (dil == 1) return na_band_reverse(x, x, len, kernel, rad, 0, 1);
+  const int32_t g = x % dil, sub_len = (len - 1 - g) / dil + 1;
+  const Band r = na_band_reverse(x / dil, x / dil, sub_len, kernel, rad, 0, 1);
+  return Band{g + dil * r.start, r.count};
+}
+
 // The reverse relation, for the backward: bit c of an axis mask says whether the
 // window of query coordinate c holds key coordinate x. Wrapped windows are
 // symmetric (c + dil * t = x mod L with |t| <= r), so it is the window of x itself;
-// a clamped window holds its query and spans (kernel - 1) * dil cells, so only
-// those candidates are tested.
+// a clamped one is na_clamped_reverse_run.
 constexpr void na_axis_reverse_mask(int32_t x, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil,
                                     uint64_t& lo, uint64_t& hi) {
   if (wrap) {
@@ -272,9 +276,9 @@ constexpr void na_axis_reverse_mask(int32_t x, int32_t len, int32_t kernel, int3
     return;
   }
   lo = hi = 0;
-  const int32_t reach = (kernel - 1) * dil;
-  for (int32_t c = imax(x - reach, 0); c <= imin(x + reach, len - 1); ++c) {
-    if (!na_dil_ok(na_dil_anchor(c, len, kernel, rad, wrap, dil), x, len, kernel, rad, wrap, dil)) continue;
+  const Band run = na_clamped_reverse_run(x, len, kernel, rad, dil);
+  for (int32_t u = 0; u < run.count; ++u) {
+    const int32_t c = run.start + dil * u;
     const uint64_t bit = 1ull << (c & 63);
     lo |= c < 64 ? bit : 0ull;
     hi |= c < 64 ? 0ull : bit;
@@ -454,10 +458,10 @@ constexpr uint32_t band_window_bits(int32_t c, Band b, int32_t len, int32_t kern
     }
     return m;
   }
-  for (int32_t i = 0; i < b.count; ++i) {  // clamped and dilated, the queries that see cell c
-    int32_t x = b.start + i;
-    x -= x >= len ? len : 0;
-    m |= (uint32_t)na_dil_ok(na_dil_anchor(x, len, kernel, rad, wrap, dil), c, len, kernel, rad, wrap, dil) << i;
+  const Band run = na_clamped_reverse_run(c, len, kernel, rad, dil);  // clamped and dilated: the queries that see c
+  for (int32_t u = 0; u < run.count; ++u) {
+    const int32_t i = run.start + dil * u - b.start;  // a clamped band does not wrap
+    m |= (uint32_t)i < (uint32_t)b.count ? uint32_t{1} << i : 0u;
   }
   return m;
 }

@@ -758,9 +758,9 @@ int main() {
     EXPECT(!na_rows_reverse_eligible(geom(1, 20, 20, 1, 5, 5, 1, 0, 0, 1, 1, 1), 8),
            "clamped 5-row windows near a border: 10 query rows reach the key rows 4..7");
     // the reverse band of one clamped axis against brute force, every coordinate range
-    for (int len : {1, 2, 5, 9, 20})
+    for (int len : {1, 2, 5, 9, 20, 23})
       for (int kernel : {1, 3, 5, 7})
-        for (int dil : {1, 2, 3})
+        for (int dil : {1, 2, 3, 4})
           for (int wrap : {0, 1}) {
             const NaGeom ax = geom(1, 1, len, 1, 1, kernel, 0, 0, wrap, 1, 1, dil);
             if (!geom_valid(ax)) continue;
@@ -784,6 +784,28 @@ int main() {
                   }
                   EXPECT(first && last, "clamped reverse band [%d, +%d) is tight", b.start, b.count);
                 }
+                if (!wrap && dil > 1) {  // within dil - 1 cells of a seer at each end
+                  bool first = false, last = false;
+                  for (int q = 0; q < len; ++q)
+                    for (int k = c0; k <= c1; ++k)
+                      if (na_dil_ok(na_dil_anchor(q, len, kernel, ax.rad_w, 0, dil), k, len, kernel, ax.rad_w, 0, dil)) {
+                        first |= q - b.start < dil;
+                        last |= b.start + b.count - 1 - q < dil;
+                      }
+                  EXPECT(first && last, "dilated clamped reverse band [%d, +%d) within dil of its queries (len %d k %d "
+                         "dil %d)", b.start, b.count, len, kernel, dil);
+                }
+              }
+            if (!wrap)  // the exact reverse run of a clamped axis: the queries whose enumerated window holds x
+              for (int x = 0; x < len; ++x) {
+                std::vector<int> want, got;
+                for (int q = 0; q < len; ++q)
+                  for (int c : axis_cells(q, len, kernel, 0, dil))
+                    if (c == x) want.push_back(q);
+                const Band r = na_clamped_reverse_run(x, len, kernel, ax.rad_w, dil);
+                for (int u = 0; u < r.count; ++u) got.push_back(r.start + dil * u);
+                EXPECT(got == want, "clamped reverse run of %d: %zu queries, want %zu (len %d k %d dil %d)", x,
+                       got.size(), want.size(), len, kernel, dil);
               }
           }
     EXPECT(na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), 10), "20x20x20, 5x5x5 window takes the row kernel");

@@ -103,6 +103,10 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (17, 48, 7, 3, 0, 0, 1, 1)),               # clamped: reverse rectangles near the borders
     ("na2d", (24, 36, 3, 7, 1, 0, 2, 1)),               # dilated rows, clamped columns
     ("na2d", (33, 64, 5, 9, 0, 1, 1, 2)),               # a 32-column band: dilated, wrapped columns
+    ("na2d", (40, 64, 7, 7, 0, 0, 2, 2)),               # clamped and dilated (tight clamped bands)
+    ("na2d", (30, 50, 5, 5, 0, 0, 3, 3)),               # dilation 3, clamped
+    # the tile kernels with the reverse query runs of clamped axes
+    ("na3d", (10, 12, 14, 3, 3, 3, 0, 0, 0, 2, 2, 3)),
 ])
 def test_bwd_neighbourhood(mode, geo, d):
     import exact_attention_68_amd as A

@@ -136,3 +136,28 @@ def test_attn_bwd_neighbourhood_kernels(name, dq, dkv):
     assert len(kernels) == 2 and dq in kernels[0] and dkv in kernels[1], kernels
     assert others == [], others
 
+
+def test_clamped_dilated_na2d_takes_patch_kernels():
+    """Clamped windows are pushed inwards at the borders but otherwise span rad * dil either side of
+    their query, so a clamped 7x7 window of dilation 2 on a 64x64 grid has the same 20-row bands as
+    the wrapped one and takes the patch kernels forward and backward."""
+    import exact_attention_68_amd as A
+
+    B, H, N, d = 1, 2, 64 * 64, 32
+    q, k, v = _inputs(B, H, N, d, 4)
+    params = A.na2d_params(64, 64, 7, 7, 0, 0, 2, 2)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    kernels, others = _split(_dispatches(
+        lambda: A.attn_fwd_ex(q, k, v, o, lse, d ** -0.5, A.ATTN_MASK_NA2D, params, None)))
+    assert len(kernels) == 1 and "attn_fwd_na_patch_kernel" in kernels[0], kernels
+    assert others == [], others
+    do = torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16)
+    ws = torch.empty(A.attn_bwd_workspace_size(B, H, N, N, d, A.ATTN_MASK_NA2D, params), dtype=torch.uint8,
+                     device="cuda")
+    grads = [torch.empty_like(t) for t in (q, k, v)]
+    kernels, others = _split(_dispatches(
+        lambda: A.attn_bwd(q, k, v, o, do, lse, *grads, d ** -0.5, A.ATTN_MASK_NA2D, params, ws)))
+    assert len(kernels) == 2 and "attn_bwd_dq_patch_kernel" in kernels[0] and "attn_bwd_dkv_patch_kernel" in kernels[1], \
+        kernels
+    assert others == [], others
