@@ -40,9 +40,18 @@ attn::SplitPlan plan_for(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t 
   return attn::split_plan(mask_mode, n_tiles, (int32_t)attn::cdiv(Nkv, attn::tile_keys(d)), cus);
 }
 
-// Kernel mask kind for a checked problem: the patch kernel for undilated 2D
-// windows whose patch bands fit it (na_patch_eligible, d = 32 or 64); the row
-// kernel for other windows on grids at most 32 wide (na_rows_eligible, d = 32); the
+// Key rows per LDS stage of the forward row kernel for this window, 0 if it fits neither
+// the narrow nor the wide stages.
+int32_t rows_stage(int64_t d, const attn::NaGeom& g) {
+  const int32_t narrow = attn::rows_lds_rows(d), wide = attn::rows_wide_lds(d);
+  if (narrow > 0 && attn::na_rows_eligible(g, narrow)) return narrow;
+  if (wide > 0 && attn::na_rows_eligible(g, wide)) return wide;
+  return 0;
+}
+
+// Kernel mask kind for a checked problem: the patch kernel for 2D windows whose
+// patch bands fit it (na_patch_eligible, d = 32 or 64); the row kernel for other
+// windows on grids at most 32 wide whose bands fit its stages (rows_stage, d = 32); the
 // block-masked neighbourhood kernel for other undilated 2D windows on grids of
 // width 32, 64, 96 or 128; the grid-mask kernel for other grids of width 4..124
 // with rows and planes <= 128; the element predicate for the rest.
@@ -54,8 +63,7 @@ int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
     const int64_t patches = p.B * p.H * attn::cdiv(g.grid_h, attn::kPatchRows) * attn::cdiv(g.grid_w, attn::kPatchCols);
     if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
   }
-  const int32_t rows_rows = attn::rows_lds_rows(p.d);
-  if (rows_rows > 0 && attn::na_rows_eligible(g, rows_rows)) {
+  if (rows_stage(p.d, g) > 0) {
     const int64_t groups = p.B * p.H * (int64_t)g.grid_d * attn::cdiv(g.grid_h, attn::kRowsGroup);
     if (groups <= INT32_MAX) return attn::MASK_NA_ROWS;
   }
@@ -101,6 +109,7 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   if (mask == attn::MASK_NA_ROWS) {
     a.patch_nx = 1;
     a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kRowsGroup);
+    a.rows_stage = rows_stage(p.d, a.na);
     n_wg = a.BH * a.na.grid_d * a.patch_ny;
   }
   if (split != nullptr && split->rem > 0) {
@@ -266,8 +275,13 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     const int32_t dq_lds = attn::bwd_dq_rows_lds(d), dkv_lds = attn::bwd_dkv_rows_lds(d);
     a.row_groups = (int32_t)attn::cdiv(a.na.grid_h, attn::kRowsGroup);
     const bool groups_fit = (int64_t)a.BH * a.na.grid_d * a.row_groups <= INT32_MAX;
-    a.dq_rows = groups_fit && dq_lds > 0 && attn::na_rows_eligible(a.na, dq_lds) ? 1 : 0;
-    a.dkv_rows = groups_fit && dkv_lds > 0 && attn::na_rows_reverse_eligible(a.na, dkv_lds) ? 1 : 0;
+    const int32_t wide = attn::rows_wide_lds(d);
+    if (groups_fit) {  // the narrow stages where they fit, else the wide ones
+      a.dq_rows = dq_lds > 0 && attn::na_rows_eligible(a.na, dq_lds) ? dq_lds
+                  : wide > 0 && attn::na_rows_eligible(a.na, wide) ? wide : 0;
+      a.dkv_rows = dkv_lds > 0 && attn::na_rows_reverse_eligible(a.na, dkv_lds) ? dkv_lds
+                   : wide > 0 && attn::na_rows_reverse_eligible(a.na, wide) ? wide : 0;
+    }
     // wider single-plane grids: the patch kernels (the row kernels keep the narrow ones)
     const int32_t patch_lds = attn::bwd_patch_lds(d);
     a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);

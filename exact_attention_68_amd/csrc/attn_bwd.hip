@@ -645,10 +645,10 @@ __device__ __forceinline__ int32_t band_plane(const Band& bz, int32_t i_own, int
 // dQ by query rows: per visible key row (32 keys) S^T = K Q^T, dP^T = V dO^T,
 // P = 2^(c s - lse2) (hidden keys 0), dS = P (dP - D), dQ^T += K^T dS^T; also
 // forms D of its queries for the dK/dV kernel, as the tile kernel does.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 ? 2 : 1)))
+template <int D, int ROWS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 && ROWS <= 10 ? 2 : 1)))
 void attn_bwd_dq_rows_kernel(BwdArgs a) {
-  using R = RowStage<D, bwd_dq_rows_lds(D)>;
+  using R = RowStage<D, ROWS>;
   constexpr int KB = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][R::ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][R::ELEMS];
@@ -772,11 +772,12 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
 // reverse window masks deciding); per visible query row (32 queries) S = Q K^T,
 // dP = dO V^T, P = 2^(c s - lse2) (hidden pairs 0), dS = P (dP - D), dV^T +=
 // dO^T P, dK^T += Q^T dS. Each stage also holds its queries' lse2 and D.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 ? 2 : 1)))
+template <int D, int ROWS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 && ROWS <= 8 ? 2 : 1)))
 void attn_bwd_dkv_rows_kernel(BwdArgs a) {
-  using R = RowStage<D, bwd_dkv_rows_lds(D)>;
+  using R = RowStage<D, ROWS>;
   constexpr int KB = D / 16, DT = D / 32, TOK = R::ROWS * 32;
+  constexpr int ST = (TOK + 255) / 256;  // statistics per thread and stage (tokens tid + 256 s)
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][R::ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds[2][R::ELEMS];
   __shared__ __attribute__((aligned(16))) float l2_lds[2][TOK];
@@ -804,22 +805,35 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
   i_own += i_own < 0 ? g.grid_d : 0;
   const i32x4_t q_rsrc = head_rsrc(a.q + head * D, head_bytes);
   const i32x4_t g_rsrc = head_rsrc(a.dout + head * D, head_bytes);
-  // lse2 and D of the stage's tokens (thread t < TOK: token t = 32 r + x), +inf and 0
-  // past the band and the width (P = 0 there)
-  auto stats = [&](int32_t zq, float& l2v, float& dlv) {
-    l2v = INFINITY;
-    dlv = 0.f;
-    const int32_t r = tid / 32, x = tid % 32;
-    if (tid < TOK && r < by.count && x < W) {
-      int32_t yq = by.start + r;
-      yq -= yq >= H ? H : 0;
-      const int32_t qi = (zq * H + yq) * W + x;
-      l2v = a.lse[head + qi] * kLog2e;
-      dlv = a.delta[head + qi];
+  // lse2 and D of the stage's tokens (thread tid: tokens t = tid + 256 s = 32 r + x), +inf
+  // and 0 past the band and the width (P = 0 there)
+  auto stats = [&](int32_t zq, float (&l2v)[ST], float (&dlv)[ST]) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int32_t t = tid + 256 * st, r = t / 32, x = t % 32;
+      l2v[st] = INFINITY;
+      dlv[st] = 0.f;
+      if (t < TOK && r < by.count && x < W) {
+        int32_t yq = by.start + r;
+        yq -= yq >= H ? H : 0;
+        const int32_t qi = (zq * H + yq) * W + x;
+        l2v[st] = a.lse[head + qi] * kLog2e;
+        dlv[st] = a.delta[head + qi];
+      }
+    }
+  };
+  auto put_stats = [&](int stage, const float (&l2v)[ST], const float (&dlv)[ST]) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int32_t t = tid + 256 * st;
+      if (t < TOK) {
+        l2_lds[stage][t] = l2v[st];
+        dl_lds[stage][t] = dlv[st];
+      }
     }
   };
   load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[0], g_lds[0], z, by, H, W, head_bytes, wave, tid);
-  float l2n, dln;
+  float l2n[ST], dln[ST];
   stats(z, l2n, dln);
 
   // scale < 0: K's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
@@ -855,10 +869,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16_t{};
 
-  if (tid < TOK) {  // the first stage's statistics (published by the loop's first barrier)
-    l2_lds[0][tid] = l2n;
-    dl_lds[0][tid] = dln;
-  }
+  put_stats(0, l2n, dln);  // the first stage's statistics (published by the loop's first barrier)
   for (int32_t i = 0, stage = 0; i < bz.count; stage ^= 1) {
     const int32_t i_next = next_plane(i + 1);
     const bool more = i_next < bz.count;
@@ -915,10 +926,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
                                  wave, tid);
       stats(z_next, l2n, dln);
     }
-    if (more && tid < TOK) {  // the other stage's statistics were last read before this step's barrier
-      l2_lds[stage ^ 1][tid] = l2n;
-      dl_lds[stage ^ 1][tid] = dln;
-    }
+    if (more) put_stats(stage ^ 1, l2n, dln);  // the other stage's were last read before this step's barrier
     i = i_next;
   }
   store_rows_scaled<D>(a.dk + head * D, k_row, N, half, dk, a.scale);
@@ -1260,7 +1268,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const dim3 rows_grid(dq_rows || dkv_rows ? a.BH * a.na.grid_d * a.row_groups : 1);
   const dim3 patch_grid(dq_patch || dkv_patch ? a.BH * a.patch_nx * a.patch_ny : 1);
   if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
-    if (dq_rows) hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+    if (dq_rows && a.dq_rows == bwd_dq_rows_lds(D))
+      hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D, bwd_dq_rows_lds(D)>), rows_grid, dim3(256), 0, stream, a);
+    if constexpr (rows_wide_lds(D) > 0) {
+      if (dq_rows && a.dq_rows == rows_wide_lds(D))
+        hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<D, rows_wide_lds(D)>), rows_grid, dim3(256), 0, stream, a);
+    }
   }
   if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     if (dq_patch)
@@ -1271,7 +1284,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
-    if (dkv_rows) hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D>), rows_grid, dim3(256), 0, stream, a);
+    if (dkv_rows && a.dkv_rows == bwd_dkv_rows_lds(D))
+      hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D, bwd_dkv_rows_lds(D)>), rows_grid, dim3(256), 0, stream, a);
+    if constexpr (rows_wide_lds(D) > 0) {
+      if (dkv_rows && a.dkv_rows == rows_wide_lds(D))
+        hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<D, rows_wide_lds(D)>), rows_grid, dim3(256), 0, stream, a);
+    }
   }
   if constexpr (MASK == MASK_NA && (D == 32 || D == 64)) {
     if (dkv_patch)

@@ -1284,21 +1284,21 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
 // the next row's scores issued before this row's exponentials (row_scores,
 // row_update), with the lane's column bits as the exponent's addend. (Four rows per
 // step through window_step, with no overlap between steps, ran 0.75x.)
-template <int D>
+template <int D, int ROWS_>
 struct RowsCfg {
-  static constexpr int ROWS = 10;  // key rows per stage: 20 KB of K or V at d = 32
+  static constexpr int ROWS = ROWS_;  // key rows per stage: 20 KB of K or V at d = 32 and 10 rows
   static constexpr int ROW_CHUNKS = D / 8;
   static constexpr int CHUNKS = ROWS * 32 * ROW_CHUNKS;  // 16-byte chunks of a stage of K (or V)
   static_assert(CHUNKS % 256 == 0, "a stage is copied in whole rounds of 256 lanes");
   static constexpr int LOADS = CHUNKS / 256;  // per lane, stage and tensor
   static constexpr int ELEMS = CHUNKS * 8;
 };
-static_assert(RowsCfg<32>::ROWS == rows_lds_rows(32), "host eligibility and kernel LDS must agree");
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// two work-groups per CU with the narrow stages (80 KB of LDS each), one with the wide ones
+template <int D, int ROWS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS <= 10 ? 2 : 1)))
 void attn_fwd_na_rows_kernel(KernelArgs a) {
-  using R = RowsCfg<D>;
+  using R = RowsCfg<D, ROWS>;
   constexpr int KB = D / 16, DT = D / 32, RC = D / 8;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][R::ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][R::ELEMS];
@@ -1495,9 +1495,17 @@ static hipError_t launch_d(const KernelArgs& a, int32_t mask, int32_t n_wg, int3
       }
       return hipErrorInvalidValue;
     case MASK_NA_ROWS:
-      if constexpr (D == 32) {
-        hipLaunchKernelGGL((attn_fwd_na_rows_kernel<D>), dim3(n_wg), dim3(256), 0, stream, a);
-        return hipGetLastError();
+      if constexpr (rows_lds_rows(D) > 0) {
+        if (a.rows_stage == rows_lds_rows(D)) {
+          hipLaunchKernelGGL((attn_fwd_na_rows_kernel<D, rows_lds_rows(D)>), dim3(n_wg), dim3(256), 0, stream, a);
+          return hipGetLastError();
+        }
+      }
+      if constexpr (rows_wide_lds(D) > 0) {
+        if (a.rows_stage == rows_wide_lds(D)) {
+          hipLaunchKernelGGL((attn_fwd_na_rows_kernel<D, rows_wide_lds(D)>), dim3(n_wg), dim3(256), 0, stream, a);
+          return hipGetLastError();
+        }
       }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;

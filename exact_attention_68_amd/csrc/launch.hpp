@@ -34,6 +34,7 @@ struct KernelArgs {
   int32_t causal_group; // causal: heads per XCD dispatched together (causal_item)
   int32_t patch_nx, patch_ny;  // MASK_NA_PATCH: patches per grid row and per grid column;
                                // MASK_NA_ROWS: patch_ny groups of rows per plane
+  int32_t rows_stage;  // MASK_NA_ROWS: key rows per LDS stage (rows_lds_rows or rows_wide_lds)
 };
 
 // Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
@@ -60,6 +61,12 @@ constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 24 : d == 64 ? 17
 // Key rows per LDS stage of the row kernel of narrow grids for head size d (0: none).
 // (d = 64 with 8-row stages, one wavefront per SIMD, ran 0.89x the tile kernel on the 20x20x20 volume.)
 constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : 0; }
+
+// The wide stages of the three row kernels (forward, backward dQ and dK/dV) at d = 32: 12
+// rows, for bands past the narrow stages (windows of 5 at dilation 2; clamped windows
+// whose reverse bands near a border pass 8 rows). Their two stages take 96-102 KB of LDS:
+// one work-group per CU.
+constexpr int32_t rows_wide_lds(int64_t d) { return d == 32 ? 12 : 0; }
 
 // Work-groups of the backward kernels resident per CU: two at d <= 64 and one at d = 128
 // (their register and LDS budgets). The causal dispatch order sizes its head groups with it.
@@ -93,9 +100,10 @@ struct BwdArgs {
   int32_t na_grid;   // 1: per-axis window masks (na_grid_eligible), else the element test
   int32_t group_q;   // causal: heads per XCD dispatched together by the dQ kernel (causal_group)
   int32_t group_k;   // and by the dK/dV kernel
-  // neighbourhood windows on grids at most 32 wide: the row kernels (1) or the tile kernels (0)
-  int32_t dq_rows;   // dQ by query rows (na_rows_eligible with bwd_dq_rows_lds(d))
-  int32_t dkv_rows;  // dK/dV by key rows (na_rows_reverse_eligible with bwd_dkv_rows_lds(d))
+  // neighbourhood windows on grids at most 32 wide: the row kernels, with this many rows per
+  // LDS stage (bwd_dq_rows_lds / bwd_dkv_rows_lds, else rows_wide_lds), or the tile kernels (0)
+  int32_t dq_rows;   // dQ by query rows (na_rows_eligible)
+  int32_t dkv_rows;  // dK/dV by key rows (na_rows_reverse_eligible)
   int32_t row_groups;  // groups of kRowsGroup rows per plane (either row kernel)
   // neighbourhood windows of one plane whose bands fit 32 columns: the patch kernels
   int32_t dq_patch;    // dQ by 8 x 16 query patches (na_patch_bwd_eligible, forward bands)

@@ -735,7 +735,7 @@ int main() {
   }
   {
     // row kernel: narrow 2D and 3D grids, wrap and clamp per axis, dilation
-    int eligible = 0, eligible_rev = 0, tried = 0;
+    int eligible = 0, eligible_rev = 0, tried = 0, wide = 0, wide_rev = 0;
     for (int D : {1, 5})
       for (int H : {4, 9, 20})
         for (int W : {7, 20, 32})
@@ -749,7 +749,18 @@ int main() {
                 eligible += check_rows(g, 10);
                 if (W % 2 == 1) check_rows(g, 8);  // the backward dQ row kernel's stages at d = 64
                 eligible_rev += check_rows_reverse(g, 8);
+                // the wide 12-row stages, where the narrow ones do not fit
+                if (!na_rows_eligible(g, 10)) wide += check_rows(g, 12);
+                if (!na_rows_reverse_eligible(g, 8)) wide_rev += check_rows_reverse(g, 12);
               }
+    EXPECT(wide > 10 && wide_rev > 10, "wide row stages take %d (forward) and %d (reverse) more shapes", wide,
+           wide_rev);
+    EXPECT(!na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 10) &&
+               na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 12) &&
+               na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 12),
+           "20x20x20, 5x5x5 window of dilation 2: 12-row bands, the wide stages");
+    EXPECT(na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 0, 0, 0, 1, 1, 1), 12),
+           "clamped 5x5x5 windows: the 10-row reverse bands near the borders fit the wide stages");
     EXPECT(eligible > 100 && eligible < tried, "row-kernel eligibility covers %d of %d shapes", eligible, tried);
     EXPECT(eligible_rev > 80 && eligible_rev < eligible, "dK/dV row-kernel eligibility covers %d of %d shapes",
            eligible_rev, tried);

@@ -107,6 +107,10 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (30, 50, 5, 5, 0, 0, 3, 3)),               # dilation 3, clamped
     # the tile kernels with the reverse query runs of clamped axes
     ("na3d", (10, 12, 14, 3, 3, 3, 0, 0, 0, 2, 2, 3)),
+    # the row kernels' wide 12-row stages at d = 32
+    ("na3d", (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)),  # dilation 2: all three row kernels wide
+    ("na3d", (6, 20, 12, 3, 5, 5, 0, 0, 0, 1, 1, 1)),   # clamped: dK/dV's 10-row reverse bands near the borders
+    ("na3d", (7, 13, 9, 3, 5, 3, 0, 0, 1, 2, 2, 1)),    # clamped and dilated: dQ wide, dK/dV on the tile kernel
 ])
 def test_bwd_neighbourhood(mode, geo, d):
     import exact_attention_68_amd as A

@@ -122,6 +122,8 @@ def test_d128_na2d(gh, gw, kh, kw, wh, ww):
     (16, 4, 4, 3, 3, 3, 1, 1, 1, 1, 1, 1),    # planes of 16 tokens: a key tile spans 8 planes
     (6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2),     # dilated
     (10, 9, 8, 3, 3, 3, 0, 0, 0, 3, 3, 2),    # clamped and dilated
+    (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1),  # 12-row bands at dilation 2: the row kernel's wide stages (d = 32)
+    (7, 13, 9, 3, 5, 3, 0, 0, 1, 2, 2, 1),    # clamped and dilated, wide stages
 ])
 def test_na3d_shapes(geo, d):
     import exact_attention_68_amd as A
