@@ -78,6 +78,11 @@ WORKLOADS = {
         Workload("na2d_wrap_64x64_k7_dil2", 2, 4, 4096, 32, "na2d", f32(1 / math.sqrt(32)), 6809,
                  na=dict(grid_h=64, grid_w=64, kernel_h=7, kernel_w=7, wrap_h=1, wrap_w=1, dil_h=2, dil_w=2),
                  note="2D neighbourhood attention, 64x64 grid, 7x7 window dilated by 2, wrapping both axes, d32"),
+        Workload("na3d_wrap_20x20x20_k5_dil2", 2, 4, 8000, 32, "na3d", f32(1 / math.sqrt(32)), 6810,
+                 na=dict(grid_d=20, grid_h=20, grid_w=20, kernel_d=5, kernel_h=5, kernel_w=5,
+                         wrap_d=1, wrap_h=1, wrap_w=0, dil_d=2, dil_h=2, dil_w=2),
+                 note="3D neighbourhood attention, 20x20x20 volume, 5x5x5 window dilated by 2 on every axis, "
+                      "wrapping depth and rows, d32"),
     ]
 }
 
