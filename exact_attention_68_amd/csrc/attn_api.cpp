@@ -64,7 +64,7 @@ int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
     if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
   }
   if (rows_stage(p.d, g) > 0) {
-    const int64_t groups = p.B * p.H * (int64_t)g.grid_d * attn::cdiv(g.grid_h, attn::kRowsGroup);
+    const int64_t groups = p.B * p.H * (int64_t)g.grid_d * attn::na_row_groups(g);
     if (groups <= INT32_MAX) return attn::MASK_NA_ROWS;
   }
   const bool blocks = g.grid_d == 1 && g.dil_h == 1 && g.dil_w == 1 && g.grid_w % 32 == 0 && g.grid_w <= 128;
@@ -108,7 +108,7 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   }
   if (mask == attn::MASK_NA_ROWS) {
     a.patch_nx = 1;
-    a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kRowsGroup);
+    a.patch_ny = attn::na_row_groups(a.na);
     a.rows_stage = rows_stage(p.d, a.na);
     n_wg = a.BH * a.na.grid_d * a.patch_ny;
   }
@@ -273,7 +273,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     a.na_grid = attn::na_grid_eligible(a.na) ? 1 : 0;
     mask = attn::MASK_NA;
     const int32_t dq_lds = attn::bwd_dq_rows_lds(d), dkv_lds = attn::bwd_dkv_rows_lds(d);
-    a.row_groups = (int32_t)attn::cdiv(a.na.grid_h, attn::kRowsGroup);
+    a.row_groups = attn::na_row_groups(a.na);
     const bool groups_fit = (int64_t)a.BH * a.na.grid_d * a.row_groups <= INT32_MAX;
     const int32_t wide = attn::rows_wide_lds(d);
     if (groups_fit) {  // the narrow stages where they fit, else the wide ones

@@ -586,7 +586,8 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Neighbourhood windows on grids at most 32 wide (na_rows_eligible,
 // na_rows_reverse_eligible): the forward row kernel's layout. A work-group holds
-// 4 rows of one plane, a wavefront one row and a lane one column (lanes past the
+// a group of 4 rows of one plane (RowGroup: consecutive, or of one residue mod the
+// dilation), a wavefront one row and a lane one column (lanes past the
 // width idle); the band rows of each plane that the work-group's windows reach
 // stream through two LDS stages (32 tokens per row, columns past the width read
 // as zero); each wavefront visits only its own visible rows, in order, and the
@@ -612,8 +613,8 @@ struct RowStage {
 // rows past the band read as zero (an offset past the head).
 template <int D, int ROWS>
 __device__ __forceinline__ void load_row_stage(i32x4_t ra, i32x4_t rb, const uint16_t* la, const uint16_t* lb,
-                                               int32_t z, Band by, int32_t H, int32_t W, uint32_t head_bytes,
-                                               int wave, int tid) {
+                                               int32_t z, const RowGroup& rg, int32_t H, int32_t W,
+                                               uint32_t head_bytes, int wave, int tid) {
   using R = RowStage<D, ROWS>;
   const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds_addr(la) + wave * 1024);
   const uint32_t b_base = __builtin_amdgcn_readfirstlane(lds_addr(lb) + wave * 1024);
@@ -623,9 +624,8 @@ __device__ __forceinline__ void load_row_stage(i32x4_t ra, i32x4_t rb, const uin
     const int32_t tok = p / R::RC, r = tok / 32, x = tok % 32;
     const int32_t chunk = (p % R::RC) ^ chunk_swizzle<D>(tok);
     uint32_t voff = head_bytes;
-    if (r < by.count && x < W) {
-      int32_t y = by.start + r;
-      y -= y >= H ? H : 0;
+    if (r < rg.band.count && x < W) {
+      const int32_t y = row_group_row(rg, r);
       voff = (uint32_t)((z * H + y) * W + x) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
     }
     dma_lds16(ra, a_base + (uint32_t)j * 4096u, voff, 0u);
@@ -661,9 +661,10 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
   const int32_t groups = a.row_groups, per_head = g.grid_d * groups;
   const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = item / per_head, rest = item - bh * per_head;
-  const int32_t z = rest / groups, y0 = (rest - z * groups) * kRowsGroup;
-  const int32_t y = y0 + wave;  // this wavefront's grid row
-  const bool row_in = y < H;
+  const int32_t z = rest / groups;
+  const RowGroup rg = na_row_group(g, rest - z * groups, false);
+  const int32_t y = rg.rho + rg.stride * (rg.u0 + wave);  // this wavefront's grid row
+  const bool row_in = rg.u0 + wave < rg.len;
   const bool q_ok = row_in && col < W;
   const int32_t my_q = (z * H + y) * W + col;
   const int32_t q_row = q_ok ? my_q : N;  // past the last row: zero fragments, no store
@@ -671,12 +672,12 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
   const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
 
   const Band bz = na_band(z, z, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
-  const Band by = na_rows_band(y0, g);  // by.count <= R::ROWS
+  const Band by = rg.band;  // by.count <= R::ROWS
   int32_t i_own = z - bz.start;  // the own plane is in its windows: its stage goes first
   i_own += i_own < 0 ? g.grid_d : 0;
   const i32x4_t k_rsrc = head_rsrc(a.k + head * D, head_bytes);
   const i32x4_t v_rsrc = head_rsrc(a.v + head * D, head_bytes);
-  load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[0], v_lds[0], z, by, H, W, head_bytes, wave, tid);
+  load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[0], v_lds[0], z, rg, H, W, head_bytes, wave, tid);
 
   // scale < 0: Q's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
   bf16x8_t qf[KB], gf[KB];
@@ -693,9 +694,7 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
   for (int e = 0; e < 16; ++e) add[e] = ((cm16 >> e) & 1u) ? -l2 : -INFINITY;
   uint32_t rows_vis = 0;  // bit r: band row r in this wavefront's row window
   for (int32_t r = 0; r < by.count; ++r) {
-    int32_t yk = by.start + r;
-    yk -= yk >= H ? H : 0;
-    rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, yk) << r;
+    rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, row_group_row(rg, r)) << r;
   }
   rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
   auto next_plane = [&](int32_t j) {  // first visit from j whose plane is in the window (uniform)
@@ -727,7 +726,7 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
     __syncthreads();       // published; the other stage was last read before this barrier
     if (!kSerialTiles && more)
       load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[stage ^ 1], v_lds[stage ^ 1],
-                                 band_plane(bz, i_own, i_next, g.grid_d), by, H, W, head_bytes, wave, tid);
+                                 band_plane(bz, i_own, i_next, g.grid_d), rg, H, W, head_bytes, wave, tid);
     // the wavefront's visible rows of the stage, in order: the next row's products are
     // issued before this row's exponentials
     const uint16_t* ks = k_lds[stage];
@@ -761,7 +760,7 @@ void attn_bwd_dq_rows_kernel(BwdArgs a) {
     }
     if (kSerialTiles && more)  // race check: the next stage's loads only after this stage's compute
       load_row_stage<D, R::ROWS>(k_rsrc, v_rsrc, k_lds[stage ^ 1], v_lds[stage ^ 1],
-                                 band_plane(bz, i_own, i_next, g.grid_d), by, H, W, head_bytes, wave, tid);
+                                 band_plane(bz, i_own, i_next, g.grid_d), rg, H, W, head_bytes, wave, tid);
     i = i_next;
   }
   store_rows_scaled<D>(a.dq + head * D, q_row, N, half, dq, a.scale);
@@ -790,9 +789,10 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
   const int32_t groups = a.row_groups, per_head = g.grid_d * groups;
   const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = item / per_head, rest = item - bh * per_head;
-  const int32_t z = rest / groups, y0 = (rest - z * groups) * kRowsGroup;
-  const int32_t y = y0 + wave;  // this wavefront's key row
-  const bool row_in = y < H;
+  const int32_t z = rest / groups;
+  const RowGroup rg = na_row_group(g, rest - z * groups, true);
+  const int32_t y = rg.rho + rg.stride * (rg.u0 + wave);  // this wavefront's key row
+  const bool row_in = rg.u0 + wave < rg.len;
   const bool k_ok = row_in && col < W;
   const int32_t my_k = (z * H + y) * W + col;
   const int32_t k_row = k_ok ? my_k : N;
@@ -800,7 +800,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
   const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
 
   const Band bz = na_band_reverse(z, z, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
-  const Band by = na_rows_reverse_band(y0, g);  // by.count <= R::ROWS
+  const Band by = rg.band;  // by.count <= R::ROWS
   int32_t i_own = z - bz.start;  // a key's own plane sees it: its stage goes first
   i_own += i_own < 0 ? g.grid_d : 0;
   const i32x4_t q_rsrc = head_rsrc(a.q + head * D, head_bytes);
@@ -814,8 +814,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
       l2v[st] = INFINITY;
       dlv[st] = 0.f;
       if (t < TOK && r < by.count && x < W) {
-        int32_t yq = by.start + r;
-        yq -= yq >= H ? H : 0;
+        const int32_t yq = row_group_row(rg, r);
         const int32_t qi = (zq * H + yq) * W + x;
         l2v[st] = a.lse[head + qi] * kLog2e;
         dlv[st] = a.delta[head + qi];
@@ -832,7 +831,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
       }
     }
   };
-  load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[0], g_lds[0], z, by, H, W, head_bytes, wave, tid);
+  load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[0], g_lds[0], z, rg, H, W, head_bytes, wave, tid);
   float l2n[ST], dln[ST];
   stats(z, l2n, dln);
 
@@ -850,9 +849,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
   for (int e = 0; e < 16; ++e) bias[e] = ((cm16 >> e) & 1u) ? 0.f : -INFINITY;
   uint32_t rows_vis = 0;  // bit r: band query row r reaches this wavefront's key row
   for (int32_t r = 0; r < by.count; ++r) {
-    int32_t yq = by.start + r;
-    yq -= yq >= H ? H : 0;
-    rows_vis |= (uint32_t)bit128(rm.y0, rm.y1, yq) << r;
+    rows_vis |= (uint32_t)bit128(rm.y0, rm.y1, row_group_row(rg, r)) << r;
   }
   rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
   auto next_plane = [&](int32_t j) {
@@ -877,7 +874,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
     wait_tile_loads<0>();
     __syncthreads();
     if (!kSerialTiles && more) {
-      load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[stage ^ 1], g_lds[stage ^ 1], z_next, by, H, W, head_bytes,
+      load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[stage ^ 1], g_lds[stage ^ 1], z_next, rg, H, W, head_bytes,
                                  wave, tid);
       stats(z_next, l2n, dln);
     }
@@ -922,7 +919,7 @@ void attn_bwd_dkv_rows_kernel(BwdArgs a) {
       }
     }
     if (kSerialTiles && more) {  // race check: the next stage's loads only after this stage's compute
-      load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[stage ^ 1], g_lds[stage ^ 1], z_next, by, H, W, head_bytes,
+      load_row_stage<D, R::ROWS>(q_rsrc, g_rsrc, q_lds[stage ^ 1], g_lds[stage ^ 1], z_next, rg, H, W, head_bytes,
                                  wave, tid);
       stats(z_next, l2n, dln);
     }

@@ -1275,7 +1275,7 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
 
 // ---------------------------------------------------------------------------
 // Neighbourhood windows on grids at most 32 wide by grid rows (MASK_NA_ROWS,
-// na_rows_eligible): wavefront w of a work-group holds grid row y0 + w of plane z
+// na_rows_eligible): wavefront w of a work-group holds row w of its row group (RowGroup) of plane z
 // (lane column = grid column). The planes the windows reach stream through two LDS
 // stages; a stage holds the work-group's band of key rows of one plane, each row
 // as one 32-key block. A wavefront's window over a stage is uniform in its rows
@@ -1312,9 +1312,10 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
   const int32_t groups = a.patch_ny, per_head = g.grid_d * groups;
   const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = item / per_head, rest = item - bh * per_head;
-  const int32_t z = rest / groups, y0 = (rest - z * groups) * kRowsGroup;
-  const int32_t y = y0 + wave;  // this wavefront's grid row
-  const bool row_in = y < H;
+  const int32_t z = rest / groups;
+  const RowGroup rg = na_row_group(g, rest - z * groups, false);
+  const int32_t y = rg.rho + rg.stride * (rg.u0 + wave);  // this wavefront's grid row
+  const bool row_in = rg.u0 + wave < rg.len;
   const bool q_ok = row_in && col < W;
   const int32_t my_q = (z * H + y) * W + col;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -1328,7 +1329,7 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
     qraw[kb] = *reinterpret_cast<const u32x4_t*>(a.q + head + (size_t)q_row * D + kb * 16 + half * 8);
 
   const Band bz = na_band(z, z, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
-  const Band by = na_rows_band(y0, g);  // by.count <= R::ROWS
+  const Band by = rg.band;  // by.count <= R::ROWS
   // Planes are visited from the work-group's own plane (always in its window, so its
   // stage can be requested before any mask is built) through the band, circularly.
   int32_t i_own = z - bz.start;
@@ -1355,8 +1356,7 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
       const int32_t chunk = (p % RC) ^ chunk_swizzle<D>(key);
       uint32_t voff = head_bytes;
       if (r < by.count && x < W) {
-        int32_t yk = by.start + r;
-        yk -= yk >= H ? H : 0;
+        const int32_t yk = row_group_row(rg, r);
         voff = (uint32_t)((zk * H + yk) * W + x) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
       }
       dma_lds16(k_rsrc, k_base + (uint32_t)j * 4096u, voff, 0u);
@@ -1376,9 +1376,7 @@ void attn_fwd_na_rows_kernel(KernelArgs a) {
   for (int e = 0; e < 16; ++e) bias[e] = ((cm16 >> e) & 1u) ? 0.f : -INFINITY;
   uint32_t rows_vis = 0;  // bit r: band row r in this wavefront's row window
   for (int32_t r = 0; r < by.count; ++r) {
-    int32_t yk = by.start + r;
-    yk -= yk >= H ? H : 0;
-    rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, yk) << r;
+    rows_vis |= (uint32_t)bit128(gm.y0, gm.y1, row_group_row(rg, r)) << r;
   }
   rows_vis = row_in ? __builtin_amdgcn_readfirstlane(rows_vis) : 0u;
   auto next_plane = [&](int32_t j) {  // first visit from j whose plane is in the window (uniform)

@@ -33,7 +33,7 @@ struct KernelArgs {
   int32_t split_parts;  // parts per split tile
   int32_t causal_group; // causal: heads per XCD dispatched together (causal_item)
   int32_t patch_nx, patch_ny;  // MASK_NA_PATCH: patches per grid row and per grid column;
-                               // MASK_NA_ROWS: patch_ny groups of rows per plane
+                               // MASK_NA_ROWS: patch_ny row groups per plane (na_row_groups)
   int32_t rows_stage;  // MASK_NA_ROWS: key rows per LDS stage (rows_lds_rows or rows_wide_lds)
 };
 
@@ -104,7 +104,7 @@ struct BwdArgs {
   // LDS stage (bwd_dq_rows_lds / bwd_dkv_rows_lds, else rows_wide_lds), or the tile kernels (0)
   int32_t dq_rows;   // dQ by query rows (na_rows_eligible)
   int32_t dkv_rows;  // dK/dV by key rows (na_rows_reverse_eligible)
-  int32_t row_groups;  // groups of kRowsGroup rows per plane (either row kernel)
+  int32_t row_groups;  // row groups per plane, na_row_groups (either row kernel)
   // neighbourhood windows of one plane whose bands fit 32 columns: the patch kernels
   int32_t dq_patch;    // dQ by 8 x 16 query patches (na_patch_bwd_eligible, forward bands)
   int32_t dkv_patch;   // dK/dV by 8 x 16 key patches (reverse bands)

@@ -489,8 +489,8 @@ constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool rev
 // Grid rows of narrow grids (MASK_NA_ROWS).
 //
 // On a grid at most 32 wide, a wavefront holds one grid row of queries (lane column
-// = grid column; lanes past the width idle) and a work-group 4 consecutive rows of
-// one plane. Every key row is then one 32-key block (its columns, padded with keys
+// = grid column; lanes past the width idle) and a work-group 4 rows of one plane
+// (consecutive, or of one residue mod the dilation: RowGroup). Every key row is then one 32-key block (its columns, padded with keys
 // read as zero), so a query's window bits in any block are its own column bits, and
 // whether a key row (plane, row) lies in the window is the same for every lane of a
 // wavefront. The work-group streams the planes its windows reach (na_band of its
@@ -498,8 +498,63 @@ constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool rev
 // of those rows); each wavefront scores only its own visible rows of a stage.
 constexpr int32_t kRowsGroup = 4;
 
-constexpr Band na_rows_band(int32_t y0, const NaGeom& g) {
-  return na_band(y0, imin(y0 + kRowsGroup, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
+// The rows of a group. With dilation along the rows (and, on a wrapped axis, a row
+// count the dilation divides), the grid rows congruent to rho mod dil form a
+// sub-grid on which every window is an undilated window: clamped, na_dil_anchor
+// takes it inside that sub-grid; wrapped, it steps dil rows at a time around a
+// cycle of grid_h / dil of them. A group then takes 4 consecutive rows of one
+// sub-grid and its band is 4 + 2 rad sub-grid rows rather than 4 + 2 rad dil grid
+// rows. Otherwise (dilation 1, or a wrapped axis the dilation does not divide) the
+// sub-grid is the whole axis (rho 0, stride 1). Wavefront w holds grid row
+// rho + stride (u0 + w) while u0 + w < len; band row r is the grid row of sub-grid
+// cell (band.start + r) mod len.
+struct RowGroup {
+  int32_t rho, stride, len, u0;
+  Band band;
+};
+
+constexpr bool na_rows_strided(const NaGeom& g) { return g.dil_h > 1 && (!g.wrap_h || g.grid_h % g.dil_h == 0); }
+
+constexpr int32_t na_rows_sub_len(const NaGeom& g, int32_t rho) { return (g.grid_h - 1 - rho) / g.dil_h + 1; }
+
+// Groups per plane (both row kernels).
+constexpr int32_t na_row_groups(const NaGeom& g) {
+  if (!na_rows_strided(g)) return (int32_t)cdiv(g.grid_h, kRowsGroup);
+  int32_t n = 0;
+  for (int32_t rho = 0; rho < g.dil_h; ++rho) n += (int32_t)cdiv(na_rows_sub_len(g, rho), kRowsGroup);
+  return n;
+}
+
+// Group i of a plane with the band of rows its windows reach (reverse = false: the key
+// rows of its query rows; true: the query rows whose windows reach its key rows).
+constexpr RowGroup na_row_group(const NaGeom& g, int32_t i, bool reverse) {
+  RowGroup rg{0, 1, g.grid_h, i * kRowsGroup, Band{0, 0}};
+  int32_t dil = g.dil_h;
+  if (na_rows_strided(g)) {
+    rg.stride = g.dil_h;
+    dil = 1;
+    for (int32_t rho = 0; rho < g.dil_h; ++rho) {
+      const int32_t len = na_rows_sub_len(g, rho), n = (int32_t)cdiv(len, kRowsGroup);
+      if (i < n || rho == g.dil_h - 1) {
+        rg.rho = rho;
+        rg.len = len;
+        rg.u0 = i * kRowsGroup;
+        break;
+      }
+      i -= n;
+    }
+  }
+  const int32_t u1 = imin(rg.u0 + kRowsGroup, rg.len) - 1;
+  rg.band = reverse ? na_band_reverse(rg.u0, u1, rg.len, g.kernel_h, g.rad_h, g.wrap_h, dil)
+                    : na_band(rg.u0, u1, rg.len, g.kernel_h, g.rad_h, g.wrap_h, dil);
+  return rg;
+}
+
+// Grid row of band row r of a group.
+constexpr int32_t row_group_row(const RowGroup& rg, int32_t r) {
+  int32_t u = rg.band.start + r;
+  u -= u >= rg.len ? rg.len : 0;
+  return rg.rho + rg.stride * u;
 }
 
 // At most 32 columns (one block per key row), axes of at most 128 cells (the
@@ -507,25 +562,18 @@ constexpr Band na_rows_band(int32_t y0, const NaGeom& g) {
 // `lds_rows` rows per stage.
 constexpr bool na_rows_eligible(const NaGeom& g, int32_t lds_rows) {
   if (g.grid_w > 32 || g.grid_h > 128 || g.grid_d > 128) return false;
-  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kRowsGroup)
-    if (na_rows_band(y0, g).count > lds_rows) return false;
+  for (int32_t i = 0, n = na_row_groups(g); i < n; ++i)
+    if (na_row_group(g, i, false).band.count > lds_rows) return false;
   return true;
 }
 
-// Backward of the row kernel: the same grids, with key rows in the wavefronts
-// (dK and dV of 4 key rows of one plane per work-group) and the queries whose
-// windows reach them streamed (na_band_reverse per axis): the query rows of one
-// plane whose windows reach the key rows [y0, y0 + kRowsGroup).
-constexpr Band na_rows_reverse_band(int32_t y0, const NaGeom& g) {
-  return na_band_reverse(y0, imin(y0 + kRowsGroup, g.grid_h) - 1, g.grid_h, g.kernel_h, g.rad_h, g.wrap_h, g.dil_h);
-}
-
 // The dK/dV row kernel's condition: na_rows_eligible's grid limits, and every
-// group's band of query rows within `lds_rows` rows per stage.
+// group's band of query rows (dK and dV of 4 key rows of one plane per work-group,
+// the query rows whose windows reach them streamed) within `lds_rows` rows per stage.
 constexpr bool na_rows_reverse_eligible(const NaGeom& g, int32_t lds_rows) {
   if (g.grid_w > 32 || g.grid_h > 128 || g.grid_d > 128) return false;
-  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kRowsGroup)
-    if (na_rows_reverse_band(y0, g).count > lds_rows) return false;
+  for (int32_t i = 0, n = na_row_groups(g); i < n; ++i)
+    if (na_row_group(g, i, true).band.count > lds_rows) return false;
   return true;
 }
 

@@ -283,6 +283,29 @@ static int check_patch(const NaGeom& g, int lds_rows) {
   return 1;
 }
 
+// The row groups of a plane: every grid row held by exactly one wavefront of one group,
+// and a group's band rows distinct grid rows.
+static void check_row_groups(const NaGeom& g) {
+  std::vector<int> held(g.grid_h, 0);
+  for (int gi = 0; gi < na_row_groups(g); ++gi)
+    for (bool rev : {false, true}) {
+      const RowGroup rg = na_row_group(g, gi, rev);
+      if (!rev)
+        for (int w = 0; w < kRowsGroup; ++w)
+          if (rg.u0 + w < rg.len) {
+            const int y = rg.rho + rg.stride * (rg.u0 + w);
+            EXPECT(y >= 0 && y < g.grid_h, "group %d wavefront %d holds row %d", gi, w, y);
+            if (y >= 0 && y < g.grid_h) ++held[y];
+          }
+      std::set<int> rows;
+      for (int r = 0; r < rg.band.count; ++r) rows.insert(row_group_row(rg, r));
+      EXPECT((int)rows.size() == rg.band.count, "group %d: %zu distinct band rows of %d", gi, rows.size(),
+             rg.band.count);
+    }
+  for (int y = 0; y < g.grid_h; ++y)
+    EXPECT(held[y] == 1, "grid row %d held %d times (H %d dil %d wrap %d)", y, held[y], g.grid_h, g.dil_h, g.wrap_h);
+}
+
 // The row kernel (MASK_NA_ROWS) as it walks its stages: for every plane, group of
 // rows, wavefront and lane, the cells it marks visible (visible planes of the plane
 // band, visible rows of the group's row band, the lane's column bits) are exactly the
@@ -290,15 +313,17 @@ static int check_patch(const NaGeom& g, int lds_rows) {
 static int check_rows(const NaGeom& g, int lds_rows) {
   if (!na_rows_eligible(g, lds_rows)) return 0;
   const int H = g.grid_h, W = g.grid_w, D = g.grid_d;
+  check_row_groups(g);
   for (int z = 0; z < D; ++z)
-    for (int y0 = 0; y0 < H; y0 += kRowsGroup) {
+    for (int gi = 0; gi < na_row_groups(g); ++gi) {
       const Band bz = na_band(z, z, D, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
-      const Band by = na_rows_band(y0, g);
-      EXPECT(by.count >= 1 && by.count <= lds_rows && bz.count >= 1 && bz.count <= D, "rows bands %d, %d", by.count,
-             bz.count);
+      const RowGroup rg = na_row_group(g, gi, false);
+      const Band by = rg.band;
+      EXPECT(by.count >= 1 && by.count <= lds_rows && by.count <= rg.len && bz.count >= 1 && bz.count <= D,
+             "rows bands %d, %d", by.count, bz.count);
       for (int w = 0; w < kRowsGroup; ++w) {
-        const int y = y0 + w;
-        if (y >= H) continue;
+        if (rg.u0 + w >= rg.len) continue;
+        const int y = rg.rho + rg.stride * (rg.u0 + w);
         for (int x = 0; x < W; ++x) {
           const GridMasks gm = na_grid_masks(z, y, x, g);
           std::vector<int> seen;
@@ -306,7 +331,8 @@ static int check_rows(const NaGeom& g, int lds_rows) {
             const int zk = (bz.start + i) % D;
             if (!bit128(gm.z0, gm.z1, zk)) continue;
             for (int r = 0; r < by.count; ++r) {
-              const int yk = (by.start + r) % H;
+              const int yk = row_group_row(rg, r);
+              EXPECT(yk >= 0 && yk < H, "band row %d of the group maps to grid row %d", r, yk);
               if (!bit128(gm.y0, gm.y1, yk)) continue;
               for (int xk = 0; xk < 32; ++xk)
                 if ((((uint32_t)gm.x0 >> xk) & 1u) != 0) {
@@ -338,18 +364,20 @@ static int check_rows_reverse(const NaGeom& g, int lds_rows) {
   std::vector<std::set<int>> seers(N);
   for (int q = 0; q < N; ++q)
     for (int k : window_keys(g, q)) seers[k].insert(q);
+  check_row_groups(g);
   for (int z = 0; z < D; ++z)
-    for (int y0 = 0; y0 < H; y0 += kRowsGroup) {
+    for (int gi = 0; gi < na_row_groups(g); ++gi) {
       const Band bz = na_band_reverse(z, z, D, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
-      const Band by = na_rows_reverse_band(y0, g);
-      EXPECT(by.count >= 1 && by.count <= lds_rows && bz.count >= 1 && bz.count <= D, "reverse bands %d, %d",
-             by.count, bz.count);
+      const RowGroup rg = na_row_group(g, gi, true);
+      const Band by = rg.band;
+      EXPECT(by.count >= 1 && by.count <= lds_rows && by.count <= rg.len && bz.count >= 1 && bz.count <= D,
+             "reverse bands %d, %d", by.count, bz.count);
       int own = z - bz.start;
       own += own < 0 ? D : 0;
       EXPECT(own >= 0 && own < bz.count, "the key plane %d lies in its reverse band", z);
       for (int w = 0; w < kRowsGroup; ++w) {
-        const int y = y0 + w;
-        if (y >= H) continue;
+        if (rg.u0 + w >= rg.len) continue;
+        const int y = rg.rho + rg.stride * (rg.u0 + w);
         for (int x = 0; x < W; ++x) {
           const GridMasks rm = na_grid_reverse_masks(z, y, x, g);
           std::vector<int> seen;
@@ -357,7 +385,8 @@ static int check_rows_reverse(const NaGeom& g, int lds_rows) {
             const int zq = (bz.start + i) % D;
             if (!bit128(rm.z0, rm.z1, zq)) continue;
             for (int r = 0; r < by.count; ++r) {
-              const int yq = (by.start + r) % H;
+              const int yq = row_group_row(rg, r);
+              EXPECT(yq >= 0 && yq < H, "band row %d of the group maps to grid row %d", r, yq);
               if (!bit128(rm.y0, rm.y1, yq)) continue;
               for (int xq = 0; xq < 32; ++xq)
                 if ((((uint32_t)rm.x0 >> xq) & 1u) != 0) {
@@ -753,15 +782,22 @@ int main() {
                 if (!na_rows_eligible(g, 10)) wide += check_rows(g, 12);
                 if (!na_rows_reverse_eligible(g, 8)) wide_rev += check_rows_reverse(g, 12);
               }
-    EXPECT(wide > 10 && wide_rev > 10, "wide row stages take %d (forward) and %d (reverse) more shapes", wide,
-           wide_rev);
-    EXPECT(!na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 10) &&
-               na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 12) &&
-               na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 12),
-           "20x20x20, 5x5x5 window of dilation 2: 12-row bands, the wide stages");
+    EXPECT(wide_rev > 10, "wide row stages take %d (forward) and %d (reverse) more shapes", wide, wide_rev);
+    // the wide forward stages: wrapped rows that the dilation does not divide keep consecutive groups
+    EXPECT(check_rows(geom(5, 15, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1), 12) == 1 &&
+               check_rows(geom(2, 13, 20, 1, 5, 5, 0, 1, 0, 1, 2, 3), 12) == 1 &&
+               check_rows_reverse(geom(5, 15, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1), 12) == 1,
+           "wide stages of consecutive dilated rows");
+    EXPECT(na_rows_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 8) &&
+               na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 2, 2, 2), 8),
+           "20x20x20, 5x5x5 window of dilation 2: groups of one residue, 8-row bands");
+    EXPECT(!na_rows_strided(geom(5, 15, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1)) &&
+               !na_rows_eligible(geom(5, 15, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1), 10) &&
+               na_rows_eligible(geom(5, 15, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1), 12),
+           "15 wrapped rows at dilation 2: consecutive rows, 12-row bands, the wide stages");
     EXPECT(na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 0, 0, 0, 1, 1, 1), 12),
            "clamped 5x5x5 windows: the 10-row reverse bands near the borders fit the wide stages");
-    EXPECT(eligible > 100 && eligible < tried, "row-kernel eligibility covers %d of %d shapes", eligible, tried);
+    EXPECT(eligible > 100 && eligible <= tried, "row-kernel eligibility covers %d of %d shapes", eligible, tried);
     EXPECT(eligible_rev > 80 && eligible_rev < eligible, "dK/dV row-kernel eligibility covers %d of %d shapes",
            eligible_rev, tried);
     EXPECT(na_rows_reverse_eligible(geom(20, 20, 20, 5, 5, 5, 1, 1, 0, 1, 1, 1), 8),

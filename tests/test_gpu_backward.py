@@ -105,12 +105,12 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (33, 64, 5, 9, 0, 1, 1, 2)),               # a 32-column band: dilated, wrapped columns
     ("na2d", (40, 64, 7, 7, 0, 0, 2, 2)),               # clamped and dilated (tight clamped bands)
     ("na2d", (30, 50, 5, 5, 0, 0, 3, 3)),               # dilation 3, clamped
-    # the tile kernels with the reverse query runs of clamped axes
-    ("na3d", (10, 12, 14, 3, 3, 3, 0, 0, 0, 2, 2, 3)),
-    # the row kernels' wide 12-row stages at d = 32
-    ("na3d", (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)),  # dilation 2: all three row kernels wide
+    ("na3d", (10, 12, 14, 3, 3, 3, 0, 0, 0, 2, 2, 3)),  # clamped, dilated (d = 128: the tile kernels' query runs)
+    # row groups of one residue mod the dilation (8-row bands), and the wide 12-row stages, at d = 32
+    ("na3d", (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)),  # 16 wrapped rows, dilation 2: groups of one residue
+    ("na3d", (10, 15, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)),  # 15 wrapped rows: consecutive groups, all three wide
     ("na3d", (6, 20, 12, 3, 5, 5, 0, 0, 0, 1, 1, 1)),   # clamped: dK/dV's 10-row reverse bands near the borders
-    ("na3d", (7, 13, 9, 3, 5, 3, 0, 0, 1, 2, 2, 1)),    # clamped and dilated: dQ wide, dK/dV on the tile kernel
+    ("na3d", (7, 13, 9, 3, 5, 3, 0, 0, 1, 2, 2, 1)),    # clamped and dilated: residue groups of 7 and 6 rows
 ])
 def test_bwd_neighbourhood(mode, geo, d):
     import exact_attention_68_amd as A
@@ -124,6 +124,8 @@ def test_bwd_neighbourhood(mode, geo, d):
 @pytest.mark.parametrize("scale", [0.0, -0.3, 1e-3])
 @pytest.mark.parametrize("mode,geo", [
     ("na3d", (6, 7, 9, 3, 5, 3, 1, 1, 0, 1, 1, 1)),   # the row kernels
+    ("na3d", (5, 13, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1)),  # their wide 12-row stages (13 rows, dilation 2)
+    ("na3d", (5, 12, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1)),  # row groups of one residue (12 rows, dilation 2)
     ("na2d", (20, 40, 5, 7, 1, 0, 1, 1)),             # the patch kernels
 ])
 def test_bwd_neighbourhood_scales(mode, geo, scale):

@@ -163,22 +163,24 @@ def test_clamped_dilated_na2d_takes_patch_kernels():
     assert others == [], others
 
 
-def test_na3d_dilated_takes_wide_row_kernels():
-    """A 5x5x5 window of dilation 2 on planes and rows reaches 12-row bands: the three row kernels with
-    their wide (12-row) stages."""
+@pytest.mark.parametrize("gh,fwd,dq,dkv", [(15, 12, 12, 12), (16, 10, 10, 8)])
+def test_na3d_dilated_row_kernel_stages(gh, fwd, dq, dkv):
+    """A 5x5x5 window of dilation 2 on planes and rows. On 16 wrapped rows a work-group takes rows of one
+    residue mod 2 (8-row bands): the narrow stages (10 rows, 8 for dK/dV). On 15 the dilation does not
+    divide the cycle, groups stay consecutive and reach 12-row bands: the wide (12-row) stages."""
     import re
 
     import exact_attention_68_amd as A
 
-    B, H, N, d = 1, 2, 10 * 16 * 12, 32
+    B, H, N, d = 1, 2, 10 * gh * 12, 32
     q, k, v = _inputs(B, H, N, d, 5)
-    params = A.na3d_params(10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)
+    params = A.na3d_params(10, gh, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
-    wide = re.compile(r"<32,\s*12>")
+    stage = lambda rows: re.compile(r"<32,\s*%d>" % rows)
     kernels, others = _split(_dispatches(
         lambda: A.attn_fwd_ex(q, k, v, o, lse, d ** -0.5, A.ATTN_MASK_NA3D, params, None)))
-    assert len(kernels) == 1 and "attn_fwd_na_rows_kernel" in kernels[0] and wide.search(kernels[0]), kernels
+    assert len(kernels) == 1 and "attn_fwd_na_rows_kernel" in kernels[0] and stage(fwd).search(kernels[0]), kernels
     assert others == [], others
     do = torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16)
     ws = torch.empty(A.attn_bwd_workspace_size(B, H, N, N, d, A.ATTN_MASK_NA3D, params), dtype=torch.uint8,
@@ -187,6 +189,6 @@ def test_na3d_dilated_takes_wide_row_kernels():
     kernels, others = _split(_dispatches(
         lambda: A.attn_bwd(q, k, v, o, do, lse, *grads, d ** -0.5, A.ATTN_MASK_NA3D, params, ws)))
     assert len(kernels) == 2, kernels
-    assert "attn_bwd_dq_rows_kernel" in kernels[0] and wide.search(kernels[0]), kernels
-    assert "attn_bwd_dkv_rows_kernel" in kernels[1] and wide.search(kernels[1]), kernels
+    assert "attn_bwd_dq_rows_kernel" in kernels[0] and stage(dq).search(kernels[0]), kernels
+    assert "attn_bwd_dkv_rows_kernel" in kernels[1] and stage(dkv).search(kernels[1]), kernels
     assert others == [], others

@@ -123,8 +123,9 @@ def test_d128_na2d(gh, gw, kh, kw, wh, ww):
     (16, 4, 4, 3, 3, 3, 1, 1, 1, 1, 1, 1),    # planes of 16 tokens: a key tile spans 8 planes
     (6, 6, 6, 3, 3, 3, 1, 0, 1, 2, 2, 2),     # dilated
     (10, 9, 8, 3, 3, 3, 0, 0, 0, 3, 3, 2),    # clamped and dilated
-    (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1),  # 12-row bands at dilation 2: the row kernel's wide stages (d = 32)
-    (7, 13, 9, 3, 5, 3, 0, 0, 1, 2, 2, 1),    # clamped and dilated, wide stages
+    (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1),  # dilation 2 on 16 wrapped rows: row groups of one residue (d = 32)
+    (10, 15, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1),  # 15 wrapped rows: consecutive groups, 12-row bands, the wide stages
+    (7, 13, 9, 3, 5, 3, 0, 0, 1, 2, 2, 1),    # clamped and dilated: residue groups of 7 and 6 rows
 ])
 def test_na3d_shapes(geo, d):
     import exact_attention_68_amd as A
@@ -135,12 +136,14 @@ def test_na3d_shapes(geo, d):
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 1e-3])
-def test_na3d_row_kernel_scales(scale):
+@pytest.mark.parametrize("geo", [(6, 7, 9, 3, 5, 3, 1, 1, 0, 1, 1, 1),
+                                 (5, 13, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1),   # the wide 12-row stages
+                                 (5, 12, 9, 3, 5, 3, 1, 1, 0, 2, 2, 1)])  # row groups of one residue
+def test_na3d_row_kernel_scales(scale, geo):
     """Scale 0, a negative scale and a tiny one through the row kernel's walk (d = 32, a grid 9 wide):
     each lane's reference maximum is set at its first visible key whatever the scale."""
     import exact_attention_68_amd as A
 
-    geo = (6, 7, 9, 3, 5, 3, 1, 1, 0, 1, 1, 1)
     N = geo[0] * geo[1] * geo[2]
     q, k, v = _qkv(1, 2, N, N, 32, 9700 + N)
     check_case(q, k, v, scale, "na3d", A.na3d_params(*geo), what=f"na3d rows scale {scale}", entry=EX)

@@ -101,14 +101,15 @@ def test_d32_four_stage_rings_equal_serial(libs, mask):
         assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
 
 
-def test_na3d_wide_rows_forward_equals_serial(libs):
-    """The forward row kernel's wide 12-row stages (10x16x12 volume, 5x5x5 window, dilation 2 on planes and
-    rows), with its logsumexp."""
+@pytest.mark.parametrize("gh", [15, 16])
+def test_na3d_dilated_rows_forward_equals_serial(libs, gh):
+    """The forward row kernel on a 10 x gh x 12 volume, 5x5x5 window dilated by 2 on planes and rows, with its
+    logsumexp: 15 wrapped rows take the wide 12-row stages, 16 the row groups of one residue."""
     import exact_attention_68_amd as A
 
     piped, serial = libs
-    q, k, v = (t.cuda() for t in workloads.make_qkv(1, 2, 1920, 32, 90))
-    params = A.na3d_params(10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)
+    q, k, v = (t.cuda() for t in workloads.make_qkv(1, 2, 10 * gh * 12, 32, 90))
+    params = A.na3d_params(10, gh, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)
     ref_o, ref_l = _fwd(serial, q, k, v, A.ATTN_MASK_NA3D, 32 ** -0.5, params, "attn_fwd_ex", True)
     for _ in range(3):
         o, lse = _fwd(piped, q, k, v, A.ATTN_MASK_NA3D, 32 ** -0.5, params, "attn_fwd_ex", True)
@@ -116,20 +117,23 @@ def test_na3d_wide_rows_forward_equals_serial(libs):
         assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
 
 
-@pytest.mark.parametrize("mask,d", [("none", 64), ("causal", 64), ("none", 128), ("na3d", 32), ("na3d_wide", 32)])
+@pytest.mark.parametrize("mask,d", [("none", 64), ("causal", 64), ("none", 128), ("na3d", 32), ("na3d_wide", 32),
+                                   ("na3d_residue", 32)])
 def test_backward_pipelined_equals_serial(libs, mask, d):
     """The tile kernels; at "na3d" (a 10x10x10 volume, 5x5x5 window) the row kernels' two-stage rings, at
-    "na3d_wide" (10x16x12, dilation 2 on planes and rows: 12-row bands) their wide stages."""
+    "na3d_wide" (10x15x12, dilation 2 on planes and 15 wrapped rows: 12-row bands) their wide stages, at
+    "na3d_residue" (10x16x12, the same window: row groups of one residue) their strided stages."""
     import exact_attention_68_amd as A
 
     piped, serial = libs
-    B, H, N = {"na3d": (2, 2, 1000), "na3d_wide": (1, 2, 1920)}.get(mask, (1, 4, 2000))
+    B, H, N = {"na3d": (2, 2, 1000), "na3d_wide": (1, 2, 1800), "na3d_residue": (1, 2, 1920)}.get(mask, (1, 4, 2000))
     q, k, v = (t.cuda() for t in workloads.make_qkv(B, H, N, d, 88))
     g = torch.Generator(device="cpu").manual_seed(89)
     do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda()
     mode = {"none": A.ATTN_MASK_NONE, "causal": A.ATTN_MASK_CAUSAL}.get(mask, A.ATTN_MASK_NA3D)
     params = {"na3d": A.na3d_params(10, 10, 10, 5, 5, 5, 1, 1, 0),
-              "na3d_wide": A.na3d_params(10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)}.get(mask)
+              "na3d_wide": A.na3d_params(10, 15, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1),
+              "na3d_residue": A.na3d_params(10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)}.get(mask)
     pp = A._params_ptr(params)
     o, lse = _fwd(piped, q, k, v, mode, d ** -0.5, params, "attn_fwd_ex", True)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
