@@ -60,7 +60,7 @@ int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
   if (p.mask == ATTN_MASK_CAUSAL) return attn::MASK_CAUSAL;
   const int32_t patch_rows = attn::patch_lds_rows(p.d);
   if (patch_rows > 0 && attn::na_patch_eligible(g, patch_rows)) {
-    const int64_t patches = p.B * p.H * attn::cdiv(g.grid_h, attn::kPatchRows) * attn::cdiv(g.grid_w, attn::kPatchCols);
+    const int64_t patches = p.B * p.H * attn::na_patch_row_groups(g) * attn::cdiv(g.grid_w, attn::kPatchCols);
     if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
   }
   if (rows_stage(p.d, g) > 0) {
@@ -103,7 +103,7 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   int32_t n_wg = a.BH * a.n_qtiles, rem = 0;
   if (mask == attn::MASK_NA_PATCH) {
     a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
-    a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kPatchRows);
+    a.patch_ny = attn::na_patch_row_groups(a.na);
     n_wg = a.BH * a.patch_nx * a.patch_ny;
   }
   if (mask == attn::MASK_NA_ROWS) {
@@ -285,7 +285,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     // wider single-plane grids: the patch kernels (the row kernels keep the narrow ones)
     const int32_t patch_lds = attn::bwd_patch_lds(d);
     a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
-    a.patch_ny = (int32_t)attn::cdiv(a.na.grid_h, attn::kPatchRows);
+    a.patch_ny = attn::na_patch_row_groups(a.na);
     const bool patches_fit = (int64_t)a.BH * a.patch_nx * a.patch_ny <= INT32_MAX;
     a.dq_patch = !a.dq_rows && patches_fit && attn::na_patch_bwd_eligible(a.na, patch_lds, false) ? 1 : 0;
     a.dkv_patch = !a.dkv_rows && patches_fit && attn::na_patch_bwd_eligible(a.na, patch_lds, true) ? 1 : 0;

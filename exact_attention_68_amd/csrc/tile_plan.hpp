@@ -381,6 +381,18 @@ constexpr void na_col_bits(int32_t cq, int32_t half, int32_t W, int32_t kernel, 
   }
 }
 
+// Rows of one residue mod the row dilation. With dilation along the rows (and, on a
+// wrapped axis, a row count the dilation divides) the grid rows congruent to rho mod
+// dil form a sub-grid on which every window is an undilated window: clamped,
+// na_dil_anchor takes it inside that sub-grid; wrapped, it steps dil rows at a time
+// around a cycle of grid_h / dil of them. The row and patch kernels then take the
+// rows of a work-group from one sub-grid, whose bands count 2 rad rows of margin
+// rather than 2 rad dil.
+constexpr bool na_rows_strided(const NaGeom& g) { return g.dil_h > 1 && (!g.wrap_h || g.grid_h % g.dil_h == 0); }
+
+// Rows of the sub-grid of residue rho.
+constexpr int32_t na_rows_sub_len(const NaGeom& g, int32_t rho) { return (g.grid_h - 1 - rho) / g.dil_h + 1; }
+
 // ---------------------------------------------------------------------------
 // Query patches of 2D neighbourhood windows (MASK_NA_PATCH), dilated or not.
 //
@@ -406,6 +418,41 @@ constexpr PatchBands na_patch_bands(int32_t y0, int32_t x0, const NaGeom& g) {
       na_band(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w)};
 }
 
+// The rows of patch row py of a plane: kPatchRows consecutive rows of the residue
+// sub-grid (na_rows_strided), else of the plane. `geom` is the window geometry in
+// that sub-grid's coordinates (grid_h its length, dil_h 1); sub-grid row u is grid
+// row rho + stride u. The patch kernels work in those coordinates throughout and map
+// to grid rows only to address tokens.
+struct PatchRowGroup {
+  int32_t rho, stride, u0;
+  NaGeom geom;
+};
+
+constexpr int32_t na_patch_row_groups(const NaGeom& g) {
+  if (!na_rows_strided(g)) return (int32_t)cdiv(g.grid_h, kPatchRows);
+  int32_t n = 0;
+  for (int32_t rho = 0; rho < g.dil_h; ++rho) n += (int32_t)cdiv(na_rows_sub_len(g, rho), kPatchRows);
+  return n;
+}
+
+constexpr PatchRowGroup na_patch_row_group(const NaGeom& g, int32_t py) {
+  PatchRowGroup pr{0, 1, py * kPatchRows, g};
+  if (!na_rows_strided(g)) return pr;
+  for (int32_t rho = 0; rho < g.dil_h; ++rho) {
+    const int32_t len = na_rows_sub_len(g, rho), n = (int32_t)cdiv(len, kPatchRows);
+    if (py < n || rho == g.dil_h - 1) {
+      pr.rho = rho;
+      pr.stride = g.dil_h;
+      pr.u0 = py * kPatchRows;
+      pr.geom.grid_h = len;
+      pr.geom.dil_h = 1;
+      break;
+    }
+    py -= n;
+  }
+  return pr;
+}
+
 // One plane; every column band within one 32-key block; a wrapped row band shorter
 // than the axis (so the band of a wavefront's two rows is one run of its
 // work-group's band); and every row band, plus the 3 rows a wavefront's last step
@@ -414,9 +461,10 @@ constexpr bool na_patch_eligible(const NaGeom& g, int32_t lds_rows) {
   if (g.grid_d != 1) return false;
   for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols)
     if (na_patch_bands(0, x0, g).cols.count > kPatchKeyCols) return false;
-  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kPatchRows) {
-    const Band rows = na_patch_bands(y0, 0, g).rows;
-    if (rows.count + 3 > lds_rows || (g.wrap_h && rows.count >= g.grid_h)) return false;
+  for (int32_t py = 0, n = na_patch_row_groups(g); py < n; ++py) {
+    const PatchRowGroup pr = na_patch_row_group(g, py);
+    const Band rows = na_patch_bands(pr.u0, 0, pr.geom).rows;
+    if (rows.count + 3 > lds_rows || (pr.geom.wrap_h && rows.count >= pr.geom.grid_h)) return false;
   }
   return true;
 }
@@ -478,9 +526,10 @@ constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool rev
     const PatchBands b = reverse ? na_patch_reverse_bands(0, x0, g) : na_patch_bands(0, x0, g);
     if (b.cols.count > kPatchKeyCols) return false;
   }
-  for (int32_t y0 = 0; y0 < g.grid_h; y0 += kPatchRows) {
-    const Band rows = (reverse ? na_patch_reverse_bands(y0, 0, g) : na_patch_bands(y0, 0, g)).rows;
-    if (rows.count > lds_rows || (g.wrap_h && rows.count >= g.grid_h)) return false;
+  for (int32_t py = 0, n = na_patch_row_groups(g); py < n; ++py) {
+    const PatchRowGroup pr = na_patch_row_group(g, py);
+    const Band rows = (reverse ? na_patch_reverse_bands(pr.u0, 0, pr.geom) : na_patch_bands(pr.u0, 0, pr.geom)).rows;
+    if (rows.count > lds_rows || (pr.geom.wrap_h && rows.count >= pr.geom.grid_h)) return false;
   }
   return true;
 }
@@ -498,13 +547,9 @@ constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool rev
 // of those rows); each wavefront scores only its own visible rows of a stage.
 constexpr int32_t kRowsGroup = 4;
 
-// The rows of a group. With dilation along the rows (and, on a wrapped axis, a row
-// count the dilation divides), the grid rows congruent to rho mod dil form a
-// sub-grid on which every window is an undilated window: clamped, na_dil_anchor
-// takes it inside that sub-grid; wrapped, it steps dil rows at a time around a
-// cycle of grid_h / dil of them. A group then takes 4 consecutive rows of one
-// sub-grid and its band is 4 + 2 rad sub-grid rows rather than 4 + 2 rad dil grid
-// rows. Otherwise (dilation 1, or a wrapped axis the dilation does not divide) the
+// The rows of a group. With strided rows (na_rows_strided) a group takes 4
+// consecutive rows of one residue sub-grid and its band is 4 + 2 rad sub-grid rows
+// rather than 4 + 2 rad dil grid rows. Otherwise (dilation 1, or a wrapped axis the dilation does not divide) the
 // sub-grid is the whole axis (rho 0, stride 1). Wavefront w holds grid row
 // rho + stride (u0 + w) while u0 + w < len; band row r is the grid row of sub-grid
 // cell (band.start + r) mod len.
@@ -512,10 +557,6 @@ struct RowGroup {
   int32_t rho, stride, len, u0;
   Band band;
 };
-
-constexpr bool na_rows_strided(const NaGeom& g) { return g.dil_h > 1 && (!g.wrap_h || g.grid_h % g.dil_h == 0); }
-
-constexpr int32_t na_rows_sub_len(const NaGeom& g, int32_t rho) { return (g.grid_h - 1 - rho) / g.dil_h + 1; }
 
 // Groups per plane (both row kernels).
 constexpr int32_t na_row_groups(const NaGeom& g) {

@@ -207,16 +207,40 @@ static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int
   check_na_geom(geom(1, gh, gw, 1, kh, kw, 0, wh, ww, 1, 1, 1), BM, BN);
 }
 
+// The patch row groups of a plane: every grid row held by exactly one patch row of
+// one group (rows pr.rho + pr.stride * (pr.u0 + i), i < kPatchRows, inside the sub-grid).
+static void check_patch_rows(const NaGeom& g) {
+  std::vector<int> held(g.grid_h, 0);
+  for (int py = 0; py < na_patch_row_groups(g); ++py) {
+    const PatchRowGroup pr = na_patch_row_group(g, py);
+    EXPECT(pr.geom.grid_w == g.grid_w && pr.geom.dil_w == g.dil_w && pr.geom.kernel_h == g.kernel_h,
+           "sub-grid geometry keeps the columns and the window");
+    for (int i = 0; i < kPatchRows; ++i)
+      if (pr.u0 + i < pr.geom.grid_h) {
+        const int y = pr.rho + pr.stride * (pr.u0 + i);
+        EXPECT(y >= 0 && y < g.grid_h, "patch row group %d row %d is grid row %d", py, i, y);
+        if (y >= 0 && y < g.grid_h) ++held[y];
+      }
+  }
+  for (int y = 0; y < g.grid_h; ++y)
+    EXPECT(held[y] == 1, "grid row %d held by %d patch rows (H %d dil %d wrap %d)", y, held[y], g.grid_h, g.dil_h,
+           g.wrap_h);
+}
+
 // The patch kernel (MASK_NA_PATCH) as it walks its LDS rectangle: for every patch,
 // wavefront and lane, the cells it marks visible are exactly the query's window
 // (enumerated independently), each once; the rectangle fits the kernel's LDS rows;
 // every step's four blocks lie inside them; and the first step holds a visible key
 // of every query (it sets the reference maximum).
-static int check_patch(const NaGeom& g, int lds_rows) {
-  if (!na_patch_eligible(g, lds_rows)) return 0;
-  const int H = g.grid_h, W = g.grid_w;
-  for (int y0 = 0; y0 < H; y0 += kPatchRows)
-    for (int x0 = 0; x0 < W; x0 += kPatchCols) {
+static int check_patch(const NaGeom& g0, int lds_rows) {
+  if (!na_patch_eligible(g0, lds_rows)) return 0;
+  check_patch_rows(g0);
+  for (int py = 0; py < na_patch_row_groups(g0); ++py)
+    for (int x0 = 0; x0 < g0.grid_w; x0 += kPatchCols) {
+      // rows in the coordinates of the patch's row sub-grid, as the kernel takes them
+      const PatchRowGroup pr = na_patch_row_group(g0, py);
+      const NaGeom& g = pr.geom;
+      const int H = g.grid_h, W = g.grid_w, y0 = pr.u0;
       const PatchBands pb = na_patch_bands(y0, x0, g);
       EXPECT(pb.cols.count >= 1 && pb.cols.count <= kPatchKeyCols && pb.rows.count >= 1 && pb.rows.count + 3 <= lds_rows,
              "patch bands %d x %d (grid %dx%d k %d,%d wrap %d%d)", pb.rows.count, pb.cols.count, H, W, g.kernel_h,
@@ -263,14 +287,14 @@ static int check_patch(const NaGeom& g, int lds_rows) {
                 if (rok && ((cm >> x) & 1u)) {
                   EXPECT(r < pb.rows.count && x < pb.cols.count && ky >= 0 && ky < H && kx >= 0 && kx < W,
                          "visible cell outside the rectangle");
-                  seen.push_back(ky * W + kx);
+                  seen.push_back((pr.rho + pr.stride * ky) * W + kx);
                   first_step = first_step || st == 0;
                 }
               }
             }
-          std::set<int> want;
-          for (int yc : axis_cells(qy, H, g.kernel_h, g.wrap_h, g.dil_h))
-            for (int xc : axis_cells(qx, W, g.kernel_w, g.wrap_w, g.dil_w)) want.insert(yc * W + xc);
+          std::set<int> want;  // the window on the grid itself
+          for (int yc : axis_cells(pr.rho + pr.stride * qy, g0.grid_h, g0.kernel_h, g0.wrap_h, g0.dil_h))
+            for (int xc : axis_cells(qx, W, g0.kernel_w, g0.wrap_w, g0.dil_w)) want.insert(yc * W + xc);
           const std::set<int> got(seen.begin(), seen.end());
           EXPECT(got.size() == seen.size() && got == want,
                  "patch window of query (%d,%d): %zu cells (%zu distinct), want %zu (grid %dx%d k %d,%d wrap %d%d)", qy, qx,
@@ -412,17 +436,22 @@ static int check_rows_reverse(const NaGeom& g, int lds_rows) {
 // cells it marks (its wavefront's band rows of the rectangle whose row bit is set, its
 // column bits) are exactly its window (the queries that see its key), each once, and
 // every rectangle fits `lds_rows` rows of 32 tokens.
-static int check_patch_bwd(const NaGeom& g, int lds_rows, bool reverse) {
-  if (!na_patch_bwd_eligible(g, lds_rows, reverse)) return 0;
-  const int H = g.grid_h, W = g.grid_w, N = H * W;
+static int check_patch_bwd(const NaGeom& g0, int lds_rows, bool reverse) {
+  if (!na_patch_bwd_eligible(g0, lds_rows, reverse)) return 0;
+  const int N = g0.grid_h * g0.grid_w;
   std::vector<std::vector<int>> want(N);  // sorted, distinct
   for (int q = 0; q < N; ++q)
-    for (int k : window_keys(g, q)) {
+    for (int k : window_keys(g0, q)) {
       if (reverse) want[k].push_back(q);  // q ascending: sorted
       else want[q].push_back(k);          // from a set: sorted
     }
-  for (int y0 = 0; y0 < H; y0 += kPatchRows)
-    for (int x0 = 0; x0 < W; x0 += kPatchCols) {
+  check_patch_rows(g0);
+  for (int py = 0; py < na_patch_row_groups(g0); ++py)
+    for (int x0 = 0; x0 < g0.grid_w; x0 += kPatchCols) {
+      // rows in the coordinates of the patch's row sub-grid, as the kernels take them
+      const PatchRowGroup pr = na_patch_row_group(g0, py);
+      const NaGeom& g = pr.geom;
+      const int H = g.grid_h, W = g.grid_w, y0 = pr.u0;
       const PatchBands pb = reverse ? na_patch_reverse_bands(y0, x0, g) : na_patch_bands(y0, x0, g);
       EXPECT(pb.rows.count >= 1 && pb.rows.count <= lds_rows && pb.cols.count >= 1 && pb.cols.count <= kPatchKeyCols,
              "patch rectangle %d x %d", pb.rows.count, pb.cols.count);
@@ -443,11 +472,11 @@ static int check_patch_bwd(const NaGeom& g, int lds_rows, bool reverse) {
           std::vector<int> seen;
           for (int r = off; r < off + wb.count; ++r) {
             if (!((rows_w >> r) & 1u)) continue;
-            const int ty = (pb.rows.start + r) % H;
+            const int ty = pr.rho + pr.stride * ((pb.rows.start + r) % H);
             for (int x = 0; x < pb.cols.count; ++x)
               if ((cm >> x) & 1u) seen.push_back(ty * W + (pb.cols.start + x) % W);
           }
-          const int me = cy * W + cx;
+          const int me = (pr.rho + pr.stride * cy) * W + cx;
           std::sort(seen.begin(), seen.end());
           EXPECT(seen == want[me],  // equal sorted lists: the same cells, each once
                  "%s patch cells of token %d: %zu, want %zu (grid %dx%d k %d,%d wrap %d%d dil %d,%d)",
@@ -757,8 +786,13 @@ int main() {
            "64x64 grid, 7x7 wrapped window: both backward patch kernels");
     const NaGeom c4 = geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 1, 1);
     EXPECT(na_patch_eligible(c4, 24) && na_patch_eligible(c4, 17), "64x64 grid, 7x7 wrapped window takes the patch kernel");
-    EXPECT(na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 24), "and with dilation 2 (20 band rows)");
-    EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 17), "not in 17 rows");
+    EXPECT(na_patch_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 17) &&
+               na_patch_bwd_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 17, false) &&
+               na_patch_bwd_eligible(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 17, true),
+           "and with dilation 2: patches of rows of one parity, 14-row bands, also in 17 rows (d = 64)");
+    EXPECT(!na_patch_eligible(geom(1, 63, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 17) &&
+               na_patch_eligible(geom(1, 63, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2), 24),
+           "63 wrapped rows at dilation 2: consecutive rows, 20-row bands, not in 17 rows");
     EXPECT(!na_patch_eligible(geom(4, 20, 20, 3, 5, 5, 1, 1, 1, 1, 1, 1), 24), "3D windows do not");
     EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 19, 0, 1, 1, 1, 1, 1), 24), "19 columns wide: the band passes 32");
   }

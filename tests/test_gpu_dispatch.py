@@ -192,3 +192,28 @@ def test_na3d_dilated_row_kernel_stages(gh, fwd, dq, dkv):
     assert "attn_bwd_dq_rows_kernel" in kernels[0] and stage(dq).search(kernels[0]), kernels
     assert "attn_bwd_dkv_rows_kernel" in kernels[1] and stage(dkv).search(kernels[1]), kernels
     assert others == [], others
+
+
+def test_na2d_dilated_d64_takes_patch_kernels():
+    """A 7x7 window of dilation 2 on a 64x64 wrapped grid: each patch takes 8 rows of one parity, whose
+    windows reach 14 rows of that parity, so even the d = 64 rectangles (17 rows) hold them."""
+    import exact_attention_68_amd as A
+
+    B, H, N, d = 1, 2, 64 * 64, 64
+    q, k, v = _inputs(B, H, N, d, 6)
+    params = A.na2d_params(64, 64, 7, 7, 1, 1, 2, 2)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    kernels, others = _split(_dispatches(
+        lambda: A.attn_fwd_ex(q, k, v, o, lse, d ** -0.5, A.ATTN_MASK_NA2D, params, None)))
+    assert len(kernels) == 1 and "attn_fwd_na_patch_kernel" in kernels[0], kernels
+    assert others == [], others
+    do = torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16)
+    ws = torch.empty(A.attn_bwd_workspace_size(B, H, N, N, d, A.ATTN_MASK_NA2D, params), dtype=torch.uint8,
+                     device="cuda")
+    grads = [torch.empty_like(t) for t in (q, k, v)]
+    kernels, others = _split(_dispatches(
+        lambda: A.attn_bwd(q, k, v, o, do, lse, *grads, d ** -0.5, A.ATTN_MASK_NA2D, params, ws)))
+    assert len(kernels) == 2 and "attn_bwd_dq_patch_kernel" in kernels[0] and "attn_bwd_dkv_patch_kernel" in kernels[1], \
+        kernels
+    assert others == [], others

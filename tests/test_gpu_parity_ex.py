@@ -159,6 +159,7 @@ def test_na3d_row_kernel_scales(scale, geo):
     (9, 40, 3, 3, 1, 0, 1, 8),
     (40, 64, 7, 7, 0, 0, 2, 2),   # clamped and dilated: the patch kernel at d = 32 (tight clamped bands)
     (30, 50, 5, 5, 0, 0, 3, 3),   # dilation 3, clamped: windows pushed inwards near every border
+    (33, 48, 5, 5, 1, 1, 2, 2),   # 33 wrapped rows at dilation 2: patches of consecutive rows
 ])
 def test_na2d_dilated(gh, gw, kh, kw, wh, ww, dh, dw, d):
     """Windows of 9 to 49 keys. With so few keys the bfloat16 rounding of the probabilities and of
