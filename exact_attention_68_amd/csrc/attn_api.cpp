@@ -60,7 +60,7 @@ int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
   if (p.mask == ATTN_MASK_CAUSAL) return attn::MASK_CAUSAL;
   const int32_t patch_rows = attn::patch_lds_rows(p.d);
   if (patch_rows > 0 && attn::na_patch_eligible(g, patch_rows)) {
-    const int64_t patches = p.B * p.H * attn::na_patch_row_groups(g) * attn::cdiv(g.grid_w, attn::kPatchCols);
+    const int64_t patches = p.B * p.H * attn::na_patch_row_groups(g) * attn::na_patch_col_groups(g, attn::na_patch_cols_strided(g));
     if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
   }
   if (rows_stage(p.d, g) > 0) {
@@ -102,7 +102,8 @@ attn_status_t run_fwd(const attn::Problem& p, const attn::SplitPlan* split, void
   a.na_phases = mask == attn::MASK_NA_BLOCKS ? a.na.grid_w / 32 : 0;
   int32_t n_wg = a.BH * a.n_qtiles, rem = 0;
   if (mask == attn::MASK_NA_PATCH) {
-    a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
+    a.patch_cols_strided = attn::na_patch_cols_strided(a.na) ? 1 : 0;
+    a.patch_nx = attn::na_patch_col_groups(a.na, a.patch_cols_strided != 0);
     a.patch_ny = attn::na_patch_row_groups(a.na);
     n_wg = a.BH * a.patch_nx * a.patch_ny;
   }
@@ -284,7 +285,8 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     }
     // wider single-plane grids: the patch kernels (the row kernels keep the narrow ones)
     const int32_t patch_lds = attn::bwd_patch_lds(d);
-    a.patch_nx = (int32_t)attn::cdiv(a.na.grid_w, attn::kPatchCols);
+    a.patch_cols_strided = attn::na_patch_cols_strided(a.na) ? 1 : 0;
+    a.patch_nx = attn::na_patch_col_groups(a.na, a.patch_cols_strided != 0);
     a.patch_ny = attn::na_patch_row_groups(a.na);
     const bool patches_fit = (int64_t)a.BH * a.patch_nx * a.patch_ny <= INT32_MAX;
     a.dq_patch = !a.dq_rows && patches_fit && attn::na_patch_bwd_eligible(a.na, patch_lds, false) ? 1 : 0;

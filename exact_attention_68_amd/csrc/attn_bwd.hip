@@ -961,7 +961,7 @@ struct BwdPatchCfg {
 // x (row cell r, column cell x); columns past the column band read as zero.
 template <int D>
 __device__ __forceinline__ void load_patch_rect(i32x4_t ra, i32x4_t rb, const uint16_t* la, const uint16_t* lb,
-                                                const PatchBands& pb, const PatchRowGroup& pr, int32_t H, int32_t W,
+                                                const PatchBands& pb, const PatchGroup& pr, int32_t H, int32_t W,
                                                 uint32_t head_bytes, int wave8, int tid) {
   using P = BwdPatchCfg<D>;
   const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds_addr(la) + wave8 * 1024);
@@ -976,7 +976,7 @@ __device__ __forceinline__ void load_patch_rect(i32x4_t ra, i32x4_t rb, const ui
       int32_t ty = pb.rows.start + r, tx = pb.cols.start + x;
       ty -= ty >= H ? H : 0;  // both start inside the axis and span at most its length
       tx -= tx >= W ? W : 0;
-      voff = (uint32_t)((pr.rho + pr.stride * ty) * W + tx) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
+      voff = (uint32_t)patch_token(pr, ty, tx) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
     }
     dma_lds16(ra, a_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
     dma_lds16(rb, b_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
@@ -1007,11 +1007,11 @@ void attn_bwd_dq_patch_kernel(BwdArgs a) {
   const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = item / per_head, pidx = item - bh * per_head;
   const int32_t py = pidx / a.patch_nx;
-  // rows in the coordinates of the patch's row sub-grid (na_patch_row_group)
-  const PatchRowGroup pr = na_patch_row_group(a.na, py);
+  // rows and columns in the coordinates of the patch's sub-grids (na_patch_group)
+  const PatchGroup pr = na_patch_group(a.na, py, pidx - py * a.patch_nx, a.patch_cols_strided != 0);
   const NaGeom& g = pr.geom;
   const int32_t H = g.grid_h, W = g.grid_w, N = a.Nq;
-  const int32_t y0 = pr.u0, x0 = (pidx - py * a.patch_nx) * kPatchCols;
+  const int32_t y0 = pr.u0, x0 = pr.v0;
   const PatchBands pb = na_patch_bands(y0, x0, g);
   const size_t head = (size_t)bh * (size_t)N;
   const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
@@ -1020,7 +1020,7 @@ void attn_bwd_dq_patch_kernel(BwdArgs a) {
 
   const int32_t qy = y0 + 2 * wave + (col >> 4), qx = x0 + (col & 15);
   const bool q_ok = qy < H && qx < W;
-  const int32_t my_q = (pr.rho + pr.stride * qy) * W + qx;
+  const int32_t my_q = patch_token(pr, qy, qx);
   const int32_t q_row = q_ok ? my_q : N;
   bf16x8_t qf[KB], gf[KB];
   row_fragment<D>(a.q + head * D, q_row, N, a.q_sign, half, qf);
@@ -1125,11 +1125,11 @@ void attn_bwd_dkv_patch_kernel(BwdArgs a) {
   const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = item / per_head, pidx = item - bh * per_head;
   const int32_t py = pidx / a.patch_nx;
-  // rows in the coordinates of the patch's row sub-grid (na_patch_row_group)
-  const PatchRowGroup pr = na_patch_row_group(a.na, py);
+  // rows and columns in the coordinates of the patch's sub-grids (na_patch_group)
+  const PatchGroup pr = na_patch_group(a.na, py, pidx - py * a.patch_nx, a.patch_cols_strided != 0);
   const NaGeom& g = pr.geom;
   const int32_t H = g.grid_h, W = g.grid_w, N = a.Nkv;
-  const int32_t y0 = pr.u0, x0 = (pidx - py * a.patch_nx) * kPatchCols;
+  const int32_t y0 = pr.u0, x0 = pr.v0;
   const PatchBands pb = na_patch_reverse_bands(y0, x0, g);
   const size_t head = (size_t)bh * (size_t)N;
   const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
@@ -1143,7 +1143,7 @@ void attn_bwd_dkv_patch_kernel(BwdArgs a) {
       int32_t ty = pb.rows.start + r, tx = pb.cols.start + x;
       ty -= ty >= H ? H : 0;
       tx -= tx >= W ? W : 0;
-      const int32_t qi = (pr.rho + pr.stride * ty) * W + tx;
+      const int32_t qi = patch_token(pr, ty, tx);
       l2v = a.lse[head + qi] * kLog2e;
       dlv = a.delta[head + qi];
     }
@@ -1153,7 +1153,7 @@ void attn_bwd_dkv_patch_kernel(BwdArgs a) {
 
   const int32_t ky = y0 + 2 * wave + (col >> 4), kx = x0 + (col & 15);
   const bool k_ok = ky < H && kx < W;
-  const int32_t my_k = (pr.rho + pr.stride * ky) * W + kx;
+  const int32_t my_k = patch_token(pr, ky, kx);
   const int32_t k_row = k_ok ? my_k : N;
   // scale < 0: K's sign bits flipped, so c S = scale * (Q K^T) with c = |scale| log2 e
   bf16x8_t kf[KB], vf[KB];

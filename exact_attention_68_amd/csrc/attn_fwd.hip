@@ -1095,12 +1095,12 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
   const int32_t item = xcd_contiguous(blockIdx.x, gridDim.x);
   const int32_t bh = item / per_head, pidx = item - bh * per_head;
   const int32_t py = pidx / a.patch_nx;
-  // rows in the coordinates of the patch's row sub-grid (na_patch_row_group): H rows,
-  // grid row pr.rho + pr.stride * row
-  const PatchRowGroup pr = na_patch_row_group(a.na, py);
+  // rows and columns in the coordinates of the patch's sub-grids (na_patch_group): H x W
+  // cells, token patch_token(pr, row, column)
+  const PatchGroup pr = na_patch_group(a.na, py, pidx - py * a.patch_nx, a.patch_cols_strided != 0);
   const NaGeom& g = pr.geom;
   const int32_t H = g.grid_h, W = g.grid_w, N = a.Nq;
-  const int32_t y0 = pr.u0, x0 = (pidx - py * a.patch_nx) * kPatchCols;
+  const int32_t y0 = pr.u0, x0 = pr.v0;
   const PatchBands pb = na_patch_bands(y0, x0, g);
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * (uint32_t)(D * 2);
@@ -1108,7 +1108,7 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
   // ---- the lane's query (loaded first, used after the rectangle has landed)
   const int32_t qy = y0 + 2 * wave + (col >> 4), qx = x0 + (col & 15);
   const bool q_ok = qy < H && qx < W;
-  const int32_t my_q = (pr.rho + pr.stride * qy) * W + qx;
+  const int32_t my_q = patch_token(pr, qy, qx);
   // every lane loads (a query outside the grid reads query 0 and zeroes it after the wait)
   const int32_t q_row = q_ok ? my_q : 0;
   u32x4_t qraw[KB];
@@ -1135,7 +1135,7 @@ void attn_fwd_na_patch_kernel(KernelArgs a) {
         int32_t ky = pb.rows.start + r, kx = pb.cols.start + x;
         ky -= ky >= H ? H : 0;  // both start inside the axis and span at most its length
         kx -= kx >= W ? W : 0;
-        voff = (uint32_t)((pr.rho + pr.stride * ky) * W + kx) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
+        voff = (uint32_t)patch_token(pr, ky, kx) * (uint32_t)(D * 2) + (uint32_t)chunk * 16u;
       }
       dma_lds16(k_rsrc, k_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);
       dma_lds16(v_rsrc, v_base + (uint32_t)j * (P::THREADS * 16u), voff, 0u);

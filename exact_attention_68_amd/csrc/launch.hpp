@@ -35,6 +35,7 @@ struct KernelArgs {
   int32_t patch_nx, patch_ny;  // MASK_NA_PATCH: patches per grid row and per grid column;
                                // MASK_NA_ROWS: patch_ny row groups per plane (na_row_groups)
   int32_t rows_stage;  // MASK_NA_ROWS: key rows per LDS stage (rows_lds_rows or rows_wide_lds)
+  int32_t patch_cols_strided;  // MASK_NA_PATCH: na_patch_cols_strided
 };
 
 // Bytes of one part slot (partial output, maximum and sums of 4 wavefronts x 64 lanes).
@@ -109,6 +110,7 @@ struct BwdArgs {
   int32_t dq_patch;    // dQ by 8 x 16 query patches (na_patch_bwd_eligible, forward bands)
   int32_t dkv_patch;   // dK/dV by 8 x 16 key patches (reverse bands)
   int32_t patch_nx, patch_ny;  // patches per grid row and per grid column
+  int32_t patch_cols_strided;  // na_patch_cols_strided
 };
 
 // Key rows per LDS stage of the dQ row kernel and query rows per stage of the dK/dV

@@ -418,39 +418,82 @@ constexpr PatchBands na_patch_bands(int32_t y0, int32_t x0, const NaGeom& g) {
       na_band(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w)};
 }
 
-// The rows of patch row py of a plane: kPatchRows consecutive rows of the residue
-// sub-grid (na_rows_strided), else of the plane. `geom` is the window geometry in
-// that sub-grid's coordinates (grid_h its length, dil_h 1); sub-grid row u is grid
-// row rho + stride u. The patch kernels work in those coordinates throughout and map
-// to grid rows only to address tokens.
-struct PatchRowGroup {
-  int32_t rho, stride, u0;
-  NaGeom geom;
+// Patches along one axis of `len` cells: `per` consecutive cells of one residue
+// sub-grid mod the dilation when the axis is strided (dilated and, if wrapped, of a
+// length the dilation divides: see na_rows_strided), else of the axis itself.
+// Sub-grid cell u is axis cell rho + stride u, u < len.
+struct AxisGroup {
+  int32_t rho, stride, len, u0;
 };
 
-constexpr int32_t na_patch_row_groups(const NaGeom& g) {
-  if (!na_rows_strided(g)) return (int32_t)cdiv(g.grid_h, kPatchRows);
+constexpr bool na_axis_strided(int32_t len, int32_t dil, int32_t wrap) { return dil > 1 && (!wrap || len % dil == 0); }
+
+constexpr int32_t na_axis_groups(int32_t len, int32_t dil, int32_t wrap, int32_t per) {
+  if (!na_axis_strided(len, dil, wrap)) return (int32_t)cdiv(len, per);
   int32_t n = 0;
-  for (int32_t rho = 0; rho < g.dil_h; ++rho) n += (int32_t)cdiv(na_rows_sub_len(g, rho), kPatchRows);
+  for (int32_t rho = 0; rho < dil; ++rho) n += (int32_t)cdiv((len - 1 - rho) / dil + 1, per);
   return n;
 }
 
-constexpr PatchRowGroup na_patch_row_group(const NaGeom& g, int32_t py) {
-  PatchRowGroup pr{0, 1, py * kPatchRows, g};
-  if (!na_rows_strided(g)) return pr;
-  for (int32_t rho = 0; rho < g.dil_h; ++rho) {
-    const int32_t len = na_rows_sub_len(g, rho), n = (int32_t)cdiv(len, kPatchRows);
-    if (py < n || rho == g.dil_h - 1) {
-      pr.rho = rho;
-      pr.stride = g.dil_h;
-      pr.u0 = py * kPatchRows;
-      pr.geom.grid_h = len;
-      pr.geom.dil_h = 1;
-      break;
-    }
-    py -= n;
+constexpr AxisGroup na_axis_group(int32_t len, int32_t dil, int32_t wrap, int32_t i, int32_t per) {
+  if (!na_axis_strided(len, dil, wrap)) return AxisGroup{0, 1, len, i * per};
+  for (int32_t rho = 0; rho < dil; ++rho) {
+    const int32_t sub = (len - 1 - rho) / dil + 1, n = (int32_t)cdiv(sub, per);
+    if (i < n || rho == dil - 1) return AxisGroup{rho, dil, sub, i * per};
+    i -= n;
   }
-  return pr;
+  return AxisGroup{0, 1, len, 0};  // not reached (dil >= 1)
+}
+
+// Patch (py, px) of a plane: its rows and columns (AxisGroup per axis, patches of
+// kPatchRows x kPatchCols sub-grid cells from (u0, v0)) and `geom`, the window
+// geometry in the sub-grids' coordinates (a strided axis has its sub-grid's length
+// and dilation 1). The patch kernels work in those coordinates throughout and map
+// to the grid only to address tokens (patch_token, with the grid's row pitch).
+struct PatchGroup {
+  int32_t rho, stride, u0;      // rows
+  int32_t rho_x, stride_x, v0;  // columns
+  int32_t pitch;                // tokens per grid row
+  NaGeom geom;
+};
+
+// Rows are always taken by residue where the axis allows (a row is a run of tokens
+// either way). Columns only where consecutive ones would not fit, a forward or reverse
+// column band past one 32-key block: columns dil apart cost coalescing (a 7x7 window
+// of dilation 2, whose 28-column bands fit, ran 0.95x forward and 0.88x backward with
+// them).
+constexpr bool na_patch_cols_strided(const NaGeom& g) {
+  if (!na_axis_strided(g.grid_w, g.dil_w, g.wrap_w)) return false;
+  for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols) {
+    const int32_t x1 = imin(x0 + kPatchCols, g.grid_w) - 1;
+    if (na_band(x0, x1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w).count > kPatchKeyCols ||
+        na_band_reverse(x0, x1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w).count > kPatchKeyCols)
+      return true;
+  }
+  return false;
+}
+
+constexpr int32_t na_patch_row_groups(const NaGeom& g) { return na_axis_groups(g.grid_h, g.dil_h, g.wrap_h, kPatchRows); }
+constexpr int32_t na_patch_col_groups(const NaGeom& g, bool cols_strided) {
+  return cols_strided ? na_axis_groups(g.grid_w, g.dil_w, g.wrap_w, kPatchCols) : (int32_t)cdiv(g.grid_w, kPatchCols);
+}
+
+// cols_strided: na_patch_cols_strided(g), decided once per problem.
+constexpr PatchGroup na_patch_group(const NaGeom& g, int32_t py, int32_t px, bool cols_strided) {
+  const AxisGroup r = na_axis_group(g.grid_h, g.dil_h, g.wrap_h, py, kPatchRows);
+  const AxisGroup c = cols_strided ? na_axis_group(g.grid_w, g.dil_w, g.wrap_w, px, kPatchCols)
+                                   : AxisGroup{0, 1, g.grid_w, px * kPatchCols};
+  PatchGroup p{r.rho, r.stride, r.u0, c.rho, c.stride, c.u0, g.grid_w, g};
+  p.geom.grid_h = r.len;
+  p.geom.dil_h = r.stride > 1 ? 1 : g.dil_h;
+  p.geom.grid_w = c.len;
+  p.geom.dil_w = c.stride > 1 ? 1 : g.dil_w;
+  return p;
+}
+
+// Token of sub-grid cell (row y, column x) of a patch's plane.
+constexpr int32_t patch_token(const PatchGroup& p, int32_t y, int32_t x) {
+  return (p.rho + p.stride * y) * p.pitch + p.rho_x + p.stride_x * x;
 }
 
 // One plane; every column band within one 32-key block; a wrapped row band shorter
@@ -459,10 +502,13 @@ constexpr PatchRowGroup na_patch_row_group(const NaGeom& g, int32_t py) {
 // of four may read past it, within the kernel's `lds_rows`.
 constexpr bool na_patch_eligible(const NaGeom& g, int32_t lds_rows) {
   if (g.grid_d != 1) return false;
-  for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols)
-    if (na_patch_bands(0, x0, g).cols.count > kPatchKeyCols) return false;
+  const bool cs = na_patch_cols_strided(g);
+  for (int32_t px = 0, n = na_patch_col_groups(g, cs); px < n; ++px) {
+    const PatchGroup pg = na_patch_group(g, 0, px, cs);
+    if (na_patch_bands(0, pg.v0, pg.geom).cols.count > kPatchKeyCols) return false;
+  }
   for (int32_t py = 0, n = na_patch_row_groups(g); py < n; ++py) {
-    const PatchRowGroup pr = na_patch_row_group(g, py);
+    const PatchGroup pr = na_patch_group(g, py, 0, cs);
     const Band rows = na_patch_bands(pr.u0, 0, pr.geom).rows;
     if (rows.count + 3 > lds_rows || (pr.geom.wrap_h && rows.count >= pr.geom.grid_h)) return false;
   }
@@ -522,12 +568,14 @@ constexpr uint32_t band_window_bits(int32_t c, Band b, int32_t len, int32_t kern
 // rows, so no rows past a band are read.
 constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool reverse) {
   if (g.grid_d != 1 || lds_rows <= 0) return false;
-  for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols) {
-    const PatchBands b = reverse ? na_patch_reverse_bands(0, x0, g) : na_patch_bands(0, x0, g);
+  const bool cs = na_patch_cols_strided(g);
+  for (int32_t px = 0, n = na_patch_col_groups(g, cs); px < n; ++px) {
+    const PatchGroup pg = na_patch_group(g, 0, px, cs);
+    const PatchBands b = reverse ? na_patch_reverse_bands(0, pg.v0, pg.geom) : na_patch_bands(0, pg.v0, pg.geom);
     if (b.cols.count > kPatchKeyCols) return false;
   }
   for (int32_t py = 0, n = na_patch_row_groups(g); py < n; ++py) {
-    const PatchRowGroup pr = na_patch_row_group(g, py);
+    const PatchGroup pr = na_patch_group(g, py, 0, cs);
     const Band rows = (reverse ? na_patch_reverse_bands(pr.u0, 0, pr.geom) : na_patch_bands(pr.u0, 0, pr.geom)).rows;
     if (rows.count > lds_rows || (pr.geom.wrap_h && rows.count >= pr.geom.grid_h)) return false;
   }

@@ -207,24 +207,31 @@ static void check_na(int gh, int gw, int kh, int kw, int wh, int ww, int BM, int
   check_na_geom(geom(1, gh, gw, 1, kh, kw, 0, wh, ww, 1, 1, 1), BM, BN);
 }
 
-// The patch row groups of a plane: every grid row held by exactly one patch row of
-// one group (rows pr.rho + pr.stride * (pr.u0 + i), i < kPatchRows, inside the sub-grid).
+// The patch groups of a plane: every token held by exactly one lane position of one
+// patch (sub-grid cells (u0 + i, v0 + j), i < kPatchRows, j < kPatchCols, inside the
+// sub-grids, at patch_token), and the sub-grid geometry keeps the window.
 static void check_patch_rows(const NaGeom& g) {
-  std::vector<int> held(g.grid_h, 0);
-  for (int py = 0; py < na_patch_row_groups(g); ++py) {
-    const PatchRowGroup pr = na_patch_row_group(g, py);
-    EXPECT(pr.geom.grid_w == g.grid_w && pr.geom.dil_w == g.dil_w && pr.geom.kernel_h == g.kernel_h,
-           "sub-grid geometry keeps the columns and the window");
-    for (int i = 0; i < kPatchRows; ++i)
-      if (pr.u0 + i < pr.geom.grid_h) {
-        const int y = pr.rho + pr.stride * (pr.u0 + i);
-        EXPECT(y >= 0 && y < g.grid_h, "patch row group %d row %d is grid row %d", py, i, y);
-        if (y >= 0 && y < g.grid_h) ++held[y];
-      }
-  }
-  for (int y = 0; y < g.grid_h; ++y)
-    EXPECT(held[y] == 1, "grid row %d held by %d patch rows (H %d dil %d wrap %d)", y, held[y], g.grid_h, g.dil_h,
-           g.wrap_h);
+  std::vector<int> held(g.grid_h * g.grid_w, 0);
+  for (int py = 0; py < na_patch_row_groups(g); ++py)
+    for (int px = 0; px < na_patch_col_groups(g, na_patch_cols_strided(g)); ++px) {
+      const PatchGroup pr = na_patch_group(g, py, px, na_patch_cols_strided(g));
+      EXPECT(pr.geom.kernel_h == g.kernel_h && pr.geom.kernel_w == g.kernel_w && pr.pitch == g.grid_w,
+             "sub-grid geometry keeps the window and the pitch");
+      for (int i = 0; i < kPatchRows; ++i)
+        for (int j = 0; j < kPatchCols; ++j)
+          if (pr.u0 + i < pr.geom.grid_h && pr.v0 + j < pr.geom.grid_w) {
+            const int y = pr.rho + pr.stride * (pr.u0 + i), x = pr.rho_x + pr.stride_x * (pr.v0 + j);
+            EXPECT(y >= 0 && y < g.grid_h && x >= 0 && x < g.grid_w, "patch (%d,%d) cell (%d,%d) is (%d,%d)", py, px,
+                   i, j, y, x);
+            if (y >= 0 && y < g.grid_h && x >= 0 && x < g.grid_w) {
+              EXPECT(patch_token(pr, pr.u0 + i, pr.v0 + j) == y * g.grid_w + x, "patch_token");
+              ++held[y * g.grid_w + x];
+            }
+          }
+    }
+  for (int t = 0; t < g.grid_h * g.grid_w; ++t)
+    EXPECT(held[t] == 1, "token %d held by %d patch cells (%dx%d dil %d,%d wrap %d%d)", t, held[t], g.grid_h, g.grid_w,
+           g.dil_h, g.dil_w, g.wrap_h, g.wrap_w);
 }
 
 // The patch kernel (MASK_NA_PATCH) as it walks its LDS rectangle: for every patch,
@@ -236,11 +243,11 @@ static int check_patch(const NaGeom& g0, int lds_rows) {
   if (!na_patch_eligible(g0, lds_rows)) return 0;
   check_patch_rows(g0);
   for (int py = 0; py < na_patch_row_groups(g0); ++py)
-    for (int x0 = 0; x0 < g0.grid_w; x0 += kPatchCols) {
-      // rows in the coordinates of the patch's row sub-grid, as the kernel takes them
-      const PatchRowGroup pr = na_patch_row_group(g0, py);
+    for (int px = 0; px < na_patch_col_groups(g0, na_patch_cols_strided(g0)); ++px) {
+      // rows and columns in the coordinates of the patch's sub-grids, as the kernel takes them
+      const PatchGroup pr = na_patch_group(g0, py, px, na_patch_cols_strided(g0));
       const NaGeom& g = pr.geom;
-      const int H = g.grid_h, W = g.grid_w, y0 = pr.u0;
+      const int H = g.grid_h, W = g.grid_w, y0 = pr.u0, x0 = pr.v0;
       const PatchBands pb = na_patch_bands(y0, x0, g);
       EXPECT(pb.cols.count >= 1 && pb.cols.count <= kPatchKeyCols && pb.rows.count >= 1 && pb.rows.count + 3 <= lds_rows,
              "patch bands %d x %d (grid %dx%d k %d,%d wrap %d%d)", pb.rows.count, pb.cols.count, H, W, g.kernel_h,
@@ -287,14 +294,15 @@ static int check_patch(const NaGeom& g0, int lds_rows) {
                 if (rok && ((cm >> x) & 1u)) {
                   EXPECT(r < pb.rows.count && x < pb.cols.count && ky >= 0 && ky < H && kx >= 0 && kx < W,
                          "visible cell outside the rectangle");
-                  seen.push_back((pr.rho + pr.stride * ky) * W + kx);
+                  seen.push_back(patch_token(pr, ky, kx));
                   first_step = first_step || st == 0;
                 }
               }
             }
           std::set<int> want;  // the window on the grid itself
           for (int yc : axis_cells(pr.rho + pr.stride * qy, g0.grid_h, g0.kernel_h, g0.wrap_h, g0.dil_h))
-            for (int xc : axis_cells(qx, W, g0.kernel_w, g0.wrap_w, g0.dil_w)) want.insert(yc * W + xc);
+            for (int xc : axis_cells(pr.rho_x + pr.stride_x * qx, g0.grid_w, g0.kernel_w, g0.wrap_w, g0.dil_w))
+              want.insert(yc * g0.grid_w + xc);
           const std::set<int> got(seen.begin(), seen.end());
           EXPECT(got.size() == seen.size() && got == want,
                  "patch window of query (%d,%d): %zu cells (%zu distinct), want %zu (grid %dx%d k %d,%d wrap %d%d)", qy, qx,
@@ -447,11 +455,11 @@ static int check_patch_bwd(const NaGeom& g0, int lds_rows, bool reverse) {
     }
   check_patch_rows(g0);
   for (int py = 0; py < na_patch_row_groups(g0); ++py)
-    for (int x0 = 0; x0 < g0.grid_w; x0 += kPatchCols) {
-      // rows in the coordinates of the patch's row sub-grid, as the kernels take them
-      const PatchRowGroup pr = na_patch_row_group(g0, py);
+    for (int px = 0; px < na_patch_col_groups(g0, na_patch_cols_strided(g0)); ++px) {
+      // rows and columns in the coordinates of the patch's sub-grids, as the kernels take them
+      const PatchGroup pr = na_patch_group(g0, py, px, na_patch_cols_strided(g0));
       const NaGeom& g = pr.geom;
-      const int H = g.grid_h, W = g.grid_w, y0 = pr.u0;
+      const int H = g.grid_h, W = g.grid_w, y0 = pr.u0, x0 = pr.v0;
       const PatchBands pb = reverse ? na_patch_reverse_bands(y0, x0, g) : na_patch_bands(y0, x0, g);
       EXPECT(pb.rows.count >= 1 && pb.rows.count <= lds_rows && pb.cols.count >= 1 && pb.cols.count <= kPatchKeyCols,
              "patch rectangle %d x %d", pb.rows.count, pb.cols.count);
@@ -472,11 +480,11 @@ static int check_patch_bwd(const NaGeom& g0, int lds_rows, bool reverse) {
           std::vector<int> seen;
           for (int r = off; r < off + wb.count; ++r) {
             if (!((rows_w >> r) & 1u)) continue;
-            const int ty = pr.rho + pr.stride * ((pb.rows.start + r) % H);
+            const int ty = (pb.rows.start + r) % H;
             for (int x = 0; x < pb.cols.count; ++x)
-              if ((cm >> x) & 1u) seen.push_back(ty * W + (pb.cols.start + x) % W);
+              if ((cm >> x) & 1u) seen.push_back(patch_token(pr, ty, (pb.cols.start + x) % W));
           }
-          const int me = (pr.rho + pr.stride * cy) * W + cx;
+          const int me = patch_token(pr, cy, cx);
           std::sort(seen.begin(), seen.end());
           EXPECT(seen == want[me],  // equal sorted lists: the same cells, each once
                  "%s patch cells of token %d: %zu, want %zu (grid %dx%d k %d,%d wrap %d%d dil %d,%d)",
@@ -795,6 +803,23 @@ int main() {
            "63 wrapped rows at dilation 2: consecutive rows, 20-row bands, not in 17 rows");
     EXPECT(!na_patch_eligible(geom(4, 20, 20, 3, 5, 5, 1, 1, 1, 1, 1, 1), 24), "3D windows do not");
     EXPECT(!na_patch_eligible(geom(1, 64, 64, 1, 7, 19, 0, 1, 1, 1, 1, 1), 24), "19 columns wide: the band passes 32");
+    // columns of one residue mod the dilation: 16 + 2 rad sub-grid columns per band
+    EXPECT(check_patch(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 4, 4), 17) == 1 &&
+               check_patch_bwd(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 4, 4), 17, false) == 1 &&
+               check_patch_bwd(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 4, 4), 17, true) == 1,
+           "64x64 grid, 7x7 window of dilation 4: patches of one residue per axis, 14 x 22 rectangles");
+    EXPECT(check_patch(geom(1, 40, 48, 1, 5, 9, 0, 0, 0, 1, 3, 3), 24) == 1 &&
+               check_patch_bwd(geom(1, 40, 48, 1, 5, 9, 0, 0, 0, 1, 3, 3), 24, false) == 1 &&
+               check_patch_bwd(geom(1, 40, 48, 1, 5, 9, 0, 0, 0, 1, 3, 3), 24, true) == 1,
+           "clamped 5x9 window of dilation 3 on 40x48: residue sub-grids of unequal lengths");
+    EXPECT(check_patch(geom(1, 33, 50, 1, 5, 5, 0, 1, 0, 1, 2, 3), 24) == 1 &&
+               check_patch_bwd(geom(1, 33, 50, 1, 5, 5, 0, 1, 0, 1, 2, 3), 24, true) == 1,
+           "33 wrapped rows (consecutive) and 50 clamped columns of dilation 3 (one residue)");
+    EXPECT(!na_patch_eligible(geom(1, 64, 66, 1, 7, 7, 0, 1, 1, 1, 4, 4), 24),
+           "66 wrapped columns at dilation 4: consecutive columns, a 40-column band");
+    EXPECT(!na_patch_cols_strided(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 2, 2)) &&
+               na_patch_cols_strided(geom(1, 64, 64, 1, 7, 7, 0, 1, 1, 1, 4, 4)),
+           "columns by residue only where consecutive ones pass 32 (dilation 2: 28 columns fit)");
   }
   {
     // row kernel: narrow 2D and 3D grids, wrap and clamp per axis, dilation

@@ -107,6 +107,8 @@ def test_bwd_after_gpu_forward(N, Nkv, d, mask):
     ("na2d", (30, 50, 5, 5, 0, 0, 3, 3)),               # dilation 3, clamped
     ("na2d", (32, 48, 5, 7, 1, 1, 2, 2)),               # patches of rows of one parity (also at d = 64)
     ("na2d", (33, 48, 5, 5, 1, 1, 2, 2)),               # 33 wrapped rows: patches of consecutive rows
+    ("na2d", (48, 64, 7, 7, 1, 1, 4, 4)),               # dilation 4: patches of one residue per axis
+    ("na2d", (40, 48, 5, 9, 0, 0, 3, 3)),               # clamped, dilation 3: residue sub-grids of unequal lengths
     ("na3d", (10, 12, 14, 3, 3, 3, 0, 0, 0, 2, 2, 3)),  # clamped, dilated (d = 128: the tile kernels' query runs)
     # row groups of one residue mod the dilation (8-row bands), and the wide 12-row stages, at d = 32
     ("na3d", (10, 16, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)),  # 16 wrapped rows, dilation 2: groups of one residue

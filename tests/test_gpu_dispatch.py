@@ -194,14 +194,16 @@ def test_na3d_dilated_row_kernel_stages(gh, fwd, dq, dkv):
     assert others == [], others
 
 
-def test_na2d_dilated_d64_takes_patch_kernels():
-    """A 7x7 window of dilation 2 on a 64x64 wrapped grid: each patch takes 8 rows of one parity, whose
-    windows reach 14 rows of that parity, so even the d = 64 rectangles (17 rows) hold them."""
+@pytest.mark.parametrize("d,dil", [(64, 2), (32, 4)])
+def test_na2d_dilated_takes_patch_kernels(d, dil):
+    """A 7x7 window of dilation 2 or 4 on a 64x64 wrapped grid: each patch takes 8 rows and 16 columns of
+    one residue per axis, whose windows reach 14 rows and 22 columns of those residues, so the d = 64
+    rectangles (17 rows) and the 32-column blocks hold them."""
     import exact_attention_68_amd as A
 
-    B, H, N, d = 1, 2, 64 * 64, 64
+    B, H, N = 1, 2, 64 * 64
     q, k, v = _inputs(B, H, N, d, 6)
-    params = A.na2d_params(64, 64, 7, 7, 1, 1, 2, 2)
+    params = A.na2d_params(64, 64, 7, 7, 1, 1, dil, dil)
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
     kernels, others = _split(_dispatches(
