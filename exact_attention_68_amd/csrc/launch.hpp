@@ -64,9 +64,9 @@ constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 24 : d == 64 ? 17
 constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : 0; }
 
 // The wide stages of the three row kernels (forward, backward dQ and dK/dV) at d = 32: 12
-// rows, for bands past the narrow stages (windows of 5 at dilation 2; clamped windows
-// whose reverse bands near a border pass 8 rows). Their two stages take 96-102 KB of LDS:
-// one work-group per CU.
+// rows, for bands past the narrow stages (clamped windows whose reverse bands near a
+// border pass 8 rows; dilated rows on a wrapped axis the dilation does not divide, whose
+// groups stay consecutive). Their two stages take 96-102 KB of LDS: one work-group per CU.
 constexpr int32_t rows_wide_lds(int64_t d) { return d == 32 ? 12 : 0; }
 
 // Work-groups of the backward kernels resident per CU: two at d <= 64 and one at d = 128
