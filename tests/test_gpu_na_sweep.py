@@ -1,0 +1,74 @@
+"""A seeded sweep of neighbourhood geometries through the forward (with its logsumexp) and the backward,
+against the float64 CPU oracle: 2D and 3D grids, wrap or clamp per axis, dilation 1 to 4 per axis, head
+sizes 32 and 64. The geometries are drawn once from a fixed generator and kept valid (odd kernels; a
+wrapped axis holds its window once, (kernel - 1) * dil < len; on a clamped one every residue sub-grid
+holds a whole window, kernel * dil <= len), so the kernels' plans (row and patch groups of one residue
+mod the dilation, tight clamped bands, reverse bands, wide row stages) meet shapes that no hand-picked
+case names. The forward is held to the larger of the benchmark spec's bound and the bound derived from its
+arithmetic (windows of a few keys), the backward to the bound of parity.check_bwd_case."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import check_bwd_case, check_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _geometries(n2: int, n3: int, seed: int):
+    """n2 2D and n3 3D valid geometries: (mode, params tuple for na2d_params / na3d_params, token count)."""
+    rng = np.random.default_rng(seed)
+    out, count = [], {"na2d": 0, "na3d": 0}
+    while count["na2d"] < n2 or count["na3d"] < n3:
+        mode = "na2d" if count["na2d"] < n2 else "na3d"
+        dims = ((int(rng.integers(4, 49)), int(rng.integers(4, 65))) if mode == "na2d"
+                else (int(rng.integers(3, 11)), int(rng.integers(4, 21)), int(rng.integers(4, 33))))
+        axes = [(L, int(rng.choice([1, 3, 3, 5, 5, 7])), int(rng.integers(0, 2)), int(rng.integers(1, 5))) for L in dims]
+        if not all(k <= L and ((k - 1) * dil < L if wrap else k * dil <= L) for L, k, wrap, dil in axes):
+            continue
+        N = int(np.prod(dims))
+        if not 16 <= N <= 2000:
+            continue
+        params = (*dims, *(a[1] for a in axes), *(a[2] for a in axes), *(a[3] for a in axes))
+        out.append((mode, params, N))
+        count[mode] += 1
+    return out
+
+
+GEOMETRIES = _geometries(12, 12, 2026)
+
+
+def _params(mode, geo):
+    import exact_attention_68_amd as A
+
+    return A.na3d_params(*geo) if mode == "na3d" else A.na2d_params(*geo)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    from exact_attention_68_amd.build import ensure_built
+
+    ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("i", range(len(GEOMETRIES)))
+def test_forward_sweep(i, d):
+    mode, geo, N = GEOMETRIES[i]
+    q, k, v = workloads.make_qkv_cross(1, 2, N, N, d, 12000 + 7 * i + d)
+    check_case(q, k, v, 1 / math.sqrt(d), mode, _params(mode, geo), what=f"sweep {i} {mode} {geo}",
+               entry="attn_fwd_ex", derived=True)
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("i", range(len(GEOMETRIES)))
+def test_backward_sweep(i, d):
+    mode, geo, N = GEOMETRIES[i]
+    q, k, v = workloads.make_qkv_cross(1, 2, N, N, d, 12500 + 7 * i + d)
+    g = torch.Generator(device="cpu").manual_seed(12900 + i)
+    do = torch.randn(1, 2, N, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    check_bwd_case(q, k, v, do, 1 / math.sqrt(d), mode, what=f"sweep {i} {mode} {geo}", params=_params(mode, geo))
