@@ -381,17 +381,16 @@ constexpr void na_col_bits(int32_t cq, int32_t half, int32_t W, int32_t kernel, 
   }
 }
 
-// Rows of one residue mod the row dilation. With dilation along the rows (and, on a
-// wrapped axis, a row count the dilation divides) the grid rows congruent to rho mod
-// dil form a sub-grid on which every window is an undilated window: clamped,
-// na_dil_anchor takes it inside that sub-grid; wrapped, it steps dil rows at a time
-// around a cycle of grid_h / dil of them. The row and patch kernels then take the
-// rows of a work-group from one sub-grid, whose bands count 2 rad rows of margin
-// rather than 2 rad dil.
-constexpr bool na_rows_strided(const NaGeom& g) { return g.dil_h > 1 && (!g.wrap_h || g.grid_h % g.dil_h == 0); }
+// Cells of one residue mod the dilation. On a dilated axis (that, when wrapped, the
+// dilation divides) the cells congruent to rho mod dil form a sub-grid on which every
+// window is an undilated window: clamped, na_dil_anchor takes it inside that
+// sub-grid; wrapped, it steps dil cells at a time around a cycle of len / dil of
+// them. The row and patch kernels then take the rows (and the patch kernels, where
+// needed, the columns) of a work-group from one sub-grid, whose bands count 2 rad
+// cells of margin rather than 2 rad dil.
+constexpr bool na_axis_strided(int32_t len, int32_t dil, int32_t wrap) { return dil > 1 && (!wrap || len % dil == 0); }
 
-// Rows of the sub-grid of residue rho.
-constexpr int32_t na_rows_sub_len(const NaGeom& g, int32_t rho) { return (g.grid_h - 1 - rho) / g.dil_h + 1; }
+constexpr bool na_rows_strided(const NaGeom& g) { return na_axis_strided(g.grid_h, g.dil_h, g.wrap_h); }
 
 // ---------------------------------------------------------------------------
 // Query patches of 2D neighbourhood windows (MASK_NA_PATCH), dilated or not.
@@ -418,15 +417,12 @@ constexpr PatchBands na_patch_bands(int32_t y0, int32_t x0, const NaGeom& g) {
       na_band(x0, imin(x0 + kPatchCols, g.grid_w) - 1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w)};
 }
 
-// Patches along one axis of `len` cells: `per` consecutive cells of one residue
-// sub-grid mod the dilation when the axis is strided (dilated and, if wrapped, of a
-// length the dilation divides: see na_rows_strided), else of the axis itself.
-// Sub-grid cell u is axis cell rho + stride u, u < len.
+// Groups of `per` cells along one axis of `len` cells: consecutive cells of one
+// residue sub-grid when the axis is strided (na_axis_strided), else of the axis
+// itself. Sub-grid cell u is axis cell rho + stride u, u < len.
 struct AxisGroup {
   int32_t rho, stride, len, u0;
 };
-
-constexpr bool na_axis_strided(int32_t len, int32_t dil, int32_t wrap) { return dil > 1 && (!wrap || len % dil == 0); }
 
 constexpr int32_t na_axis_groups(int32_t len, int32_t dil, int32_t wrap, int32_t per) {
   if (!na_axis_strided(len, dil, wrap)) return (int32_t)cdiv(len, per);
@@ -607,36 +603,17 @@ struct RowGroup {
 };
 
 // Groups per plane (both row kernels).
-constexpr int32_t na_row_groups(const NaGeom& g) {
-  if (!na_rows_strided(g)) return (int32_t)cdiv(g.grid_h, kRowsGroup);
-  int32_t n = 0;
-  for (int32_t rho = 0; rho < g.dil_h; ++rho) n += (int32_t)cdiv(na_rows_sub_len(g, rho), kRowsGroup);
-  return n;
-}
+constexpr int32_t na_row_groups(const NaGeom& g) { return na_axis_groups(g.grid_h, g.dil_h, g.wrap_h, kRowsGroup); }
 
 // Group i of a plane with the band of rows its windows reach (reverse = false: the key
 // rows of its query rows; true: the query rows whose windows reach its key rows).
 constexpr RowGroup na_row_group(const NaGeom& g, int32_t i, bool reverse) {
-  RowGroup rg{0, 1, g.grid_h, i * kRowsGroup, Band{0, 0}};
-  int32_t dil = g.dil_h;
-  if (na_rows_strided(g)) {
-    rg.stride = g.dil_h;
-    dil = 1;
-    for (int32_t rho = 0; rho < g.dil_h; ++rho) {
-      const int32_t len = na_rows_sub_len(g, rho), n = (int32_t)cdiv(len, kRowsGroup);
-      if (i < n || rho == g.dil_h - 1) {
-        rg.rho = rho;
-        rg.len = len;
-        rg.u0 = i * kRowsGroup;
-        break;
-      }
-      i -= n;
-    }
-  }
-  const int32_t u1 = imin(rg.u0 + kRowsGroup, rg.len) - 1;
-  rg.band = reverse ? na_band_reverse(rg.u0, u1, rg.len, g.kernel_h, g.rad_h, g.wrap_h, dil)
-                    : na_band(rg.u0, u1, rg.len, g.kernel_h, g.rad_h, g.wrap_h, dil);
-  return rg;
+  const AxisGroup a = na_axis_group(g.grid_h, g.dil_h, g.wrap_h, i, kRowsGroup);
+  const int32_t dil = a.stride > 1 ? 1 : g.dil_h;  // a residue sub-grid holds undilated windows
+  const int32_t u1 = imin(a.u0 + kRowsGroup, a.len) - 1;
+  const Band band = reverse ? na_band_reverse(a.u0, u1, a.len, g.kernel_h, g.rad_h, g.wrap_h, dil)
+                            : na_band(a.u0, u1, a.len, g.kernel_h, g.rad_h, g.wrap_h, dil);
+  return RowGroup{a.rho, a.stride, a.len, a.u0, band};
 }
 
 // Grid row of band row r of a group.
