@@ -60,7 +60,8 @@ int32_t kernel_mask(const attn::Problem& p, const attn::NaGeom& g) {
   if (p.mask == ATTN_MASK_CAUSAL) return attn::MASK_CAUSAL;
   const int32_t patch_rows = attn::patch_lds_rows(p.d);
   if (patch_rows > 0 && attn::na_patch_eligible(g, patch_rows)) {
-    const int64_t patches = p.B * p.H * attn::na_patch_row_groups(g) * attn::na_patch_col_groups(g, attn::na_patch_cols_strided(g));
+    const int64_t patches =
+        p.B * p.H * attn::na_patch_row_groups(g) * attn::na_patch_col_groups(g, attn::na_patch_cols_strided(g));
     if (patches <= INT32_MAX) return attn::MASK_NA_PATCH;
   }
   if (rows_stage(p.d, g) > 0) {

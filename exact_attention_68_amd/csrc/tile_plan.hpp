@@ -116,7 +116,8 @@ constexpr KvRun kv_run(int mask, int32_t Nq, int32_t Nkv, int32_t BM, int32_t BN
   const int32_t plane = g.grid_h * g.grid_w;
   const int32_t z0 = q0 / plane, z1 = q_last / plane;
   auto band = [reverse](int32_t c0, int32_t c1, int32_t len, int32_t kernel, int32_t rad, int32_t wrap, int32_t dil) {
-    return reverse ? na_band_reverse(c0, c1, len, kernel, rad, wrap, dil) : na_band(c0, c1, len, kernel, rad, wrap, dil);
+    return reverse ? na_band_reverse(c0, c1, len, kernel, rad, wrap, dil)
+                   : na_band(c0, c1, len, kernel, rad, wrap, dil);
   };
   const Band bz = band(z0, z1, g.grid_d, g.kernel_d, g.rad_d, g.wrap_d, g.dil_d);
   int32_t tok_start = bz.start * plane, tok_len = bz.count * plane;
@@ -382,15 +383,17 @@ constexpr void na_col_bits(int32_t cq, int32_t half, int32_t W, int32_t kernel, 
 }
 
 // Cells of one residue mod the dilation. On a dilated axis (that, when wrapped, the
-// dilation divides) the cells congruent to rho mod dil form a sub-grid on which every
+// dilation divides; with windows wider than one cell) the cells congruent to rho mod dil form a sub-grid on which every
 // window is an undilated window: clamped, na_dil_anchor takes it inside that
 // sub-grid; wrapped, it steps dil cells at a time around a cycle of len / dil of
 // them. The row and patch kernels then take the rows (and the patch kernels, where
 // needed, the columns) of a work-group from one sub-grid, whose bands count 2 rad
 // cells of margin rather than 2 rad dil.
-constexpr bool na_axis_strided(int32_t len, int32_t dil, int32_t wrap) { return dil > 1 && (!wrap || len % dil == 0); }
+constexpr bool na_axis_strided(int32_t len, int32_t kernel, int32_t dil, int32_t wrap) {
+  return kernel > 1 && dil > 1 && (!wrap || len % dil == 0);  // a one-cell window gains nothing
+}
 
-constexpr bool na_rows_strided(const NaGeom& g) { return na_axis_strided(g.grid_h, g.dil_h, g.wrap_h); }
+constexpr bool na_rows_strided(const NaGeom& g) { return na_axis_strided(g.grid_h, g.kernel_h, g.dil_h, g.wrap_h); }
 
 // ---------------------------------------------------------------------------
 // Query patches of 2D neighbourhood windows (MASK_NA_PATCH), dilated or not.
@@ -424,15 +427,15 @@ struct AxisGroup {
   int32_t rho, stride, len, u0;
 };
 
-constexpr int32_t na_axis_groups(int32_t len, int32_t dil, int32_t wrap, int32_t per) {
-  if (!na_axis_strided(len, dil, wrap)) return (int32_t)cdiv(len, per);
+constexpr int32_t na_axis_groups(int32_t len, int32_t kernel, int32_t dil, int32_t wrap, int32_t per) {
+  if (!na_axis_strided(len, kernel, dil, wrap)) return (int32_t)cdiv(len, per);
   int32_t n = 0;
   for (int32_t rho = 0; rho < dil; ++rho) n += (int32_t)cdiv((len - 1 - rho) / dil + 1, per);
   return n;
 }
 
-constexpr AxisGroup na_axis_group(int32_t len, int32_t dil, int32_t wrap, int32_t i, int32_t per) {
-  if (!na_axis_strided(len, dil, wrap)) return AxisGroup{0, 1, len, i * per};
+constexpr AxisGroup na_axis_group(int32_t len, int32_t kernel, int32_t dil, int32_t wrap, int32_t i, int32_t per) {
+  if (!na_axis_strided(len, kernel, dil, wrap)) return AxisGroup{0, 1, len, i * per};
   for (int32_t rho = 0; rho < dil; ++rho) {
     const int32_t sub = (len - 1 - rho) / dil + 1, n = (int32_t)cdiv(sub, per);
     if (i < n || rho == dil - 1) return AxisGroup{rho, dil, sub, i * per};
@@ -459,7 +462,7 @@ struct PatchGroup {
 // of dilation 2, whose 28-column bands fit, ran 0.95x forward and 0.88x backward with
 // them).
 constexpr bool na_patch_cols_strided(const NaGeom& g) {
-  if (!na_axis_strided(g.grid_w, g.dil_w, g.wrap_w)) return false;
+  if (!na_axis_strided(g.grid_w, g.kernel_w, g.dil_w, g.wrap_w)) return false;
   for (int32_t x0 = 0; x0 < g.grid_w; x0 += kPatchCols) {
     const int32_t x1 = imin(x0 + kPatchCols, g.grid_w) - 1;
     if (na_band(x0, x1, g.grid_w, g.kernel_w, g.rad_w, g.wrap_w, g.dil_w).count > kPatchKeyCols ||
@@ -469,15 +472,18 @@ constexpr bool na_patch_cols_strided(const NaGeom& g) {
   return false;
 }
 
-constexpr int32_t na_patch_row_groups(const NaGeom& g) { return na_axis_groups(g.grid_h, g.dil_h, g.wrap_h, kPatchRows); }
+constexpr int32_t na_patch_row_groups(const NaGeom& g) {
+  return na_axis_groups(g.grid_h, g.kernel_h, g.dil_h, g.wrap_h, kPatchRows);
+}
 constexpr int32_t na_patch_col_groups(const NaGeom& g, bool cols_strided) {
-  return cols_strided ? na_axis_groups(g.grid_w, g.dil_w, g.wrap_w, kPatchCols) : (int32_t)cdiv(g.grid_w, kPatchCols);
+  return cols_strided ? na_axis_groups(g.grid_w, g.kernel_w, g.dil_w, g.wrap_w, kPatchCols)
+                      : (int32_t)cdiv(g.grid_w, kPatchCols);
 }
 
 // cols_strided: na_patch_cols_strided(g), decided once per problem.
 constexpr PatchGroup na_patch_group(const NaGeom& g, int32_t py, int32_t px, bool cols_strided) {
-  const AxisGroup r = na_axis_group(g.grid_h, g.dil_h, g.wrap_h, py, kPatchRows);
-  const AxisGroup c = cols_strided ? na_axis_group(g.grid_w, g.dil_w, g.wrap_w, px, kPatchCols)
+  const AxisGroup r = na_axis_group(g.grid_h, g.kernel_h, g.dil_h, g.wrap_h, py, kPatchRows);
+  const AxisGroup c = cols_strided ? na_axis_group(g.grid_w, g.kernel_w, g.dil_w, g.wrap_w, px, kPatchCols)
                                    : AxisGroup{0, 1, g.grid_w, px * kPatchCols};
   PatchGroup p{r.rho, r.stride, r.u0, c.rho, c.stride, c.u0, g.grid_w, g};
   p.geom.grid_h = r.len;
@@ -583,12 +589,13 @@ constexpr bool na_patch_bwd_eligible(const NaGeom& g, int32_t lds_rows, bool rev
 //
 // On a grid at most 32 wide, a wavefront holds one grid row of queries (lane column
 // = grid column; lanes past the width idle) and a work-group 4 rows of one plane
-// (consecutive, or of one residue mod the dilation: RowGroup). Every key row is then one 32-key block (its columns, padded with keys
-// read as zero), so a query's window bits in any block are its own column bits, and
-// whether a key row (plane, row) lies in the window is the same for every lane of a
-// wavefront. The work-group streams the planes its windows reach (na_band of its
-// plane) through two LDS stages, each the band of key rows of its 4 rows (na_band
-// of those rows); each wavefront scores only its own visible rows of a stage.
+// (consecutive, or of one residue mod the dilation: RowGroup). Every key row is then
+// one 32-key block (its columns, padded with keys read as zero), so a query's window
+// bits in any block are its own column bits, and whether a key row (plane, row) lies
+// in the window is the same for every lane of a wavefront. The work-group streams the
+// planes its windows reach (na_band of its plane) through two LDS stages, each the
+// band of key rows of its 4 rows (na_row_group); each wavefront scores only its own
+// visible rows of a stage.
 constexpr int32_t kRowsGroup = 4;
 
 // The rows of a group. With strided rows (na_rows_strided) a group takes 4
@@ -603,12 +610,14 @@ struct RowGroup {
 };
 
 // Groups per plane (both row kernels).
-constexpr int32_t na_row_groups(const NaGeom& g) { return na_axis_groups(g.grid_h, g.dil_h, g.wrap_h, kRowsGroup); }
+constexpr int32_t na_row_groups(const NaGeom& g) {
+  return na_axis_groups(g.grid_h, g.kernel_h, g.dil_h, g.wrap_h, kRowsGroup);
+}
 
 // Group i of a plane with the band of rows its windows reach (reverse = false: the key
 // rows of its query rows; true: the query rows whose windows reach its key rows).
 constexpr RowGroup na_row_group(const NaGeom& g, int32_t i, bool reverse) {
-  const AxisGroup a = na_axis_group(g.grid_h, g.dil_h, g.wrap_h, i, kRowsGroup);
+  const AxisGroup a = na_axis_group(g.grid_h, g.kernel_h, g.dil_h, g.wrap_h, i, kRowsGroup);
   const int32_t dil = a.stride > 1 ? 1 : g.dil_h;  // a residue sub-grid holds undilated windows
   const int32_t u1 = imin(a.u0 + kRowsGroup, a.len) - 1;
   const Band band = reverse ? na_band_reverse(a.u0, u1, a.len, g.kernel_h, g.rad_h, g.wrap_h, dil)
