@@ -45,7 +45,7 @@ def test_workload_with_lse(name):
 
 
 @pytest.mark.parametrize("name", ["selfattn_n4096_d128", "na3d_wrap_20x20x20_k5", "na2d_wrap_64x64_k7_dil2",
-                                  "na3d_wrap_20x20x20_k5_dil2"])
+                                  "na3d_wrap_20x20x20_k5_dil2", "na2d_clamp_64x64_k7"])
 def test_workload_sampled_rows(name):
     w = workloads.WORKLOADS[name]
     q, k, v = workloads.workload_qkv(w)

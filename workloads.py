@@ -83,6 +83,9 @@ WORKLOADS = {
                          wrap_d=1, wrap_h=1, wrap_w=0, dil_d=2, dil_h=2, dil_w=2),
                  note="3D neighbourhood attention, 20x20x20 volume, 5x5x5 window dilated by 2 on every axis, "
                       "wrapping depth and rows, d32"),
+        Workload("na2d_clamp_64x64_k7", 2, 4, 4096, 32, "na2d", f32(1 / math.sqrt(32)), 6811,
+                 na=dict(grid_h=64, grid_w=64, kernel_h=7, kernel_w=7, wrap_h=0, wrap_w=0),
+                 note="2D neighbourhood attention, 64x64 grid, 7x7 window clamped at the borders on both axes, d32"),
     ]
 }
 
