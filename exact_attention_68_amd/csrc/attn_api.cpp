@@ -51,7 +51,7 @@ int32_t rows_stage(int64_t d, const attn::NaGeom& g) {
 
 // Kernel mask kind for a checked problem: the patch kernel for 2D windows whose
 // patch bands fit it (na_patch_eligible, d = 32 or 64); the row kernel for other
-// windows on grids at most 32 wide whose bands fit its stages (rows_stage, d = 32); the
+// windows on grids at most 32 wide whose bands fit its stages (rows_stage, d = 32 or 64); the
 // block-masked neighbourhood kernel for other undilated 2D windows on grids of
 // width 32, 64, 96 or 128; the grid-mask kernel for other grids of width 4..124
 // with rows and planes <= 128; the element predicate for the rest.

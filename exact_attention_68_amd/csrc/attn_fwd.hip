@@ -1297,9 +1297,10 @@ struct RowsCfg {
   static constexpr int ELEMS = CHUNKS * 8;
 };
 
-// two work-groups per CU with the narrow stages (80 KB of LDS each), one with the wide ones
+// two work-groups per CU with the narrow stages at d = 32 (80 KB of LDS each), one with the wide
+// ones and at d = 64 (128 KB)
 template <int D, int ROWS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS <= 10 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 32 && ROWS <= 10 ? 2 : 1)))
 void attn_fwd_na_rows_kernel(KernelArgs a) {
   using R = RowsCfg<D, ROWS>;
   constexpr int KB = D / 16, DT = D / 32, RC = D / 8;

@@ -59,9 +59,10 @@ hipError_t static_scratch(void** ptr);
 // head size d (0: no patch kernel at that size).
 constexpr int32_t patch_lds_rows(int64_t d) { return d == 32 ? 24 : d == 64 ? 17 : 0; }
 
-// Key rows per LDS stage of the row kernel of narrow grids for head size d (0: none).
-// (d = 64 with 8-row stages, one wavefront per SIMD, ran 0.89x the tile kernel on the 20x20x20 volume.)
-constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : 0; }
+// Key rows per LDS stage of the row kernel of narrow grids for head size d (0: none). At
+// d = 64 the two 8-row stages take 128 KB: one work-group, one wavefront per SIMD, per CU
+// (1.11x the tile kernel on the 20x20x20 volume with a 5x5x5 window, 1.72x at dilation 2).
+constexpr int32_t rows_lds_rows(int64_t d) { return d == 32 ? 10 : d == 64 ? 8 : 0; }
 
 // The wide stages of the three row kernels (forward, backward dQ and dK/dV) at d = 32: 12
 // rows, for bands past the narrow stages (clamped windows whose reverse bands near a

@@ -219,3 +219,20 @@ def test_na2d_dilated_takes_patch_kernels(d, dil):
     assert len(kernels) == 2 and "attn_bwd_dq_patch_kernel" in kernels[0] and "attn_bwd_dkv_patch_kernel" in kernels[1], \
         kernels
     assert others == [], others
+
+
+def test_na3d_d64_takes_row_kernel():
+    """At d = 64 the forward row kernel runs with 8-row stages (one work-group per CU)."""
+    import re
+
+    import exact_attention_68_amd as A
+
+    B, H, N, d = 1, 2, 8 * 8 * 8, 64
+    q, k, v = _inputs(B, H, N, d, 7)
+    params = A.na3d_params(8, 8, 8, 5, 5, 5, 1, 1, 0)
+    o = torch.empty_like(q)
+    kernels, others = _split(_dispatches(
+        lambda: A.attn_fwd_ex(q, k, v, o, None, d ** -0.5, A.ATTN_MASK_NA3D, params, None)))
+    assert len(kernels) == 1 and "attn_fwd_na_rows_kernel" in kernels[0] and re.search(r"<64,\s*8>", kernels[0]), \
+        kernels
+    assert others == [], others

@@ -101,18 +101,19 @@ def test_d32_four_stage_rings_equal_serial(libs, mask):
         assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
 
 
-@pytest.mark.parametrize("gh", [15, 16])
-def test_na3d_dilated_rows_forward_equals_serial(libs, gh):
+@pytest.mark.parametrize("gh,d", [(15, 32), (16, 32), (16, 64)])
+def test_na3d_dilated_rows_forward_equals_serial(libs, gh, d):
     """The forward row kernel on a 10 x gh x 12 volume, 5x5x5 window dilated by 2 on planes and rows, with its
-    logsumexp: 15 wrapped rows take the wide 12-row stages, 16 the row groups of one residue."""
+    logsumexp: 15 wrapped rows take the wide 12-row stages, 16 the row groups of one residue (at d = 64 the
+    8-row stages)."""
     import exact_attention_68_amd as A
 
     piped, serial = libs
-    q, k, v = (t.cuda() for t in workloads.make_qkv(1, 2, 10 * gh * 12, 32, 90))
+    q, k, v = (t.cuda() for t in workloads.make_qkv(1, 2, 10 * gh * 12, d, 90))
     params = A.na3d_params(10, gh, 12, 5, 5, 5, 1, 1, 0, 2, 2, 1)
-    ref_o, ref_l = _fwd(serial, q, k, v, A.ATTN_MASK_NA3D, 32 ** -0.5, params, "attn_fwd_ex", True)
+    ref_o, ref_l = _fwd(serial, q, k, v, A.ATTN_MASK_NA3D, d ** -0.5, params, "attn_fwd_ex", True)
     for _ in range(3):
-        o, lse = _fwd(piped, q, k, v, A.ATTN_MASK_NA3D, 32 ** -0.5, params, "attn_fwd_ex", True)
+        o, lse = _fwd(piped, q, k, v, A.ATTN_MASK_NA3D, d ** -0.5, params, "attn_fwd_ex", True)
         assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
         assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
 
