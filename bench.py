@@ -437,7 +437,7 @@ def main():
                    "workspace_bytes": 0 if ws is None else ws.numel()},
         "roofline": roof,
     }
-    # matrix-core utilisation and HBM bandwidth (spec item 4), from the live passes
+    # matrix-core utilisation and HBM bandwidth (the measurement contract), from the live passes
     line["mfma_util"] = prof.get("mfma_util") if prof else None
     line["mfma_util_source"] = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES / (4 x CUs) / (GRBM_GUI_ACTIVE / XCDs) of "
                                 "the attention kernel, median over dispatches" if line["mfma_util"] is not None

@@ -18,7 +18,7 @@ def tolerance(ref: np.ndarray) -> np.ndarray:
 
 
 def compare(got: np.ndarray, ref: np.ndarray, what: str, tol: np.ndarray | None = None) -> float:
-    """Assert got is within tolerance of ref everywhere (the benchmark spec's bound unless `tol` is
+    """Assert got is within tolerance of ref everywhere (the parity bound unless `tol` is
     given); returns the worst err/tol ratio."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
@@ -87,7 +87,7 @@ def lse_tolerance(ref: np.ndarray) -> np.ndarray:
 
 
 def derived_tolerance(q, k, v, scale, mask, na, ref) -> np.ndarray:
-    """Per-element tolerance for rows sharper than the benchmark's: the larger of the north-star
+    """Per-element tolerance for rows sharper than the benchmark's: the larger of the parity
     bound and the bound derived from the kernel's arithmetic (bfloat16 probabilities whose row sum
     is taken of the rounded values, bfloat16 output; kernel_model.derived_bound)."""
     from kernel_model import derived_bound
@@ -104,7 +104,7 @@ def check_case(q, k, v, scale, mask: str, params=None, rows=None, what="", entry
                want_lse=None, derived=False) -> float:
     """Run the HIP path and the oracle on the same bf16 inputs and compare (all rows or `rows`).
     With attn_fwd_ex the logsumexp is compared too (unless want_lse is False). With derived=True
-    the output bound is derived_tolerance (all rows only); the worst ratio against the north-star
+    the output bound is derived_tolerance (all rows only); the worst ratio against the parity
     bound is printed as well."""
     mode = MASK_MODES[mask]
     want_lse = entry == "attn_fwd_ex" if want_lse is None else want_lse
@@ -122,7 +122,7 @@ def check_case(q, k, v, scale, mask: str, params=None, rows=None, what="", entry
         assert rows is None, "the derived bound is computed for whole heads"
         tol = derived_tolerance(to_f64(q), to_f64(k), to_f64(v), scale, mask, oracle_na(params), ref)
         ns = float((np.abs(got - ref) / tolerance(ref)).max())
-        print(f"[parity] {what}: worst err / north-star bound {ns:.3f}", flush=True)
+        print(f"[parity] {what}: worst err / parity bound {ns:.3f}", flush=True)
     worst = compare(got, ref, what or mask, tol)
     if want_lse:
         g = lse.cpu().numpy().astype(np.float64)

@@ -4,7 +4,7 @@ sizes 32 and 64. The geometries are drawn once from a fixed generator and kept v
 wrapped axis holds its window once, (kernel - 1) * dil < len; on a clamped one every residue sub-grid
 holds a whole window, kernel * dil <= len), so the kernels' plans (row and patch groups of one residue
 mod the dilation, tight clamped bands, reverse bands, wide row stages) meet shapes that no hand-picked
-case names. The forward is held to the larger of the benchmark spec's bound and the bound derived from its
+case names. The forward is held to the larger of the parity bound and the bound derived from its
 arithmetic (windows of a few keys), the backward to the bound of parity.check_bwd_case."""
 import math
 

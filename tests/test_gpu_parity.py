@@ -187,7 +187,7 @@ def test_edge_shapes(N, mask, d):
     check_case(q, k, v, 1 / math.sqrt(d), mask, what=f"edge N{N}")
 
 
-# Rows up to score std 2 (scale 0.125 with Q doubled, or scale 0.25) meet the benchmark spec's bound.
+# Rows up to score std 2 (scale 0.125 with Q doubled, or scale 0.25) meet the parity bound.
 @pytest.mark.parametrize("scale,q_gain", [(0.0, 1.0), (-0.2, 1.0), (0.125, 2.0), (0.25, 1.0), (1e-3, 1.0)])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_scales_and_peaky_rows(scale, q_gain, mask):
@@ -197,7 +197,7 @@ def test_scales_and_peaky_rows(scale, q_gain, mask):
 
 # Sharper rows: score std 4 (Q x 4 at scale 1/8) and 8 (scale 1 at d = 64). With so much of a row's
 # weight on few keys, rounding the probabilities to bfloat16 can move single outputs past the
-# spec bound (tests/test_kernel_model.py: the modelled arithmetic reaches 1.16 of it on seed
+# parity bound (tests/test_kernel_model.py: the modelled arithmetic reaches 1.16 of it on seed
 # 2003 and 1.07 on seed 2000 at scale 1). These rows are held to the bound derived from that
 # arithmetic (parity.derived_tolerance), element by element.
 @pytest.mark.parametrize("scale,q_gain,seed", [(0.125, 4.0, 2000), (0.125, 4.0, 2003), (1.0, 1.0, 2000),

@@ -163,10 +163,10 @@ def test_na3d_row_kernel_scales(scale, geo):
 ])
 def test_na2d_dilated(gh, gw, kh, kw, wh, ww, dh, dw, d):
     """Windows of 9 to 49 keys. With so few keys the bfloat16 rounding of the probabilities and of
-    the output can pass the benchmark spec's bound on single elements: seed 10022 (16x20, 3x5, d = 128)
+    the output can pass the parity bound on single elements: seed 10022 (16x20, 3x5, d = 128)
     gives one of 81920 elements at 1.058 of it, the same bfloat16 value the CPU model of the
     kernel's arithmetic gives (tests/test_kernel_model.py). The windows are held to the larger of
-    the benchmark spec's bound and the bound derived from that arithmetic."""
+    the parity bound and the bound derived from that arithmetic."""
     import exact_attention_68_amd as A
 
     N = gh * gw
